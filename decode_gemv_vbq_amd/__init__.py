@@ -1,0 +1,257 @@
+"""decode_gemv_vbq_amd -- MI355X (gfx950) decode path of Variable Bit-width
+Quantization: packed mixed-width (1/2/4/8-bit per 64-weight group) weights and
+a fused dequantize-and-multiply GEMV for M <= 16 tokens.
+
+This module is a thin ctypes binding over ``libvbq.so`` (``include/vbq.h``).
+It only marshals arguments: device memory and streams come from PyTorch, every
+step of the path runs in the HIP kernels of the library.  There is no CPU
+fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvbq.so")
+
+VBQ_F32, VBQ_F16 = 0, 1
+
+STATUS = {
+    0: "VBQ_OK", 1: "VBQ_ERR_INVALID_ARG", 2: "VBQ_ERR_SHAPE", 3: "VBQ_ERR_BATCH", 4: "VBQ_ERR_BITS",
+    5: "VBQ_ERR_CODE_RANGE", 6: "VBQ_ERR_ALIGN", 7: "VBQ_ERR_WORKSPACE", 8: "VBQ_ERR_LAYOUT", 9: "VBQ_ERR_HIP",
+}
+
+#: every symbol include/vbq.h declares
+EXPORTS = (
+    "vbq_version", "vbq_status_string", "vbq_last_error", "vbq_layout_init", "vbq_layout_from_header",
+    "vbq_pack_plan_workspace", "vbq_pack_plan", "vbq_pack", "vbq_status_check", "vbq_dequant",
+    "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_dense_f16_gemv",
+)
+
+
+class VbqError(RuntimeError):
+    def __init__(self, code: int, what: str, detail: str = ""):
+        name = STATUS.get(code, str(code))
+        super().__init__(f"{what}: {name}" + (f" ({detail})" if detail else ""))
+        self.code = code
+        self.name = name
+
+
+class Layout(ctypes.Structure):
+    """Mirror of ``vbq_layout`` (bytes 0..95 of the blob header)."""
+    _fields_ = [(n, ctypes.c_uint32) for n in ("magic", "version", "N", "K", "G", "S", "nS", "row_pad")] + \
+               [(n, ctypes.c_uint64) for n in ("off_row_off", "off_slice_off", "off_wmap", "off_scales", "off_codes",
+                                               "total_bytes", "code_bytes", "code_bytes_padded")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """Load libvbq.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m decode_gemv_vbq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        LP = ctypes.POINTER(Layout)
+        L.vbq_version.restype = ctypes.c_char_p
+        L.vbq_status_string.restype = ctypes.c_char_p
+        L.vbq_status_string.argtypes = [i]
+        L.vbq_last_error.restype = ctypes.c_char_p
+        L.vbq_layout_init.argtypes = [i, i, LP]
+        L.vbq_layout_from_header.argtypes = [P, LP]
+        L.vbq_pack_plan_workspace.argtypes = [i]
+        L.vbq_pack_plan_workspace.restype = sz
+        L.vbq_pack_plan.argtypes = [i, i, P, LP, P, sz, P]
+        L.vbq_pack.argtypes = [LP, P, P, P, P, P, P]
+        L.vbq_status_check.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
+        L.vbq_dequant.argtypes = [LP, P, P, i, P]
+        L.vbq_workspace_size.argtypes = [LP, i, ctypes.POINTER(sz)]
+        L.vbq_workspace_clear.argtypes = [P, sz, P]
+        L.vbq_gemv.argtypes = [LP, P, P, P, i, P, sz, P]
+        L.vbq_gemv_batched.argtypes = [LP, P, i, P, i, P, i, i, P, sz, P]
+        L.vbq_dense_f16_gemv.argtypes = [i, i, i, P, P, i, P, i, i, P]
+        for f in EXPORTS:
+            if f not in ("vbq_version", "vbq_status_string", "vbq_last_error", "vbq_pack_plan_workspace"):
+                getattr(L, f).restype = i
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        detail = lib().vbq_last_error().decode() if rc == 9 else ""
+        raise VbqError(rc, what, detail)
+
+
+def version() -> str:
+    return lib().vbq_version().decode()
+
+
+# ------------------------------------------------------------ torch plumbing
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("expected contiguous device tensors")
+
+
+def _empty_aligned(nbytes: int, device, align: int = 256):
+    """A uint8 device buffer whose data pointer is `align`-byte aligned."""
+    torch = _torch()
+    buf = torch.empty(nbytes + align, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % align
+    return buf[off:off + nbytes]
+
+
+# ------------------------------------------------------------------- layout
+
+def layout_init(N: int, K: int) -> Layout:
+    L = Layout()
+    _check(lib().vbq_layout_init(N, K, ctypes.byref(L)), "vbq_layout_init")
+    return L
+
+
+def layout_from_header(header: bytes) -> Layout:
+    if len(header) < 256:
+        raise ValueError("header needs 256 bytes")
+    buf = ctypes.create_string_buffer(bytes(header[:256]), 256)
+    L = Layout()
+    _check(lib().vbq_layout_from_header(ctypes.cast(buf, ctypes.c_void_p), ctypes.byref(L)), "vbq_layout_from_header")
+    return L
+
+
+def layout_of(blob) -> Layout:
+    """Layout read back from a device blob's header."""
+    return layout_from_header(blob[:256].cpu().numpy().tobytes())
+
+
+# --------------------------------------------------------------------- pack
+
+def pack_plan(bits, K: int) -> Layout:
+    """Plan a blob for widths bits[N][G] (uint8, device). Synchronizes."""
+    torch = _torch()
+    _need_cuda(bits)
+    N = bits.shape[0]
+    ws = torch.empty(lib().vbq_pack_plan_workspace(N), dtype=torch.uint8, device=bits.device)
+    L = Layout()
+    _check(lib().vbq_pack_plan(N, K, _ptr(bits), ctypes.byref(L), _ptr(ws), ws.numel(), _stream()), "vbq_pack_plan")
+    return L
+
+
+def pack(q, bits, scales, L: Layout | None = None, check: bool = True):
+    """Pack q[N][K] u8, bits[N][G] u8, scales[N][G] fp16 -> (blob u8 device tensor, Layout)."""
+    torch = _torch()
+    _need_cuda(q, bits, scales)
+    if L is None:
+        L = pack_plan(bits, q.shape[1])
+    blob = _empty_aligned(L.total_bytes, q.device)
+    status = torch.empty(1, dtype=torch.int32, device=q.device)
+    _check(lib().vbq_pack(ctypes.byref(L), _ptr(q), _ptr(bits), _ptr(scales), _ptr(blob), _ptr(status), _stream()),
+           "vbq_pack")
+    if check:
+        status_check(status)
+    return blob, L
+
+
+def status_check(status):
+    raw = ctypes.c_uint32(0)
+    _check(lib().vbq_status_check(_ptr(status), ctypes.byref(raw), _stream()), "vbq_pack (device status)")
+    return raw.value
+
+
+# ------------------------------------------------------------------ dequant
+
+def dequant(L: Layout, blob, dtype=None):
+    torch = _torch()
+    dtype = dtype or torch.float32
+    w = torch.empty((L.N, L.K), dtype=dtype, device=blob.device)
+    wt = VBQ_F32 if dtype == torch.float32 else VBQ_F16
+    _check(lib().vbq_dequant(ctypes.byref(L), _ptr(blob), _ptr(w), wt, _stream()), "vbq_dequant")
+    return w
+
+
+# --------------------------------------------------------------------- GEMV
+
+def workspace_size(L: Layout, M: int = 1) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vbq_workspace_size(ctypes.byref(L), M, ctypes.byref(n)), "vbq_workspace_size")
+    return n.value
+
+
+def workspace(L: Layout, M: int = 16, device="cuda"):
+    """A zeroed GEMV workspace for up to M tokens (None when not needed)."""
+    n = workspace_size(L, M)
+    if n == 0:
+        return None
+    ws = _empty_aligned(n, device)
+    _check(lib().vbq_workspace_clear(_ptr(ws), n, _stream()), "vbq_workspace_clear")
+    return ws
+
+
+def gemv(L: Layout, blob, x, out=None, out_dtype=None, ws=None):
+    """y[N] = W x for x fp16[K]."""
+    torch = _torch()
+    _need_cuda(blob, x)
+    out_dtype = out_dtype or torch.float16
+    if out is None:
+        out = torch.empty(L.N, dtype=out_dtype, device=x.device)
+    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    if ws is None:
+        ws = workspace(L, 1, x.device)
+    _check(lib().vbq_gemv(ctypes.byref(L), _ptr(blob), _ptr(x), _ptr(out), yt, _ptr(ws),
+                          0 if ws is None else ws.numel(), _stream()), "vbq_gemv")
+    return out
+
+
+def gemv_batched(L: Layout, blob, x, out=None, out_dtype=None, ws=None):
+    """Y[M][N] = X[M][K] W^T for 1 <= M <= 16 (x fp16, rows may be strided)."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a [M][K] device tensor with unit column stride")
+    M = x.shape[0]
+    out_dtype = out_dtype or torch.float16
+    if out is None:
+        out = torch.empty((M, L.N), dtype=out_dtype, device=x.device)
+    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    if ws is None:
+        ws = workspace(L, M, x.device)
+    _check(lib().vbq_gemv_batched(ctypes.byref(L), _ptr(blob), M, _ptr(x), x.stride(0), _ptr(out), out.stride(0), yt,
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream()), "vbq_gemv_batched")
+    return out
+
+
+def dense_f16_gemv(w16, x, out=None, out_dtype=None):
+    """Dense fp16 control: y[M][N] = x[M][K] W16^T (or y[N] for 1-D x)."""
+    torch = _torch()
+    _need_cuda(w16)
+    one = x.dim() == 1
+    x2 = x.view(1, -1) if one else x
+    M = x2.shape[0]
+    N, K = w16.shape
+    out_dtype = out_dtype or torch.float16
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    _check(lib().vbq_dense_f16_gemv(N, K, M, _ptr(w16), _ptr(x2), x2.stride(0), _ptr(out), out.stride(0), yt,
+                                    _stream()), "vbq_dense_f16_gemv")
+    return out[0] if one else out

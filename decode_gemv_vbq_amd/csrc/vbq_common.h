@@ -1,0 +1,69 @@
+// Shared device helpers for the VBQ1 layout (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "vbq.h"
+
+namespace vbq {
+
+constexpr uint32_t kMagic = 0x31514256u;
+constexpr int kGroup = 64;      // weights per group
+constexpr int kSlice = 32;      // groups per K-slice
+constexpr int kRowPad = 128;    // row record padding, bytes
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+struct __attribute__((aligned(8))) U2 {
+    uint32_t v[2];
+};
+struct __attribute__((aligned(8))) U4 {
+    uint32_t v[4];
+};
+
+__device__ __forceinline__ uint32_t lo_plane(const uint32_t *wmap, uint64_t rs) { return wmap[2 * rs]; }
+__device__ __forceinline__ uint32_t hi_plane(const uint32_t *wmap, uint64_t rs) { return wmap[2 * rs + 1]; }
+
+// Masks of the groups of one row-slice whose width code (log2 b) is c.
+struct WidthMasks {
+    uint32_t m[4];
+};
+
+__device__ __forceinline__ WidthMasks width_masks(uint32_t p0, uint32_t p1, int ng)
+{
+    uint32_t valid = ng >= 32 ? 0xffffffffu : ((1u << ng) - 1u);
+    WidthMasks w;
+    w.m[0] = ~p0 & ~p1 & valid;
+    w.m[1] = p0 & ~p1 & valid;
+    w.m[2] = ~p0 & p1 & valid;
+    w.m[3] = p0 & p1 & valid;
+    return w;
+}
+
+// Element c of a 4-array without dynamic register indexing (no scratch).
+template <typename T>
+__device__ __forceinline__ T pick4(const T *v, int c)
+{
+    return c == 0 ? v[0] : c == 1 ? v[1] : c == 2 ? v[2] : v[3];
+}
+
+// Byte offset, inside its slice record, of group gi (0..31) of width code c.
+__device__ __forceinline__ uint32_t group_offset_in_slice(const WidthMasks &w, int c, int gi)
+{
+    uint32_t units = 0; // 8-byte units
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++)
+        if (cc < c)
+            units += (uint32_t)__popc(w.m[cc]) << cc;
+    units += (uint32_t)__popc(pick4(w.m, c) & ((1u << gi) - 1u)) << c;
+    return units * 8u;
+}
+
+__device__ __forceinline__ int width_code(uint32_t p0, uint32_t p1, int gi)
+{
+    return (int)((p0 >> gi) & 1u) | (int)(((p1 >> gi) & 1u) << 1);
+}
+
+} // namespace vbq

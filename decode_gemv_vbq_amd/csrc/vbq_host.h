@@ -1,0 +1,32 @@
+// Host-side helpers shared by the C-ABI translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vbq.h"
+
+namespace vbq {
+
+// Record a HIP error for vbq_last_error(); returns VBQ_ERR_HIP, or VBQ_OK.
+vbq_status hip_status(hipError_t e);
+
+// hip_status(hipGetLastError()) after a launch.
+inline vbq_status launch_status() { return hip_status(hipGetLastError()); }
+
+// Host check of a layout struct: magic, version and geometry.
+vbq_status check_layout(const vbq_layout *L);
+
+// Zero `bytes` (multiple of 4) at p with a fill kernel (graph-capture safe).
+vbq_status zero_words(void *p, uint64_t bytes, hipStream_t stream);
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+} // namespace vbq
+
+#define VBQ_TRY(expr)                                                                                                 \
+    do {                                                                                                              \
+        vbq_status _st = (expr);                                                                                      \
+        if (_st != VBQ_OK)                                                                                            \
+            return _st;                                                                                               \
+    } while (0)

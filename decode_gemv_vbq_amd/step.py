@@ -1,0 +1,142 @@
+"""One decode step: the stage-ordered VBQ GEMVs of a synthetic decoder, resident in HBM.
+
+Builds every weight matrix of a workload on the device (seeded draw -> vbq_pack),
+keeps the packed blobs, activations, outputs and workspaces, and runs the step
+as back-to-back vbq_gemv launches on one stream -- eagerly, or replayed from a
+captured HIP graph (one host launch per step).  The bench times exactly this
+object and the full-size parity test checks exactly this object.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import decode_gemv_vbq_amd as v
+from decode_gemv_vbq_amd import accounting as acc
+from decode_gemv_vbq_amd import workload as wl
+
+
+class Matrix:
+    __slots__ = ("spec", "L", "blob", "x", "y", "ws", "sample_rows", "sample", "w16", "y16")
+
+    def __init__(self, spec, L, blob, x, y, ws):
+        self.spec, self.L, self.blob, self.x, self.y, self.ws = spec, L, blob, x, y, ws
+        self.sample_rows = None
+        self.sample = None
+        self.w16 = None
+        self.y16 = None
+
+
+class DecodeStep:
+    def __init__(self, name: str = "decode9b", M: int = 1, variant: str = "clustered", device="cuda",
+                 keep_rows: int = 0, out_dtype=None, log=None):
+        import torch
+        self.torch = torch
+        self.W = wl.workload(name, M=M, variant=variant)
+        self.M = M
+        self.device = torch.device(device)
+        self.out_dtype = out_dtype or torch.float16
+        self.mats: list[Matrix] = []
+        self.graph = None
+        self.graph16 = None
+        rng = np.random.default_rng(12345)
+        for i, spec in enumerate(self.W.mats):
+            q, bits, s, x = wl.draw_matrix_torch(spec, self.W.wid, M, self.W.outliers, device=self.device)
+            blob, L = v.pack(q, bits, s.view(torch.float16))
+            y = torch.empty((M, spec.N), dtype=self.out_dtype, device=self.device)
+            ws = v.workspace(L, M, self.device)
+            m = Matrix(spec, L, blob, x, y, ws)
+            if keep_rows:
+                rows = np.unique(np.concatenate([[0, spec.N - 1], rng.choice(spec.N, size=keep_rows, replace=False)]))
+                idx = torch.from_numpy(rows).to(self.device)
+                m.sample_rows = rows
+                m.sample = (q.index_select(0, idx).cpu().numpy(), bits.index_select(0, idx).cpu().numpy(),
+                            s.index_select(0, idx).cpu().numpy().view(np.uint16),
+                            x.cpu().numpy().view(np.uint16))
+            del q, bits, s
+            self.mats.append(m)
+            if log and (i % 40 == 0 or i == len(self.W.mats) - 1):
+                log(f"built {i + 1}/{len(self.W.mats)} matrices")
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------- the step
+    def run(self):
+        """Enqueue every GEMV of the step, in stage order, on the current stream."""
+        for m in self.mats:
+            if self.M == 1:
+                v.gemv(m.L, m.blob, m.x[0], out=m.y[0], ws=m.ws)
+            else:
+                v.gemv_batched(m.L, m.blob, m.x, out=m.y, ws=m.ws)
+
+    def run_timed_kernels(self):
+        """Like run(), with an event pair around every launch; returns the pairs."""
+        torch = self.torch
+        ev = []
+        for m in self.mats:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if self.M == 1:
+                v.gemv(m.L, m.blob, m.x[0], out=m.y[0], ws=m.ws)
+            else:
+                v.gemv_batched(m.L, m.blob, m.x, out=m.y, ws=m.ws)
+            b.record()
+            ev.append((a, b))
+        return ev
+
+    def capture(self):
+        torch = self.torch
+        self.run()  # first launches set kernel attributes outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+
+    # ------------------------------------------------------- fp16 control
+    def build_control(self):
+        torch = self.torch
+        for m in self.mats:
+            m.w16 = v.dequant(m.L, m.blob, torch.float16)
+            m.y16 = torch.empty((self.M, m.spec.N), dtype=self.out_dtype, device=self.device)
+        torch.cuda.synchronize()
+
+    def run_control(self):
+        for m in self.mats:
+            v.dense_f16_gemv(m.w16, m.x, out=m.y16)
+
+    def capture_control(self):
+        torch = self.torch
+        self.run_control()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_control()
+        torch.cuda.synchronize()
+        self.graph16 = g
+        return g
+
+    def free_control(self):
+        for m in self.mats:
+            m.w16 = None
+            m.y16 = None
+        self.graph16 = None
+
+    # ----------------------------------------------------------- accounting
+    def alg_bytes(self) -> int:
+        return sum(acc.vbq_read_bytes(m.L, self.M) for m in self.mats)
+
+    def layout_bytes(self) -> int:
+        return sum(acc.vbq_layout_bytes(m.L, self.M) for m in self.mats)
+
+    def dense_bytes(self) -> int:
+        return sum(acc.dense_read_bytes(m.spec.N, m.spec.K, self.M) for m in self.mats)
+
+    def weights(self) -> int:
+        return sum(m.spec.N * m.spec.K for m in self.mats)
+
+    def mean_bits(self) -> float:
+        return 8.0 * sum(int(m.L.code_bytes) for m in self.mats) / (64.0 * sum(m.spec.N * m.spec.G for m in self.mats))

@@ -1,0 +1,181 @@
+/*
+ * vbq.h -- C ABI of libvbq.so, the MI355X (gfx950) decode path of Variable
+ * Bit-width Quantization (VBQ).
+ *
+ * Method ("Variable Bit-width Quantization", mlsanity.com page, Abstract):
+ * every contiguous group of 64 weights carries its own bit-width from
+ * {1, 2, 4, 8}; the frozen allocation is stored as packed low-bit codes and
+ * autoregressive decode, which is memory-bandwidth bound, multiplies them
+ * with fused dequantize-and-multiply kernels.  The pages fix neither the
+ * dequant rule nor the storage; this library fixes them as follows:
+ *
+ *   - one fp16 scale s per group; code q in [0, 2^b - 1];
+ *     w = s * (q - (2^b - 1)/2), exact in fp32 for every finite s;
+ *   - groups run along K (the reduction axis); K % 64 == 0;
+ *   - packed layout "VBQ1", byte for byte:
+ *       header (256 B): u32 magic 0x31514256, version 1, N, K, G=K/64,
+ *         S=32 (groups per K-slice), nS=ceil(G/32), row_pad=128; u64 section
+ *         offsets row_off, slice_off, wmap, scales, codes; u64 total_bytes,
+ *         code_bytes (sum of 8*b), code_bytes_padded; zeros to byte 255.
+ *       sections at 256-byte aligned offsets:
+ *         row_off   u32[N+1]     row n's code record start, 128-byte units
+ *         slice_off u32[N][nS]   byte offset of slice t in row n's record
+ *         wmap      u32[N][nS][2] bit planes of log2(b) for groups 32t+i
+ *         scales    u16[N][G]    fp16 bits, natural order
+ *         codes     per-row records padded with zeros to 128 B; inside a
+ *                   slice, groups are bucketed by width (1,2,4,8), ascending
+ *                   g in a bucket, 8*b bytes per group
+ *       group encoding: halves H0 = codes 0..31 and H1 = codes 32..63 are
+ *         packed LSB-first into 16-bit units (code j at bit j*b of its half);
+ *         32-bit word d = H0 unit d | H1 unit d << 16.
+ *
+ * Conventions for every call below:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *     memory (blob, q, bits, scales, x, y, w, workspaces, status words); the
+ *     library never allocates device memory and keeps no global state.
+ *   - Calls are asynchronous on `stream` unless marked SYNC.  Argument checks
+ *     run on the host before any launch; a call that returns an error has
+ *     launched nothing.  VBQ_ERR_HIP carries the HIP error text in
+ *     vbq_last_error().
+ *   - Calls are reentrant.  Calls that share a workspace must be ordered (same
+ *     stream); concurrent calls need distinct workspaces.
+ */
+#ifndef VBQ_H
+#define VBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vbq_status {
+    VBQ_OK = 0,
+    VBQ_ERR_INVALID_ARG = 1, /* null pointer, bad enum */
+    VBQ_ERR_SHAPE = 2,       /* N < 1, K < 64, K % 64 != 0, ld too small */
+    VBQ_ERR_BATCH = 3,       /* M outside [1, 16] */
+    VBQ_ERR_BITS = 4,        /* a width outside {1, 2, 4, 8} */
+    VBQ_ERR_CODE_RANGE = 5,  /* a code q > 2^b - 1 */
+    VBQ_ERR_ALIGN = 6,       /* blob not 256-byte aligned, or x/y/w not element aligned */
+    VBQ_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
+    VBQ_ERR_LAYOUT = 8,      /* bad magic/version/sizes, or blob inconsistent with its widths */
+    VBQ_ERR_HIP = 9          /* a HIP runtime call failed */
+} vbq_status;
+
+typedef enum vbq_dtype { VBQ_F32 = 0, VBQ_F16 = 1 } vbq_dtype;
+
+/* Host mirror of bytes 0..95 of the blob header. */
+typedef struct vbq_layout {
+    uint32_t magic, version, N, K, G, S, nS, row_pad;
+    uint64_t off_row_off, off_slice_off, off_wmap, off_scales, off_codes;
+    uint64_t total_bytes, code_bytes, code_bytes_padded;
+} vbq_layout;
+
+/* Device status-word bits set by vbq_pack (read with vbq_status_check). */
+#define VBQ_STATUS_BITS 0x1u   /* some width outside {1,2,4,8} */
+#define VBQ_STATUS_CODES 0x2u  /* some code above 2^b - 1 */
+#define VBQ_STATUS_LAYOUT 0x4u /* widths disagree with the planned layout */
+
+/* Library version string, e.g. "vbq 0.1.0 (VBQ1 layout)". */
+const char *vbq_version(void);
+
+/* Static text for a status code. */
+const char *vbq_status_string(vbq_status st);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char *vbq_last_error(void);
+
+/*
+ * Host only.  Fill the shape-dependent fields of a layout (dims and section
+ * offsets); the code sizes and total_bytes need the widths (vbq_pack_plan).
+ */
+vbq_status vbq_layout_init(int N, int K, vbq_layout *L /* host */);
+
+/*
+ * Host only.  Validate a blob header copied to the host (>= 256 bytes) and
+ * return its layout.  VBQ_ERR_LAYOUT on a bad magic, version or geometry.
+ */
+vbq_status vbq_layout_from_header(const void *header /* host, 256 B */, vbq_layout *L /* host */);
+
+/* Workspace bytes vbq_pack_plan needs for N rows. */
+size_t vbq_pack_plan_workspace(int N);
+
+/*
+ * SYNC.  Plan a blob for widths bits[N][G] (u8, device): computes the per-row
+ * 128-byte-padded record sizes and fills L completely (total_bytes is what
+ * the caller must allocate).  Returns VBQ_ERR_BITS if any width is invalid.
+ * ws: device scratch of vbq_pack_plan_workspace(N) bytes, any contents.
+ */
+vbq_status vbq_pack_plan(int N, int K, const uint8_t *bits, vbq_layout *L /* host */, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * Pack q[N][K] (u8 codes), bits[N][G] (u8 widths), scales[N][G] (fp16 bits)
+ * into blob (L->total_bytes bytes, 256-byte aligned, any prior contents).
+ * Every blob byte is written; the result is the unique VBQ1 byte string.
+ * Data errors found on the device (bad width, code out of range, widths that
+ * differ from the plan) set VBQ_STATUS_* bits in *status_word (device u32,
+ * cleared by this call); no write ever leaves [blob, blob + total_bytes).
+ */
+vbq_status vbq_pack(const vbq_layout *L /* host */, const uint8_t *q, const uint8_t *bits, const uint16_t *scales,
+                    void *blob, uint32_t *status_word, hipStream_t stream);
+
+/*
+ * SYNC.  Read a status word written by vbq_pack: VBQ_OK, or the first error
+ * among VBQ_ERR_BITS, VBQ_ERR_CODE_RANGE, VBQ_ERR_LAYOUT.  *raw (host, may be
+ * NULL) receives the word.
+ */
+vbq_status vbq_status_check(const uint32_t *status_word, uint32_t *raw /* host */, hipStream_t stream);
+
+/*
+ * Expand a blob to dense weights w[N][K] (row-major): VBQ_F32 gives the exact
+ * value of s*(q - (2^b-1)/2); VBQ_F16 gives its round-to-nearest-even fp16.
+ */
+vbq_status vbq_dequant(const vbq_layout *L /* host */, const void *blob, void *w, vbq_dtype wt, hipStream_t stream);
+
+/*
+ * Workspace bytes vbq_gemv / vbq_gemv_batched need for layout L and M tokens
+ * (0 when K <= 2048, i.e. a single K-slice).  The workspace holds per-tile
+ * counters (first, at a fixed offset) and split-K partial sums; it must be
+ * zero-filled once before its first use (vbq_workspace_clear), and every GEMV
+ * leaves the counters at zero again, so it can be reused without clearing.
+ * A workspace sized for M tokens serves every call with M' <= M tokens.
+ */
+vbq_status vbq_workspace_size(const vbq_layout *L /* host */, int M, size_t *bytes /* host */);
+
+/* Zero-fill a GEMV workspace with a kernel (safe inside HIP graph capture). */
+vbq_status vbq_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * y = W x for one token: x fp16[K], y[N] in yt (VBQ_F16 rounds to nearest
+ * even).  Accumulation is fp32; |y - y_exact| <= 1e-3 * sum_k |w_k||x_k| per
+ * output.  Outputs that meet a non-finite weight (inf/NaN scale) with a
+ * nonzero x are non-finite.  Same as vbq_gemv_batched with M = 1.
+ */
+vbq_status vbq_gemv(const vbq_layout *L /* host */, const void *blob, const uint16_t *x, void *y, vbq_dtype yt,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Y = X W^T for M tokens (1 <= M <= 16): x fp16 [M][ldx] (ldx >= K),
+ * y [M][ldy] (ldy >= N).  Each packed code is unpacked once per call and
+ * reused for all M tokens.  Error bound as vbq_gemv, per token and output.
+ */
+vbq_status vbq_gemv_batched(const vbq_layout *L /* host */, const void *blob, int M, const uint16_t *x, int ldx,
+                            void *y, int ldy, vbq_dtype yt, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dense fp16 control at the same shapes: y[M][ldy] = W16 x with W16 fp16
+ * [N][K] row-major (typically vbq_dequant(..., VBQ_F16)), fp32 accumulate.
+ * K % 8 == 0, 1 <= M <= 16.
+ */
+vbq_status vbq_dense_f16_gemv(int N, int K, int M, const uint16_t *w16, const uint16_t *x, int ldx, void *y, int ldy,
+                              vbq_dtype yt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VBQ_H */
