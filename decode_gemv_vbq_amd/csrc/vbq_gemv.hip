@@ -3,31 +3,32 @@
 // The decode path of "Variable Bit-width Quantization" (mlsanity.com page,
 // Abstract): weights in contiguous 64-weight groups, each with its own width in
 // {1,2,4,8}, read as packed codes and multiplied without ever materialising the
-// dense matrix.  Decode is bound by memory bandwidth, so every byte of the
-// packed stream is read exactly once, with wide loads, and the arithmetic is
-// shaped to stay under that bound on CDNA4:
+// dense matrix.  Decode is bound by memory bandwidth, so every packed byte is
+// read exactly once and the arithmetic is shaped to stay under that bound:
 //
-//  * A workgroup owns a tile of R rows x one K-slice of 32 groups (2048 K).
-//    It stages the slice of x in LDS as fp16 pairs (x_p, x_{p+32}) per group,
-//    XOR-swizzled by group so that lanes on different groups hit different
-//    LDS bank groups.
-//  * The R*32 groups of the tile are listed per width in LDS (a slot table
-//    built from the width bit planes), so a wavefront always works on 64
-//    groups of ONE width: no divergence between 1/2/4/8-bit paths.
-//  * Lane = one group.  Each 32-bit code word is turned into fp16 pairs with a
-//    single v_and_or_b32 (8-bit: v_perm_b32): the code field lands in the
-//    mantissa of a power-of-two "magic" 2^(10-pos), so the half equals
-//    2^(10-pos) + q exactly.  v_dot2_f32_f16 then multiplies two weights per
-//    instruction with fp32 accumulation.  The magic offsets and the centre
-//    (2^b-1)/2 are removed once per group through a per-(group, width)
-//    constant computed from x during staging:
-//        sum_j (q_j - c_b) x_j = acc - C_b,g,   C = sum_p magic_p (x_p + x_p+32) + c_b sum_j x_j
+//  * Persistent workgroups own whole rows (no split-K, hence no cross-workgroup
+//    traffic or fences).  Each stages x once as fp16 pairs (x_p, x_{p+32}) per
+//    group in LDS, XOR-swizzled by group so lanes on different groups hit
+//    different LDS bank groups, then walks its row tiles.
+//  * A unit = R rows x SG K-slices.  Its groups are listed per width in an LDS
+//    slot table built from the width bit planes, so a wavefront always works on
+//    64 groups of ONE width: no divergence between the 1/2/4/8-bit paths.
+//  * Lane = one group.  Each 32-bit code word becomes fp16 pairs with a single
+//    v_and_or_b32 (8-bit: v_perm_b32): the code field lands in the mantissa of
+//    a power-of-two "magic" 2^(10-pos), so each half equals 2^(10-pos) + q
+//    exactly, and v_dot2_f32_f16 multiplies two weights per instruction into
+//    an fp32 accumulator.  The magic offsets and the centre (2^b-1)/2 are
+//    removed once per group with a per-(group, width) constant of x:
+//        sum_j (q_j - c_b) x_j = acc - C,  C = sum_p magic_p (x_p + x_{p+32}) + c_b sum_j x_j
 //    and the group's fp16 scale multiplies the difference.
-//  * Per-group partials land in LDS and are summed per row in natural group
-//    order (deterministic).  K > 2048 is split over slices; the last
-//    workgroup of a row tile (atomic ticket) adds the slice partials in slice
-//    order and writes y.  No MFMA: M <= 16 is not a dense contraction.
+//  * Code loads of the next pass are issued before the current pass computes,
+//    and the next unit's tables are fetched while this unit computes.
+//  * Per-group partials are summed per row in natural group order, units in
+//    K order: the result does not depend on the launch shape's timing.
+//  * No MFMA: M <= 16 tokens is not a dense contraction.
 #include <stdio.h>
+
+#include <algorithm>
 
 #include "vbq_common.h"
 #include "vbq_host.h"
@@ -38,8 +39,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxR = 32;
-constexpr int kPsumStride = 33; // floats per psum row (pads away bank conflicts)
+constexpr int kMaxRS = 64;    // row-slices per unit (one wave lane each)
+constexpr int kMaxRows = 32;  // rows per tile
 
 struct GemvArgs {
     const uint8_t *blob;
@@ -51,9 +52,11 @@ struct GemvArgs {
     void *y;
     int ldy;
     int yt;
-    float *partial;    // [nS][M][N] when nS > 1
-    uint32_t *tickets; // [tiles] when nS > 1
-    int R;             // rows per tile (<= 32)
+    int R;        // rows per tile (<= 32)
+    int SG;       // K-slices per unit (R * SG <= 64, R * SG * 32 <= slot capacity)
+    int CHK;      // K-slices of x resident in LDS at a time
+    int tiles;    // ceil(N / R)
+    int slots;    // slot-table capacity
 };
 
 // fp16 bits of 2^(10-pos), in both halves.
@@ -139,34 +142,213 @@ __device__ __forceinline__ void load_codes(const uint8_t *__restrict__ p, uint32
     }
 }
 
-struct RowInfo {
-    uint32_t p0, p1;   // width bit planes of this row-slice
-    uint32_t base;     // row-slice record start, 8-byte units from the codes section
-    uint16_t bb[4];    // bucket starts inside the slice record, 8-byte units
-    uint16_t pre[4];   // slots of width c in earlier rows of the tile
+// One row-slice of the current unit, as seen by the slot-table build.
+struct RowSlice {
+    uint32_t p0, p1;  // width bit planes
+    uint32_t base;    // record start of this row-slice, 8-byte units from the codes section
+    uint16_t bb[4];   // bucket starts inside the row-slice record, 8-byte units
+    uint16_t pre[4];  // slots of width c in earlier row-slices of the unit
 };
 
-// One pass: 64 slots of width B; lane = group.
-template <int B, int MT>
-__device__ __forceinline__ void run_pass(const GemvArgs &a, int slot, int nslots, const uint64_t *table,
-                                         const uint32_t *xim, const float *corr, float *psum, int c,
-                                         const uint8_t *codes)
+// Work unit of a workgroup: rows [tile*R, tile*R + R) x slices [t0, t0 + ns).
+struct Unit {
+    int tile, t0, ns;
+};
+
+__device__ __forceinline__ bool unit_valid(const Unit &u, const GemvArgs &a) { return u.tile < a.tiles; }
+
+__device__ __forceinline__ Unit first_unit(const GemvArgs &a)
 {
-    if (slot >= nslots)
+    Unit u;
+    u.tile = blockIdx.x;
+    u.t0 = 0;
+    u.ns = min(a.SG, min(a.CHK, a.nS));
+    return u;
+}
+
+// Units run slice-group by slice-group inside an x chunk, chunks in order,
+// then the next row tile of this workgroup.
+__device__ __forceinline__ Unit next_unit(const Unit &u, const GemvArgs &a)
+{
+    Unit n = u;
+    int t = u.t0 + u.ns;
+    if (t >= a.nS) {
+        n.tile = u.tile + gridDim.x;
+        t = 0;
+    }
+    int chunk_end = min(a.nS, (t / a.CHK + 1) * a.CHK);
+    n.t0 = t;
+    n.ns = min(a.SG, chunk_end - t);
+    return n;
+}
+
+// Metadata of one unit held in registers until the slot table is built.
+struct UnitMeta {
+    uint32_t p0, p1, row_off, slice_off; // lane-owned row-slice (wave 0)
+    uint32_t scale[4];                   // up to 4 group items per thread
+};
+
+template <int MT>
+__device__ __forceinline__ void fetch_meta(const Unit &u, const GemvArgs &a, UnitMeta &m)
+{
+    const int tid = threadIdx.x;
+    m.p0 = m.p1 = m.row_off = m.slice_off = 0;
+    if (!unit_valid(u, a))
         return;
-    uint64_t e = table[slot];
-    uint32_t lo = (uint32_t)e, hi = (uint32_t)(e >> 32);
-    int g = (hi >> 16) & 0xff, r = hi >> 24;
-    float s = __half2float(__ushort_as_half((unsigned short)(hi & 0xffffu)));
+    const uint32_t *row_off = reinterpret_cast<const uint32_t *>(a.blob + a.off_row_off);
+    const uint32_t *slice_off = reinterpret_cast<const uint32_t *>(a.blob + a.off_slice_off);
+    const uint32_t *wmap = reinterpret_cast<const uint32_t *>(a.blob + a.off_wmap);
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.blob + a.off_scales);
+    const int n0 = u.tile * a.R;
+    if (tid < a.R * u.ns) {
+        int r = tid / u.ns, s = tid % u.ns;
+        int n = n0 + r;
+        if (n < a.N) {
+            uint64_t rs = (uint64_t)n * a.nS + u.t0 + s;
+            m.p0 = wmap[2 * rs];
+            m.p1 = wmap[2 * rs + 1];
+            m.row_off = row_off[n];
+            m.slice_off = slice_off[rs];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        int i = tid + k * kThreads; // item = (row-slice, group in slice)
+        int l = i >> 5, gi = i & 31;
+        int r = l / u.ns, s = l % u.ns;
+        int n = n0 + r;
+        int g = 32 * (u.t0 + s) + gi;
+        m.scale[k] = 0;
+        if (l < a.R * u.ns && n < a.N && g < a.G)
+            m.scale[k] = scales[(uint64_t)n * a.G + g];
+    }
+}
+
+// Stage x for slices [t0, t0 + ns) of the chunk as swizzled pairs, then the
+// per-(token, group, width) corrections.
+template <int MT>
+__device__ void stage_x(const GemvArgs &a, int t0, int ns, uint32_t *xim, float *corr)
+{
+    const int tid = threadIdx.x;
+    const int CHG = a.CHK * 32;
+    const int gch = min(ns * 32, a.G - 32 * t0);
+    for (int i = tid; i < a.M * gch * 32; i += kThreads) {
+        int p = i & 31, g = (i >> 5) % gch, m = (i >> 5) / gch;
+        const uint16_t *xs = a.x + (uint64_t)m * a.ldx + 64ull * (32 * t0 + g);
+        uint32_t v = (uint32_t)xs[p] | ((uint32_t)xs[p + 32] << 16);
+        xim[(m * CHG + g) * 32 + ((((p >> 2) ^ (g & 7)) << 2) | (p & 3))] = v;
+    }
+    __syncthreads();
+    // C_b = sum_p magic_b(p) (x_p + x_{p+32}) + c_b sum_j x_j, where magic_b(p)
+    // depends on p only through p mod 16/8/4 for b = 1/2/4 (and is 1024 for b = 8).
+    for (int i = tid; i < a.M * gch; i += kThreads) {
+        int g = i % gch, m = i / gch;
+        const uint32_t *xg = xim + (m * CHG + g) * 32;
+        float X2[32];
+#pragma unroll
+        for (int p = 0; p < 32; p++)
+            X2[p] = dot2(xg[(((p >> 2) ^ (g & 7)) << 2) | (p & 3)], 0x3c003c00u, 0.f);
+        float S16[16], S8[8], S4[4];
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            S16[j] = X2[j] + X2[j + 16];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            S8[j] = S16[j] + S16[j + 8];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            S4[j] = S8[j] + S8[j + 4];
+        float C0 = 0.f, C1 = 0.f, C2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            C0 = fmaf((float)(1 << (10 - pair_pos<1>(j))), S16[j], C0);
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            C1 = fmaf((float)(1 << (10 - pair_pos<2>(j))), S8[j], C1);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            C2 = fmaf((float)(1 << (10 - pair_pos<4>(j))), S4[j], C2);
+        float X = (S4[0] + S4[1]) + (S4[2] + S4[3]);
+        float4 cv = make_float4(fmaf(0.5f, X, C0), fmaf(1.5f, X, C1), fmaf(7.5f, X, C2), fmaf(127.5f, X, 1024.f * X));
+        *reinterpret_cast<float4 *>(corr + (m * CHG + g) * 4) = cv;
+    }
+    __syncthreads();
+}
+
+// Pending pass: the lane's table entry and its loaded code words.
+struct Pending {
+    int c;          // width code of the pass (wave-uniform), -1 when none
+    bool live;      // lane has a slot
+    uint32_t lo, hi;
+    U4 w[4];
+};
+
+__device__ __forceinline__ int pass_width(int pi, const int *pbase)
+{
+    int c = 0;
+#pragma unroll
+    for (int cc = 1; cc < 4; cc++)
+        c += pi >= pbase[cc] ? 1 : 0;
+    return c;
+}
+
+__device__ __forceinline__ void issue_pass(Pending &p, int pi, int npass, const int *pbase, const int *tbase,
+                                           const int *total, const uint64_t *table, const uint8_t *codes)
+{
+    const int lane = threadIdx.x & 63;
+    p.c = -1;
+    p.live = false;
+    if (pi >= npass)
+        return;
+    int c = pass_width(pi, pbase);
+    int slot = (pi - pbase[c]) * 64 + lane;
+    p.c = c;
+    p.live = slot < total[c];
+    if (!p.live)
+        return;
+    uint64_t e = table[tbase[c] + slot];
+    p.lo = (uint32_t)e;
+    p.hi = (uint32_t)(e >> 32);
+    const uint8_t *src = codes + 8ull * p.lo;
+    switch (c) {
+    case 0: {
+        U2 v = *reinterpret_cast<const U2 *>(src);
+        p.w[0].v[0] = v.v[0];
+        p.w[0].v[1] = v.v[1];
+        break;
+    }
+    case 1: p.w[0] = *reinterpret_cast<const U4 *>(src); break;
+    case 2:
+        p.w[0] = *reinterpret_cast<const U4 *>(src);
+        p.w[1] = *reinterpret_cast<const U4 *>(src + 16);
+        break;
+    default:
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            p.w[k] = *reinterpret_cast<const U4 *>(src + 16 * k);
+        break;
+    }
+}
+
+template <int B, int MT>
+__device__ __forceinline__ void compute_slot(const Pending &p, const GemvArgs &a, const uint32_t *xim,
+                                             const float *corr, float *psum, int gbase, int pstride, int prow)
+{
     uint32_t w[2 * B];
-    load_codes<B>(codes + 8ull * lo, w);
+#pragma unroll
+    for (int d = 0; d < 2 * B; d++)
+        w[d] = p.w[d / 4].v[d % 4];
     uint32_t h[32];
     unpack_pairs<B>(w, h);
+    const int gl = (p.hi >> 16) & 0xff, r = p.hi >> 24;
+    const int g = gbase + gl;
+    const float s = __half2float(__ushort_as_half((unsigned short)(p.hi & 0xffffu)));
+    const int CHG = a.CHK * 32;
     const int swz = g & 7;
 #pragma unroll
     for (int m = 0; m < MT; m++) {
         if (m < a.M) {
-            const uint32_t *xg = xim + (m * 32 + g) * 32;
+            const uint32_t *xg = xim + (m * CHG + g) * 32;
             float acc = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; k++) {
@@ -176,8 +358,8 @@ __device__ __forceinline__ void run_pass(const GemvArgs &a, int slot, int nslots
                 acc = dot2(h[4 * k + 2], xv.v[2], acc);
                 acc = dot2(h[4 * k + 3], xv.v[3], acc);
             }
-            float C = corr[(m * 4 + c) * 32 + g];
-            psum[(m * kMaxR + r) * kPsumStride + g] = s * (acc - C);
+            float C = corr[(m * CHG + g) * 4 + (B == 1 ? 0 : B == 2 ? 1 : B == 4 ? 2 : 3)];
+            psum[m * pstride + r * prow + gl] = s * (acc - C);
         }
     }
 }
@@ -186,240 +368,726 @@ template <int MT>
 __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    uint32_t *xim = reinterpret_cast<uint32_t *>(smem);                        // [MT][32][32] fp16 pairs
-    float *corr = reinterpret_cast<float *>(xim + MT * 32 * 32);               // [MT][4][32]
-    float *psum = corr + MT * 4 * 32;                                          // [MT][kMaxR][kPsumStride]
-    uint64_t *table = reinterpret_cast<uint64_t *>(
-        reinterpret_cast<uint8_t *>(psum) + ((MT * kMaxR * kPsumStride * 4 + 7) / 8) * 8); // [R*32]
-    __shared__ RowInfo rows[kMaxR];
-    __shared__ int s_total[4], s_tbase[5], s_pbase[5];
-    __shared__ int s_last;
+    const int CHG = a.CHK * 32;
+    uint32_t *xim = reinterpret_cast<uint32_t *>(smem);             // [MT][CHG][32] fp16 pairs
+    float *corr = reinterpret_cast<float *>(xim + MT * CHG * 32);   // [MT][CHG][4]
+    uint64_t *table = reinterpret_cast<uint64_t *>(corr + MT * CHG * 4); // [slots]
+    float *psum = reinterpret_cast<float *>(table + a.slots);      // [MT][R][SG*32 + 1]
+    __shared__ RowSlice rsl[kMaxRS];
+    __shared__ float acc_tile[MT][kMaxRows];
+    __shared__ int s_total[4], s_tbase[4], s_pbase[5];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t = blockIdx.x, tile = blockIdx.y;
-    const int R = a.R;
-    const int n0 = tile * R;
-    const int ng = min(32, a.G - 32 * t);
+    const uint8_t *codes = a.blob + a.off_codes;
+    const int prow = a.SG * 32 + 1;
+    const int pstride = a.R * prow;
+
+    Unit u = first_unit(a);
+    UnitMeta meta;
+    fetch_meta<MT>(u, a, meta);
+    int staged = -1;
+
+    while (unit_valid(u, a)) {
+        const Unit nu = next_unit(u, a);
+        const int n0 = u.tile * a.R;
+        const int chunk = u.t0 / a.CHK;
+        if (chunk != staged) {
+            __syncthreads(); // previous readers of xim/corr are done
+            stage_x<MT>(a, chunk * a.CHK, min(a.CHK, a.nS - chunk * a.CHK), xim, corr);
+            staged = chunk;
+        }
+        // acc_tile[m][r] belongs to thread 32*(m*R + r) (the row's reducing lane 0)
+        if (u.t0 == 0) {
+            for (int i = tid >> 5; i < a.M * a.R; i += kThreads / 32)
+                if ((tid & 31) == 0)
+                    acc_tile[i / a.R][i % a.R] = 0.f;
+        }
+
+        // ---- slot table, part 1: per row-slice counts and prefix sums (wave 0)
+        if (wave == 0) {
+            const int nrs = a.R * u.ns;
+            bool live = lane < nrs && n0 + lane / u.ns < a.N;
+            int s = lane % u.ns;
+            int ng = max(0, min(32, a.G - 32 * (u.t0 + s)));
+            int cnt[4] = {0, 0, 0, 0};
+            WidthMasks wm = width_masks(meta.p0, meta.p1, ng);
+            if (live) {
+#pragma unroll
+                for (int c = 0; c < 4; c++)
+                    cnt[c] = __popc(wm.m[c]);
+            }
+            int incl[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                int v = cnt[c];
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    int t = __shfl_up(v, off, 64);
+                    if (lane >= off)
+                        v += t;
+                }
+                incl[c] = v;
+            }
+            if (lane < nrs) {
+                RowSlice rs;
+                rs.p0 = live ? meta.p0 : 0u;
+                rs.p1 = live ? meta.p1 : 0u;
+                rs.base = (uint32_t)((128ull * meta.row_off + meta.slice_off) >> 3);
+                int bb = 0;
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    rs.bb[c] = (uint16_t)bb;
+                    bb += cnt[c] << c;
+                    rs.pre[c] = (uint16_t)(incl[c] - cnt[c]);
+                }
+                rsl[lane] = rs;
+            }
+            if (lane == 63) {
+                int tb = 0, pb = 0;
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    s_total[c] = incl[c];
+                    s_tbase[c] = tb;
+                    s_pbase[c] = pb;
+                    tb += incl[c];
+                    pb += (incl[c] + 63) / 64;
+                }
+                s_pbase[4] = pb;
+            }
+        }
+        __syncthreads();
+
+        // ---- slot table, part 2: one entry per group (width-major, then row-slice, then g)
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            int i = tid + k * kThreads;
+            int l = i >> 5, gi = i & 31;
+            if (l >= a.R * u.ns)
+                continue;
+            int r = l / u.ns, s = l % u.ns;
+            if (n0 + r >= a.N || 32 * (u.t0 + s) + gi >= a.G)
+                continue;
+            RowSlice rs = rsl[l];
+            int ng = min(32, a.G - 32 * (u.t0 + s));
+            WidthMasks wm = width_masks(rs.p0, rs.p1, ng);
+            int c = width_code(rs.p0, rs.p1, gi);
+            int rank = __popc(pick4(wm.m, c) & ((1u << gi) - 1u));
+            uint32_t lo = rs.base + pick4(rs.bb, c) + ((uint32_t)rank << c);
+            uint32_t gl = (uint32_t)(32 * s + gi);
+            uint32_t hi = (meta.scale[k] & 0xffffu) | (gl << 16) | ((uint32_t)r << 24);
+            table[s_tbase[c] + pick4(rs.pre, c) + rank] = (uint64_t)lo | ((uint64_t)hi << 32);
+        }
+        __syncthreads();
+
+        // ---- next unit's metadata in flight while this unit computes
+        fetch_meta<MT>(nu, a, meta);
+
+        // ---- passes: 64 groups of one width each; loads one pass ahead
+        const int npass = s_pbase[4];
+        const int gbase = (u.t0 - chunk * a.CHK) * 32;
+        int pb[5], tb[4], tot[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            pb[c] = s_pbase[c];
+            tb[c] = s_tbase[c];
+            tot[c] = s_total[c];
+        }
+        pb[4] = npass;
+        Pending cur, nxt;
+        int pi = wave;
+        issue_pass(cur, pi, npass, pb, tb, tot, table, codes);
+        while (pi < npass) {
+            issue_pass(nxt, pi + kWaves, npass, pb, tb, tot, table, codes);
+            if (cur.live) {
+                switch (cur.c) {
+                case 0: compute_slot<1, MT>(cur, a, xim, corr, psum, gbase, pstride, prow); break;
+                case 1: compute_slot<2, MT>(cur, a, xim, corr, psum, gbase, pstride, prow); break;
+                case 2: compute_slot<4, MT>(cur, a, xim, corr, psum, gbase, pstride, prow); break;
+                default: compute_slot<8, MT>(cur, a, xim, corr, psum, gbase, pstride, prow); break;
+                }
+            }
+            cur = nxt;
+            pi += kWaves;
+        }
+        __syncthreads();
+
+        // ---- row sums of this unit: 32 lanes per row, fixed order (lane j adds
+        // groups j, j+32, ...; then a fixed butterfly), units added in K order
+        const int gcount = min(u.ns * 32, a.G - 32 * u.t0);
+        const bool last = u.t0 + u.ns >= a.nS;
+        for (int i = tid >> 5; i < ((a.M * a.R + 7) & ~7); i += kThreads / 32) {
+            const int j = tid & 31;
+            const int m = i / a.R, r = i % a.R;
+            const bool row_live = i < a.M * a.R && n0 + r < a.N;
+            float v = 0.f;
+            if (row_live) {
+                const float *ps = psum + m * pstride + r * prow;
+                for (int g = j; g < gcount; g += 32)
+                    v += ps[g];
+            }
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1)
+                v += __shfl_xor(v, off, 32);
+            if (row_live && j == 0) {
+                float t = acc_tile[m][r] + v;
+                acc_tile[m][r] = t;
+                if (last) {
+                    int n = n0 + r;
+                    if (a.yt == VBQ_F16)
+                        reinterpret_cast<__half *>(a.y)[(uint64_t)m * a.ldy + n] = __float2half_rn(t);
+                    else
+                        reinterpret_cast<float *>(a.y)[(uint64_t)m * a.ldy + n] = t;
+                }
+            }
+        }
+        u = nu;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-independent variant for M <= 2 (the decode case).  x is staged once per
+// workgroup for the whole K; after that single barrier every wavefront owns
+// whole row tiles and runs its own units with no further synchronisation, so
+// eight independent instruction streams per CU keep loads in flight.
+//
+// x record per (token, group): 32 fp16 pairs (x_p, x_{p+32}) + the 4 width
+// corrections, 144 bytes.  The odd number of 16-byte chunks per record staggers
+// the LDS bank groups of consecutive groups without any address swizzle, so
+// every LDS read of a slot uses one base address plus constant offsets.
+
+constexpr int kWThreads = 512;
+constexpr int kWWaves = kWThreads / 64;
+constexpr int kXRec = 36; // dwords per x record
+
+// passes per batch for width code c (16 code words per lane)
+__host__ __device__ constexpr int batch_passes(int c) { return c == 0 ? 8 : c == 1 ? 4 : c == 2 ? 2 : 1; }
+
+struct WUnit {
+    int tile, t0, ns;
+};
+
+struct WMeta {
+    uint32_t p0, p1, row_off, slice_off; // lane = row-slice of the unit
+};
+
+// Row-slice record of the current unit (48 bytes, lane-owned while built).
+struct RS2 {
+    uint32_t p0, p1;
+    uint32_t m[4];     // groups of width code c
+    uint32_t base;     // record start, bytes from the unit's first code byte
+    uint32_t rs;       // row | slice << 8
+    uint32_t bbpre[4]; // slot base of (width c, groups 0..15) (low 16) | bucket start, 8-byte units (high 16)
+    uint32_t pre1[4];  // slot base of (width c, groups 16..31)
+};
+
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ WUnit wunit_next(WUnit u, const GemvArgs &a, int tw)
+{
+    int t = u.t0 + u.ns;
+    if (t >= a.nS) {
+        u.tile += tw;
+        t = 0;
+    }
+    u.t0 = t;
+    u.ns = min(a.SG, a.nS - t);
+    return u;
+}
+
+// lane = row-slice l = r * ns + s (ns is 1 or the whole row, so no division
+// is needed: the host makes SG either 1 or nS and passes its row-slice map)
+__device__ __forceinline__ void wfetch_meta(const WUnit &u, const GemvArgs &a, WMeta &m)
+{
+    const int lane = threadIdx.x & 63;
+    m.p0 = m.p1 = m.row_off = m.slice_off = 0;
+    if (u.tile >= a.tiles || lane >= a.R * u.ns)
+        return;
+    const int r = u.ns == 1 ? lane : lane / u.ns;
+    const int s = lane - r * u.ns;
+    const int n = u.tile * a.R + r;
+    if (n >= a.N)
+        return;
     const uint32_t *row_off = reinterpret_cast<const uint32_t *>(a.blob + a.off_row_off);
     const uint32_t *slice_off = reinterpret_cast<const uint32_t *>(a.blob + a.off_slice_off);
     const uint32_t *wmap = reinterpret_cast<const uint32_t *>(a.blob + a.off_wmap);
-    const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.blob + a.off_scales);
-    const uint8_t *codes = a.blob + a.off_codes;
+    const uint32_t rs = (uint32_t)n * a.nS + u.t0 + s;
+    m.p0 = wmap[2 * (uint64_t)rs];
+    m.p1 = wmap[2 * (uint64_t)rs + 1];
+    m.row_off = row_off[n];
+    m.slice_off = slice_off[rs];
+}
 
-    // ---- phase 0a: per-row bucket counts and prefix sums (wave 0, lane = row)
-    if (wave == 0) {
-        int r = lane;
-        int n = n0 + r;
-        bool live = r < R && n < a.N;
-        uint32_t p0 = 0, p1 = 0, base = 0;
-        int cnt[4] = {0, 0, 0, 0};
-        if (live) {
-            uint64_t rs = (uint64_t)n * a.nS + t;
-            p0 = wmap[2 * rs];
-            p1 = wmap[2 * rs + 1];
-            base = (uint32_t)((128ull * row_off[n] + slice_off[rs]) >> 3);
-            WidthMasks m = width_masks(p0, p1, ng);
+struct WState { // wave-uniform bookkeeping of the current unit
+    int total[4], tbase[4], n0, t0;
+    const uint8_t *codes;   // first code byte of the unit
+    const uint16_t *scales; // scale of (row n0, group 32*t0)
+};
+
+// Passes of ONE width held in registers: entries, scales and code words.
+template <int B>
+struct BatchT {
+    static constexpr int C = B == 1 ? 0 : B == 2 ? 1 : B == 4 ? 2 : 3;
+    static constexpr int BP = batch_passes(C);
+    uint32_t hi[BP], sc[BP];
+    uint32_t w[2 * B * BP];
+};
+
+template <int B>
+__device__ __forceinline__ void issue_t(BatchT<B> &bt, int first, const WState &st, const GemvArgs &a,
+                                        const uint2 *table)
+{
+    constexpr int C = BatchT<B>::C, BP = BatchT<B>::BP;
+    const int lane = threadIdx.x & 63;
+    uint2 ent[BP];
 #pragma unroll
-            for (int c = 0; c < 4; c++)
-                cnt[c] = __popc(m.m[c]);
-        }
-        int incl[4];
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            int v = cnt[c];
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                int u = __shfl_up(v, off, 64);
-                if (lane >= off)
-                    v += u;
-            }
-            incl[c] = v;
-        }
-        if (r < kMaxR) {
-            RowInfo ri;
-            ri.p0 = p0;
-            ri.p1 = p1;
-            ri.base = base;
-            int bb = 0;
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                ri.bb[c] = (uint16_t)bb;
-                bb += cnt[c] << c;
-                ri.pre[c] = (uint16_t)(incl[c] - cnt[c]);
-            }
-            rows[r] = ri;
-        }
-        if (lane == 63) {
-            int tb = 0, pb = 0;
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                s_total[c] = incl[c];
-                s_tbase[c] = tb;
-                s_pbase[c] = pb;
-                tb += incl[c];
-                pb += (incl[c] + 63) / 64;
-            }
-            s_tbase[4] = tb;
-            s_pbase[4] = pb;
-        }
+    for (int j = 0; j < BP; j++) { // all table reads first, one LDS round trip
+        const int slot = (first + j) * 64 + lane;
+        ent[j] = slot < st.total[C] ? table[st.tbase[C] + slot] : make_uint2(0u, 0xffffffffu);
     }
-
-    // ---- phase 0b: x slice -> LDS pairs (x_p, x_{p+32}), chunk k at k ^ (g & 7)
-    for (int i = tid; i < a.M * ng * 32; i += kThreads) {
-        int p = i & 31, g = (i >> 5) % ng, m = (i >> 5) / ng;
-        const uint16_t *xs = a.x + (uint64_t)m * a.ldx + 64ull * (32 * t + g);
-        uint32_t v = (uint32_t)xs[p] | ((uint32_t)xs[p + 32] << 16);
-        xim[(m * 32 + g) * 32 + ((((p >> 2) ^ (g & 7)) << 2) | (p & 3))] = v;
+#pragma unroll
+    for (int j = 0; j < BP; j++) {
+        uint32_t hi = 0xffffffffu, sc = 0;
+        if (ent[j].y != 0xffffffffu) {
+            const uint2 e = ent[j];
+            hi = e.y;
+            const uint8_t *src = st.codes + e.x;
+            if constexpr (B == 1) {
+                U2 v = *reinterpret_cast<const U2 *>(src);
+                bt.w[2 * j] = v.v[0];
+                bt.w[2 * j + 1] = v.v[1];
+            } else {
+#pragma unroll
+                for (int k = 0; k < B / 2; k++) {
+                    U4 v = *reinterpret_cast<const U4 *>(src + 16 * k);
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        bt.w[2 * B * j + 4 * k + q] = v.v[q];
+                }
+            }
+            const uint32_t r = hi >> 16, gl = hi & 0xffffu;
+            sc = st.scales[r * (uint32_t)a.G + gl];
+        }
+        bt.hi[j] = hi;
+        bt.sc[j] = sc;
     }
-    __syncthreads();
+}
 
-    // ---- phase 0c: slot table (one entry per group of the tile)
-    for (int i = tid; i < R * ng; i += kThreads) {
-        int r = i / ng, gi = i % ng;
-        int n = n0 + r;
-        if (n >= a.N)
+template <int B, int MT>
+__device__ __forceinline__ void compute_t(const BatchT<B> &bt, const WState &st, const GemvArgs &a,
+                                          const uint32_t *xrec, float *racc)
+{
+    constexpr int C = BatchT<B>::C, BP = BatchT<B>::BP;
+    const uint32_t CHG = (uint32_t)a.nS * 32;
+#pragma unroll
+    for (int j = 0; j < BP; j++) {
+        if (bt.hi[j] == 0xffffffffu)
             continue;
-        RowInfo ri = rows[r];
-        WidthMasks m = width_masks(ri.p0, ri.p1, ng);
-        int c = width_code(ri.p0, ri.p1, gi);
-        int rank = __popc(pick4(m.m, c) & ((1u << gi) - 1u));
-        uint32_t lo = ri.base + pick4(ri.bb, c) + ((uint32_t)rank << c);
-        uint32_t sc = scales[(uint64_t)n * a.G + 32 * t + gi];
-        uint32_t hi = sc | ((uint32_t)gi << 16) | ((uint32_t)r << 24);
-        table[s_tbase[c] + pick4(ri.pre, c) + rank] = (uint64_t)lo | ((uint64_t)hi << 32);
-    }
-
-    // ---- phase 0d: correction constants C[m][c][g]
-    for (int i = tid; i < a.M * ng * 4; i += kThreads) {
-        int c = i & 3, g = (i >> 2) % ng, m = (i >> 2) / ng;
-        const uint32_t *xg = xim + (m * 32 + g) * 32;
-        float C = 0.f, X = 0.f;
+        uint32_t h[32];
+        unpack_pairs<B>(&bt.w[2 * B * j], h);
+        const uint32_t r = bt.hi[j] >> 16, gl = bt.hi[j] & 0xffffu;
+        const float s = __half2float(__ushort_as_half((unsigned short)bt.sc[j]));
 #pragma unroll
-        for (int p = 0; p < 32; p++) {
-            uint32_t xv = xg[(((p >> 2) ^ (g & 7)) << 2) | (p & 3)];
-            uint32_t mp;
-            switch (c) {
-            case 0: mp = magic_pair(pair_pos<1>(p & 15)); break;
-            case 1: mp = magic_pair(pair_pos<2>(p & 7)); break;
-            case 2: mp = magic_pair(pair_pos<4>(p & 3)); break;
-            default: mp = 0x64006400u; break;
+        for (int m = 0; m < MT; m++) {
+            if (m < a.M) {
+                const uint32_t *xr = xrec + (m * CHG + 32 * st.t0 + gl) * kXRec;
+                float acc0 = 0.f, acc1 = 0.f; // two chains for instruction-level parallelism
+#pragma unroll
+                for (int k = 0; k < 8; k += 2) {
+                    U4 xa = *reinterpret_cast<const U4 *>(xr + 4 * k);
+                    U4 xb = *reinterpret_cast<const U4 *>(xr + 4 * k + 4);
+                    acc0 = dot2(h[4 * k + 0], xa.v[0], acc0);
+                    acc1 = dot2(h[4 * k + 4], xb.v[0], acc1);
+                    acc0 = dot2(h[4 * k + 1], xa.v[1], acc0);
+                    acc1 = dot2(h[4 * k + 5], xb.v[1], acc1);
+                    acc0 = dot2(h[4 * k + 2], xa.v[2], acc0);
+                    acc1 = dot2(h[4 * k + 6], xb.v[2], acc1);
+                    acc0 = dot2(h[4 * k + 3], xa.v[3], acc0);
+                    acc1 = dot2(h[4 * k + 7], xb.v[3], acc1);
+                }
+                const float Cc = __uint_as_float(xr[32 + C]);
+                __hip_atomic_fetch_add(&racc[m * kMaxRows + r], s * ((acc0 + acc1) - Cc), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
             }
-            C = dot2(xv, mp, C);
-            X = dot2(xv, 0x3c003c00u, X);
-        }
-        float cb = 0.5f * (float)((1 << (1 << c)) - 1);
-        corr[(m * 4 + c) * 32 + g] = C + cb * X;
-    }
-    __syncthreads();
-
-    // ---- phase 1: width-uniform passes, 64 groups each, spread over waves
-    const int npass = s_pbase[4];
-    for (int pi = wave; pi < npass; pi += kWaves) {
-        int c = 0;
-#pragma unroll
-        for (int cc = 1; cc < 4; cc++)
-            c += pi >= s_pbase[cc] ? 1 : 0;
-        int slot = (pi - s_pbase[c]) * 64 + lane;
-        const uint64_t *tb = table + s_tbase[c];
-        switch (c) {
-        case 0: run_pass<1, MT>(a, slot, s_total[0], tb, xim, corr, psum, 0, codes); break;
-        case 1: run_pass<2, MT>(a, slot, s_total[1], tb, xim, corr, psum, 1, codes); break;
-        case 2: run_pass<4, MT>(a, slot, s_total[2], tb, xim, corr, psum, 2, codes); break;
-        default: run_pass<8, MT>(a, slot, s_total[3], tb, xim, corr, psum, 3, codes); break;
         }
     }
-    __syncthreads();
+}
 
-    // ---- phase 2: per-row sums in natural group order
-    const bool split = a.nS > 1;
-    for (int i = tid; i < a.M * R; i += kThreads) {
-        int m = i / R, r = i % R;
-        int n = n0 + r;
-        if (n >= a.N)
-            continue;
-        const float *ps = psum + (m * kMaxR + r) * kPsumStride;
-        float v = 0.f;
-        for (int g = 0; g < ng; g++)
-            v += ps[g];
-        if (split) {
-            a.partial[((uint64_t)t * a.M + m) * a.N + n] = v;
-        } else if (a.yt == VBQ_F16) {
-            reinterpret_cast<__half *>(a.y)[(uint64_t)m * a.ldy + n] = __float2half_rn(v);
+template <int B, int MT>
+__device__ __forceinline__ void run_width(BatchT<B> &bt, const WState &st, const GemvArgs &a, const uint2 *table,
+                                          const uint32_t *xrec, float *racc)
+{
+    constexpr int C = BatchT<B>::C, BP = BatchT<B>::BP;
+    const int np = (st.total[C] + 63) / 64;
+    if (np == 0)
+        return;
+    compute_t<B, MT>(bt, st, a, xrec, racc);
+    for (int f = BP; f < np; f += BP) { // overflow batches (wide mixes)
+        issue_t<B>(bt, f, st, a, table);
+        compute_t<B, MT>(bt, st, a, xrec, racc);
+    }
+}
+
+// x records for all of K: pairs, then C_b = sum_p magic_b(p)(x_p + x_{p+32}) + c_b sum x.
+template <int MT>
+__device__ void stage_xrec(const GemvArgs &a, uint32_t *xrec)
+{
+    const int tid = threadIdx.x;
+    const int CHG = a.nS * 32;
+    const bool vec = (a.ldx % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
+    // 4 pairs per item: x[p..p+3] with x[p+32..p+35]
+    for (int i = tid; i < a.M * a.G * 8; i += kWThreads) {
+        int q = i & 7, g = (i >> 3) % a.G, m = (i >> 3) / a.G;
+        const uint16_t *xs = a.x + (uint64_t)m * a.ldx + 64ull * g + 4 * q;
+        uint32_t lo0, lo1, hi0, hi1;
+        if (vec) {
+            uint2 va = *reinterpret_cast<const uint2 *>(xs);
+            uint2 vb = *reinterpret_cast<const uint2 *>(xs + 32);
+            lo0 = va.x; lo1 = va.y; hi0 = vb.x; hi1 = vb.y;
         } else {
-            reinterpret_cast<float *>(a.y)[(uint64_t)m * a.ldy + n] = v;
+            lo0 = xs[0] | ((uint32_t)xs[1] << 16);
+            lo1 = xs[2] | ((uint32_t)xs[3] << 16);
+            hi0 = xs[32] | ((uint32_t)xs[33] << 16);
+            hi1 = xs[34] | ((uint32_t)xs[35] << 16);
         }
+        U4 o;
+        o.v[0] = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u); // (x_p, x_{p+32})
+        o.v[1] = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
+        o.v[2] = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
+        o.v[3] = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
+        *reinterpret_cast<U4 *>(xrec + (m * CHG + g) * kXRec + 4 * q) = o;
     }
-    if (!split)
-        return;
+    __syncthreads();
+    for (int i = tid; i < a.M * a.G; i += kWThreads) {
+        int g = i % a.G, m = i / a.G;
+        uint32_t *xr = xrec + (m * CHG + g) * kXRec;
+        float X2[32];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            U4 v = *reinterpret_cast<const U4 *>(xr + 4 * k);
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                X2[4 * k + q] = dot2(v.v[q], 0x3c003c00u, 0.f);
+        }
+        float S16[16], S8[8], S4[4];
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            S16[j] = X2[j] + X2[j + 16];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            S8[j] = S16[j] + S16[j + 8];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            S4[j] = S8[j] + S8[j + 4];
+        float C0 = 0.f, C1 = 0.f, C2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            C0 = fmaf((float)(1 << (10 - pair_pos<1>(j))), S16[j], C0);
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            C1 = fmaf((float)(1 << (10 - pair_pos<2>(j))), S8[j], C1);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            C2 = fmaf((float)(1 << (10 - pair_pos<4>(j))), S4[j], C2);
+        float X = (S4[0] + S4[1]) + (S4[2] + S4[3]);
+        xr[32] = __float_as_uint(fmaf(0.5f, X, C0));
+        xr[33] = __float_as_uint(fmaf(1.5f, X, C1));
+        xr[34] = __float_as_uint(fmaf(7.5f, X, C2));
+        xr[35] = __float_as_uint(fmaf(127.5f, X, 1024.f * X));
+    }
+    __syncthreads();
+}
 
-    // ---- phase 3: the last workgroup of this row tile adds the slices in order
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t old = __hip_atomic_fetch_add(&a.tickets[tile], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = old == (uint32_t)(a.nS - 1);
+template <int MT>
+__global__ __launch_bounds__(kWThreads) void k_gemv_wave(GemvArgs a)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t xbytes = (size_t)MT * a.nS * 32 * kXRec * 4;
+    const size_t wbytes = (size_t)a.slots * 8 + MT * kMaxRows * 4 + kMaxRS * sizeof(RS2);
+    uint32_t *xrec = reinterpret_cast<uint32_t *>(smem);
+    uint8_t *wmem = smem + xbytes + wave * wbytes;
+    uint2 *table = reinterpret_cast<uint2 *>(wmem);
+    float *racc = reinterpret_cast<float *>(table + a.slots);
+    RS2 *rsl = reinterpret_cast<RS2 *>(racc + MT * kMaxRows);
+    const uint8_t *codes = a.blob + a.off_codes;
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.blob + a.off_scales);
+
+    stage_xrec<MT>(a, xrec);
+
+    const int tw = gridDim.x * kWWaves;
+    WUnit u;
+    u.tile = blockIdx.x * kWWaves + wave;
+    u.t0 = 0;
+    u.ns = min(a.SG, a.nS);
+    WMeta meta;
+    wfetch_meta(u, a, meta);
+    if (lane < MT * kMaxRows / 2) {
+        racc[lane] = 0.f;
+        racc[lane + MT * kMaxRows / 2] = 0.f;
     }
-    __syncthreads();
-    if (!s_last)
-        return;
-    __threadfence();
-    for (int i = tid; i < a.M * R; i += kThreads) {
-        int m = i / R, r = i % R;
-        int n = n0 + r;
-        if (n >= a.N)
-            continue;
-        float v = 0.f;
-        for (int s = 0; s < a.nS; s++)
-            v += a.partial[((uint64_t)s * a.M + m) * a.N + n];
-        if (a.yt == VBQ_F16)
-            reinterpret_cast<__half *>(a.y)[(uint64_t)m * a.ldy + n] = __float2half_rn(v);
-        else
-            reinterpret_cast<float *>(a.y)[(uint64_t)m * a.ldy + n] = v;
+
+    while (u.tile < a.tiles) {
+        const WUnit nu = wunit_next(u, a, tw);
+        WState st;
+        st.n0 = u.tile * a.R;
+        st.t0 = u.t0;
+        const int nrs = a.R * u.ns;
+        // ---- row-slice records and slot prefix sums (lane = row-slice)
+        {
+            const int r = u.ns == 1 ? lane : lane / u.ns;
+            const int s = lane - r * u.ns;
+            const bool live = lane < nrs && st.n0 + r < a.N;
+            const int ng = max(0, min(32, a.G - 32 * (u.t0 + s)));
+            WidthMasks wm = width_masks(meta.p0, meta.p1, ng);
+            // record starts relative to lane 0's (row n0, slice t0): they fit in 32 bits
+            const uint64_t ubase = 128ull * __builtin_amdgcn_readfirstlane(meta.row_off) +
+                                   __builtin_amdgcn_readfirstlane(meta.slice_off);
+            const uint64_t start = 128ull * meta.row_off + meta.slice_off;
+            // slots of width c are ordered (group half, row-slice, rank): a 16-lane
+            // LDS phase then reads x records of equal g (broadcast) or of distinct
+            // g inside one 16-group window (distinct bank groups): no conflicts
+            int cnt[4], c0[4], incl0[4], incl1[4], tot0[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                cnt[c] = live ? __popc(wm.m[c]) : 0;
+                c0[c] = live ? __popc(wm.m[c] & 0xffffu) : 0;
+                int v0 = c0[c], v1 = cnt[c] - c0[c];
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    int t0 = __shfl_up(v0, off, 64);
+                    int t1 = __shfl_up(v1, off, 64);
+                    if (lane >= off) {
+                        v0 += t0;
+                        v1 += t1;
+                    }
+                }
+                incl0[c] = v0;
+                incl1[c] = v1;
+            }
+            int tb = 0;
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                tot0[c] = __builtin_amdgcn_readlane(incl0[c], 63);
+                st.total[c] = tot0[c] + __builtin_amdgcn_readlane(incl1[c], 63);
+                st.tbase[c] = tb;
+                tb += st.total[c];
+            }
+            if (lane < nrs) {
+                RS2 rr;
+                rr.p0 = live ? meta.p0 : 0u;
+                rr.p1 = live ? meta.p1 : 0u;
+#pragma unroll
+                for (int c = 0; c < 4; c++)
+                    rr.m[c] = live ? wm.m[c] : 0u;
+                rr.base = (uint32_t)(start - ubase);
+                rr.rs = (uint32_t)r | ((uint32_t)s << 8) | (live ? 0u : 0x80000000u);
+                int bb = 0;
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    rr.bbpre[c] = (uint32_t)(st.tbase[c] + incl0[c] - c0[c]) | ((uint32_t)bb << 16);
+                    rr.pre1[c] = (uint32_t)(st.tbase[c] + tot0[c] + incl1[c] - (cnt[c] - c0[c]));
+                    bb += cnt[c] << c;
+                }
+                rsl[lane] = rr;
+            }
+            st.codes = codes + ubase;
+            st.scales = scales + (uint64_t)st.n0 * a.G + 32 * u.t0;
+        }
+        wave_lds_sync();
+        // ---- slot table: one entry per group, width-major then row-slice then g
+        const int nitems = nrs * 32;
+        for (int i = lane; i < nitems; i += 64) {
+            const RS2 &rr = rsl[i >> 5];
+            const int gi = i & 31;
+            const uint32_t rs = rr.rs;
+            if ((rs & 0x80000000u) || !((rr.m[0] | rr.m[1] | rr.m[2] | rr.m[3]) >> gi & 1u))
+                continue;
+            const int c = (int)((rr.p0 >> gi) & 1u) | (int)(((rr.p1 >> gi) & 1u) << 1);
+            const uint32_t mask = rr.m[c];
+            const uint32_t bp = rr.bbpre[c];
+            const uint32_t rank = __popc(mask & ((1u << gi) - 1u));
+            const uint32_t rank1 = __popc(mask & ((1u << gi) - 1u) & 0xffff0000u);
+            const uint32_t slot = gi < 16 ? (bp & 0xffffu) + rank : rr.pre1[c] + rank1;
+            const uint32_t lo = rr.base + 8u * ((bp >> 16) + (rank << c));
+            const uint32_t hi = (32u * ((rs >> 8) & 0xffu) + (uint32_t)gi) | ((rs & 0xffu) << 16);
+            table[slot] = make_uint2(lo, hi);
+        }
+        wave_lds_sync();
+        // ---- next unit's metadata in flight during this unit
+        wfetch_meta(nu, a, meta);
+        // ---- every width's first batch in flight at once, then the arithmetic
+        {
+            BatchT<1> b1;
+            BatchT<2> b2;
+            BatchT<4> b4;
+            BatchT<8> b8;
+            issue_t<1>(b1, 0, st, a, table);
+            issue_t<2>(b2, 0, st, a, table);
+            issue_t<4>(b4, 0, st, a, table);
+            issue_t<8>(b8, 0, st, a, table);
+            run_width<1, MT>(b1, st, a, table, xrec, racc);
+            run_width<2, MT>(b2, st, a, table, xrec, racc);
+            run_width<4, MT>(b4, st, a, table, xrec, racc);
+            run_width<8, MT>(b8, st, a, table, xrec, racc);
+        }
+        // ---- a finished tile: row sums to y, accumulators back to zero
+        if (u.t0 + u.ns >= a.nS) {
+            wave_lds_sync();
+            const int n = st.n0 + lane;
+            if (lane < a.R) {
+#pragma unroll
+                for (int m = 0; m < MT; m++) {
+                    if (m >= a.M)
+                        continue;
+                    const float t = racc[m * kMaxRows + lane];
+                    racc[m * kMaxRows + lane] = 0.f;
+                    if (n < a.N) {
+                        if (a.yt == VBQ_F16)
+                            reinterpret_cast<__half *>(a.y)[(uint64_t)m * a.ldy + n] = __float2half_rn(t);
+                        else
+                            reinterpret_cast<float *>(a.y)[(uint64_t)m * a.ldy + n] = t;
+                    }
+                }
+            }
+            wave_lds_sync();
+        }
+        u = nu;
     }
-    if (tid == 0)
-        __hip_atomic_store(&a.tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct WavePlan {
+    bool ok;
+    int R, SG, slots, tiles;
+    size_t smem;
+};
+
+size_t wave_bytes(int MT, int slots)
+{
+    return (size_t)slots * 8 + (size_t)MT * kMaxRows * 4 + kMaxRS * sizeof(RS2);
+}
+
+WavePlan make_wave_plan(const vbq_layout *L, int MT, int cus)
+{
+    WavePlan p;
+    p.ok = false;
+    if (MT > 2)
+        return p;
+    const int G = (int)L->G, nS = (int)L->nS, N = (int)L->N;
+    const size_t xbytes = (size_t)MT * nS * 32 * kXRec * 4;
+    const size_t cap = 160 * 1024;
+    const int slots = 512;
+    int R, SG;
+    if (G <= slots && nS <= kMaxRS) {
+        SG = nS; // whole rows per unit
+        int rmax = std::min(std::min(kMaxRows, slots / G), kMaxRS / nS);
+        int total_waves = cus * kWWaves;
+        R = std::max(1, std::min(rmax, (N + total_waves - 1) / total_waves));
+    } else {
+        SG = 1; // one slice at a time
+        R = std::min(kMaxRows, slots / 32);
+    }
+    size_t smem = xbytes + (size_t)kWWaves * wave_bytes(MT, slots);
+    if (smem > cap)
+        return p;
+    p.ok = true;
+    p.R = R;
+    p.SG = SG;
+    p.slots = slots;
+    p.tiles = (N + R - 1) / R;
+    p.smem = smem;
+    return p;
 }
 
 int tokens_template(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
-size_t smem_bytes(int MT)
-{
-    size_t b = (size_t)MT * 32 * 32 * 4 + (size_t)MT * 4 * 32 * 4;
-    b += (((size_t)MT * kMaxR * kPsumStride * 4 + 7) / 8) * 8;
-    b += (size_t)kMaxR * 32 * 8;
-    return b;
-}
+struct Plan {
+    int R, SG, CHK, slots, tiles;
+    size_t smem;
+};
 
-int rows_per_tile(const vbq_layout *L, int MT)
+Plan make_plan(const vbq_layout *L, int MT)
 {
-    // Enough workgroups to fill 256 CUs several times over, larger tiles when
-    // the matrix allows (more groups per width bucket, fewer partial passes).
-    uint64_t slices = L->nS;
+    Plan p;
+    int nS = (int)L->nS;
+    p.CHK = std::min(nS, std::max(1, 16 / MT));       // x image <= 64 KiB
+    p.slots = MT <= 2 ? 1024 : MT == 4 ? 512 : 256;   // slot-table capacity
+    // tall tiles when there are enough rows to keep every CU busy
     int R = 32;
-    while (R > 8 && ((uint64_t)L->N + R - 1) / R * slices < 2048)
+    while (R > 8 && ((int64_t)L->N + R - 1) / R < 1024)
         R /= 2;
-    (void)MT;
-    return R;
+    R = std::min(R, p.slots / 32);
+    p.R = std::max(1, R);
+    p.SG = std::max(1, std::min(p.CHK, std::min(p.slots / (32 * p.R), kMaxRS / p.R)));
+    p.tiles = (int)(((int64_t)L->N + p.R - 1) / p.R);
+    size_t chg = (size_t)p.CHK * 32;
+    p.smem = (size_t)MT * chg * 32 * 4 + (size_t)MT * chg * 4 * 4 + (size_t)p.slots * 8 +
+             (size_t)MT * p.R * (p.SG * 32 + 1) * 4;
+    return p;
 }
 
 template <int MT>
-vbq_status launch(const GemvArgs &a, int tiles, hipStream_t stream)
+vbq_status launch(GemvArgs a, const Plan &p, hipStream_t stream)
 {
-    size_t sm = smem_bytes(MT);
-    static bool configured = false;
+    static int configured = 0;
+    static int cus = 0;
     if (!configured) {
         VBQ_TRY(hip_status(hipFuncSetAttribute((const void *)k_gemv<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)sm)));
-        configured = true;
+                                               96 * 1024)));
+        int dev = 0;
+        VBQ_TRY(hip_status(hipGetDevice(&dev)));
+        VBQ_TRY(hip_status(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)));
+        configured = 1;
     }
-    hipLaunchKernelGGL(k_gemv<MT>, dim3(a.nS, tiles), dim3(kThreads), sm, stream, a);
+    int per_cu = 0;
+    VBQ_TRY(hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv<MT>, kThreads,
+                                                                     p.smem)));
+    if (per_cu < 1)
+        return VBQ_ERR_SHAPE;
+    int grid = std::min(p.tiles, per_cu * cus);
+    a.R = p.R;
+    a.SG = p.SG;
+    a.CHK = p.CHK;
+    a.tiles = p.tiles;
+    a.slots = p.slots;
+    hipLaunchKernelGGL(k_gemv<MT>, dim3(grid), dim3(kThreads), p.smem, stream, a);
     return launch_status();
 }
 
-uint64_t partial_bytes(const vbq_layout *L, int M) { return L->nS > 1 ? 4ull * L->nS * (uint64_t)M * L->N : 0; }
 
-// One counter per row tile, sized for the smallest tile height (8 rows).
-uint64_t ticket_bytes(const vbq_layout *L) { return align_up(4 * (((uint64_t)L->N + 7) / 8), 256); }
+template <int MT>
+vbq_status launch_wave(GemvArgs a, const WavePlan &p, int cus, hipStream_t stream)
+{
+    static int configured = 0;
+    if (!configured) {
+        VBQ_TRY(hip_status(hipFuncSetAttribute((const void *)k_gemv_wave<MT>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)));
+        configured = 1;
+    }
+    int per_cu = 0;
+    VBQ_TRY(hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv_wave<MT>,
+                                                                     kWThreads, p.smem)));
+    if (per_cu < 1)
+        return VBQ_ERR_SHAPE;
+    int grid = std::min(per_cu * cus, (p.tiles + kWWaves - 1) / kWWaves);
+    a.R = p.R;
+    a.SG = p.SG;
+    a.CHK = (int)a.nS;
+    a.tiles = p.tiles;
+    a.slots = p.slots;
+    hipLaunchKernelGGL(k_gemv_wave<MT>, dim3(grid), dim3(kWThreads), p.smem, stream, a);
+    return launch_status();
+}
+
+int device_cus()
+{
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 256;
+    }
+    return cus;
+}
 
 } // namespace
 
@@ -432,19 +1100,15 @@ vbq_status vbq_workspace_size(const vbq_layout *L, int M, size_t *bytes)
     VBQ_TRY(check_layout(L));
     if (M < 1 || M > 16)
         return VBQ_ERR_BATCH;
-    if (L->nS <= 1) {
-        *bytes = 0;
-        return VBQ_OK;
-    }
-    // [tickets | partials]: the tickets come first, at an offset that does not
-    // depend on M, so one cleared workspace serves every M up to its size.
-    *bytes = (size_t)(ticket_bytes(L) + align_up(partial_bytes(L, M), 256));
+    *bytes = 0; // rows are never split across workgroups
     return VBQ_OK;
 }
 
 vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const uint16_t *x, int ldx, void *y, int ldy,
                             vbq_dtype yt, void *ws, size_t ws_bytes, hipStream_t stream)
 {
+    (void)ws;
+    (void)ws_bytes;
     if (!blob || !x || !y)
         return VBQ_ERR_INVALID_ARG;
     if (yt != VBQ_F32 && yt != VBQ_F16)
@@ -456,16 +1120,10 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
         return VBQ_ERR_SHAPE;
     if ((uintptr_t)blob % 256 || (uintptr_t)x % 2 || (uintptr_t)y % (yt == VBQ_F32 ? 4 : 2))
         return VBQ_ERR_ALIGN;
-    size_t need = 0;
-    VBQ_TRY(vbq_workspace_size(L, M, &need));
-    if (need && (!ws || ws_bytes < need))
-        return VBQ_ERR_WORKSPACE;
-    if (need && (uintptr_t)ws % 256)
-        return VBQ_ERR_ALIGN;
-
     int MT = tokens_template(M);
-    int R = rows_per_tile(L, MT);
-    int tiles = (int)(((uint64_t)L->N + R - 1) / R);
+    const int cus = device_cus();
+    WavePlan wp = make_wave_plan(L, MT, cus);
+    Plan p = make_plan(L, MT);
     GemvArgs a;
     a.blob = (const uint8_t *)blob;
     a.off_row_off = L->off_row_off;
@@ -483,15 +1141,14 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
     a.y = y;
     a.ldy = ldy;
     a.yt = (int)yt;
-    a.tickets = need ? (uint32_t *)ws : nullptr;
-    a.partial = need ? (float *)((uint8_t *)ws + ticket_bytes(L)) : nullptr;
-    a.R = R;
+    if (wp.ok)
+        return MT == 1 ? launch_wave<1>(a, wp, cus, stream) : launch_wave<2>(a, wp, cus, stream);
     switch (MT) {
-    case 1: return launch<1>(a, tiles, stream);
-    case 2: return launch<2>(a, tiles, stream);
-    case 4: return launch<4>(a, tiles, stream);
-    case 8: return launch<8>(a, tiles, stream);
-    default: return launch<16>(a, tiles, stream);
+    case 1: return launch<1>(a, p, stream);
+    case 2: return launch<2>(a, p, stream);
+    case 4: return launch<4>(a, p, stream);
+    case 8: return launch<8>(a, p, stream);
+    default: return launch<16>(a, p, stream);
     }
 }
 

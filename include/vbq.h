@@ -137,12 +137,10 @@ vbq_status vbq_status_check(const uint32_t *status_word, uint32_t *raw /* host *
 vbq_status vbq_dequant(const vbq_layout *L /* host */, const void *blob, void *w, vbq_dtype wt, hipStream_t stream);
 
 /*
- * Workspace bytes vbq_gemv / vbq_gemv_batched need for layout L and M tokens
- * (0 when K <= 2048, i.e. a single K-slice).  The workspace holds per-tile
- * counters (first, at a fixed offset) and split-K partial sums; it must be
- * zero-filled once before its first use (vbq_workspace_clear), and every GEMV
- * leaves the counters at zero again, so it can be reused without clearing.
- * A workspace sized for M tokens serves every call with M' <= M tokens.
+ * Workspace bytes vbq_gemv / vbq_gemv_batched need for layout L and M tokens.
+ * This version never splits a row across workgroups and needs none (0): the
+ * ws arguments of the GEMV calls may be NULL / 0.  The query and the clear
+ * call stay so that callers are ready for shapes that would need one.
  */
 vbq_status vbq_workspace_size(const vbq_layout *L /* host */, int M, size_t *bytes /* host */);
 

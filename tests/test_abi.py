@@ -88,8 +88,9 @@ def test_gemv_argument_checks_fail_before_launch():
     null = P(0)
     ref = ctypes.byref(L)
     sz = ctypes.c_size_t(0)
-    assert lib.vbq_workspace_size(ref, 1, ctypes.byref(sz)) == 0 and sz.value > 0
-    need = sz.value
+    assert lib.vbq_workspace_size(ref, 16, ctypes.byref(sz)) == 0
+    need = sz.value  # rows are never split across workgroups: no workspace
+    assert need == 0
 
     def call(M=1, blob=fake, x=fake, ldx=4096, y=fake, ldy=4, yt=1, ws=fake, wsb=None):
         return v.STATUS[lib.vbq_gemv_batched(ref, blob, M, x, ldx, y, ldy, yt, ws, need if wsb is None else wsb, null)]
@@ -102,8 +103,6 @@ def test_gemv_argument_checks_fail_before_launch():
     assert call(ldx=4095) == "VBQ_ERR_SHAPE"
     assert call(ldy=3) == "VBQ_ERR_SHAPE"
     assert call(blob=odd) == "VBQ_ERR_ALIGN"
-    assert call(ws=null) == "VBQ_ERR_WORKSPACE"
-    assert call(wsb=need - 1) == "VBQ_ERR_WORKSPACE"
     bad = v.Layout.from_buffer_copy(bytes(L))
     bad.magic = 0
     assert v.STATUS[lib.vbq_gemv(ctypes.byref(bad), fake, fake, fake, 1, fake, need, null)] == "VBQ_ERR_LAYOUT"
@@ -116,7 +115,3 @@ def test_gemv_argument_checks_fail_before_launch():
     assert v.STATUS[lib.vbq_pack_plan(4, 128, fake, ctypes.byref(v.Layout()), fake, 8, null)] == "VBQ_ERR_WORKSPACE"
     assert v.STATUS[lib.vbq_pack(ref, null, fake, fake, fake, fake, null)] == "VBQ_ERR_INVALID_ARG"
     assert v.STATUS[lib.vbq_workspace_size(ref, 0, ctypes.byref(sz))] == "VBQ_ERR_BATCH"
-    # single-slice matrices need no workspace
-    blob1 = oracle.pack(np.zeros((2, 2048), np.uint8), np.ones((2, 32), np.uint8), np.ones((2, 32), np.uint16))
-    L1 = v.layout_from_header(blob1[:256].tobytes())
-    assert v.workspace_size(L1, 16) == 0
