@@ -555,9 +555,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a)
 // the LDS bank groups of consecutive groups without any address swizzle, so
 // every LDS read of a slot uses one base address plus constant offsets.
 
-constexpr int kWThreads = 512;
+constexpr int kWThreads = 1024;
 constexpr int kWWaves = kWThreads / 64;
-constexpr int kXRec = 36; // dwords per x record
+constexpr int kXRec = 36;   // dwords per x record
+constexpr int kMaxRSW = 32; // row-slices per wave unit
 
 // passes per batch for width code c (16 code words per lane)
 __host__ __device__ constexpr int batch_passes(int c) { return c == 0 ? 8 : c == 1 ? 4 : c == 2 ? 2 : 1; }
@@ -570,17 +571,28 @@ struct WMeta {
     uint32_t p0, p1, row_off, slice_off; // lane = row-slice of the unit
 };
 
-// Row-slice record of the current unit (48 bytes, lane-owned while built).
+// Row-slice record of the current unit (64 bytes).  Built by the lane that
+// owns the row-slice, read back by the 32 lanes that own its groups.
 struct RS2 {
-    uint32_t p0, p1;
-    uint32_t m[4];     // groups of width code c
-    uint32_t base;     // record start, bytes from the unit's first code byte
-    uint32_t rs;       // row | slice << 8
-    uint32_t bbpre[4]; // slot base of (width c, groups 0..15) (low 16) | bucket start, 8-byte units (high 16)
-    uint32_t pre1[4];  // slot base of (width c, groups 16..31)
+    uint32_t p0, p1, base, rs;   // planes; record start from the unit's first code byte; row | slice << 8 | ng << 16
+    uint32_t m[4];               // groups of width code c
+    uint32_t bbpre[4];           // slot base of (width c, groups 0..15) | bucket start in 8-byte units << 16
+    uint32_t pre1[4];            // slot base of (width c, groups 16..31)
 };
 
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row broadcasts.
+__device__ __forceinline__ int wave_scan_incl(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31
+    return v;
+}
 
 __device__ __forceinline__ WUnit wunit_next(WUnit u, const GemvArgs &a, int tw)
 {
@@ -594,8 +606,7 @@ __device__ __forceinline__ WUnit wunit_next(WUnit u, const GemvArgs &a, int tw)
     return u;
 }
 
-// lane = row-slice l = r * ns + s (ns is 1 or the whole row, so no division
-// is needed: the host makes SG either 1 or nS and passes its row-slice map)
+// lane = row-slice l = r * ns + s
 __device__ __forceinline__ void wfetch_meta(const WUnit &u, const GemvArgs &a, WMeta &m)
 {
     const int lane = threadIdx.x & 63;
@@ -618,7 +629,7 @@ __device__ __forceinline__ void wfetch_meta(const WUnit &u, const GemvArgs &a, W
 }
 
 struct WState { // wave-uniform bookkeeping of the current unit
-    int total[4], tbase[4], n0, t0;
+    int total[4], tbase[4], n0, t0, ns;
     const uint8_t *codes;   // first code byte of the unit
     const uint16_t *scales; // scale of (row n0, group 32*t0)
 };
@@ -646,11 +657,9 @@ __device__ __forceinline__ void issue_t(BatchT<B> &bt, int first, const WState &
     }
 #pragma unroll
     for (int j = 0; j < BP; j++) {
-        uint32_t hi = 0xffffffffu, sc = 0;
+        uint32_t sc = 0;
         if (ent[j].y != 0xffffffffu) {
-            const uint2 e = ent[j];
-            hi = e.y;
-            const uint8_t *src = st.codes + e.x;
+            const uint8_t *src = st.codes + ent[j].x;
             if constexpr (B == 1) {
                 U2 v = *reinterpret_cast<const U2 *>(src);
                 bt.w[2 * j] = v.v[0];
@@ -664,27 +673,28 @@ __device__ __forceinline__ void issue_t(BatchT<B> &bt, int first, const WState &
                         bt.w[2 * B * j + 4 * k + q] = v.v[q];
                 }
             }
-            const uint32_t r = hi >> 16, gl = hi & 0xffffu;
+            const uint32_t r = ent[j].y >> 16, gl = ent[j].y & 0xffffu;
             sc = st.scales[r * (uint32_t)a.G + gl];
         }
-        bt.hi[j] = hi;
+        bt.hi[j] = ent[j].y;
         bt.sc[j] = sc;
     }
 }
 
 template <int B, int MT>
-__device__ __forceinline__ void compute_t(const BatchT<B> &bt, const WState &st, const GemvArgs &a,
-                                          const uint32_t *xrec, float *racc)
+__device__ __forceinline__ void compute_t(const BatchT<B> &bt, int first, const WState &st, const GemvArgs &a,
+                                          const uint32_t *xrec, float *psum)
 {
     constexpr int C = BatchT<B>::C, BP = BatchT<B>::BP;
     const uint32_t CHG = (uint32_t)a.nS * 32;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int j = 0; j < BP; j++) {
         if (bt.hi[j] == 0xffffffffu)
             continue;
         uint32_t h[32];
         unpack_pairs<B>(&bt.w[2 * B * j], h);
-        const uint32_t r = bt.hi[j] >> 16, gl = bt.hi[j] & 0xffffu;
+        const uint32_t gl = bt.hi[j] & 0xffffu;
         const float s = __half2float(__ushort_as_half((unsigned short)bt.sc[j]));
 #pragma unroll
         for (int m = 0; m < MT; m++) {
@@ -705,25 +715,25 @@ __device__ __forceinline__ void compute_t(const BatchT<B> &bt, const WState &st,
                     acc1 = dot2(h[4 * k + 7], xb.v[3], acc1);
                 }
                 const float Cc = __uint_as_float(xr[32 + C]);
-                __hip_atomic_fetch_add(&racc[m * kMaxRows + r], s * ((acc0 + acc1) - Cc), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
+                // partial of (row-slice, group) in natural group order: distinct
+                // addresses, no atomics, and row-slice sums read 32 contiguous floats
+                psum[m * a.slots + (bt.hi[j] >> 16) * (uint32_t)st.ns * 32u + gl] = s * ((acc0 + acc1) - Cc);
             }
         }
     }
 }
 
+// All passes of width B, one register batch at a time.
 template <int B, int MT>
-__device__ __forceinline__ void run_width(BatchT<B> &bt, const WState &st, const GemvArgs &a, const uint2 *table,
-                                          const uint32_t *xrec, float *racc)
+__device__ __forceinline__ void run_width(const WState &st, const GemvArgs &a, const uint2 *table,
+                                          const uint32_t *xrec, float *psum)
 {
     constexpr int C = BatchT<B>::C, BP = BatchT<B>::BP;
     const int np = (st.total[C] + 63) / 64;
-    if (np == 0)
-        return;
-    compute_t<B, MT>(bt, st, a, xrec, racc);
-    for (int f = BP; f < np; f += BP) { // overflow batches (wide mixes)
+    for (int f = 0; f < np; f += BP) {
+        BatchT<B> bt;
         issue_t<B>(bt, f, st, a, table);
-        compute_t<B, MT>(bt, st, a, xrec, racc);
+        compute_t<B, MT>(bt, f, st, a, xrec, psum);
     }
 }
 
@@ -733,7 +743,7 @@ __device__ void stage_xrec(const GemvArgs &a, uint32_t *xrec)
 {
     const int tid = threadIdx.x;
     const int CHG = a.nS * 32;
-    const bool vec = (a.ldx % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
+    const bool vec = (a.ldx % 4) == 0 && ((uintptr_t)a.x % 8) == 0;
     // 4 pairs per item: x[p..p+3] with x[p+32..p+35]
     for (int i = tid; i < a.M * a.G * 8; i += kWThreads) {
         int q = i & 7, g = (i >> 3) % a.G, m = (i >> 3) / a.G;
@@ -803,11 +813,12 @@ __global__ __launch_bounds__(kWThreads) void k_gemv_wave(GemvArgs a)
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const size_t xbytes = (size_t)MT * a.nS * 32 * kXRec * 4;
-    const size_t wbytes = (size_t)a.slots * 8 + MT * kMaxRows * 4 + kMaxRS * sizeof(RS2);
+    const size_t wbytes = (size_t)a.slots * 8 + (size_t)MT * a.slots * 4 + MT * kMaxRows * 4 + kMaxRSW * sizeof(RS2);
     uint32_t *xrec = reinterpret_cast<uint32_t *>(smem);
     uint8_t *wmem = smem + xbytes + wave * wbytes;
     uint2 *table = reinterpret_cast<uint2 *>(wmem);
-    float *racc = reinterpret_cast<float *>(table + a.slots);
+    float *psum = reinterpret_cast<float *>(table + a.slots);
+    float *racc = psum + MT * a.slots;
     RS2 *rsl = reinterpret_cast<RS2 *>(racc + MT * kMaxRows);
     const uint8_t *codes = a.blob + a.off_codes;
     const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.blob + a.off_scales);
@@ -831,6 +842,7 @@ __global__ __launch_bounds__(kWThreads) void k_gemv_wave(GemvArgs a)
         WState st;
         st.n0 = u.tile * a.R;
         st.t0 = u.t0;
+        st.ns = u.ns;
         const int nrs = a.R * u.ns;
         // ---- row-slice records and slot prefix sums (lane = row-slice)
         {
@@ -851,18 +863,8 @@ __global__ __launch_bounds__(kWThreads) void k_gemv_wave(GemvArgs a)
             for (int c = 0; c < 4; c++) {
                 cnt[c] = live ? __popc(wm.m[c]) : 0;
                 c0[c] = live ? __popc(wm.m[c] & 0xffffu) : 0;
-                int v0 = c0[c], v1 = cnt[c] - c0[c];
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    int t0 = __shfl_up(v0, off, 64);
-                    int t1 = __shfl_up(v1, off, 64);
-                    if (lane >= off) {
-                        v0 += t0;
-                        v1 += t1;
-                    }
-                }
-                incl0[c] = v0;
-                incl1[c] = v1;
+                incl0[c] = wave_scan_incl(c0[c]);
+                incl1[c] = wave_scan_incl(cnt[c] - c0[c]);
             }
             int tb = 0;
 #pragma unroll
@@ -876,11 +878,11 @@ __global__ __launch_bounds__(kWThreads) void k_gemv_wave(GemvArgs a)
                 RS2 rr;
                 rr.p0 = live ? meta.p0 : 0u;
                 rr.p1 = live ? meta.p1 : 0u;
+                rr.base = (uint32_t)(start - ubase);
+                rr.rs = (uint32_t)r | ((uint32_t)s << 8) | (live ? 0u : 0x80000000u);
 #pragma unroll
                 for (int c = 0; c < 4; c++)
                     rr.m[c] = live ? wm.m[c] : 0u;
-                rr.base = (uint32_t)(start - ubase);
-                rr.rs = (uint32_t)r | ((uint32_t)s << 8) | (live ? 0u : 0x80000000u);
                 int bb = 0;
 #pragma unroll
                 for (int c = 0; c < 4; c++) {
@@ -894,41 +896,73 @@ __global__ __launch_bounds__(kWThreads) void k_gemv_wave(GemvArgs a)
             st.scales = scales + (uint64_t)st.n0 * a.G + 32 * u.t0;
         }
         wave_lds_sync();
-        // ---- slot table: one entry per group, width-major then row-slice then g
-        const int nitems = nrs * 32;
-        for (int i = lane; i < nitems; i += 64) {
-            const RS2 &rr = rsl[i >> 5];
-            const int gi = i & 31;
-            const uint32_t rs = rr.rs;
-            if ((rs & 0x80000000u) || !((rr.m[0] | rr.m[1] | rr.m[2] | rr.m[3]) >> gi & 1u))
-                continue;
-            const int c = (int)((rr.p0 >> gi) & 1u) | (int)(((rr.p1 >> gi) & 1u) << 1);
-            const uint32_t mask = rr.m[c];
-            const uint32_t bp = rr.bbpre[c];
-            const uint32_t rank = __popc(mask & ((1u << gi) - 1u));
-            const uint32_t rank1 = __popc(mask & ((1u << gi) - 1u) & 0xffff0000u);
-            const uint32_t slot = gi < 16 ? (bp & 0xffffu) + rank : rr.pre1[c] + rank1;
-            const uint32_t lo = rr.base + 8u * ((bp >> 16) + (rank << c));
-            const uint32_t hi = (32u * ((rs >> 8) & 0xffu) + (uint32_t)gi) | ((rs & 0xffu) << 16);
-            table[slot] = make_uint2(lo, hi);
+        // ---- slot table: item i -> row-slice i/32 (shared by a half-wave: broadcast
+        // LDS reads), group i%32; all reads of an item are independent of its width
+        {
+            const int gi = lane & 31;
+            const uint32_t lt = (1u << gi) - 1u;
+            for (int k = 0; k < nrs; k += 2) {
+                const int l = k + (lane >> 5);
+                if (l >= nrs)
+                    continue;
+                const RS2 rr = rsl[l];
+                const bool ok = !(rr.rs & 0x80000000u) && ((rr.m[0] | rr.m[1] | rr.m[2] | rr.m[3]) >> gi & 1u);
+                if (!ok)
+                    continue;
+                const int c = (int)((rr.p0 >> gi) & 1u) | (int)(((rr.p1 >> gi) & 1u) << 1);
+                const uint32_t mask = pick4(rr.m, c);
+                const uint32_t bp = pick4(rr.bbpre, c);
+                const uint32_t p1 = pick4(rr.pre1, c);
+                const uint32_t rank = __popc(mask & lt);
+                const uint32_t slot = gi < 16 ? (bp & 0xffffu) + rank : p1 + __popc(mask & lt & 0xffff0000u);
+                const uint32_t lo = rr.base + 8u * ((bp >> 16) + (rank << c));
+                const uint32_t hi = (32u * ((rr.rs >> 8) & 0xffu) + (uint32_t)gi) | ((rr.rs & 0xffu) << 16);
+                table[slot] = make_uint2(lo, hi);
+            }
         }
         wave_lds_sync();
         // ---- next unit's metadata in flight during this unit
         wfetch_meta(nu, a, meta);
-        // ---- every width's first batch in flight at once, then the arithmetic
-        {
-            BatchT<1> b1;
-            BatchT<2> b2;
-            BatchT<4> b4;
-            BatchT<8> b8;
-            issue_t<1>(b1, 0, st, a, table);
-            issue_t<2>(b2, 0, st, a, table);
-            issue_t<4>(b4, 0, st, a, table);
-            issue_t<8>(b8, 0, st, a, table);
-            run_width<1, MT>(b1, st, a, table, xrec, racc);
-            run_width<2, MT>(b2, st, a, table, xrec, racc);
-            run_width<4, MT>(b4, st, a, table, xrec, racc);
-            run_width<8, MT>(b8, st, a, table, xrec, racc);
+        // ---- widths one after the other, one register batch at a time
+        run_width<1, MT>(st, a, table, xrec, psum);
+        run_width<2, MT>(st, a, table, xrec, psum);
+        run_width<4, MT>(st, a, table, xrec, psum);
+        run_width<8, MT>(st, a, table, xrec, psum);
+        wave_lds_sync();
+        // ---- per row-slice: its groups' partials in natural order; then per
+        // row over its row-slices
+        if (lane < nrs) {
+            const int sl = lane - (u.ns == 1 ? lane : lane / u.ns) * u.ns;
+            const int ng = max(0, min(32, a.G - 32 * (u.t0 + sl)));
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+                if (m >= a.M)
+                    continue;
+                const float4 *ps = reinterpret_cast<const float4 *>(psum + m * a.slots + lane * 32);
+                float v = 0.f;
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    const float4 q = ps[k];
+                    v += 4 * k + 0 < ng ? q.x : 0.f;
+                    v += 4 * k + 1 < ng ? q.y : 0.f;
+                    v += 4 * k + 2 < ng ? q.z : 0.f;
+                    v += 4 * k + 3 < ng ? q.w : 0.f;
+                }
+                reinterpret_cast<float *>(table)[m * kMaxRSW + lane] = v; // table is free now
+            }
+        }
+        wave_lds_sync();
+        if (lane < a.R) {
+            const float *rsum = reinterpret_cast<const float *>(table);
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+                if (m >= a.M)
+                    continue;
+                float v = racc[m * kMaxRows + lane];
+                for (int sl = 0; sl < u.ns; sl++)
+                    v += rsum[m * kMaxRSW + lane * u.ns + sl];
+                racc[m * kMaxRows + lane] = v;
+            }
         }
         // ---- a finished tile: row sums to y, accumulators back to zero
         if (u.t0 + u.ns >= a.nS) {
@@ -949,8 +983,8 @@ __global__ __launch_bounds__(kWThreads) void k_gemv_wave(GemvArgs a)
                     }
                 }
             }
-            wave_lds_sync();
         }
+        wave_lds_sync();
         u = nu;
     }
 }
@@ -963,7 +997,7 @@ struct WavePlan {
 
 size_t wave_bytes(int MT, int slots)
 {
-    return (size_t)slots * 8 + (size_t)MT * kMaxRows * 4 + kMaxRS * sizeof(RS2);
+    return (size_t)slots * 8 + (size_t)MT * slots * 4 + (size_t)MT * kMaxRows * 4 + kMaxRSW * sizeof(RS2);
 }
 
 WavePlan make_wave_plan(const vbq_layout *L, int MT, int cus)
@@ -975,26 +1009,28 @@ WavePlan make_wave_plan(const vbq_layout *L, int MT, int cus)
     const int G = (int)L->G, nS = (int)L->nS, N = (int)L->N;
     const size_t xbytes = (size_t)MT * nS * 32 * kXRec * 4;
     const size_t cap = 160 * 1024;
-    const int slots = 512;
-    int R, SG;
-    if (G <= slots && nS <= kMaxRS) {
-        SG = nS; // whole rows per unit
-        int rmax = std::min(std::min(kMaxRows, slots / G), kMaxRS / nS);
-        int total_waves = cus * kWWaves;
-        R = std::max(1, std::min(rmax, (N + total_waves - 1) / total_waves));
-    } else {
-        SG = 1; // one slice at a time
-        R = std::min(kMaxRows, slots / 32);
-    }
-    size_t smem = xbytes + (size_t)kWWaves * wave_bytes(MT, slots);
-    if (smem > cap)
+    for (int slots : {512, 256}) {
+        int R, SG;
+        if (G <= slots && nS <= kMaxRSW) {
+            SG = nS; // whole rows per unit
+            int rmax = std::min(std::min(kMaxRows, slots / G), kMaxRSW / nS);
+            int total_waves = cus * kWWaves;
+            R = std::max(1, std::min(rmax, (N + total_waves - 1) / total_waves));
+        } else {
+            SG = 1; // one slice at a time
+            R = std::min(kMaxRSW, slots / 32);
+        }
+        size_t smem = xbytes + (size_t)kWWaves * wave_bytes(MT, slots);
+        if (smem > cap)
+            continue;
+        p.ok = true;
+        p.R = R;
+        p.SG = SG;
+        p.slots = slots;
+        p.tiles = (N + R - 1) / R;
+        p.smem = smem;
         return p;
-    p.ok = true;
-    p.R = R;
-    p.SG = SG;
-    p.slots = slots;
-    p.tiles = (N + R - 1) / R;
-    p.smem = smem;
+    }
     return p;
 }
 
