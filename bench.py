@@ -53,6 +53,20 @@ def time_steps(torch, fn, steps):
     return a.elapsed_time(b) / steps  # ms per step
 
 
+def sleep_cycles(torch, seconds):
+    """Device-clock cycles of torch's bounded sleep kernel that last about `seconds`."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cyc = 1_000_000
+    torch.cuda._sleep(cyc)  # warm up
+    torch.cuda.synchronize()
+    a.record()
+    torch.cuda._sleep(cyc)
+    b.record()
+    torch.cuda.synchronize()
+    per_s = cyc / max(a.elapsed_time(b) * 1e-3, 1e-6)
+    return int(per_s * seconds)
+
+
 def cpu_baseline(step, budget_s):
     """The oracle (plain C, one thread) on a bounded row sample of every matrix of
     the step, scaled by N / rows to a whole step."""
@@ -97,6 +111,7 @@ def main(argv=None):
     import torch
 
     import decode_gemv_vbq_amd as v
+    from decode_gemv_vbq_amd import accounting as acc
     from decode_gemv_vbq_amd.step import DecodeStep
 
     v.lib()
@@ -117,18 +132,39 @@ def main(argv=None):
     ms = time_steps(torch, fn, args.steps)
     log(f"step: {ms * 1e3:.1f} us ({args.mode}), {alg / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
 
-    # per-launch kernel durations (events on the launch stream, eager launches)
+    # per-launch kernel durations: events on the launch stream around every
+    # launch, all launches queued behind a bounded device sleep so they run back
+    # to back (the host enqueues far slower than the GPU executes)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step.run_timed_kernels()
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - t0
+    hold = sleep_cycles(torch, 2.0 * host_s + 0.005)
+    per_kind = {}
     kern_ms = 0.0
     for _ in range(args.kernel_steps):
-        ev = step.run_timed_kernels()
+        ev = step.run_timed_kernels(hold_cycles=hold)
         torch.cuda.synchronize()
-        kern_ms += sum(a.elapsed_time(b) for a, b in ev)
+        for m, (a, b) in zip(step.mats, ev):
+            t = a.elapsed_time(b)
+            kern_ms += t
+            k = per_kind.setdefault(m.spec.name, [0.0, 0, 0])
+            k[0] += t
+            k[1] += 1
     kern_ms /= args.kernel_steps
+    for m in step.mats:
+        per_kind[m.spec.name][2] += acc.vbq_read_bytes(m.L, step.M)
+    kinds = {}
+    for name, (t, n, bts) in per_kind.items():
+        cnt = n // args.kernel_steps
+        kinds[name] = {"launches": cnt, "us": round(1e3 * t / n, 2),
+                       "GBps": round((bts / cnt) / (t / n * 1e-3) / 1e9, 1)}
     avg_launch_s = kern_ms * 1e-3 / n_launch
     alg_per_launch = alg / n_launch
     achieved = alg_per_launch / avg_launch_s
-    log(f"kernels: {kern_ms * 1e3:.1f} us summed, {avg_launch_s * 1e6:.2f} us/launch avg, {achieved / 1e9:.0f} GB/s")
+    log(f"kernels: {kern_ms * 1e3:.1f} us summed, {avg_launch_s * 1e6:.2f} us/launch avg, {achieved / 1e9:.0f} GB/s; "
+        + ", ".join(f"{k} {d['us']} us {d['GBps']} GB/s" for k, d in kinds.items()))
 
     control = None
     if not args.no_control:
@@ -179,8 +215,8 @@ def main(argv=None):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4), "traffic": None,
-            "kernel": "k_gemv<1> (vbq_gemv)", "alg_bytes_per_launch": round(alg_per_launch),
-            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "kernel": "k_gemv_wave<1> (vbq_gemv)", "alg_bytes_per_launch": round(alg_per_launch),
+            "avg_launch_us": round(avg_launch_s * 1e6, 3), "per_matrix": kinds,
         },
         "cpu_baseline": cpu,
     }

@@ -36,13 +36,13 @@ def build(asm_dir: str | None = None, verbose: bool = False) -> str:
     extra = []
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
-        extra = ["-save-temps=obj"]
+        extra = ["-save-temps"]
     cmd = command(tmp, extra)
     if verbose:
         print(" ".join(cmd), flush=True)
     cwd = asm_dir or None
     if asm_dir:
-        # -save-temps=obj writes next to the object path; build from the asm dir
+        # -save-temps writes the intermediates into the working directory
         cmd = [c for c in cmd]
     subprocess.check_call(cmd, cwd=cwd)
     os.replace(tmp, LIB)

@@ -22,6 +22,23 @@ vbq_status zero_words(void *p, uint64_t bytes, hipStream_t stream);
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
+// One GEMV request after host-side validation.
+struct GemvCall {
+    const vbq_layout *L;
+    const void *blob;
+    int M;
+    const uint16_t *x;
+    int ldx;
+    void *y;
+    int ldy;
+    vbq_dtype yt;
+    hipStream_t stream;
+};
+
+// Launches the streaming kernel when it applies (M <= 2 and every row record
+// fits one LDS sub-unit); returns false, launching nothing, when it does not.
+bool stream_gemv(const GemvCall &g, vbq_status *st);
+
 } // namespace vbq
 
 #define VBQ_TRY(expr)                                                                                                 \

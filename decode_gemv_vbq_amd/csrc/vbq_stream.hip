@@ -1,0 +1,668 @@
+// Streaming GEMV over the VBQ1 layout for M = 1..2 tokens (gfx950).
+//
+// The decode path of "Variable Bit-width Quantization" (mlsanity.com page,
+// Abstract): every contiguous group of 64 weights carries its own width in
+// {1,2,4,8} and a scale, and decode multiplies by the dequantized weights
+// without materialising them.  Decode is bound by HBM bandwidth, so this
+// kernel is organised around one continuous stream of packed bytes per CU:
+//
+//  * One 1024-thread workgroup per CU owns a contiguous block of rows.  Its
+//    rows' metadata (row offsets, slice offsets, width bit planes) and the
+//    activations are read once at the start; x is kept in LDS as fp16 pairs
+//    (x_p, x_{p+32}) per group plus four per-width correction constants.
+//  * The block is cut into sub-units of whole rows holding at most 32 KiB of
+//    code bytes (less when K is long).  A sub-unit's code bytes and scales are
+//    contiguous in HBM, so they are copied straight into a two-slot LDS ring
+//    with global_load_lds_dwordx4 (1 KiB per wave instruction, no VGPRs) while
+//    the previous sub-unit computes: HBM sees a steady stream.
+//  * Inside a sub-unit the groups are listed per width in a slot table, so a
+//    wavefront always runs 64 groups of ONE width (no divergence between the
+//    1/2/4/8-bit paths); the 16 waves take passes from an LDS counter.
+//    Slots of a width are ordered (group half, row-slice, rank): a 16-lane LDS
+//    phase then reads x records of equal groups or of distinct groups within
+//    a 16-group window, which sit in distinct bank groups.
+//  * Lane = one group: code words from LDS become fp16 pairs 2^(10-pos) + q
+//    with one v_and_or_b32 each (8-bit: v_perm_b32), v_dot2_f32_f16 multiplies
+//    two weights per instruction into fp32, and the group result is
+//        s * (acc - C_b(g)),  C_b(g) = sum_p magic_p (x_p + x_{p+32}) + (2^b-1)/2 sum_j x_j.
+//  * Partials land in LDS in natural (row, group) order and each row is
+//    summed by 16 lanes in a fixed order: results do not depend on timing.
+#include <algorithm>
+
+#include "vbq_common.h"
+#include "vbq_host.h"
+#include "vbq_unpack.h"
+
+using namespace vbq;
+
+namespace {
+
+constexpr int kT = 1024;                  // threads per workgroup (one per CU)
+constexpr int kW = kT / 64;               // waves per workgroup
+constexpr int kMaxCap = 32768;            // code bytes of one sub-unit, at most
+constexpr int kMaxRS = 128;               // row-slices of one sub-unit
+constexpr int kRing = 2;                  // sub-units resident: one computing, one in flight
+constexpr int kMaxSlots = kMaxRS * 32 + 4 * 64;   // slot table incl. per-width pass padding
+constexpr int kMetaRS = 1024;             // row-slices of metadata per workgroup
+constexpr int kXRec = 36;                 // dwords per x record: 32 pairs + 4 constants
+constexpr int kInfo = 16;                 // dwords per row-slice descriptor
+constexpr int kPsum = kMaxRS * 32;        // partials per token
+
+// Scale bytes of a sub-unit (+ 16-byte alignment slack), and its ring slot.
+__host__ __device__ constexpr uint32_t scale_area(int cap) { return (uint32_t)(cap / 4 + 128); }
+__host__ __device__ constexpr uint32_t slot_bytes(int cap) { return (uint32_t)cap + scale_area(cap); }
+
+struct SArgs {
+    const uint8_t *blob;
+    uint64_t off_row_off, off_slice_off, off_wmap, off_scales, off_codes;
+    int N, G, nS, M;
+    const uint16_t *x;
+    int ldx;
+    void *y;
+    int ldy, yt;
+    int rows;   // rows per workgroup
+    int cap;    // code bytes per sub-unit (multiple of 1024, <= kMaxCap)
+    int inv_nS; // ceil(65536 / nS): i / nS == (i * inv_nS) >> 16 for i < kMaxRS
+};
+
+// LDS carve-up, computed identically on the host (size) and the device.
+struct SLayout {
+    uint32_t x, rowoff, sloff, wmap, ring, info, hdr, table, psum, total;
+};
+
+__host__ __device__ inline uint32_t s_take(uint32_t &o, uint32_t bytes)
+{
+    uint32_t r = o;
+    o += (bytes + 15u) & ~15u;
+    return r;
+}
+
+__host__ __device__ inline SLayout s_layout(int MT, int G, int rows, int nS, int cap)
+{
+    SLayout l;
+    uint32_t o = 0;
+    l.x = s_take(o, (uint32_t)(MT * G * kXRec * 4));
+    l.rowoff = s_take(o, (uint32_t)((rows + 1) * 4));
+    l.sloff = s_take(o, (uint32_t)(rows * nS * 4));
+    l.wmap = s_take(o, (uint32_t)(rows * nS * 8));
+    l.ring = s_take(o, kRing * slot_bytes(cap));
+    l.info = s_take(o, (uint32_t)(2 * kMaxRS * kInfo * 4));
+    l.hdr = s_take(o, 2 * 16 * 4);
+    l.table = s_take(o, kMaxSlots * 4);
+    l.psum = s_take(o, (uint32_t)(MT * kPsum * 4));
+    l.total = o;
+    return l;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (m0 = lds_base, wave-uniform).  Written as asm so the compiler does not tie
+// every later LDS read to it with a full vmcnt wait: completion is awaited
+// explicitly (wait_vm) before the barrier that publishes a sub-unit.  The
+// leading s_nop separates the compiler's m0 write from the LDS-DMA load.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a run-time n (clamped: a smaller n only waits longer).
+__device__ __forceinline__ void wait_vm(int n)
+{
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    }
+}
+
+// Inclusive prefix sum over the 64 lanes (DPP row shifts and row broadcasts).
+__device__ __forceinline__ int scan64(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31
+    return v;
+}
+
+struct Ctx {
+    SArgs a;
+    int n0, R;
+    uint8_t *smem;
+    SLayout L;
+};
+
+// First row after the sub-unit that starts at row ra: as many whole rows as
+// fit `cap` code bytes and kMaxRS row-slices (at least one row).
+__device__ __forceinline__ int next_end(const Ctx &c, int ra)
+{
+    if (ra >= c.R)
+        return c.R;
+    const uint32_t *rowoff = reinterpret_cast<const uint32_t *>(c.smem + c.L.rowoff);
+    const int lane = threadIdx.x & 63;
+    const int kmax = min(kMaxRS / c.a.nS, c.R - ra);
+    const uint32_t base = rowoff[ra], cap = (uint32_t)c.a.cap;
+    int n = 0;
+#pragma unroll
+    for (int h = 0; h < kMaxRS / 64; h++) {
+        const int k = lane + 1 + 64 * h;
+        const bool ok = k <= kmax && (rowoff[min(ra + k, c.R)] - base) * 128u <= cap;
+        n += (int)__popcll(__ballot(ok)); // the condition is monotone in k
+    }
+    return ra + n;
+}
+
+// Copy the code bytes and scales of rows [ra, rb) into ring slot `slot`.
+// Chunk j (1 KiB) goes to wave (j + v) % kW; returns this wave's chunk count.
+__device__ __forceinline__ int issue_subunit(const Ctx &c, int ra, int rb, int slot, int v)
+{
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t *rowoff = reinterpret_cast<const uint32_t *>(c.smem + c.L.rowoff);
+    uint8_t *dst = c.smem + c.L.ring + slot * slot_bytes(c.a.cap);
+    const uint64_t c0 = (uint64_t)rowoff[ra] * 128u;
+    const uint32_t clen = (rowoff[rb] - rowoff[ra]) * 128u;
+    const uint64_t s0 = (uint64_t)(c.n0 + ra) * c.a.G * 2u;
+    const uint64_t s0a = s0 & ~15ull;
+    const uint32_t slen = (uint32_t)((uint64_t)(c.n0 + rb) * c.a.G * 2u - s0a);
+    const int nc = (int)((clen + 1023u) >> 10);
+    const int ns = (int)((slen + 1023u) >> 10);
+    const uint8_t *gc = c.a.blob + c.a.off_codes + c0;
+    const uint8_t *gs = c.a.blob + c.a.off_scales + s0a;
+    int cnt = 0;
+    for (int j = (wave - v % kW + kW) % kW; j < nc + ns; j += kW) {
+        if (j < nc) {
+            const uint32_t off = (uint32_t)j * 1024u + lane * 16u;
+            if (off < clen)
+                dma16(gc + off, lds_addr(dst + j * 1024));
+        } else {
+            const uint32_t off = (uint32_t)(j - nc) * 1024u + lane * 16u;
+            if (off < slen)
+                dma16(gs + off, lds_addr(dst + c.a.cap + (j - nc) * 1024));
+        }
+        cnt++;
+    }
+    return cnt;
+}
+
+// Descriptors of the row-slices of rows [ra, rb), built by one wave (lane l
+// holds row-slices 2l and 2l+1):
+//   d0, d1    width bit planes
+//   d2        row in sub-unit << 12 | first group column of the slice << 19
+//   d3        valid groups
+//   d4+3c     groups of width c (mask)
+//   d5+3c     slot of the first half-0 group of width c | (slot of the first
+//             half-1 group - half-0 groups of width c) << 16
+//   d6+3c     record start / 8 + bucket start / 8 of width c
+// Slots of width c are ordered (group half, row-slice, rank) and each width
+// starts on a 64-slot pass boundary.  Also resets the sub-unit's pass counter.
+__device__ void build_info(const Ctx &c, int ra, int rb, int buf)
+{
+    const int lane = threadIdx.x & 63;
+    const int nS = c.a.nS, G = c.a.G;
+    const uint32_t *rowoff = reinterpret_cast<const uint32_t *>(c.smem + c.L.rowoff);
+    const uint32_t *sloff = reinterpret_cast<const uint32_t *>(c.smem + c.L.sloff);
+    const uint32_t *wmap = reinterpret_cast<const uint32_t *>(c.smem + c.L.wmap);
+    uint32_t *info = reinterpret_cast<uint32_t *>(c.smem + c.L.info) + buf * kMaxRS * kInfo;
+    uint32_t *hdr = reinterpret_cast<uint32_t *>(c.smem + c.L.hdr) + buf * 16;
+    const int nrs = (rb - ra) * nS;
+    const uint32_t base0 = rowoff[ra];
+    uint32_t p0[2], p1[2], m[2][4], rec8[2];
+    int ng[2], r[2], s[2], cnt[2][4], h0[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int i = 2 * lane + j;
+        const bool live = i < nrs;
+        r[j] = (int)(((uint32_t)i * (uint32_t)c.a.inv_nS) >> 16);
+        s[j] = i - r[j] * nS;
+        const int w = live ? ra * nS + i : 0;
+        p0[j] = live ? wmap[2 * w] : 0u;
+        p1[j] = live ? wmap[2 * w + 1] : 0u;
+        rec8[j] = live ? ((rowoff[ra + r[j]] - base0) * 128u + sloff[w]) >> 3 : 0u;
+        ng[j] = live ? max(0, min(32, G - 32 * s[j])) : 0;
+        const WidthMasks wm = width_masks(p0[j], p1[j], ng[j]);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            m[j][k] = wm.m[k];
+            cnt[j][k] = __popc(wm.m[k]);
+            h0[j][k] = __popc(wm.m[k] & 0xffffu);
+        }
+    }
+    // two widths per 32-bit scan (16-bit fields; a sub-unit has <= 4096 groups)
+    uint32_t A[2], B[2], eA[2], eB[2], tA[2], tB[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int k0 = 2 * q, k1 = 2 * q + 1;
+        A[q] = (uint32_t)(h0[0][k0] + h0[1][k0]) | ((uint32_t)(h0[0][k1] + h0[1][k1]) << 16);
+        B[q] = (uint32_t)(cnt[0][k0] - h0[0][k0] + cnt[1][k0] - h0[1][k0]) |
+               ((uint32_t)(cnt[0][k1] - h0[0][k1] + cnt[1][k1] - h0[1][k1]) << 16);
+        const uint32_t ia = (uint32_t)scan64((int)A[q]), ib = (uint32_t)scan64((int)B[q]);
+        tA[q] = (uint32_t)__builtin_amdgcn_readlane((int)ia, 63);
+        tB[q] = (uint32_t)__builtin_amdgcn_readlane((int)ib, 63);
+        eA[q] = ia - A[q];
+        eB[q] = ib - B[q];
+    }
+    int tot0[4], tot[4], pb[4], np = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const int sh = 16 * (k & 1);
+        tot0[k] = (int)((tA[k >> 1] >> sh) & 0xffffu);
+        tot[k] = tot0[k] + (int)((tB[k >> 1] >> sh) & 0xffffu);
+        pb[k] = np;
+        np += (tot[k] + 63) >> 6;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int i = 2 * lane + j;
+        if (i < nrs) {
+            uint32_t *d = info + i * kInfo;
+            reinterpret_cast<uint4 *>(d)[0] =
+                make_uint4(p0[j], p1[j], ((uint32_t)r[j] << 12) | ((uint32_t)(32 * s[j]) << 19), (uint32_t)ng[j]);
+            uint32_t bb = 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const int sh = 16 * (k & 1);
+                int x0 = (int)((eA[k >> 1] >> sh) & 0xffffu), x1 = (int)((eB[k >> 1] >> sh) & 0xffffu);
+                if (j == 1) { // after this lane's first row-slice
+                    x0 += h0[0][k];
+                    x1 += cnt[0][k] - h0[0][k];
+                }
+                const uint32_t sb0 = (uint32_t)(64 * pb[k] + x0);
+                const uint32_t sb1 = (uint32_t)(64 * pb[k] + tot0[k] + x1 - h0[j][k]);
+                d[4 + 3 * k] = m[j][k];
+                d[5 + 3 * k] = sb0 | (sb1 << 16);
+                d[6 + 3 * k] = rec8[j] + bb;
+                bb += (uint32_t)cnt[j][k] << k;
+            }
+        }
+    }
+    if (lane == 0) {
+        reinterpret_cast<uint4 *>(hdr)[0] = make_uint4((uint32_t)np, (uint32_t)pb[1], (uint32_t)pb[2], (uint32_t)pb[3]);
+        reinterpret_cast<uint4 *>(hdr)[1] = make_uint4((uint32_t)tot[0], (uint32_t)tot[1], (uint32_t)tot[2], (uint32_t)tot[3]);
+        hdr[8] = 0u; // pass counter
+    }
+}
+
+// Slot-table entries of rows [ra, rb): thread = (row-slice, group).
+// entry = code offset / 8 (12 bits) | row in sub-unit (7 bits) << 12 | group column << 19
+__device__ __forceinline__ void build_table(const Ctx &c, int ra, int rb, int buf)
+{
+    constexpr int kPer = kMaxRS * 32 / kT; // (row-slice, group) items per thread
+    const int tid = threadIdx.x;
+    const int nrs = (rb - ra) * c.a.nS;
+    const uint32_t *info = reinterpret_cast<const uint32_t *>(c.smem + c.L.info) + buf * kMaxRS * kInfo;
+    uint32_t *table = reinterpret_cast<uint32_t *>(c.smem + c.L.table);
+    const uint32_t g = tid & 31;
+    const uint32_t lt = (1u << g) - 1u, hsh = g < 16 ? 0u : 16u, gx = g << 19;
+    // all descriptor reads first: two LDS round trips for the whole table
+    uint4 d0[kPer];
+    bool on[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = (tid >> 5) + k * (kT / 32);
+        d0[k] = i < nrs ? *reinterpret_cast<const uint4 *>(info + i * kInfo) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t cc[kPer], m[kPer], sb[kPer], cb[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = (tid >> 5) + k * (kT / 32);
+        on[k] = g < d0[k].w; // zero for row-slices past the sub-unit
+        cc[k] = ((d0[k].x >> g) & 1u) | (((d0[k].y >> g) & 1u) << 1);
+        const uint32_t *dc = info + (on[k] ? i : 0) * kInfo + 4 + 3 * cc[k];
+        m[k] = dc[0];
+        sb[k] = dc[1];
+        cb[k] = dc[2];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        if (on[k]) {
+            const uint32_t rank = (uint32_t)__popc(m[k] & lt);
+            const uint32_t slot = ((sb[k] >> hsh) & 0xffffu) + rank;
+            table[slot] = (cb[k] + (rank << cc[k])) + d0[k].z + gx;
+        }
+    }
+}
+
+// One pass: 64 slots of width B.
+template <int B, int MT>
+__device__ __forceinline__ void run_pass(const Ctx &c, int p, int end_slot, const uint32_t *table,
+                                         const uint8_t *codes, const uint16_t *scales, const uint32_t *xrec,
+                                         float *psum)
+{
+    constexpr int C = B == 1 ? 0 : B == 2 ? 1 : B == 4 ? 2 : 3;
+    const int slot = p * 64 + (int)(threadIdx.x & 63);
+    if (slot >= end_slot)
+        return;
+    const uint32_t e = table[slot];
+    const uint32_t code8 = e & 0xfffu, row = (e >> 12) & 127u, xcol = e >> 19;
+    const uint32_t sidx = row * (uint32_t)c.a.G + xcol;
+    uint32_t w[2 * B];
+    const U2 *src = reinterpret_cast<const U2 *>(codes + code8 * 8u);
+#pragma unroll
+    for (int k = 0; k < B; k++) {
+        const U2 v = src[k];
+        w[2 * k] = v.v[0];
+        w[2 * k + 1] = v.v[1];
+    }
+    uint32_t h[32];
+    unpack_pairs<B>(w, h);
+    const float s = __half2float(__ushort_as_half(scales[sidx]));
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+        const uint32_t *xr = xrec + ((uint32_t)m * c.a.G + xcol) * kXRec;
+        float acc0 = 0.f, acc1 = 0.f; // two chains for instruction-level parallelism
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+            const U4 xa = *reinterpret_cast<const U4 *>(xr + 4 * k);
+            const U4 xb = *reinterpret_cast<const U4 *>(xr + 4 * k + 4);
+            acc0 = dot2(h[4 * k + 0], xa.v[0], acc0);
+            acc1 = dot2(h[4 * k + 4], xb.v[0], acc1);
+            acc0 = dot2(h[4 * k + 1], xa.v[1], acc0);
+            acc1 = dot2(h[4 * k + 5], xb.v[1], acc1);
+            acc0 = dot2(h[4 * k + 2], xa.v[2], acc0);
+            acc1 = dot2(h[4 * k + 6], xb.v[2], acc1);
+            acc0 = dot2(h[4 * k + 3], xa.v[3], acc0);
+            acc1 = dot2(h[4 * k + 7], xb.v[3], acc1);
+        }
+        const float cc = __uint_as_float(xr[32 + C]);
+        psum[m * kPsum + sidx] = s * ((acc0 + acc1) - cc);
+    }
+}
+
+// x records for all of K: fp16 pairs (x_p, x_{p+32}), then per width
+// C_b = sum_p 2^(10-pos_b(p)) (x_p + x_{p+32}) + (2^b-1)/2 sum_j x_j.
+// Item = (token, group, quarter q): pairs 4q..4q+3.  Loads are issued by the
+// caller's loop all at once; the 8 items of a group are 8 adjacent lanes.
+template <int MT>
+__device__ __forceinline__ void stage_x(const Ctx &c, uint32_t *xrec)
+{
+    const int tid = threadIdx.x;
+    const int G = c.a.G;
+    const int items = MT * G * 8;
+    const bool vec = (c.a.ldx % 4) == 0 && ((uintptr_t)c.a.x % 8) == 0;
+    constexpr int kPer = (MT * 256 * 8 + kT - 1) / kT; // items per thread (G < 256)
+    uint32_t lo0[kPer], lo1[kPer], hi0[kPer], hi1[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = tid + k * kT;
+        lo0[k] = lo1[k] = hi0[k] = hi1[k] = 0u;
+        if (i < items) {
+            const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
+            const uint16_t *xs = c.a.x + (uint64_t)m * c.a.ldx + 64ull * g + 4 * q;
+            if (vec) {
+                const uint2 va = *reinterpret_cast<const uint2 *>(xs);
+                const uint2 vb = *reinterpret_cast<const uint2 *>(xs + 32);
+                lo0[k] = va.x;
+                lo1[k] = va.y;
+                hi0[k] = vb.x;
+                hi1[k] = vb.y;
+            } else {
+                lo0[k] = xs[0] | ((uint32_t)xs[1] << 16);
+                lo1[k] = xs[2] | ((uint32_t)xs[3] << 16);
+                hi0[k] = xs[32] | ((uint32_t)xs[33] << 16);
+                hi1[k] = xs[34] | ((uint32_t)xs[35] << 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = tid + k * kT;
+        if (i >= items) // whole groups of 8 lanes drop out together
+            break;
+        const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
+        U4 o;
+        o.v[0] = __builtin_amdgcn_perm(hi0[k], lo0[k], 0x05040100u); // (x_p, x_{p+32})
+        o.v[1] = __builtin_amdgcn_perm(hi0[k], lo0[k], 0x07060302u);
+        o.v[2] = __builtin_amdgcn_perm(hi1[k], lo1[k], 0x05040100u);
+        o.v[3] = __builtin_amdgcn_perm(hi1[k], lo1[k], 0x07060302u);
+        uint32_t *xr = xrec + ((uint32_t)m * G + g) * kXRec;
+        *reinterpret_cast<U4 *>(xr + 4 * q) = o;
+        float X = 0.f, c1 = 0.f, c2 = 0.f, c4 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int t = 4 * q + j; // pair index in the group
+            const float sp = dot2(o.v[j], 0x3c003c00u, 0.f); // x_t + x_{t+32}, exact in fp32
+            X += sp;
+            // the mantissa position of pair t depends on its index inside its word
+            c1 = fmaf((float)(1 << (10 - pair_pos<1>(t & 15))), sp, c1);
+            c2 = fmaf((float)(1 << (10 - pair_pos<2>(t & 7))), sp, c2);
+            c4 = fmaf((float)(1 << (10 - pair_pos<4>(t & 3))), sp, c4);
+        }
+#pragma unroll
+        for (int d = 1; d < 8; d <<= 1) { // fixed-order tree over the 8 quarters
+            X += __shfl_xor(X, d, 8);
+            c1 += __shfl_xor(c1, d, 8);
+            c2 += __shfl_xor(c2, d, 8);
+            c4 += __shfl_xor(c4, d, 8);
+        }
+        if (q == 0)
+            *reinterpret_cast<U4 *>(xr + 32) = U4{{__float_as_uint(fmaf(0.5f, X, c1)),
+                                                    __float_as_uint(fmaf(1.5f, X, c2)),
+                                                    __float_as_uint(fmaf(7.5f, X, c4)),
+                                                    __float_as_uint(fmaf(127.5f, X, 1024.f * X))}};
+    }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    Ctx c;
+    c.a = a;
+    c.n0 = blockIdx.x * a.rows;
+    if (c.n0 >= a.N)
+        return;
+    c.R = min(a.rows, a.N - c.n0);
+    c.smem = smem;
+    c.L = s_layout(MT, a.G, a.rows, a.nS, a.cap);
+    const int nS = a.nS, G = a.G, R = c.R;
+    const uint32_t sbytes = slot_bytes(a.cap);
+    uint32_t *rowoff = reinterpret_cast<uint32_t *>(smem + c.L.rowoff);
+    uint32_t *sloff = reinterpret_cast<uint32_t *>(smem + c.L.sloff);
+    uint32_t *wmap = reinterpret_cast<uint32_t *>(smem + c.L.wmap);
+    uint32_t *xrec = reinterpret_cast<uint32_t *>(smem + c.L.x);
+    const uint32_t *table = reinterpret_cast<const uint32_t *>(smem + c.L.table);
+    float *psum = reinterpret_cast<float *>(smem + c.L.psum);
+
+    // ---- metadata of this workgroup's rows, and the activations
+    {
+        const uint32_t *g_row = reinterpret_cast<const uint32_t *>(a.blob + a.off_row_off) + c.n0;
+        const uint32_t *g_slo = reinterpret_cast<const uint32_t *>(a.blob + a.off_slice_off) + (uint64_t)c.n0 * nS;
+        const uint32_t *g_wm = reinterpret_cast<const uint32_t *>(a.blob + a.off_wmap) + 2ull * c.n0 * nS;
+        const int nrs = R * nS;
+        uint32_t r0 = 0, r1 = 0, sl = 0, w0 = 0, w1 = 0;
+        if (tid <= R)
+            r0 = g_row[tid];
+        if (tid + kT <= R)
+            r1 = g_row[tid + kT];
+        if (tid < nrs)
+            sl = g_slo[tid];
+        if (tid < 2 * nrs)
+            w0 = g_wm[tid];
+        if (tid + kT < 2 * nrs)
+            w1 = g_wm[tid + kT];
+        stage_x<MT>(c, xrec);
+        if (tid <= R)
+            rowoff[tid] = r0;
+        if (tid + kT <= R)
+            rowoff[tid + kT] = r1;
+        if (tid < nrs)
+            sloff[tid] = sl;
+        if (tid < 2 * nrs)
+            wmap[tid] = w0;
+        if (tid + kT < 2 * nrs)
+            wmap[tid + kT] = w1;
+    }
+    __syncthreads();
+
+    // ---- sub-units u and u+1 start at rows ra and rb; rc ends u+1
+    int ra = 0, rb = next_end(c, 0), rc = next_end(c, rb);
+    int slot = 0;
+    issue_subunit(c, ra, rb, 0, 0);
+    if (wave == 0)
+        build_info(c, ra, rb, 0);
+    __syncthreads();
+
+    for (int u = 0; ra < R; u++) {
+        const int buf = u & 1;
+        // prefetch u+1 into the slot that u-1 used (its passes are done)
+        int l1 = 0;
+        if (rb < R)
+            l1 = issue_subunit(c, rb, rc, slot ^ 1, u + 1);
+        build_table(c, ra, rb, buf);
+        wait_vm(l1); // this wave's chunks of u have landed
+        __syncthreads();
+
+        // ---- passes of u, handed out through an LDS counter; wave 0 first
+        // describes u+1
+        {
+            if (wave == 0 && rb < R)
+                build_info(c, rb, rc, buf ^ 1);
+            uint32_t *hdr = reinterpret_cast<uint32_t *>(smem + c.L.hdr) + buf * 16;
+            const uint4 h0 = *reinterpret_cast<const uint4 *>(hdr);
+            const uint4 h1 = *reinterpret_cast<const uint4 *>(hdr + 4);
+            const int np = (int)h0.x, pb1 = (int)h0.y, pb2 = (int)h0.z, pb3 = (int)h0.w;
+            const uint8_t *codes = smem + c.L.ring + slot * sbytes;
+            const uint64_t s0 = (uint64_t)(c.n0 + ra) * G * 2u;
+            const uint16_t *scales = reinterpret_cast<const uint16_t *>(codes + a.cap + (s0 & 15u));
+            for (;;) {
+                int p = 0;
+                if (lane == 0)
+                    p = (int)atomicAdd(hdr + 8, 1u);
+                p = __builtin_amdgcn_readfirstlane(p);
+                if (p >= np)
+                    break;
+                if (p < pb1)
+                    run_pass<1, MT>(c, p, (int)h1.x, table, codes, scales, xrec, psum);
+                else if (p < pb2)
+                    run_pass<2, MT>(c, p, 64 * pb1 + (int)h1.y, table, codes, scales, xrec, psum);
+                else if (p < pb3)
+                    run_pass<4, MT>(c, p, 64 * pb2 + (int)h1.z, table, codes, scales, xrec, psum);
+                else
+                    run_pass<8, MT>(c, p, 64 * pb3 + (int)h1.w, table, codes, scales, xrec, psum);
+            }
+        }
+        __syncthreads();
+
+        // ---- rows of u: 8 lanes per row, fixed summation order
+        {
+            const int nr = rb - ra;
+            const int j = tid >> 3, q = tid & 7;
+            if (j < nr) {
+#pragma unroll
+                for (int m = 0; m < MT; m++) {
+                    const float *ps = psum + m * kPsum + j * G;
+                    float v = 0.f;
+                    for (int k = q; k < G; k += 8)
+                        v += ps[k];
+                    v += __shfl_xor(v, 4, 8);
+                    v += __shfl_xor(v, 2, 8);
+                    v += __shfl_xor(v, 1, 8);
+                    if (q == 0) {
+                        const uint64_t o = (uint64_t)m * a.ldy + c.n0 + ra + j;
+                        if (a.yt == VBQ_F16)
+                            reinterpret_cast<__half *>(a.y)[o] = __float2half_rn(v);
+                        else
+                            reinterpret_cast<float *>(a.y)[o] = v;
+                    }
+                }
+            }
+        }
+        // ---- advance
+        ra = rb;
+        rb = rc;
+        rc = next_end(c, rc);
+        slot ^= 1;
+    }
+}
+
+int device_cus()
+{
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 256;
+    }
+    return cus;
+}
+
+template <int MT>
+vbq_status launch_stream(const SArgs &a, int grid, size_t smem, hipStream_t stream)
+{
+    static bool configured = false;
+    if (!configured) {
+        VBQ_TRY(hip_status(hipFuncSetAttribute((const void *)k_gemv_stream<MT>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)));
+        configured = true;
+    }
+    hipLaunchKernelGGL(k_gemv_stream<MT>, dim3(grid), dim3(kT), smem, stream, a);
+    return launch_status();
+}
+
+} // namespace
+
+namespace vbq {
+
+bool stream_gemv(const GemvCall &g, vbq_status *st)
+{
+    const vbq_layout *L = g.L;
+    if (g.M < 1 || g.M > 2)
+        return false;
+    const int N = (int)L->N, G = (int)L->G, nS = (int)L->nS;
+    if (nS > kMaxRS)
+        return false;
+    const int cus = device_cus();
+    int rows = (N + cus - 1) / cus;
+    rows = std::max(1, std::min(rows, kMetaRS / nS));
+    const int grid = (N + rows - 1) / rows;
+    // the largest sub-unit that fits LDS; every row record (8 bytes per bit of
+    // width, padded to 128) must fit one sub-unit
+    int cap = 0;
+    for (int cand : {kMaxCap, 24576, 16384}) {
+        if ((uint64_t)G * 64u + 128u > (uint64_t)cand)
+            break;
+        if (s_layout(g.M, G, rows, nS, cand).total <= 160u * 1024u) {
+            cap = cand;
+            break;
+        }
+    }
+    if (!cap)
+        return false;
+    const SLayout l = s_layout(g.M, G, rows, nS, cap);
+    SArgs a;
+    a.blob = (const uint8_t *)g.blob;
+    a.off_row_off = L->off_row_off;
+    a.off_slice_off = L->off_slice_off;
+    a.off_wmap = L->off_wmap;
+    a.off_scales = L->off_scales;
+    a.off_codes = L->off_codes;
+    a.N = N;
+    a.G = G;
+    a.nS = nS;
+    a.M = g.M;
+    a.x = g.x;
+    a.ldx = g.ldx;
+    a.y = g.y;
+    a.ldy = g.ldy;
+    a.yt = (int)g.yt;
+    a.rows = rows;
+    a.cap = cap;
+    a.inv_nS = (65536 + nS - 1) / nS;
+    *st = g.M == 1 ? launch_stream<1>(a, grid, l.total, g.stream) : launch_stream<2>(a, grid, l.total, g.stream);
+    return true;
+}
+
+} // namespace vbq

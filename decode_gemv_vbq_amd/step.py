@@ -67,9 +67,15 @@ class DecodeStep:
             else:
                 v.gemv_batched(m.L, m.blob, m.x, out=m.y, ws=m.ws)
 
-    def run_timed_kernels(self):
-        """Like run(), with an event pair around every launch; returns the pairs."""
+    def run_timed_kernels(self, hold_cycles: int = 0):
+        """Like run(), with an event pair around every launch; returns the pairs.
+
+        With hold_cycles > 0 a bounded device sleep is queued first, so that all
+        launches are enqueued before the GPU reaches them: the pairs then time the
+        kernels back to back rather than the host's launch rate."""
         torch = self.torch
+        if hold_cycles:
+            torch.cuda._sleep(int(hold_cycles))
         ev = []
         for m in self.mats:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
