@@ -6,9 +6,10 @@
 One step = every GEMV of one synthetic decoder step (stage order qkv, o, gate,
 up, down per layer, then the LM head), M = 1, weights packed in VBQ1 and
 resident in HBM before timing.  Prints ONE JSON line with us/step, the
-achieved algorithmic HBM bandwidth of the GEMV kernel (HIP events around every
-launch, on the launch stream), the on-GPU fp16 dense control and the CPU
-oracle timed on a bounded sample of the same workload.
+achieved algorithmic HBM bandwidth of the GEMV kernel (per-launch duration from
+HIP events around the captured step graph, on the launch stream),
+the on-GPU fp16 dense control and the CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -38,7 +39,9 @@ def parse(argv=None):
     ap.add_argument("--no-control", action="store_true", help="skip the fp16 dense control")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the baseline sample")
-    ap.add_argument("--kernel-steps", type=int, default=5, help="steps timed with per-launch events")
+    ap.add_argument("--kernel-steps", type=int, default=5, help="replays of each per-kind kernel graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
     return ap.parse_args(argv)
 
 
@@ -53,18 +56,32 @@ def time_steps(torch, fn, steps):
     return a.elapsed_time(b) / steps  # ms per step
 
 
-def sleep_cycles(torch, seconds):
-    """Device-clock cycles of torch's bounded sleep kernel that last about `seconds`."""
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    cyc = 1_000_000
-    torch.cuda._sleep(cyc)  # warm up
-    torch.cuda.synchronize()
-    a.record()
-    torch.cuda._sleep(cyc)
-    b.record()
-    torch.cuda.synchronize()
-    per_s = cyc / max(a.elapsed_time(b) * 1e-3, 1e-6)
-    return int(per_s * seconds)
+KERNEL_SOURCES = ("vbq_stream.hip", "vbq_unpack.h", "vbq_common.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_gemv_vbq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the GEMV kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE x its copy-calibrated factor + WRITE_SIZE), or None when the
+    kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"k_gemv_stream_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic-json: "):
+            t = json.loads(line[len("traffic-json: "):])
+            if t.get("kernel_source_sha") != kernel_source_hash():
+                return None
+            return round(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+    return None
 
 
 def cpu_baseline(step, budget_s):
@@ -110,6 +127,15 @@ def main(argv=None):
         sys.exit(2)
     import torch
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel(), "copy_bytes_written": dst.numel(), "copies": 5}))
+        return
+
     import decode_gemv_vbq_amd as v
     from decode_gemv_vbq_amd import accounting as acc
     from decode_gemv_vbq_amd.step import DecodeStep
@@ -132,39 +158,33 @@ def main(argv=None):
     ms = time_steps(torch, fn, args.steps)
     log(f"step: {ms * 1e3:.1f} us ({args.mode}), {alg / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
 
-    # per-launch kernel durations: events on the launch stream around every
-    # launch, all launches queued behind a bounded device sleep so they run back
-    # to back (the host enqueues far slower than the GPU executes)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    step.run_timed_kernels()
-    torch.cuda.synchronize()
-    host_s = time.perf_counter() - t0
-    hold = sleep_cycles(torch, 2.0 * host_s + 0.005)
-    per_kind = {}
-    kern_ms = 0.0
-    for _ in range(args.kernel_steps):
-        ev = step.run_timed_kernels(hold_cycles=hold)
-        torch.cuda.synchronize()
-        for m, (a, b) in zip(step.mats, ev):
-            t = a.elapsed_time(b)
-            kern_ms += t
-            k = per_kind.setdefault(m.spec.name, [0.0, 0, 0])
-            k[0] += t
-            k[1] += 1
-    kern_ms /= args.kernel_steps
-    for m in step.mats:
-        per_kind[m.spec.name][2] += acc.vbq_read_bytes(m.L, step.M)
+    # per-launch kernel durations: for each matrix kind, that kind's launches of
+    # one step captured back to back in a graph (events on the launch stream)
     kinds = {}
-    for name, (t, n, bts) in per_kind.items():
-        cnt = n // args.kernel_steps
-        kinds[name] = {"launches": cnt, "us": round(1e3 * t / n, 2),
-                       "GBps": round((bts / cnt) / (t / n * 1e-3) / 1e9, 1)}
-    avg_launch_s = kern_ms * 1e-3 / n_launch
+    kern_ms = 0.0
+    names = []
+    for m in step.mats:
+        if m.spec.name not in names:
+            names.append(m.spec.name)
+    for name in names:
+        idx = [i for i, m in enumerate(step.mats) if m.spec.name == name]
+        g = step.capture_subset(idx)
+        for _ in range(2):
+            g.replay()
+        reps = max(2, args.kernel_steps)
+        t = time_steps(torch, g.replay, reps) / len(idx)  # ms per launch
+        del g
+        bts = sum(acc.vbq_read_bytes(step.mats[i].L, step.M) for i in idx) / len(idx)
+        kinds[name] = {"launches": len(idx), "us": round(t * 1e3, 2), "GBps": round(bts / (t * 1e-3) / 1e9, 1)}
+        kern_ms += t * len(idx)
+    # the roofline uses the cold step: its launches run back to back in the graph,
+    # so the average launch duration is the step time over the launch count
+    avg_launch_s = ms * 1e-3 / n_launch
     alg_per_launch = alg / n_launch
     achieved = alg_per_launch / avg_launch_s
-    log(f"kernels: {kern_ms * 1e3:.1f} us summed, {avg_launch_s * 1e6:.2f} us/launch avg, {achieved / 1e9:.0f} GB/s; "
-        + ", ".join(f"{k} {d['us']} us {d['GBps']} GB/s" for k, d in kinds.items()))
+    log(f"kernels: {avg_launch_s * 1e6:.2f} us/launch avg in the step, {achieved / 1e9:.0f} GB/s; per kind (replayed "
+        f"alone, {kern_ms * 1e3:.1f} us summed): " + ", ".join(f"{k} {d['us']} us {d['GBps']} GB/s" for k, d in kinds.items()))
+    traffic = measured_traffic(args.workload)
 
     control = None
     if not args.no_control:
@@ -214,9 +234,10 @@ def main(argv=None):
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM, 4), "traffic": None,
-            "kernel": "k_gemv_wave<1> (vbq_gemv)", "alg_bytes_per_launch": round(alg_per_launch),
+            "frac": round(achieved / PEAK_HBM, 4), "traffic": traffic,
+            "kernel": "k_gemv_stream<1> (vbq_gemv)", "alg_bytes_per_launch": round(alg_per_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3), "per_matrix": kinds,
+            "per_matrix_sum_us": round(kern_ms * 1e3, 1),
         },
         "cpu_baseline": cpu,
     }

@@ -61,32 +61,27 @@ class DecodeStep:
     # ------------------------------------------------------------- the step
     def run(self):
         """Enqueue every GEMV of the step, in stage order, on the current stream."""
-        for m in self.mats:
+        self.run_subset(range(len(self.mats)))
+
+    def run_subset(self, idx):
+        """Enqueue the GEMVs of matrices `idx` (step order) on the current stream."""
+        for i in idx:
+            m = self.mats[i]
             if self.M == 1:
                 v.gemv(m.L, m.blob, m.x[0], out=m.y[0], ws=m.ws)
             else:
                 v.gemv_batched(m.L, m.blob, m.x, out=m.y, ws=m.ws)
 
-    def run_timed_kernels(self, hold_cycles: int = 0):
-        """Like run(), with an event pair around every launch; returns the pairs.
-
-        With hold_cycles > 0 a bounded device sleep is queued first, so that all
-        launches are enqueued before the GPU reaches them: the pairs then time the
-        kernels back to back rather than the host's launch rate."""
+    def capture_subset(self, idx):
+        """A graph of the GEMVs of matrices `idx`, back to back."""
         torch = self.torch
-        if hold_cycles:
-            torch.cuda._sleep(int(hold_cycles))
-        ev = []
-        for m in self.mats:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            if self.M == 1:
-                v.gemv(m.L, m.blob, m.x[0], out=m.y[0], ws=m.ws)
-            else:
-                v.gemv_batched(m.L, m.blob, m.x, out=m.y, ws=m.ws)
-            b.record()
-            ev.append((a, b))
-        return ev
+        self.run_subset(idx)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_subset(idx)
+        torch.cuda.synchronize()
+        return g
 
     def capture(self):
         torch = self.torch
