@@ -14,7 +14,8 @@
 //    code bytes (less when K is long).  A sub-unit's code bytes and scales are
 //    contiguous in HBM, so they are copied straight into a two-slot LDS ring
 //    with global_load_lds_dwordx4 (1 KiB per wave instruction, no VGPRs) while
-//    the previous sub-unit computes: HBM sees a steady stream.
+//    the previous sub-unit computes: HBM sees a steady stream.  A block that
+//    fits both slots is a single sub-unit (one table, no second round).
 //  * Inside a sub-unit the groups are listed per width in a slot table, so a
 //    wavefront always runs 64 groups of ONE width (no divergence between the
 //    1/2/4/8-bit paths); the 16 waves take passes from an LDS counter.
@@ -48,9 +49,11 @@ constexpr int kXRec = 36;                 // dwords per x record: 32 pairs + 4 c
 constexpr int kInfo = 16;                 // dwords per row-slice descriptor
 constexpr int kPsum = kMaxRS * 32;        // partials per token
 
-// Scale bytes of a sub-unit (+ 16-byte alignment slack), and its ring slot.
+// Scale bytes of a sub-unit (+ 16-byte alignment slack).  The ring holds the
+// code areas of its slots back to back, then their scale areas back to back,
+// so that all slots together can serve as one double-size sub-unit.
 __host__ __device__ constexpr uint32_t scale_area(int cap) { return (uint32_t)(cap / 4 + 128); }
-__host__ __device__ constexpr uint32_t slot_bytes(int cap) { return (uint32_t)cap + scale_area(cap); }
+__host__ __device__ constexpr uint32_t ring_bytes(int cap) { return (uint32_t)kRing * ((uint32_t)cap + scale_area(cap)); }
 
 struct SArgs {
     const uint8_t *blob;
@@ -61,13 +64,13 @@ struct SArgs {
     void *y;
     int ldy, yt;
     int rows;   // rows per workgroup
-    int cap;    // code bytes per sub-unit (multiple of 1024, <= kMaxCap)
+    int cap;    // code bytes per sub-unit (multiple of 1024, 8192..kMaxCap)
     int inv_nS; // ceil(65536 / nS): i / nS == (i * inv_nS) >> 16 for i < kMaxRS
 };
 
 // LDS carve-up, computed identically on the host (size) and the device.
 struct SLayout {
-    uint32_t x, rowoff, sloff, wmap, ring, info, hdr, table, psum, total;
+    uint32_t x, rowoff, sloff, wmap, ring, info, hdr, table, psum, ybuf, total;
 };
 
 __host__ __device__ inline uint32_t s_take(uint32_t &o, uint32_t bytes)
@@ -85,11 +88,12 @@ __host__ __device__ inline SLayout s_layout(int MT, int G, int rows, int nS, int
     l.rowoff = s_take(o, (uint32_t)((rows + 1) * 4));
     l.sloff = s_take(o, (uint32_t)(rows * nS * 4));
     l.wmap = s_take(o, (uint32_t)(rows * nS * 8));
-    l.ring = s_take(o, kRing * slot_bytes(cap));
+    l.ring = s_take(o, ring_bytes(cap));
     l.info = s_take(o, (uint32_t)(2 * kMaxRS * kInfo * 4));
     l.hdr = s_take(o, 2 * 16 * 4);
     l.table = s_take(o, kMaxSlots * 4);
     l.psum = s_take(o, (uint32_t)(MT * kPsum * 4));
+    l.ybuf = s_take(o, (uint32_t)(MT * rows * 4));
     l.total = o;
     return l;
 }
@@ -163,42 +167,71 @@ __device__ __forceinline__ int next_end(const Ctx &c, int ra)
     return ra + n;
 }
 
-// Copy the code bytes and scales of rows [ra, rb) into ring slot `slot`.
-// Chunk j (1 KiB) goes to wave (j + v) % kW; returns this wave's chunk count.
-__device__ __forceinline__ int issue_subunit(const Ctx &c, int ra, int rb, int slot, int v)
+// The copy of one sub-unit into a ring slot: code bytes [128*o0, 128*o1) of
+// the codes section, then the scales of its rows, in 1 KiB chunks.  Chunk j
+// belongs to wave (j + v) % kW; each wave issues its chunks in order, one at
+// a time (issue_next), so the copy can be spread over the passes of the
+// previous sub-unit instead of stalling every wave at once.
+struct Copy {
+    const uint8_t *gc, *gs;
+    uint32_t dst, sdst, clen, slen;
+    int nc, n, j; // code chunks, all chunks, this wave's next chunk
+};
+
+__device__ __forceinline__ uint32_t slot_codes(const Ctx &c, int slot) { return c.L.ring + (uint32_t)(slot * c.a.cap); }
+__device__ __forceinline__ uint32_t slot_scales(const Ctx &c, int slot)
 {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t *rowoff = reinterpret_cast<const uint32_t *>(c.smem + c.L.rowoff);
-    uint8_t *dst = c.smem + c.L.ring + slot * slot_bytes(c.a.cap);
-    const uint64_t c0 = (uint64_t)rowoff[ra] * 128u;
-    const uint32_t clen = (rowoff[rb] - rowoff[ra]) * 128u;
-    const uint64_t s0 = (uint64_t)(c.n0 + ra) * c.a.G * 2u;
-    const uint64_t s0a = s0 & ~15ull;
-    const uint32_t slen = (uint32_t)((uint64_t)(c.n0 + rb) * c.a.G * 2u - s0a);
-    const int nc = (int)((clen + 1023u) >> 10);
-    const int ns = (int)((slen + 1023u) >> 10);
-    const uint8_t *gc = c.a.blob + c.a.off_codes + c0;
-    const uint8_t *gs = c.a.blob + c.a.off_scales + s0a;
-    int cnt = 0;
-    for (int j = (wave - v % kW + kW) % kW; j < nc + ns; j += kW) {
-        if (j < nc) {
-            const uint32_t off = (uint32_t)j * 1024u + lane * 16u;
-            if (off < clen)
-                dma16(gc + off, lds_addr(dst + j * 1024));
-        } else {
-            const uint32_t off = (uint32_t)(j - nc) * 1024u + lane * 16u;
-            if (off < slen)
-                dma16(gs + off, lds_addr(dst + c.a.cap + (j - nc) * 1024));
-        }
-        cnt++;
+    return c.L.ring + (uint32_t)(kRing * c.a.cap) + (uint32_t)slot * scale_area(c.a.cap);
+}
+
+__device__ __forceinline__ Copy make_copy(const Ctx &c, uint32_t o0, uint32_t o1, int ra, int rb, int slot, int v)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Copy k;
+    const uint64_t s0a = ((uint64_t)(c.n0 + ra) * c.a.G * 2u) & ~15ull;
+    k.clen = (o1 - o0) * 128u;
+    k.slen = (uint32_t)((uint64_t)(c.n0 + rb) * c.a.G * 2u - s0a);
+    k.nc = (int)((k.clen + 1023u) >> 10);
+    k.n = k.nc + (int)((k.slen + 1023u) >> 10);
+    k.gc = c.a.blob + c.a.off_codes + (uint64_t)o0 * 128u;
+    k.gs = c.a.blob + c.a.off_scales + s0a;
+    k.dst = lds_addr(c.smem + slot_codes(c, slot));
+    k.sdst = lds_addr(c.smem + slot_scales(c, slot));
+    k.j = (wave - v % kW + kW) % kW;
+    return k;
+}
+
+// Issues this wave's next chunk, if any; returns 1 if it issued one.
+__device__ __forceinline__ int issue_next(const Ctx &c, Copy &k)
+{
+    if (k.j >= k.n)
+        return 0;
+    const int lane = threadIdx.x & 63;
+    if (k.j < k.nc) {
+        const uint32_t off = (uint32_t)k.j * 1024u + lane * 16u;
+        if (off < k.clen)
+            dma16(k.gc + off, k.dst + k.j * 1024u);
+    } else {
+        const uint32_t off = (uint32_t)(k.j - k.nc) * 1024u + lane * 16u;
+        if (off < k.slen)
+            dma16(k.gs + off, k.sdst + (k.j - k.nc) * 1024u);
     }
+    k.j += kW;
+    return 1;
+}
+
+__device__ __forceinline__ int issue_all(const Ctx &c, Copy &k)
+{
+    int cnt = 0;
+    while (issue_next(c, k))
+        cnt++;
     return cnt;
 }
 
 // Descriptors of the row-slices of rows [ra, rb), built by one wave (lane l
 // holds row-slices 2l and 2l+1):
 //   d0, d1    width bit planes
-//   d2        row in sub-unit << 12 | first group column of the slice << 19
+//   d2        row in sub-unit << 13 | first group column of the slice << 20
 //   d3        valid groups
 //   d4+3c     groups of width c (mask)
 //   d5+3c     slot of the first half-0 group of width c | (slot of the first
@@ -267,7 +300,7 @@ __device__ void build_info(const Ctx &c, int ra, int rb, int buf)
         if (i < nrs) {
             uint32_t *d = info + i * kInfo;
             reinterpret_cast<uint4 *>(d)[0] =
-                make_uint4(p0[j], p1[j], ((uint32_t)r[j] << 12) | ((uint32_t)(32 * s[j]) << 19), (uint32_t)ng[j]);
+                make_uint4(p0[j], p1[j], ((uint32_t)r[j] << 13) | ((uint32_t)(32 * s[j]) << 20), (uint32_t)ng[j]);
             uint32_t bb = 0;
 #pragma unroll
             for (int k = 0; k < 4; k++) {
@@ -293,26 +326,23 @@ __device__ void build_info(const Ctx &c, int ra, int rb, int buf)
     }
 }
 
-// Slot-table entries of rows [ra, rb): thread = (row-slice, group).
-// entry = code offset / 8 (12 bits) | row in sub-unit (7 bits) << 12 | group column << 19
-__device__ __forceinline__ void build_table(const Ctx &c, int ra, int rb, int buf)
+template <int kPer> // rounds of 32 row-slices
+__device__ __forceinline__ void build_table_n(const Ctx &c, int nrs, int buf)
 {
-    constexpr int kPer = kMaxRS * 32 / kT; // (row-slice, group) items per thread
     const int tid = threadIdx.x;
-    const int nrs = (rb - ra) * c.a.nS;
     const uint32_t *info = reinterpret_cast<const uint32_t *>(c.smem + c.L.info) + buf * kMaxRS * kInfo;
     uint32_t *table = reinterpret_cast<uint32_t *>(c.smem + c.L.table);
     const uint32_t g = tid & 31;
-    const uint32_t lt = (1u << g) - 1u, hsh = g < 16 ? 0u : 16u, gx = g << 19;
+    const uint32_t lt = (1u << g) - 1u, hsh = g < 16 ? 0u : 16u, gx = g << 20;
     // all descriptor reads first: two LDS round trips for the whole table
     uint4 d0[kPer];
-    bool on[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         const int i = (tid >> 5) + k * (kT / 32);
         d0[k] = i < nrs ? *reinterpret_cast<const uint4 *>(info + i * kInfo) : make_uint4(0u, 0u, 0u, 0u);
     }
     uint32_t cc[kPer], m[kPer], sb[kPer], cb[kPer];
+    bool on[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         const int i = (tid >> 5) + k * (kT / 32);
@@ -333,6 +363,19 @@ __device__ __forceinline__ void build_table(const Ctx &c, int ra, int rb, int bu
     }
 }
 
+// Slot-table entries of rows [ra, rb): thread = (row-slice, group).
+// entry = code offset / 8 (13 bits) | row in sub-unit (7 bits) << 13 | group column << 20
+__device__ __forceinline__ void build_table(const Ctx &c, int ra, int rb, int buf)
+{
+    const int nrs = (rb - ra) * c.a.nS;
+    switch ((nrs + 31) >> 5) {
+    case 1: build_table_n<1>(c, nrs, buf); break;
+    case 2: build_table_n<2>(c, nrs, buf); break;
+    case 3: build_table_n<3>(c, nrs, buf); break;
+    default: build_table_n<4>(c, nrs, buf); break;
+    }
+}
+
 // One pass: 64 slots of width B.
 template <int B, int MT>
 __device__ __forceinline__ void run_pass(const Ctx &c, int p, int end_slot, const uint32_t *table,
@@ -344,8 +387,8 @@ __device__ __forceinline__ void run_pass(const Ctx &c, int p, int end_slot, cons
     if (slot >= end_slot)
         return;
     const uint32_t e = table[slot];
-    const uint32_t code8 = e & 0xfffu, row = (e >> 12) & 127u, xcol = e >> 19;
-    const uint32_t sidx = row * (uint32_t)c.a.G + xcol;
+    const uint32_t code8 = e & 0x1fffu, row = (e >> 13) & 127u, xcol = e >> 20;
+    const uint32_t sidx = __umul24(row, (uint32_t)c.a.G) + xcol;
     uint32_t w[2 * B];
     const U2 *src = reinterpret_cast<const U2 *>(codes + code8 * 8u);
 #pragma unroll
@@ -381,50 +424,63 @@ __device__ __forceinline__ void run_pass(const Ctx &c, int p, int end_slot, cons
 
 // x records for all of K: fp16 pairs (x_p, x_{p+32}), then per width
 // C_b = sum_p 2^(10-pos_b(p)) (x_p + x_{p+32}) + (2^b-1)/2 sum_j x_j.
-// Item = (token, group, quarter q): pairs 4q..4q+3.  Loads are issued by the
-// caller's loop all at once; the 8 items of a group are 8 adjacent lanes.
+// Item = (token, group, quarter q): pairs 4q..4q+3; the 8 items of a group are
+// 8 adjacent lanes.  Loading and storing are separate so the loads can be
+// issued together with the other prologue loads.
 template <int MT>
-__device__ __forceinline__ void stage_x(const Ctx &c, uint32_t *xrec)
+struct XStage {
+    static constexpr int kPer = (MT * 256 * 8 + kT - 1) / kT; // items per thread (G < 256)
+    uint32_t lo0[kPer], lo1[kPer], hi0[kPer], hi1[kPer];
+};
+
+template <int MT>
+__device__ __forceinline__ void stage_x_load(const Ctx &c, XStage<MT> &xs)
 {
     const int tid = threadIdx.x;
     const int G = c.a.G;
     const int items = MT * G * 8;
     const bool vec = (c.a.ldx % 4) == 0 && ((uintptr_t)c.a.x % 8) == 0;
-    constexpr int kPer = (MT * 256 * 8 + kT - 1) / kT; // items per thread (G < 256)
-    uint32_t lo0[kPer], lo1[kPer], hi0[kPer], hi1[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; k++) {
+    for (int k = 0; k < XStage<MT>::kPer; k++) {
         const int i = tid + k * kT;
-        lo0[k] = lo1[k] = hi0[k] = hi1[k] = 0u;
+        xs.lo0[k] = xs.lo1[k] = xs.hi0[k] = xs.hi1[k] = 0u;
         if (i < items) {
             const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
-            const uint16_t *xs = c.a.x + (uint64_t)m * c.a.ldx + 64ull * g + 4 * q;
+            const uint16_t *p = c.a.x + (uint64_t)m * c.a.ldx + 64ull * g + 4 * q;
             if (vec) {
-                const uint2 va = *reinterpret_cast<const uint2 *>(xs);
-                const uint2 vb = *reinterpret_cast<const uint2 *>(xs + 32);
-                lo0[k] = va.x;
-                lo1[k] = va.y;
-                hi0[k] = vb.x;
-                hi1[k] = vb.y;
+                const uint2 va = *reinterpret_cast<const uint2 *>(p);
+                const uint2 vb = *reinterpret_cast<const uint2 *>(p + 32);
+                xs.lo0[k] = va.x;
+                xs.lo1[k] = va.y;
+                xs.hi0[k] = vb.x;
+                xs.hi1[k] = vb.y;
             } else {
-                lo0[k] = xs[0] | ((uint32_t)xs[1] << 16);
-                lo1[k] = xs[2] | ((uint32_t)xs[3] << 16);
-                hi0[k] = xs[32] | ((uint32_t)xs[33] << 16);
-                hi1[k] = xs[34] | ((uint32_t)xs[35] << 16);
+                xs.lo0[k] = p[0] | ((uint32_t)p[1] << 16);
+                xs.lo1[k] = p[2] | ((uint32_t)p[3] << 16);
+                xs.hi0[k] = p[32] | ((uint32_t)p[33] << 16);
+                xs.hi1[k] = p[34] | ((uint32_t)p[35] << 16);
             }
         }
     }
+}
+
+template <int MT>
+__device__ __forceinline__ void stage_x_store(const Ctx &c, const XStage<MT> &xs, uint32_t *xrec)
+{
+    const int tid = threadIdx.x;
+    const int G = c.a.G;
+    const int items = MT * G * 8;
 #pragma unroll
-    for (int k = 0; k < kPer; k++) {
+    for (int k = 0; k < XStage<MT>::kPer; k++) {
         const int i = tid + k * kT;
         if (i >= items) // whole groups of 8 lanes drop out together
             break;
         const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
         U4 o;
-        o.v[0] = __builtin_amdgcn_perm(hi0[k], lo0[k], 0x05040100u); // (x_p, x_{p+32})
-        o.v[1] = __builtin_amdgcn_perm(hi0[k], lo0[k], 0x07060302u);
-        o.v[2] = __builtin_amdgcn_perm(hi1[k], lo1[k], 0x05040100u);
-        o.v[3] = __builtin_amdgcn_perm(hi1[k], lo1[k], 0x07060302u);
+        o.v[0] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x05040100u); // (x_p, x_{p+32})
+        o.v[1] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x07060302u);
+        o.v[2] = __builtin_amdgcn_perm(xs.hi1[k], xs.lo1[k], 0x05040100u);
+        o.v[3] = __builtin_amdgcn_perm(xs.hi1[k], xs.lo1[k], 0x07060302u);
         uint32_t *xr = xrec + ((uint32_t)m * G + g) * kXRec;
         *reinterpret_cast<U4 *>(xr + 4 * q) = o;
         float X = 0.f, c1 = 0.f, c2 = 0.f, c4 = 0.f;
@@ -467,20 +523,30 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
     c.smem = smem;
     c.L = s_layout(MT, a.G, a.rows, a.nS, a.cap);
     const int nS = a.nS, G = a.G, R = c.R;
-    const uint32_t sbytes = slot_bytes(a.cap);
     uint32_t *rowoff = reinterpret_cast<uint32_t *>(smem + c.L.rowoff);
     uint32_t *sloff = reinterpret_cast<uint32_t *>(smem + c.L.sloff);
     uint32_t *wmap = reinterpret_cast<uint32_t *>(smem + c.L.wmap);
     uint32_t *xrec = reinterpret_cast<uint32_t *>(smem + c.L.x);
     const uint32_t *table = reinterpret_cast<const uint32_t *>(smem + c.L.table);
     float *psum = reinterpret_cast<float *>(smem + c.L.psum);
+    float *ybuf = reinterpret_cast<float *>(smem + c.L.ybuf);
 
-    // ---- metadata of this workgroup's rows, and the activations
+    // ---- metadata of this workgroup's rows, the activations, and (in every
+    // wave) the row offsets of the first kMaxRS rows: the first sub-unit's copy
+    // is issued as soon as they arrive, before x is staged
+    int ra = 0, rb, rc;
     {
         const uint32_t *g_row = reinterpret_cast<const uint32_t *>(a.blob + a.off_row_off) + c.n0;
         const uint32_t *g_slo = reinterpret_cast<const uint32_t *>(a.blob + a.off_slice_off) + (uint64_t)c.n0 * nS;
         const uint32_t *g_wm = reinterpret_cast<const uint32_t *>(a.blob + a.off_wmap) + 2ull * c.n0 * nS;
         const int nrs = R * nS;
+        uint32_t win[kMaxRS / 64];
+#pragma unroll
+        for (int h = 0; h < kMaxRS / 64; h++)
+            win[h] = g_row[min(lane + 1 + 64 * h, R)];
+        const uint32_t win0 = g_row[0];
+        XStage<MT> xs;
+        stage_x_load<MT>(c, xs);
         uint32_t r0 = 0, r1 = 0, sl = 0, w0 = 0, w1 = 0;
         if (tid <= R)
             r0 = g_row[tid];
@@ -492,7 +558,37 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
             w0 = g_wm[tid];
         if (tid + kT < 2 * nrs)
             w1 = g_wm[tid + kT];
-        stage_x<MT>(c, xrec);
+        {
+            // rows of the first sub-unit, from registers (same rule as next_end).
+            // When the whole block fits both ring slots it is one sub-unit.
+            const int kmax = min(kMaxRS / nS, R);
+            uint32_t endR = 0;
+#pragma unroll
+            for (int h = 0; h < kMaxRS / 64; h++)
+                if ((R - 1) >> 6 == h)
+                    endR = __shfl(win[h], (R - 1) & 63);
+            const bool single = R <= kmax && (endR - win0) * 128u <= 2u * (uint32_t)a.cap;
+            const uint32_t cap = single ? 2u * (uint32_t)a.cap : (uint32_t)a.cap;
+            int n = 0;
+#pragma unroll
+            for (int h = 0; h < kMaxRS / 64; h++) {
+                const int k = lane + 1 + 64 * h;
+                n += (int)__popcll(__ballot(k <= kmax && (win[h] - win0) * 128u <= cap));
+            }
+            rb = n;
+            // the row offset that ends it: lane (rb - 1) % 64 of window half (rb - 1) / 64
+            const int src = (rb - 1) & 63;
+            uint32_t end = __shfl(win[0], src);
+#pragma unroll
+            for (int h = 1; h < kMaxRS / 64; h++)
+                if ((rb - 1) >> 6 == h)
+                    end = __shfl(win[h], src);
+            Copy k0 = make_copy(c, win0, end, 0, rb, 0, 0);
+            issue_all(c, k0);
+        }
+        // no global loads after this point of the prologue: the compiler's waits
+        // for the loads above cannot pick up the copy just issued
+        stage_x_store<MT>(c, xs, xrec);
         if (tid <= R)
             rowoff[tid] = r0;
         if (tid + kT <= R)
@@ -507,39 +603,41 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
     __syncthreads();
 
     // ---- sub-units u and u+1 start at rows ra and rb; rc ends u+1
-    int ra = 0, rb = next_end(c, 0), rc = next_end(c, rb);
+    rc = next_end(c, rb);
     int slot = 0;
-    issue_subunit(c, ra, rb, 0, 0);
     if (wave == 0)
         build_info(c, ra, rb, 0);
     __syncthreads();
 
     for (int u = 0; ra < R; u++) {
         const int buf = u & 1;
-        // prefetch u+1 into the slot that u-1 used (its passes are done)
-        int l1 = 0;
-        if (rb < R)
-            l1 = issue_subunit(c, rb, rc, slot ^ 1, u + 1);
         build_table(c, ra, rb, buf);
-        wait_vm(l1); // this wave's chunks of u have landed
+        wait_vm(0); // this wave's chunks of u (the only vector-memory ops in the loop)
         __syncthreads();
 
         // ---- passes of u, handed out through an LDS counter; wave 0 first
-        // describes u+1
+        // describes u+1.  The copy of u+1 into the slot that u-1 used goes out
+        // one chunk per pass.
+        int l1 = 0;
         {
+            const uint32_t *rowoff_l = rowoff;
+            Copy k1 = make_copy(c, rowoff_l[rb], rowoff_l[rc], rb, rc, slot ^ 1, u + 1);
+            if (rb >= R)
+                k1.n = 0;
             if (wave == 0 && rb < R)
                 build_info(c, rb, rc, buf ^ 1);
             uint32_t *hdr = reinterpret_cast<uint32_t *>(smem + c.L.hdr) + buf * 16;
             const uint4 h0 = *reinterpret_cast<const uint4 *>(hdr);
             const uint4 h1 = *reinterpret_cast<const uint4 *>(hdr + 4);
             const int np = (int)h0.x, pb1 = (int)h0.y, pb2 = (int)h0.z, pb3 = (int)h0.w;
-            const uint8_t *codes = smem + c.L.ring + slot * sbytes;
+            const uint8_t *codes = smem + slot_codes(c, slot);
             const uint64_t s0 = (uint64_t)(c.n0 + ra) * G * 2u;
-            const uint16_t *scales = reinterpret_cast<const uint16_t *>(codes + a.cap + (s0 & 15u));
+            const uint16_t *scales = reinterpret_cast<const uint16_t *>(smem + slot_scales(c, slot) + (s0 & 15u));
             for (;;) {
                 int p = 0;
                 if (lane == 0)
                     p = (int)atomicAdd(hdr + 8, 1u);
+                l1 += issue_next(c, k1);
                 p = __builtin_amdgcn_readfirstlane(p);
                 if (p >= np)
                     break;
@@ -552,6 +650,7 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
                 else
                     run_pass<8, MT>(c, p, 64 * pb3 + (int)h1.w, table, codes, scales, xrec, psum);
             }
+            l1 += issue_all(c, k1);
         }
         __syncthreads();
 
@@ -569,21 +668,28 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
                     v += __shfl_xor(v, 4, 8);
                     v += __shfl_xor(v, 2, 8);
                     v += __shfl_xor(v, 1, 8);
-                    if (q == 0) {
-                        const uint64_t o = (uint64_t)m * a.ldy + c.n0 + ra + j;
-                        if (a.yt == VBQ_F16)
-                            reinterpret_cast<__half *>(a.y)[o] = __float2half_rn(v);
-                        else
-                            reinterpret_cast<float *>(a.y)[o] = v;
-                    }
+                    if (q == 0)
+                        ybuf[m * a.rows + ra + j] = v;
                 }
             }
         }
         // ---- advance
+        (void)l1;
         ra = rb;
         rb = rc;
         rc = next_end(c, rc);
         slot ^= 1;
+    }
+    // ---- y of this workgroup's rows, coalesced
+    __syncthreads();
+    for (int i = tid; i < MT * R; i += kT) {
+        const int m = i / R, r = i - m * R;
+        const float v = ybuf[m * a.rows + r];
+        const uint64_t o = (uint64_t)m * a.ldy + c.n0 + r;
+        if (a.yt == VBQ_F16)
+            reinterpret_cast<__half *>(a.y)[o] = __float2half_rn(v);
+        else
+            reinterpret_cast<float *>(a.y)[o] = v;
     }
 }
 
@@ -628,10 +734,10 @@ bool stream_gemv(const GemvCall &g, vbq_status *st)
     int rows = (N + cus - 1) / cus;
     rows = std::max(1, std::min(rows, kMetaRS / nS));
     const int grid = (N + rows - 1) / rows;
-    // the largest sub-unit that fits LDS; every row record (8 bytes per bit of
-    // width, padded to 128) must fit one sub-unit
+    // the largest sub-unit (1 KiB steps) that fits LDS; every row record
+    // (8 bytes per bit of width, padded to 128) must fit one sub-unit
     int cap = 0;
-    for (int cand : {kMaxCap, 24576, 16384}) {
+    for (int cand = kMaxCap; cand >= 8192; cand -= 1024) {
         if ((uint64_t)G * 64u + 128u > (uint64_t)cand)
             break;
         if (s_layout(g.M, G, rows, nS, cand).total <= 160u * 1024u) {
