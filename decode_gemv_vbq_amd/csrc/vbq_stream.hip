@@ -239,17 +239,41 @@ __device__ __forceinline__ int issue_all(const Ctx &c, Copy &k)
 //   d6+3c     record start / 8 + bucket start / 8 of width c
 // Slots of width c are ordered (group half, row-slice, rank) and each width
 // starts on a 64-slot pass boundary.  Also resets the sub-unit's pass counter.
-__device__ void build_info(const Ctx &c, int ra, int rb, int buf)
+// Inputs of build_info for lane l's row-slices 2l and 2l+1 of the sub-unit
+// starting at row ra: width planes, slice offset, row offset relative to row ra.
+struct InfoIn {
+    uint32_t p0[2], p1[2], slo[2], roff[2];
+};
+
+__device__ __forceinline__ void info_in_lds(const Ctx &c, int ra, int rb, InfoIn &in)
 {
     const int lane = threadIdx.x & 63;
-    const int nS = c.a.nS, G = c.a.G;
+    const int nS = c.a.nS;
     const uint32_t *rowoff = reinterpret_cast<const uint32_t *>(c.smem + c.L.rowoff);
     const uint32_t *sloff = reinterpret_cast<const uint32_t *>(c.smem + c.L.sloff);
     const uint32_t *wmap = reinterpret_cast<const uint32_t *>(c.smem + c.L.wmap);
+    const int nrs = (rb - ra) * nS;
+    const uint32_t base0 = rowoff[ra];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int i = 2 * lane + j;
+        const bool live = i < nrs;
+        const int r = (int)(((uint32_t)i * (uint32_t)c.a.inv_nS) >> 16);
+        const int w = live ? ra * nS + i : 0;
+        in.p0[j] = live ? wmap[2 * w] : 0u;
+        in.p1[j] = live ? wmap[2 * w + 1] : 0u;
+        in.slo[j] = live ? sloff[w] : 0u;
+        in.roff[j] = live ? rowoff[ra + r] - base0 : 0u;
+    }
+}
+
+__device__ void build_info(const Ctx &c, int ra, int rb, int buf, const InfoIn &in)
+{
+    const int lane = threadIdx.x & 63;
+    const int nS = c.a.nS, G = c.a.G;
     uint32_t *info = reinterpret_cast<uint32_t *>(c.smem + c.L.info) + buf * kMaxRS * kInfo;
     uint32_t *hdr = reinterpret_cast<uint32_t *>(c.smem + c.L.hdr) + buf * 16;
     const int nrs = (rb - ra) * nS;
-    const uint32_t base0 = rowoff[ra];
     uint32_t p0[2], p1[2], m[2][4], rec8[2];
     int ng[2], r[2], s[2], cnt[2][4], h0[2][4];
 #pragma unroll
@@ -258,10 +282,9 @@ __device__ void build_info(const Ctx &c, int ra, int rb, int buf)
         const bool live = i < nrs;
         r[j] = (int)(((uint32_t)i * (uint32_t)c.a.inv_nS) >> 16);
         s[j] = i - r[j] * nS;
-        const int w = live ? ra * nS + i : 0;
-        p0[j] = live ? wmap[2 * w] : 0u;
-        p1[j] = live ? wmap[2 * w + 1] : 0u;
-        rec8[j] = live ? ((rowoff[ra + r[j]] - base0) * 128u + sloff[w]) >> 3 : 0u;
+        p0[j] = live ? in.p0[j] : 0u;
+        p1[j] = live ? in.p1[j] : 0u;
+        rec8[j] = live ? (in.roff[j] * 128u + in.slo[j]) >> 3 : 0u;
         ng[j] = live ? max(0, min(32, G - 32 * s[j])) : 0;
         const WidthMasks wm = width_masks(p0[j], p1[j], ng[j]);
 #pragma unroll
@@ -533,7 +556,7 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
 
     // ---- metadata of this workgroup's rows, the activations, and (in every
     // wave) the row offsets of the first kMaxRS rows: the first sub-unit's copy
-    // is issued as soon as they arrive, before x is staged
+    // is issued and described as soon as they arrive, before x is staged
     int ra = 0, rb, rc;
     {
         const uint32_t *g_row = reinterpret_cast<const uint32_t *>(a.blob + a.off_row_off) + c.n0;
@@ -547,6 +570,21 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
         const uint32_t win0 = g_row[0];
         XStage<MT> xs;
         stage_x_load<MT>(c, xs);
+        // wave 0 also reads the first sub-unit's row-slice inputs into registers
+        // (up to kMaxRS row-slices; build_info masks those past the sub-unit)
+        InfoIn in0;
+        if (wave == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int i = 2 * lane + j;
+                const bool live = i < nrs;
+                const int r = (int)(((uint32_t)i * (uint32_t)a.inv_nS) >> 16);
+                in0.p0[j] = live ? g_wm[2 * i] : 0u;
+                in0.p1[j] = live ? g_wm[2 * i + 1] : 0u;
+                in0.slo[j] = live ? g_slo[i] : 0u;
+                in0.roff[j] = live ? g_row[r] : 0u; // made relative after the loads land
+            }
+        }
         uint32_t r0 = 0, r1 = 0, sl = 0, w0 = 0, w1 = 0;
         if (tid <= R)
             r0 = g_row[tid];
@@ -585,6 +623,11 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
                     end = __shfl(win[h], src);
             Copy k0 = make_copy(c, win0, end, 0, rb, 0, 0);
             issue_all(c, k0);
+            if (wave == 0) {
+                in0.roff[0] -= win0;
+                in0.roff[1] -= win0;
+                build_info(c, 0, rb, 0, in0);
+            }
         }
         // no global loads after this point of the prologue: the compiler's waits
         // for the loads above cannot pick up the copy just issued
@@ -605,9 +648,6 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
     // ---- sub-units u and u+1 start at rows ra and rb; rc ends u+1
     rc = next_end(c, rb);
     int slot = 0;
-    if (wave == 0)
-        build_info(c, ra, rb, 0);
-    __syncthreads();
 
     for (int u = 0; ra < R; u++) {
         const int buf = u & 1;
@@ -624,8 +664,11 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
             Copy k1 = make_copy(c, rowoff_l[rb], rowoff_l[rc], rb, rc, slot ^ 1, u + 1);
             if (rb >= R)
                 k1.n = 0;
-            if (wave == 0 && rb < R)
-                build_info(c, rb, rc, buf ^ 1);
+            if (wave == 0 && rb < R) {
+                InfoIn in;
+                info_in_lds(c, rb, rc, in);
+                build_info(c, rb, rc, buf ^ 1, in);
+            }
             uint32_t *hdr = reinterpret_cast<uint32_t *>(smem + c.L.hdr) + buf * 16;
             const uint4 h0 = *reinterpret_cast<const uint4 *>(hdr);
             const uint4 h1 = *reinterpret_cast<const uint4 *>(hdr + 4);
