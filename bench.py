@@ -3,9 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode9b]
 
-One step = every GEMV of one synthetic decoder step (stage order qkv, o, gate,
-up, down per layer, then the LM head), M = 1, weights packed in VBQ1 and
-resident in HBM before timing.  Prints ONE JSON line with us/step, the
+One step = every GEMV of one synthetic decoder step (stage order qkv, o,
+gate||up, down per layer, then the LM head; gate and up read the same
+activations and share one launch), M = 1, weights packed in VBQ1 and resident
+in HBM before timing.  Prints ONE JSON line with us/step, the
 achieved algorithmic HBM bandwidth of the GEMV kernel (per-launch duration from
 HIP events around the captured step graph, on the launch stream),
 the on-GPU fp16 dense control and the CPU oracle timed on a bounded sample of
@@ -144,9 +145,9 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench needs a GPU"
     log(f"{v.version()} on {torch.cuda.get_device_name(0)}")
     step = DecodeStep(args.workload, M=1, log=log)
-    n_launch = len(step.mats)
+    n_launch = len(step.stages)
     alg = step.alg_bytes()
-    log(f"{args.workload}: {n_launch} GEMVs, {step.weights() / 1e9:.3f} B weights, mean {step.mean_bits():.3f} bits, "
+    log(f"{args.workload}: {len(step.mats)} GEMVs in {n_launch} launches, {step.weights() / 1e9:.3f} B weights, mean {step.mean_bits():.3f} bits, "
         f"{alg / 1e6:.1f} MB algorithmic, {step.layout_bytes() / 1e6:.1f} MB with row padding")
 
     fn = step.run
@@ -158,25 +159,25 @@ def main(argv=None):
     ms = time_steps(torch, fn, args.steps)
     log(f"step: {ms * 1e3:.1f} us ({args.mode}), {alg / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
 
-    # per-launch kernel durations: for each matrix kind, that kind's launches of
+    # per-launch kernel durations: for each stage kind, that kind's launches of
     # one step captured back to back in a graph (events on the launch stream)
     kinds = {}
     kern_ms = 0.0
     names = []
-    for m in step.mats:
-        if m.spec.name not in names:
-            names.append(m.spec.name)
+    for st in step.stages:
+        if step.stage_name(st) not in names:
+            names.append(step.stage_name(st))
     for name in names:
-        idx = [i for i, m in enumerate(step.mats) if m.spec.name == name]
-        g = step.capture_subset(idx)
+        sts = [st for st in step.stages if step.stage_name(st) == name]
+        g = step.capture_stages(sts)
         for _ in range(2):
             g.replay()
         reps = max(2, args.kernel_steps)
-        t = time_steps(torch, g.replay, reps) / len(idx)  # ms per launch
+        t = time_steps(torch, g.replay, reps) / len(sts)  # ms per launch
         del g
-        bts = sum(acc.vbq_read_bytes(step.mats[i].L, step.M) for i in idx) / len(idx)
-        kinds[name] = {"launches": len(idx), "us": round(t * 1e3, 2), "GBps": round(bts / (t * 1e-3) / 1e9, 1)}
-        kern_ms += t * len(idx)
+        bts = sum(acc.vbq_read_bytes(step.mats[i].L, step.M) for st in sts for i in st) / len(sts)
+        kinds[name] = {"launches": len(sts), "us": round(t * 1e3, 2), "GBps": round(bts / (t * 1e-3) / 1e9, 1)}
+        kern_ms += t * len(sts)
     # the roofline uses the cold step: its launches run back to back in the graph,
     # so the average launch duration is the step time over the launch count
     avg_launch_s = ms * 1e-3 / n_launch
@@ -224,7 +225,8 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": args.workload, "M": 1, "gemvs_per_step": n_launch, "launch": args.mode,
+            "workload": args.workload, "M": 1, "gemvs_per_step": len(step.mats), "launches_per_step": n_launch,
+            "launch": args.mode,
             "weights": step.weights(), "mean_bits": round(step.mean_bits(), 4),
             "alg_bytes_per_step": alg, "layout_bytes_per_step": step.layout_bytes(),
             "GBps_step": round(gbps, 1), "pct_peak_step": round(100 * gbps * 1e9 / PEAK_HBM, 2),

@@ -26,8 +26,10 @@ STATUS = {
 EXPORTS = (
     "vbq_version", "vbq_status_string", "vbq_last_error", "vbq_layout_init", "vbq_layout_from_header",
     "vbq_pack_plan_workspace", "vbq_pack_plan", "vbq_pack", "vbq_status_check", "vbq_dequant",
-    "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_dense_f16_gemv",
+    "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_shared",
+    "vbq_dense_f16_gemv",
 )
+MAX_SHARED = 4
 
 
 class VbqError(RuntimeError):
@@ -36,6 +38,11 @@ class VbqError(RuntimeError):
         super().__init__(f"{what}: {name}" + (f" ({detail})" if detail else ""))
         self.code = code
         self.name = name
+
+
+class GemvItem(ctypes.Structure):
+    """Mirror of ``vbq_gemv_item``."""
+    _fields_ = [("L", ctypes.c_void_p), ("blob", ctypes.c_void_p), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int)]
 
 
 class Layout(ctypes.Structure):
@@ -76,6 +83,7 @@ def lib():
         L.vbq_workspace_clear.argtypes = [P, sz, P]
         L.vbq_gemv.argtypes = [LP, P, P, P, i, P, sz, P]
         L.vbq_gemv_batched.argtypes = [LP, P, i, P, i, P, i, i, P, sz, P]
+        L.vbq_gemv_shared.argtypes = [ctypes.POINTER(GemvItem), i, i, P, i, i, P]
         L.vbq_dense_f16_gemv.argtypes = [i, i, i, P, P, i, P, i, i, P]
         for f in EXPORTS:
             if f not in ("vbq_version", "vbq_status_string", "vbq_last_error", "vbq_pack_plan_workspace"):
@@ -238,6 +246,32 @@ def gemv_batched(L: Layout, blob, x, out=None, out_dtype=None, ws=None):
     _check(lib().vbq_gemv_batched(ctypes.byref(L), _ptr(blob), M, _ptr(x), x.stride(0), _ptr(out), out.stride(0), yt,
                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream()), "vbq_gemv_batched")
     return out
+
+
+def gemv_shared(mats, x, outs=None, out_dtype=None):
+    """[W_i x for (L_i, blob_i) in mats] in one launch where possible: the
+    matrices share K and the activations x ([M][K], or [K] for one token)."""
+    torch = _torch()
+    one = x.dim() == 1
+    x2 = x.view(1, -1) if one else x
+    if x2.dim() != 2 or x2.stride(1) != 1 or not x2.is_cuda:
+        raise ValueError("x must be a [M][K] device tensor with unit column stride")
+    M = x2.shape[0]
+    out_dtype = out_dtype or torch.float16
+    if outs is None:
+        outs = [torch.empty((M, L.N), dtype=out_dtype, device=x.device) for L, _ in mats]
+    items = (GemvItem * len(mats))()
+    ys = []
+    for k, ((L, blob), out) in enumerate(zip(mats, outs)):
+        _need_cuda(blob)
+        y2 = out.view(1, -1) if out.dim() == 1 else out
+        if y2.stride(1) != 1 or y2.dtype != outs[0].dtype:
+            raise ValueError("outputs must be [M][N] with unit column stride and one dtype")
+        items[k] = GemvItem(ctypes.addressof(L), _ptr(blob), _ptr(y2), y2.stride(0))
+        ys.append(y2)
+    yt = VBQ_F32 if outs[0].dtype == torch.float32 else VBQ_F16
+    _check(lib().vbq_gemv_shared(items, len(mats), M, _ptr(x2), x2.stride(0), yt, _stream()), "vbq_gemv_shared")
+    return outs
 
 
 def dense_f16_gemv(w16, x, out=None, out_dtype=None):

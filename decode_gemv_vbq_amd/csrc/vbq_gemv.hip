@@ -1130,6 +1130,38 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
     }
 }
 
+vbq_status vbq_gemv_shared(const vbq_gemv_item *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
+                           hipStream_t stream)
+{
+    if (!items || n < 1 || n > VBQ_MAX_SHARED || !x)
+        return VBQ_ERR_INVALID_ARG;
+    if (yt != VBQ_F32 && yt != VBQ_F16)
+        return VBQ_ERR_INVALID_ARG;
+    if (M < 1 || M > 16)
+        return VBQ_ERR_BATCH;
+    StreamItem st_items[VBQ_MAX_SHARED];
+    for (int i = 0; i < n; i++) {
+        const vbq_gemv_item &it = items[i];
+        if (!it.L || !it.blob || !it.y)
+            return VBQ_ERR_INVALID_ARG;
+        VBQ_TRY(check_layout(it.L));
+        if (it.L->K != items[0].L->K || ldx < (int)it.L->K || it.ldy < (int)it.L->N)
+            return VBQ_ERR_SHAPE;
+        if ((uintptr_t)it.blob % 256 || (uintptr_t)it.y % (yt == VBQ_F32 ? 4 : 2))
+            return VBQ_ERR_ALIGN;
+        st_items[i] = StreamItem{it.L, it.blob, it.y, it.ldy};
+    }
+    if ((uintptr_t)x % 2)
+        return VBQ_ERR_ALIGN;
+    vbq_status st;
+    if (stream_gemv_shared(st_items, n, M, x, ldx, yt, stream, &st))
+        return st;
+    for (int i = 0; i < n; i++) // one launch per matrix where the streaming kernel does not apply
+        VBQ_TRY(vbq_gemv_batched(items[i].L, items[i].blob, M, x, ldx, items[i].y, items[i].ldy, yt, nullptr, 0,
+                                 stream));
+    return VBQ_OK;
+}
+
 vbq_status vbq_gemv(const vbq_layout *L, const void *blob, const uint16_t *x, void *y, vbq_dtype yt, void *ws,
                     size_t ws_bytes, hipStream_t stream)
 {

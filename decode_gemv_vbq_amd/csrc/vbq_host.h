@@ -39,6 +39,19 @@ struct GemvCall {
 // fits one LDS sub-unit); returns false, launching nothing, when it does not.
 bool stream_gemv(const GemvCall &g, vbq_status *st);
 
+// One matrix of a shared-activation launch.
+struct StreamItem {
+    const vbq_layout *L;
+    const void *blob;
+    void *y;
+    int ldy;
+};
+
+// One streaming launch for up to 4 matrices with the same K that read the same
+// x; false (nothing launched) when the streaming kernel does not apply.
+bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
+                        hipStream_t stream, vbq_status *st);
+
 } // namespace vbq
 
 #define VBQ_TRY(expr)                                                                                                 \

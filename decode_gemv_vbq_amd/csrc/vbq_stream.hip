@@ -40,11 +40,11 @@ namespace {
 
 constexpr int kT = 1024;                  // threads per workgroup (one per CU)
 constexpr int kW = kT / 64;               // waves per workgroup
-constexpr int kMaxCap = 32768;            // code bytes of one sub-unit, at most
-constexpr int kMaxRS = 128;               // row-slices of one sub-unit
+constexpr int kMaxCap = kT * 32;          // code bytes of one sub-unit, at most
+constexpr int kMaxRS = kT / 8;            // row-slices of one sub-unit (8 lanes per row in the row phase)
 constexpr int kRing = 2;                  // sub-units resident: one computing, one in flight
 constexpr int kMaxSlots = kMaxRS * 32 + 4 * 64;   // slot table incl. per-width pass padding
-constexpr int kMetaRS = 1024;             // row-slices of metadata per workgroup
+constexpr int kMetaRS = kT;               // row-slices of metadata per workgroup (one load round each)
 constexpr int kXRec = 36;                 // dwords per x record: 32 pairs + 4 constants
 constexpr int kInfo = 16;                 // dwords per row-slice descriptor
 constexpr int kPsum = kMaxRS * 32;        // partials per token
@@ -55,17 +55,31 @@ constexpr int kPsum = kMaxRS * 32;        // partials per token
 __host__ __device__ constexpr uint32_t scale_area(int cap) { return (uint32_t)(cap / 4 + 128); }
 __host__ __device__ constexpr uint32_t ring_bytes(int cap) { return (uint32_t)kRing * ((uint32_t)cap + scale_area(cap)); }
 
-struct SArgs {
+constexpr int kMaxMats = 4; // matrices sharing x in one launch
+
+// One matrix of a launch: its blob, outputs and first workgroup.
+struct SMat {
     const uint8_t *blob;
     uint64_t off_row_off, off_slice_off, off_wmap, off_scales, off_codes;
-    int N, G, nS, M;
-    const uint16_t *x;
-    int ldx;
     void *y;
-    int ldy, yt;
+    int N, ldy, wg0;
+};
+
+struct SArgs {
+    // the matrix of this workgroup, filled from mats[] at kernel start
+    const uint8_t *blob;
+    uint64_t off_row_off, off_slice_off, off_wmap, off_scales, off_codes;
+    void *y;
+    int N, ldy;
+    // shared by all matrices of the launch (same K)
+    int G, nS, M;
+    const uint16_t *x;
+    int ldx, yt;
     int rows;   // rows per workgroup
     int cap;    // code bytes per sub-unit (multiple of 1024, 8192..kMaxCap)
     int inv_nS; // ceil(65536 / nS): i / nS == (i * inv_nS) >> 16 for i < kMaxRS
+    int nmat;
+    SMat mats[kMaxMats];
 };
 
 // LDS carve-up, computed identically on the host (size) and the device.
@@ -349,7 +363,7 @@ __device__ void build_info(const Ctx &c, int ra, int rb, int buf, const InfoIn &
     }
 }
 
-template <int kPer> // rounds of 32 row-slices
+template <int kPer> // rounds of kT / 32 row-slices
 __device__ __forceinline__ void build_table_n(const Ctx &c, int nrs, int buf)
 {
     const int tid = threadIdx.x;
@@ -391,7 +405,9 @@ __device__ __forceinline__ void build_table_n(const Ctx &c, int nrs, int buf)
 __device__ __forceinline__ void build_table(const Ctx &c, int ra, int rb, int buf)
 {
     const int nrs = (rb - ra) * c.a.nS;
-    switch ((nrs + 31) >> 5) {
+    constexpr int kRoundRS = kT / 32; // row-slices per round
+    static_assert(kMaxRS <= 4 * kRoundRS, "at most four rounds");
+    switch ((nrs + kRoundRS - 1) / kRoundRS) {
     case 1: build_table_n<1>(c, nrs, buf); break;
     case 2: build_table_n<2>(c, nrs, buf); break;
     case 3: build_table_n<3>(c, nrs, buf); break;
@@ -533,13 +549,31 @@ __device__ __forceinline__ void stage_x_store(const Ctx &c, const XStage<MT> &xs
 }
 
 template <int MT>
-__global__ __launch_bounds__(kT) void k_gemv_stream(SArgs a)
+__global__ __launch_bounds__(kT) void k_gemv_stream(SArgs args)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // this workgroup's matrix: the last one whose first workgroup is <= blockIdx.x
+    SArgs a = args;
+    int wg0 = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxMats; i++) {
+        if (i < args.nmat && (int)blockIdx.x >= args.mats[i].wg0) {
+            a.blob = args.mats[i].blob;
+            a.off_row_off = args.mats[i].off_row_off;
+            a.off_slice_off = args.mats[i].off_slice_off;
+            a.off_wmap = args.mats[i].off_wmap;
+            a.off_scales = args.mats[i].off_scales;
+            a.off_codes = args.mats[i].off_codes;
+            a.y = args.mats[i].y;
+            a.N = args.mats[i].N;
+            a.ldy = args.mats[i].ldy;
+            wg0 = args.mats[i].wg0;
+        }
+    }
     Ctx c;
     c.a = a;
-    c.n0 = blockIdx.x * a.rows;
+    c.n0 = ((int)blockIdx.x - wg0) * a.rows;
     if (c.n0 >= a.N)
         return;
     c.R = min(a.rows, a.N - c.n0);
@@ -761,57 +795,105 @@ vbq_status launch_stream(const SArgs &a, int grid, size_t smem, hipStream_t stre
     return launch_status();
 }
 
+// Launch plan for n matrices of the same K sharing x, one workgroup per CU:
+// rows per workgroup, grid, sub-unit cap and LDS bytes.  False when the
+// streaming kernel does not apply.
+struct Plan {
+    int rows, grid, cap;
+    uint32_t smem;
+};
+
+bool make_plan(const StreamItem *items, int n, int M, Plan &p)
+{
+    const int G = (int)items[0].L->G, nS = (int)items[0].L->nS;
+    if (nS > kMaxRS)
+        return false;
+    int64_t total = 0;
+    for (int i = 0; i < n; i++)
+        total += items[i].L->N;
+    const int wgs = device_cus();
+    int rows = (int)((total + wgs - 1) / wgs);
+    rows = std::max(1, std::min(rows, kMetaRS / nS));
+    const uint32_t budget = 160u * 1024u;
+    // the largest sub-unit (1 KiB steps) that fits; every row record (8 bytes
+    // per bit of width, padded to 128) must fit one sub-unit
+    p.cap = 0;
+    for (int cand = kMaxCap; cand >= 8192; cand -= 1024) {
+        if ((uint64_t)G * 64u + 128u > (uint64_t)cand)
+            break;
+        if (s_layout(M, G, rows, nS, cand).total <= budget) {
+            p.cap = cand;
+            break;
+        }
+    }
+    if (!p.cap)
+        return false;
+    p.rows = rows;
+    p.smem = s_layout(M, G, rows, nS, p.cap).total;
+    p.grid = 0;
+    for (int i = 0; i < n; i++)
+        p.grid += ((int)items[i].L->N + rows - 1) / rows;
+    return true;
+}
+
+template <int MT>
+vbq_status run(const StreamItem *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt, const Plan &p,
+               hipStream_t stream)
+{
+    const int G = (int)items[0].L->G, nS = (int)items[0].L->nS;
+    SArgs a = {};
+    a.G = G;
+    a.nS = nS;
+    a.M = M;
+    a.x = x;
+    a.ldx = ldx;
+    a.yt = (int)yt;
+    a.rows = p.rows;
+    a.cap = p.cap;
+    a.inv_nS = (65536 + nS - 1) / nS;
+    a.nmat = n;
+    int wg = 0;
+    for (int i = 0; i < n; i++) {
+        const vbq_layout *L = items[i].L;
+        SMat &m = a.mats[i];
+        m.blob = (const uint8_t *)items[i].blob;
+        m.off_row_off = L->off_row_off;
+        m.off_slice_off = L->off_slice_off;
+        m.off_wmap = L->off_wmap;
+        m.off_scales = L->off_scales;
+        m.off_codes = L->off_codes;
+        m.y = items[i].y;
+        m.N = (int)L->N;
+        m.ldy = items[i].ldy;
+        m.wg0 = wg;
+        wg += (m.N + p.rows - 1) / p.rows;
+    }
+    return launch_stream<MT>(a, p.grid, p.smem, stream);
+}
+
 } // namespace
 
 namespace vbq {
 
+bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
+                        hipStream_t stream, vbq_status *st)
+{
+    if (M < 1 || M > 2 || n < 1 || n > kMaxMats)
+        return false;
+    for (int i = 1; i < n; i++)
+        if (items[i].L->K != items[0].L->K)
+            return false;
+    Plan p;
+    if (!make_plan(items, n, M, p))
+        return false;
+    *st = M == 1 ? run<1>(items, n, M, x, ldx, yt, p, stream) : run<2>(items, n, M, x, ldx, yt, p, stream);
+    return true;
+}
+
 bool stream_gemv(const GemvCall &g, vbq_status *st)
 {
-    const vbq_layout *L = g.L;
-    if (g.M < 1 || g.M > 2)
-        return false;
-    const int N = (int)L->N, G = (int)L->G, nS = (int)L->nS;
-    if (nS > kMaxRS)
-        return false;
-    const int cus = device_cus();
-    int rows = (N + cus - 1) / cus;
-    rows = std::max(1, std::min(rows, kMetaRS / nS));
-    const int grid = (N + rows - 1) / rows;
-    // the largest sub-unit (1 KiB steps) that fits LDS; every row record
-    // (8 bytes per bit of width, padded to 128) must fit one sub-unit
-    int cap = 0;
-    for (int cand = kMaxCap; cand >= 8192; cand -= 1024) {
-        if ((uint64_t)G * 64u + 128u > (uint64_t)cand)
-            break;
-        if (s_layout(g.M, G, rows, nS, cand).total <= 160u * 1024u) {
-            cap = cand;
-            break;
-        }
-    }
-    if (!cap)
-        return false;
-    const SLayout l = s_layout(g.M, G, rows, nS, cap);
-    SArgs a;
-    a.blob = (const uint8_t *)g.blob;
-    a.off_row_off = L->off_row_off;
-    a.off_slice_off = L->off_slice_off;
-    a.off_wmap = L->off_wmap;
-    a.off_scales = L->off_scales;
-    a.off_codes = L->off_codes;
-    a.N = N;
-    a.G = G;
-    a.nS = nS;
-    a.M = g.M;
-    a.x = g.x;
-    a.ldx = g.ldx;
-    a.y = g.y;
-    a.ldy = g.ldy;
-    a.yt = (int)g.yt;
-    a.rows = rows;
-    a.cap = cap;
-    a.inv_nS = (65536 + nS - 1) / nS;
-    *st = g.M == 1 ? launch_stream<1>(a, grid, l.total, g.stream) : launch_stream<2>(a, grid, l.total, g.stream);
-    return true;
+    const StreamItem it{g.L, g.blob, g.y, g.ldy};
+    return stream_gemv_shared(&it, 1, g.M, g.x, g.ldx, g.yt, g.stream, st);
 }
 
 } // namespace vbq

@@ -2,8 +2,10 @@
 
 Builds every weight matrix of a workload on the device (seeded draw -> vbq_pack),
 keeps the packed blobs, activations, outputs and workspaces, and runs the step
-as back-to-back vbq_gemv launches on one stream -- eagerly, or replayed from a
-captured HIP graph (one host launch per step).  The bench times exactly this
+as back-to-back launches on one stream -- eagerly, or replayed from a captured
+HIP graph (one host launch per step).  A stage is one GEMV, or the gate and up
+projections of a layer, which read the same activations and run as one
+vbq_gemv_shared launch.  The bench times exactly this
 object and the full-size parity test checks exactly this object.
 """
 from __future__ import annotations
@@ -39,8 +41,18 @@ class DecodeStep:
         self.graph = None
         self.graph16 = None
         rng = np.random.default_rng(12345)
+        self.stages: list[list[int]] = []
         for i, spec in enumerate(self.W.mats):
             q, bits, s, x = wl.draw_matrix_torch(spec, self.W.wid, M, self.W.outliers, device=self.device)
+            # the up projection reads the same activations as the gate projection
+            # of its layer: one stage, one launch
+            shares = (spec.name == "up" and self.mats and self.mats[-1].spec.name == "gate"
+                      and self.mats[-1].spec.layer == spec.layer and self.mats[-1].spec.K == spec.K)
+            if shares:
+                x = self.mats[-1].x
+                self.stages[-1].append(i)
+            else:
+                self.stages.append([i])
             blob, L = v.pack(q, bits, s.view(torch.float16))
             y = torch.empty((M, spec.N), dtype=self.out_dtype, device=self.device)
             ws = v.workspace(L, M, self.device)
@@ -61,27 +73,37 @@ class DecodeStep:
     # ------------------------------------------------------------- the step
     def run(self):
         """Enqueue every GEMV of the step, in stage order, on the current stream."""
-        self.run_subset(range(len(self.mats)))
+        self.run_stages(self.stages)
 
-    def run_subset(self, idx):
-        """Enqueue the GEMVs of matrices `idx` (step order) on the current stream."""
-        for i in idx:
-            m = self.mats[i]
+    def run_stage(self, st):
+        """Enqueue one stage: a single GEMV, or one launch for matrices sharing x."""
+        if len(st) == 1:
+            m = self.mats[st[0]]
             if self.M == 1:
                 v.gemv(m.L, m.blob, m.x[0], out=m.y[0], ws=m.ws)
             else:
                 v.gemv_batched(m.L, m.blob, m.x, out=m.y, ws=m.ws)
+        else:
+            ms = [self.mats[i] for i in st]
+            v.gemv_shared([(m.L, m.blob) for m in ms], ms[0].x, outs=[m.y for m in ms])
 
-    def capture_subset(self, idx):
-        """A graph of the GEMVs of matrices `idx`, back to back."""
+    def run_stages(self, stages):
+        for st in stages:
+            self.run_stage(st)
+
+    def capture_stages(self, stages):
+        """A graph of the given stages, back to back."""
         torch = self.torch
-        self.run_subset(idx)
+        self.run_stages(stages)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.run_subset(idx)
+            self.run_stages(stages)
         torch.cuda.synchronize()
         return g
+
+    def stage_name(self, st) -> str:
+        return "+".join(self.mats[i].spec.name for i in st)
 
     def capture(self):
         torch = self.torch

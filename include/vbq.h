@@ -164,6 +164,32 @@ vbq_status vbq_gemv(const vbq_layout *L /* host */, const void *blob, const uint
 vbq_status vbq_gemv_batched(const vbq_layout *L /* host */, const void *blob, int M, const uint16_t *x, int ldx,
                             void *y, int ldy, vbq_dtype yt, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* One matrix of a vbq_gemv_shared call. */
+typedef struct vbq_gemv_item {
+    const vbq_layout *L; /* host */
+    const void *blob;    /* device, 256-byte aligned, from vbq_pack */
+    void *y;             /* device, [M][ldy] in the call's yt */
+    int ldy;             /* >= L->N */
+} vbq_gemv_item;
+
+#define VBQ_MAX_SHARED 4
+
+/*
+ * y_i = W_i x for n (1..VBQ_MAX_SHARED) matrices with the same K that read the
+ * same activations x [M][ldx] (1 <= M <= 16): the fused dequantize-and-multiply
+ * of "Variable Bit-width Quantization" (mlsanity.com page, Abstract) applied to
+ * projections that share their input, such as the gate and up projections of a
+ * SwiGLU MLP block.  For M <= 2 the matrices run in ONE launch that stages x
+ * once; otherwise (or for shapes the streaming kernel does not take) they are
+ * launched one after another.  Items and layouts are host memory read during
+ * the call; x and the y_i are device memory owned by the caller.  Each y_i
+ * obeys the vbq_gemv error bound.  Errors: VBQ_ERR_INVALID_ARG (null pointers,
+ * n out of range, yt), VBQ_ERR_BATCH (M), VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE
+ * (different K, ldx < K, ldy < N), VBQ_ERR_ALIGN; nothing is launched then.
+ */
+vbq_status vbq_gemv_shared(const vbq_gemv_item *items /* host */, int n, int M, const uint16_t *x, int ldx,
+                           vbq_dtype yt, hipStream_t stream);
+
 /*
  * Dense fp16 control at the same shapes: y[M][ldy] = W16 x with W16 fp16
  * [N][K] row-major (typically vbq_dequant(..., VBQ_F16)), fp32 accumulate.

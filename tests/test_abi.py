@@ -115,3 +115,36 @@ def test_gemv_argument_checks_fail_before_launch():
     assert v.STATUS[lib.vbq_pack_plan(4, 128, fake, ctypes.byref(v.Layout()), fake, 8, null)] == "VBQ_ERR_WORKSPACE"
     assert v.STATUS[lib.vbq_pack(ref, null, fake, fake, fake, fake, null)] == "VBQ_ERR_INVALID_ARG"
     assert v.STATUS[lib.vbq_workspace_size(ref, 0, ctypes.byref(sz))] == "VBQ_ERR_BATCH"
+
+
+def test_gemv_shared_argument_checks_fail_before_launch():
+    v = vbq()
+    lib = v.lib()
+    P = ctypes.c_void_p
+    fake = 1 << 20
+    bits = np.ones((4, 64), np.uint8)
+    blob = oracle.pack(np.zeros((4, 4096), np.uint8), bits, np.ones((4, 64), np.uint16))
+    L = v.layout_from_header(blob[:256].tobytes())
+    blob2 = oracle.pack(np.zeros((4, 2048), np.uint8), np.ones((4, 32), np.uint8), np.ones((4, 32), np.uint16))
+    L2 = v.layout_from_header(blob2[:256].tobytes())  # a different K
+    null = P(0)
+
+    def call(layouts, n=None, M=1, x=fake, ldx=4096, yt=1, blob=fake, ldy=4):
+        items = (v.GemvItem * max(1, len(layouts)))()
+        for k, lay in enumerate(layouts):
+            items[k] = v.GemvItem(ctypes.addressof(lay), blob, fake, ldy)
+        return v.STATUS[lib.vbq_gemv_shared(items, len(layouts) if n is None else n, M, P(x), ldx, yt, null)]
+
+    assert call([L], n=0) == "VBQ_ERR_INVALID_ARG"
+    assert call([L] * 5) == "VBQ_ERR_INVALID_ARG"
+    assert call([L], M=0) == "VBQ_ERR_BATCH"
+    assert call([L], M=17) == "VBQ_ERR_BATCH"
+    assert call([L], x=0) == "VBQ_ERR_INVALID_ARG"
+    assert call([L], yt=9) == "VBQ_ERR_INVALID_ARG"
+    assert call([L, L2]) == "VBQ_ERR_SHAPE"
+    assert call([L], ldx=4095) == "VBQ_ERR_SHAPE"
+    assert call([L], ldy=3) == "VBQ_ERR_SHAPE"
+    assert call([L], blob=fake + 64) == "VBQ_ERR_ALIGN"
+    bad = v.Layout.from_buffer_copy(bytes(L))
+    bad.magic = 0
+    assert call([L, bad]) == "VBQ_ERR_LAYOUT"

@@ -268,3 +268,36 @@ def test_dense_control_parity(N, K, M):
     y_ref, bound = oracle.dense_gemv(w16, x)
     ok, worst, _ = within_bound(y.cpu().numpy(), y_ref, bound)
     assert ok, worst
+
+
+@pytest.mark.parametrize("Ns,K,M,yt", [((5632, 5632), 2048, 1, "f16"), ((300, 77, 1000), 4096, 1, "f32"),
+                                        ((640, 33, 200, 129), 2112, 2, "f16"), ((96, 64), 768, 4, "f32")])
+def test_gemv_shared_parity_and_equal_to_single(Ns, K, M, yt):
+    """Matrices that share x in one launch: each output within the bound of
+    the oracle, and bit-identical to the same matrix run alone (the per-row
+    summation order does not depend on the launch)."""
+    v = vbq()
+    out_dtype = torch.float16 if yt == "f16" else torch.float32
+    spec0 = wl.MatrixSpec("t", Ns[0], K, wl.MIX_BASE, layer=K)
+    x = wl.draw_x(spec0, 91, M, outliers=0.01)
+    dx = torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
+    mats, host = [], []
+    for i, N in enumerate(Ns):
+        spec = wl.MatrixSpec("t", N, K, wl.MIX_WIDE if i % 2 else wl.MIX_BASE, layer=i + 3)
+        bits = wl.draw_bits(spec, 91)
+        q = wl.draw_codes(spec, 91, bits)
+        s = wl.draw_scales(spec, 91)
+        dq, db, ds, _ = upload(q, bits, s, x, torch)
+        blob, L = v.pack(dq, db, ds)
+        mats.append((L, blob))
+        host.append((q, bits, s))
+    outs = v.gemv_shared(mats, dx, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    for (L, blob), (q, bits, s), y in zip(mats, host, outs):
+        got = y.float().cpu().numpy().astype(np.float64)
+        y_ref, bound = oracle.gemv(q, bits, s, x)
+        ok, worst, where = within_bound(got, y_ref, bound)
+        assert ok, (Ns, L.N, worst, where)
+        alone = v.gemv_batched(L, blob, dx, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(alone, y)
