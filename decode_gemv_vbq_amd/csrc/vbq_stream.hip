@@ -19,9 +19,10 @@
 //  * Inside a sub-unit the groups are listed per width in a slot table, so a
 //    wavefront always runs 64 groups of ONE width (no divergence between the
 //    1/2/4/8-bit paths); the 16 waves take passes from an LDS counter.
-//    Slots of a width are ordered (group half, row-slice, rank): a 16-lane LDS
-//    phase then reads x records of equal groups or of distinct groups within
-//    a 16-group window, which sit in distinct bank groups.
+//    Slots of a width are ordered (group half, slice, row, rank): a 16-lane
+//    LDS phase then reads the x records of one 16-column window (equal columns
+//    broadcast, distinct ones sit in distinct banks) except where the window
+//    changes.
 //  * Lane = one group: code words from LDS become fp16 pairs 2^(10-pos) + q
 //    with one v_and_or_b32 each (8-bit: v_perm_b32), v_dot2_f32_f16 multiplies
 //    two weights per instruction into fp32, and the group result is
@@ -251,10 +252,14 @@ __device__ __forceinline__ int issue_all(const Ctx &c, Copy &k)
 //   d5+3c     slot of the first half-0 group of width c | (slot of the first
 //             half-1 group - half-0 groups of width c) << 16
 //   d6+3c     record start / 8 + bucket start / 8 of width c
-// Slots of width c are ordered (group half, row-slice, rank) and each width
-// starts on a 64-slot pass boundary.  Also resets the sub-unit's pass counter.
+// Row-slices are numbered slice-major (slice * rows + row), so slots of width
+// c are ordered (group half, slice, row, rank); each width starts on a 64-slot
+// pass boundary.  Also resets the sub-unit's pass counter.
 // Inputs of build_info for lane l's row-slices 2l and 2l+1 of the sub-unit
 // starting at row ra: width planes, slice offset, row offset relative to row ra.
+// ceil(65536 / n): (i * inv_rows(n)) >> 16 == i / n for 0 <= i < 128, 1 <= n <= 128.
+__device__ __forceinline__ uint32_t inv_rows(int n) { return (65536u + (uint32_t)n - 1u) / (uint32_t)n; }
+
 struct InfoIn {
     uint32_t p0[2], p1[2], slo[2], roff[2];
 };
@@ -266,19 +271,45 @@ __device__ __forceinline__ void info_in_lds(const Ctx &c, int ra, int rb, InfoIn
     const uint32_t *rowoff = reinterpret_cast<const uint32_t *>(c.smem + c.L.rowoff);
     const uint32_t *sloff = reinterpret_cast<const uint32_t *>(c.smem + c.L.sloff);
     const uint32_t *wmap = reinterpret_cast<const uint32_t *>(c.smem + c.L.wmap);
-    const int nrs = (rb - ra) * nS;
-    const uint32_t base0 = rowoff[ra];
+    const int Rs = rb - ra, nrs = Rs * nS;
+    const uint32_t base0 = rowoff[ra], invR = inv_rows(Rs);
 #pragma unroll
     for (int j = 0; j < 2; j++) {
-        const int i = 2 * lane + j;
+        const int i = 2 * lane + j; // slice-major: i = slice * Rs + row
         const bool live = i < nrs;
-        const int r = (int)(((uint32_t)i * (uint32_t)c.a.inv_nS) >> 16);
-        const int w = live ? ra * nS + i : 0;
+        const int s = (int)(((uint32_t)i * invR) >> 16), r = i - s * Rs;
+        const int w = live ? (ra + r) * nS + s : 0;
         in.p0[j] = live ? wmap[2 * w] : 0u;
         in.p1[j] = live ? wmap[2 * w + 1] : 0u;
         in.slo[j] = live ? sloff[w] : 0u;
         in.roff[j] = live ? rowoff[ra + r] - base0 : 0u;
     }
+}
+
+// Reorders InfoIn loaded in row-major row-slice order (lane l: row-slices 2l,
+// 2l+1 of r * nS + s) into slice-major order for a sub-unit of Rs rows.
+__device__ __forceinline__ void to_slice_major(InfoIn &in, int Rs, int nS)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t invR = inv_rows(Rs);
+    InfoIn o;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int i = 2 * lane + j;
+        const int s = (int)(((uint32_t)i * invR) >> 16), r = i - s * Rs;
+        const int src = min(r * nS + s, 127); // lanes past the sub-unit are masked later
+        const int sl = src >> 1;
+        const bool odd = src & 1;
+        const uint32_t a0 = __shfl(in.p0[0], sl), a1 = __shfl(in.p0[1], sl);
+        const uint32_t b0 = __shfl(in.p1[0], sl), b1 = __shfl(in.p1[1], sl);
+        const uint32_t c0 = __shfl(in.slo[0], sl), c1 = __shfl(in.slo[1], sl);
+        const uint32_t d0 = __shfl(in.roff[0], sl), d1 = __shfl(in.roff[1], sl);
+        o.p0[j] = odd ? a1 : a0;
+        o.p1[j] = odd ? b1 : b0;
+        o.slo[j] = odd ? c1 : c0;
+        o.roff[j] = odd ? d1 : d0;
+    }
+    in = o;
 }
 
 __device__ void build_info(const Ctx &c, int ra, int rb, int buf, const InfoIn &in)
@@ -287,15 +318,16 @@ __device__ void build_info(const Ctx &c, int ra, int rb, int buf, const InfoIn &
     const int nS = c.a.nS, G = c.a.G;
     uint32_t *info = reinterpret_cast<uint32_t *>(c.smem + c.L.info) + buf * kMaxRS * kInfo;
     uint32_t *hdr = reinterpret_cast<uint32_t *>(c.smem + c.L.hdr) + buf * 16;
-    const int nrs = (rb - ra) * nS;
+    const int Rs = rb - ra, nrs = Rs * nS;
+    const uint32_t invR = inv_rows(Rs);
     uint32_t p0[2], p1[2], m[2][4], rec8[2];
     int ng[2], r[2], s[2], cnt[2][4], h0[2][4];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
-        const int i = 2 * lane + j;
+        const int i = 2 * lane + j; // slice-major row-slice index
         const bool live = i < nrs;
-        r[j] = (int)(((uint32_t)i * (uint32_t)c.a.inv_nS) >> 16);
-        s[j] = i - r[j] * nS;
+        s[j] = (int)(((uint32_t)i * invR) >> 16);
+        r[j] = i - s[j] * Rs;
         p0[j] = live ? in.p0[j] : 0u;
         p1[j] = live ? in.p1[j] : 0u;
         rec8[j] = live ? (in.roff[j] * 128u + in.slo[j]) >> 3 : 0u;
@@ -660,6 +692,7 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs args)
             if (wave == 0) {
                 in0.roff[0] -= win0;
                 in0.roff[1] -= win0;
+                to_slice_major(in0, rb, nS);
                 build_info(c, 0, rb, 0, in0);
             }
         }
