@@ -27,7 +27,7 @@ EXPORTS = (
     "vbq_version", "vbq_status_string", "vbq_last_error", "vbq_layout_init", "vbq_layout_from_header",
     "vbq_pack_plan_workspace", "vbq_pack_plan", "vbq_pack", "vbq_status_check", "vbq_dequant",
     "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_shared",
-    "vbq_dense_f16_gemv",
+    "vbq_plan_init", "vbq_prepare", "vbq_gemv_planned", "vbq_gemv_planned_shared", "vbq_dense_f16_gemv",
 )
 MAX_SHARED = 4
 
@@ -43,6 +43,22 @@ class VbqError(RuntimeError):
 class GemvItem(ctypes.Structure):
     """Mirror of ``vbq_gemv_item``."""
     _fields_ = [("L", ctypes.c_void_p), ("blob", ctypes.c_void_p), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int)]
+
+
+class Plan(ctypes.Structure):
+    """Mirror of ``vbq_plan`` (host geometry of a prepared plan)."""
+    _fields_ = [("magic", ctypes.c_uint32)] + \
+               [(n, ctypes.c_int32) for n in ("N", "K", "G", "M", "wgs", "rows", "tile_bytes", "tiles", "first_bytes",
+                                               "psum", "lds_bytes")] + \
+               [("region_bytes", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class PlannedItem(ctypes.Structure):
+    """Mirror of ``vbq_planned_item``."""
+    _fields_ = [("P", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int)]
 
 
 class Layout(ctypes.Structure):
@@ -84,6 +100,11 @@ def lib():
         L.vbq_gemv.argtypes = [LP, P, P, P, i, P, sz, P]
         L.vbq_gemv_batched.argtypes = [LP, P, i, P, i, P, i, i, P, sz, P]
         L.vbq_gemv_shared.argtypes = [ctypes.POINTER(GemvItem), i, i, P, i, i, P]
+        PP = ctypes.POINTER(Plan)
+        L.vbq_plan_init.argtypes = [LP, P, i, i, PP, P, sz, P]
+        L.vbq_prepare.argtypes = [PP, LP, P, P, P]
+        L.vbq_gemv_planned.argtypes = [PP, P, i, P, i, P, i, i, P]
+        L.vbq_gemv_planned_shared.argtypes = [ctypes.POINTER(PlannedItem), i, i, P, i, i, P]
         L.vbq_dense_f16_gemv.argtypes = [i, i, i, P, P, i, P, i, i, P]
         for f in EXPORTS:
             if f not in ("vbq_version", "vbq_status_string", "vbq_last_error", "vbq_pack_plan_workspace"):
@@ -271,6 +292,71 @@ def gemv_shared(mats, x, outs=None, out_dtype=None):
         ys.append(y2)
     yt = VBQ_F32 if outs[0].dtype == torch.float32 else VBQ_F16
     _check(lib().vbq_gemv_shared(items, len(mats), M, _ptr(x2), x2.stride(0), yt, _stream()), "vbq_gemv_shared")
+    return outs
+
+
+# -------------------------------------------------------------- plans
+
+def plan_init(L: Layout, blob, M: int = 1, wgs: int = 0) -> Plan:
+    """Geometry of the prepared plan of (L, blob) for up to M tokens. Synchronizes."""
+    torch = _torch()
+    _need_cuda(blob)
+    ws = torch.empty(16, dtype=torch.uint8, device=blob.device)
+    P = Plan()
+    _check(lib().vbq_plan_init(ctypes.byref(L), _ptr(blob), M, wgs, ctypes.byref(P), _ptr(ws), 16, _stream()),
+           "vbq_plan_init")
+    return P
+
+
+def prepare(L: Layout, blob, M: int = 1, wgs: int = 0):
+    """Prepared plan of a packed matrix -> (plan u8 device tensor, Plan)."""
+    P = plan_init(L, blob, M, wgs)
+    plan = _empty_aligned(P.total_bytes, blob.device)
+    _check(lib().vbq_prepare(ctypes.byref(P), ctypes.byref(L), _ptr(blob), _ptr(plan), _stream()), "vbq_prepare")
+    return plan, P
+
+
+def _as_2d(x):
+    x2 = x.view(1, -1) if x.dim() == 1 else x
+    if x2.dim() != 2 or x2.stride(1) != 1 or not x2.is_cuda:
+        raise ValueError("x must be a [M][K] (or [K]) device tensor with unit column stride")
+    return x2
+
+
+def gemv_planned(P: Plan, plan, x, out=None, out_dtype=None):
+    """Y[M][N] = X[M][K] W^T from a prepared plan (y[N] for 1-D x)."""
+    torch = _torch()
+    _need_cuda(plan)
+    x2 = _as_2d(x)
+    M = x2.shape[0]
+    out_dtype = out_dtype or torch.float16
+    if out is None:
+        out = torch.empty((M, P.N) if x.dim() == 2 else (P.N,), dtype=out_dtype, device=x.device)
+    y2 = out.view(1, -1) if out.dim() == 1 else out
+    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    _check(lib().vbq_gemv_planned(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), yt,
+                                  _stream()), "vbq_gemv_planned")
+    return out
+
+
+def gemv_planned_shared(plans, x, outs=None, out_dtype=None):
+    """[W_i x for (P_i, plan_i) in plans] in one launch (shared activations x)."""
+    torch = _torch()
+    x2 = _as_2d(x)
+    M = x2.shape[0]
+    out_dtype = out_dtype or torch.float16
+    if outs is None:
+        outs = [torch.empty((M, P.N), dtype=out_dtype, device=x.device) for P, _ in plans]
+    items = (PlannedItem * len(plans))()
+    for k, ((P, plan), out) in enumerate(zip(plans, outs)):
+        _need_cuda(plan)
+        y2 = out.view(1, -1) if out.dim() == 1 else out
+        if y2.stride(1) != 1 or y2.dtype != outs[0].dtype:
+            raise ValueError("outputs must be [M][N] with unit column stride and one dtype")
+        items[k] = PlannedItem(ctypes.addressof(P), _ptr(plan), _ptr(y2), y2.stride(0))
+    yt = VBQ_F32 if outs[0].dtype == torch.float32 else VBQ_F16
+    _check(lib().vbq_gemv_planned_shared(items, len(plans), M, _ptr(x2), x2.stride(0), yt, _stream()),
+           "vbq_gemv_planned_shared")
     return outs
 
 

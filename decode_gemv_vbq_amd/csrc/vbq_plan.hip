@@ -1,0 +1,869 @@
+// Prepared GEMV plans: a one-time device re-encoding of a VBQ1 matrix into
+// the order in which the decode kernel consumes it, and that kernel.
+//
+// The method ("Variable Bit-width Quantization", mlsanity.com page, Abstract)
+// gives every contiguous group of 64 weights its own width in {1,2,4,8}, and
+// decode multiplies the packed codes without materialising the weights.  The
+// VBQ1 blob stores groups row by row, bucketed by width inside each 32-group
+// slice.  A wavefront must run 64 groups of ONE width at a time, so a kernel
+// reading VBQ1 directly has to plan each tile at run time (find every group
+// of each width, assign it a slot) before it can compute.  A plan moves that
+// work to a preparation step that runs once per matrix:
+//
+//  * The rows are split into row blocks, one per workgroup of the GEMV launch.
+//    Each block owns a fixed-size region of the plan buffer holding tiles at
+//    a fixed stride.  Tile t takes the groups (row-major order over the
+//    block) whose running byte count starts in [t*C, (t+1)*C), so a row may
+//    continue in the next tile.
+//  * Inside a tile, groups are sorted by (width 8,4,2,1; group column; row).
+//    The tile stores a 64-byte header, the code records in that order
+//    (verbatim 8*b bytes each, so each width section starts aligned to its
+//    record size), and one 32-bit word per group: its fp16 scale and the
+//    group's position e = column * rows_in_tile + row_in_tile.
+//  * Each header carries the byte size of the next tile, and the plan carries
+//    the largest first tile, so the kernel issues every copy without first
+//    reading metadata.
+//
+// The GEMV kernel: one 1024-thread workgroup per row block.  Tile 0 is copied
+// into LDS with global_load_lds_dwordx4 as soon as the kernel starts, together
+// with the activations.  Tile k+1 is copied by one wave into the other half of
+// a two-slot ring while the other waves run the passes of tile k; then every
+// wave sums the rows of tile k-1.  One barrier per tile.  A pass is 64 slots
+// of one width: codes are contiguous per lane, x is read per group column
+// (lanes of a column broadcast), partials land at e (contiguous per column).
+// Row sums follow the column order and the tile order, so the result does not
+// depend on timing.
+#include <algorithm>
+
+#include "vbq_common.h"
+#include "vbq_host.h"
+#include "vbq_unpack.h"
+
+using namespace vbq;
+
+namespace {
+
+constexpr int kT = 1024; // threads per workgroup (prepare and GEMV kernels)
+constexpr int kW = kT / 64;
+constexpr int kHdr = 64;    // tile header bytes
+constexpr int kXRec = 36;   // dwords per x record: 32 pairs (x_p, x_{p+32}) + 4 constants
+constexpr int kMaxG = 512;  // groups per row the plans support (K <= 32768)
+constexpr int kMaxTiles = 1024; // tiles per row block
+constexpr int kMaxMats = VBQ_MAX_SHARED;
+constexpr int kMaxTb = 64 * 1024; // tile stride bound (16-bit positions)
+
+// Usable bytes per tile before the last group's overhang: a group starting
+// below C ends at most 68 bytes later, and the header takes 64.
+__host__ __device__ constexpr uint32_t tile_cut(uint32_t tb) { return tb - kHdr - 68u; }
+
+// Bytes a group of width code c occupies in a tile: code record + scale/position word.
+__device__ __forceinline__ uint32_t group_bytes(int c) { return (8u << c) + 4u; }
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan of one value per thread (kT threads).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *tmp /* LDS, kW + 1 */, uint32_t &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(inc, d);
+        if (lane >= d)
+            inc += o;
+    }
+    if (lane == 63)
+        tmp[wave] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t run = 0;
+        for (int w = 0; w < kW; w++) {
+            const uint32_t t = tmp[w];
+            tmp[w] = run;
+            run += t;
+        }
+        tmp[kW] = run;
+    }
+    __syncthreads();
+    const uint32_t ex = tmp[wave] + inc - v;
+    total = tmp[kW];
+    __syncthreads(); // tmp is reused by the next call
+    return ex;
+}
+
+// Width code (log2 b) of group (row n of the matrix, column g) from the VBQ1 bit planes.
+__device__ __forceinline__ int vbq1_width(const uint32_t *wmap, int nS, int n, int g)
+{
+    const uint64_t rs = (uint64_t)n * nS + (g >> 5);
+    return width_code(wmap[2 * rs], wmap[2 * rs + 1], g & 31);
+}
+
+struct PrepArgs {
+    const uint8_t *blob;
+    uint64_t off_row_off, off_slice_off, off_wmap, off_scales, off_codes;
+    int N, G, nS, rows;
+    uint32_t tb;     // tile stride
+    uint64_t region; // bytes per block region
+    uint8_t *plan;   // null: sizing only
+    uint32_t *sizes; // sizing: [0] max tiles, [1] max first-tile bytes, [2] blocks over kMaxTiles
+};
+
+// LDS of the preparation kernel.
+struct PrepShared {
+    uint32_t tmp[kW + 1];
+    uint32_t sizes[kT];                // group sizes of the current chunk
+    uint32_t carry, prev_size, ntiles;
+    uint32_t tstart[kMaxTiles + 1];    // first group of each tile
+    uint32_t tcum[kMaxTiles + 1];      // running byte count at each tile start
+    uint32_t hist[4 * kMaxG];          // per (section, column): count, then first slot
+};
+
+// One workgroup per row block: tile boundaries from a running byte count over
+// the block's groups in row-major order; then (plan != null) each tile is
+// written: groups counted per (width, column), given slots in (width 8,4,2,1;
+// column; row) order, and their code records, scales and positions copied.
+__global__ __launch_bounds__(kT) void k_prepare(PrepArgs a)
+{
+    __shared__ PrepShared sh;
+    const int tid = threadIdx.x;
+    const int n0 = (int)blockIdx.x * a.rows;
+    if (n0 >= a.N)
+        return;
+    const int R = min(a.rows, a.N - n0);
+    const int G = a.G;
+    const uint32_t NG = (uint32_t)R * (uint32_t)G;
+    const uint32_t C = tile_cut(a.tb);
+    const uint32_t *wmap = reinterpret_cast<const uint32_t *>(a.blob + a.off_wmap);
+    if (tid == 0) {
+        sh.carry = 0;
+        sh.prev_size = 0;
+        sh.ntiles = 0;
+    }
+    __syncthreads();
+    // ---- tile boundaries: group i starts tile t = floor(start_i / C) when the
+    // previous group started in an earlier tile
+    for (uint32_t base = 0; base < NG; base += kT) {
+        const uint32_t i = base + (uint32_t)tid;
+        uint32_t s = 0;
+        if (i < NG) {
+            const int r = (int)(i / (uint32_t)G), g = (int)(i - (uint32_t)r * G);
+            s = group_bytes(vbq1_width(wmap, a.nS, n0 + r, g));
+        }
+        sh.sizes[tid] = s;
+        const uint32_t carry = sh.carry, prev_size = sh.prev_size;
+        uint32_t total;
+        const uint32_t ex = block_excl_scan(s, sh.tmp, total); // (its barriers publish sizes[])
+        if (i < NG) {
+            const uint32_t start = carry + ex;
+            const uint32_t t = start / C;
+            const uint32_t sp = tid ? sh.sizes[tid - 1] : prev_size; // size of group i-1
+            if (i == 0 || (start - sp) / C < t) {
+                if (t < (uint32_t)kMaxTiles) {
+                    sh.tstart[t] = i;
+                    sh.tcum[t] = start;
+                }
+                atomicMax(&sh.ntiles, t + 1);
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            sh.carry = carry + total;
+            const uint32_t last = min(NG - base, (uint32_t)kT) - 1;
+            sh.prev_size = sh.sizes[last];
+        }
+        __syncthreads();
+    }
+    const uint32_t total_bytes = sh.carry;
+    const uint32_t ntiles = sh.ntiles;
+    if (ntiles > (uint32_t)kMaxTiles) {
+        if (tid == 0 && a.sizes)
+            atomicAdd(a.sizes + 2, 1u);
+        return;
+    }
+    if (tid == 0) {
+        sh.tstart[ntiles] = NG;
+        sh.tcum[ntiles] = total_bytes;
+    }
+    __syncthreads();
+    if (!a.plan) {
+        if (tid == 0) {
+            atomicMax(a.sizes, ntiles);
+            atomicMax(a.sizes + 1, (uint32_t)kHdr + sh.tcum[1] - sh.tcum[0]);
+        }
+        return;
+    }
+    // ---- tiles
+    const uint32_t *rowoff = reinterpret_cast<const uint32_t *>(a.blob + a.off_row_off);
+    const uint32_t *sloff = reinterpret_cast<const uint32_t *>(a.blob + a.off_slice_off);
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.blob + a.off_scales);
+    const uint8_t *codes = a.blob + a.off_codes;
+    uint8_t *region = a.plan + (uint64_t)blockIdx.x * a.region;
+    for (uint32_t t = 0; t < ntiles; t++) {
+        const uint32_t i0 = sh.tstart[t], i1 = sh.tstart[t + 1];
+        const int ra = (int)(i0 / (uint32_t)G), rb = (int)((i1 - 1) / (uint32_t)G);
+        const int NR = rb - ra + 1;
+        for (int k = tid; k < 4 * G; k += kT)
+            sh.hist[k] = 0;
+        __syncthreads();
+        for (uint32_t i = i0 + (uint32_t)tid; i < i1; i += kT) {
+            const int r = (int)(i / (uint32_t)G), g = (int)(i - (uint32_t)r * G);
+            const int c = vbq1_width(wmap, a.nS, n0 + r, g);
+            atomicAdd(&sh.hist[(3 - c) * G + g], 1u); // sections 8,4,2,1
+        }
+        __syncthreads();
+        // exclusive prefix over (section, column): first slot of each bucket
+        {
+            uint32_t carry = 0;
+            for (int base = 0; base < 4 * G; base += kT) {
+                const int k = base + tid;
+                const uint32_t v = k < 4 * G ? sh.hist[k] : 0u;
+                uint32_t tot;
+                const uint32_t ex = block_excl_scan(v, sh.tmp, tot);
+                if (k < 4 * G)
+                    sh.hist[k] = carry + ex;
+                carry += tot;
+                __syncthreads();
+            }
+        }
+        uint8_t *tile = region + (uint64_t)t * a.tb;
+        const uint32_t n = i1 - i0;
+        uint32_t wb[4]; // first slot of sections 8,4,2,1
+        wb[0] = 0;
+        wb[1] = sh.hist[G];
+        wb[2] = sh.hist[2 * G];
+        wb[3] = sh.hist[3 * G];
+        uint32_t cnt[4];
+        cnt[0] = wb[1];
+        cnt[1] = wb[2] - wb[1];
+        cnt[2] = wb[3] - wb[2];
+        cnt[3] = n - wb[3];
+        uint32_t off[4]; // byte offset of each section's first record
+        off[0] = kHdr;
+        off[1] = off[0] + 64u * cnt[0];
+        off[2] = off[1] + 32u * cnt[1];
+        off[3] = off[2] + 16u * cnt[2];
+        const uint32_t se_off = off[3] + 8u * cnt[3];
+        // thread g walks column g's rows in order: bucket ranks follow the row
+        for (int g = tid; g < G; g += kT) {
+            uint32_t run[4] = {0, 0, 0, 0};
+            for (int r = ra; r <= rb; r++) {
+                const uint32_t i = (uint32_t)r * G + g;
+                if (i < i0 || i >= i1)
+                    continue;
+                const int nn = n0 + r;
+                const uint64_t rs = (uint64_t)nn * a.nS + (g >> 5);
+                const uint32_t p0 = wmap[2 * rs], p1 = wmap[2 * rs + 1];
+                const WidthMasks wm = width_masks(p0, p1, min(32, G - 32 * (g >> 5)));
+                const int c = width_code(p0, p1, g & 31);
+                const int sec = 3 - c;
+                const uint32_t rk = pick4(run, sec);
+                run[0] += sec == 0;
+                run[1] += sec == 1;
+                run[2] += sec == 2;
+                run[3] += sec == 3;
+                const uint32_t slot = sh.hist[sec * G + g] + rk;
+                const uint64_t src = (uint64_t)rowoff[nn] * kRowPad + sloff[rs] + group_offset_in_slice(wm, c, g & 31);
+                const uint32_t dst = pick4(off, sec) + (slot - pick4(wb, sec)) * (8u << c);
+                const uint32_t *s32 = reinterpret_cast<const uint32_t *>(codes + src);
+                uint32_t *d32 = reinterpret_cast<uint32_t *>(tile + dst);
+                for (int d = 0; d < (2 << c); d++)
+                    d32[d] = s32[d];
+                const uint32_t e = (uint32_t)g * (uint32_t)NR + (uint32_t)(r - ra);
+                reinterpret_cast<uint32_t *>(tile + se_off)[slot] = (uint32_t)scales[(uint64_t)nn * G + g] | (e << 16);
+            }
+        }
+        if (tid == 0) {
+            uint32_t *h = reinterpret_cast<uint32_t *>(tile);
+            h[0] = cnt[0];
+            h[1] = cnt[1];
+            h[2] = cnt[2];
+            h[3] = cnt[3];
+            h[4] = (uint32_t)ra;
+            h[5] = (uint32_t)NR;
+            h[6] = i0 - (uint32_t)ra * G;         // first column of row ra in this tile
+            h[7] = i1 - 1 - (uint32_t)rb * G + 1; // one past the last column of row rb
+            h[8] = NR == 1 ? 0u : (uint32_t)((0x100000000ull + (uint64_t)NR - 1) / (uint64_t)NR);
+            h[9] = t + 1 < ntiles ? (uint32_t)kHdr + sh.tcum[t + 2] - sh.tcum[t + 1] : 0u; // next tile's bytes
+            h[10] = n;
+            h[11] = se_off;
+            h[12] = se_off + 4u * n; // this tile's bytes
+            h[13] = t;
+            h[14] = ntiles;
+            h[15] = VBQ_PLAN_MAGIC;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The planned GEMV kernel.
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (m0 = lds_base, wave-uniform).  Written as asm so the compiler does not tie
+// later LDS reads to it; completion is awaited explicitly (wait_vm0) before the
+// barrier that publishes a tile.  The s_nop separates the m0 write from the load.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Copy `bytes` from global memory to LDS in 1 KiB chunks (16 bytes per lane,
+// the tail masked per 16 bytes): this wave issues chunks first, first + step, ...
+__device__ __forceinline__ void copy_chunks(const uint8_t *src, uint32_t dst, uint32_t bytes, int first, int step)
+{
+    const uint32_t lane16 = (threadIdx.x & 63) * 16u;
+    for (uint32_t j = (uint32_t)first; j * 1024u < bytes; j += (uint32_t)step) {
+        const uint32_t off = j * 1024u + lane16;
+        if (off < bytes)
+            dma16(src + off, dst + j * 1024u);
+    }
+}
+
+struct PMat {
+    const uint8_t *plan;
+    void *y;
+    uint64_t region;
+    int N, ldy, rows, wg0;
+};
+
+struct PArgs {
+    const uint16_t *x;
+    int G, ldx, yt, tb, first, ps, nmat;
+    int rows; // output staging stride in LDS: the most rows per block of any matrix
+    PMat mats[kMaxMats];
+};
+
+struct PLayout {
+    uint32_t x, ring, psum, ybuf, total;
+};
+
+__host__ __device__ inline uint32_t p_take(uint32_t &o, uint32_t bytes)
+{
+    const uint32_t r = o;
+    o += (bytes + 15u) & ~15u;
+    return r;
+}
+
+// LDS carve-up, computed identically on the host (size) and the device.
+__host__ __device__ inline PLayout p_layout(int MT, int G, int rows, int tb, int ps)
+{
+    PLayout l;
+    uint32_t o = 0;
+    l.x = p_take(o, (uint32_t)(MT * G * kXRec * 4));
+    l.ring = p_take(o, 2u * (uint32_t)tb);
+    l.psum = p_take(o, 2u * (uint32_t)(MT * ps) * 4u);
+    l.ybuf = p_take(o, (uint32_t)(MT * rows) * 4u);
+    l.total = o;
+    return l;
+}
+
+// x records: fp16 pairs (x_p, x_{p+32}), then per width the correction
+// C_b = sum_p 2^(10-pos_b(p)) (x_p + x_{p+32}) + (2^b-1)/2 sum_j x_j.
+// Item = (token, group, quarter q): pairs 4q..4q+3; the 8 items of a group are
+// 8 adjacent lanes.  Loads and stores are separate so the loads go out with
+// the first tile's copy.
+template <int MT>
+struct XRegs {
+    static constexpr int kPer = (MT * kMaxG * 8 + kT - 1) / kT;
+    uint32_t lo0[kPer], lo1[kPer], hi0[kPer], hi1[kPer];
+};
+
+template <int MT>
+__device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<MT> &xs)
+{
+    const int tid = threadIdx.x;
+    const int items = MT * G * 8;
+    const bool vec = (ldx % 4) == 0 && ((uintptr_t)x % 8) == 0;
+#pragma unroll
+    for (int k = 0; k < XRegs<MT>::kPer; k++) {
+        const int i = tid + k * kT;
+        xs.lo0[k] = xs.lo1[k] = xs.hi0[k] = xs.hi1[k] = 0u;
+        if (i < items) {
+            const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
+            const uint16_t *p = x + (uint64_t)m * ldx + 64ull * g + 4 * q;
+            if (vec) {
+                const uint2 va = *reinterpret_cast<const uint2 *>(p);
+                const uint2 vb = *reinterpret_cast<const uint2 *>(p + 32);
+                xs.lo0[k] = va.x;
+                xs.lo1[k] = va.y;
+                xs.hi0[k] = vb.x;
+                xs.hi1[k] = vb.y;
+            } else {
+                xs.lo0[k] = p[0] | ((uint32_t)p[1] << 16);
+                xs.lo1[k] = p[2] | ((uint32_t)p[3] << 16);
+                xs.hi0[k] = p[32] | ((uint32_t)p[33] << 16);
+                xs.hi1[k] = p[34] | ((uint32_t)p[35] << 16);
+            }
+        }
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void x_store(int G, const XRegs<MT> &xs, uint32_t *xrec)
+{
+    const int tid = threadIdx.x;
+    const int items = MT * G * 8;
+#pragma unroll
+    for (int k = 0; k < XRegs<MT>::kPer; k++) {
+        const int i = tid + k * kT;
+        if (i >= items) // whole groups of 8 lanes drop out together
+            break;
+        const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
+        U4 o;
+        o.v[0] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x05040100u); // (x_p, x_{p+32})
+        o.v[1] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x07060302u);
+        o.v[2] = __builtin_amdgcn_perm(xs.hi1[k], xs.lo1[k], 0x05040100u);
+        o.v[3] = __builtin_amdgcn_perm(xs.hi1[k], xs.lo1[k], 0x07060302u);
+        uint32_t *xr = xrec + ((uint32_t)m * G + g) * kXRec;
+        *reinterpret_cast<U4 *>(xr + 4 * q) = o;
+        float X = 0.f, c1 = 0.f, c2 = 0.f, c4 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int t = 4 * q + j; // pair index in the group
+            const float sp = dot2(o.v[j], 0x3c003c00u, 0.f); // x_t + x_{t+32}, exact in fp32
+            X += sp;
+            c1 = fmaf((float)(1 << (10 - pair_pos<1>(t & 15))), sp, c1);
+            c2 = fmaf((float)(1 << (10 - pair_pos<2>(t & 7))), sp, c2);
+            c4 = fmaf((float)(1 << (10 - pair_pos<4>(t & 3))), sp, c4);
+        }
+#pragma unroll
+        for (int d = 1; d < 8; d <<= 1) { // fixed-order tree over the 8 quarters
+            X += __shfl_xor(X, d, 8);
+            c1 += __shfl_xor(c1, d, 8);
+            c2 += __shfl_xor(c2, d, 8);
+            c4 += __shfl_xor(c4, d, 8);
+        }
+        if (q == 0)
+            *reinterpret_cast<U4 *>(xr + 32) = U4{{__float_as_uint(fmaf(0.5f, X, c1)),
+                                                    __float_as_uint(fmaf(1.5f, X, c2)),
+                                                    __float_as_uint(fmaf(7.5f, X, c4)),
+                                                    __float_as_uint(fmaf(127.5f, X, 1024.f * X))}};
+    }
+}
+
+// Header fields of one tile, kept in registers.
+struct Tile {
+    uint32_t cnt[4]; // groups per section (widths 8,4,2,1)
+    uint32_t ra, nr, g_first, g_end, inv_nr, next, n, se_off;
+};
+
+__device__ __forceinline__ Tile read_tile(const uint8_t *t)
+{
+    const uint4 a = *reinterpret_cast<const uint4 *>(t);
+    const uint4 b = *reinterpret_cast<const uint4 *>(t + 16);
+    const uint4 c = *reinterpret_cast<const uint4 *>(t + 32);
+    Tile h;
+    h.cnt[0] = a.x;
+    h.cnt[1] = a.y;
+    h.cnt[2] = a.z;
+    h.cnt[3] = a.w;
+    h.ra = b.x;
+    h.nr = b.y;
+    h.g_first = b.z;
+    h.g_end = b.w;
+    h.inv_nr = c.x;
+    h.next = c.y;
+    h.n = c.z;
+    h.se_off = c.w;
+    return h;
+}
+
+// One pass: slots j = 64 * q + lane of the section of width B.
+template <int B, int MT>
+__device__ __forceinline__ void plan_pass(int q, uint32_t cnt, uint32_t wb, uint32_t code_off, const uint8_t *tile,
+                                          const Tile &h, int G, int ps, const uint32_t *xrec, float *psum)
+{
+    constexpr int C = B == 1 ? 0 : B == 2 ? 1 : B == 4 ? 2 : 3;
+    const uint32_t j = 64u * (uint32_t)q + (threadIdx.x & 63);
+    if (j >= cnt)
+        return;
+    const uint32_t se = reinterpret_cast<const uint32_t *>(tile + h.se_off)[wb + j];
+    uint32_t w[2 * B];
+    const U2 *src = reinterpret_cast<const U2 *>(tile + code_off + j * (8u * B));
+#pragma unroll
+    for (int k = 0; k < B; k++) {
+        const U2 v = src[k];
+        w[2 * k] = v.v[0];
+        w[2 * k + 1] = v.v[1];
+    }
+    uint32_t hp[32];
+    unpack_pairs<B>(w, hp);
+    const uint32_t e = se >> 16;
+    const uint32_t xcol = h.nr == 1 ? e : __umulhi(e, h.inv_nr);
+    const float s = __half2float(__ushort_as_half((uint16_t)(se & 0xffffu)));
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+        const uint32_t *xr = xrec + ((uint32_t)m * G + xcol) * kXRec;
+        float acc0 = 0.f, acc1 = 0.f; // two chains for instruction-level parallelism
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+            const U4 xa = *reinterpret_cast<const U4 *>(xr + 4 * k);
+            const U4 xb = *reinterpret_cast<const U4 *>(xr + 4 * k + 4);
+            acc0 = dot2(hp[4 * k + 0], xa.v[0], acc0);
+            acc1 = dot2(hp[4 * k + 4], xb.v[0], acc1);
+            acc0 = dot2(hp[4 * k + 1], xa.v[1], acc0);
+            acc1 = dot2(hp[4 * k + 5], xb.v[1], acc1);
+            acc0 = dot2(hp[4 * k + 2], xa.v[2], acc0);
+            acc1 = dot2(hp[4 * k + 6], xb.v[2], acc1);
+            acc0 = dot2(hp[4 * k + 3], xa.v[3], acc0);
+            acc1 = dot2(hp[4 * k + 7], xb.v[3], acc1);
+        }
+        const float cc = __uint_as_float(xr[32 + C]);
+        psum[m * ps + e] = s * ((acc0 + acc1) - cc);
+    }
+}
+
+// Rows per row-sum item (8 lanes per row).
+constexpr int kSumRows = 8;
+
+// Row-sum item t of a tile: rows 8t..8t+7 of the tile.  The partials of row j
+// sit at column * nr + j for the tile's columns of that row; they are summed
+// in column order (four interleaved chains, fixed) and added to ybuf, tiles in
+// order.
+template <int MT>
+__device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps, int rows, const float *psum,
+                                            float *ybuf)
+{
+    const int lane = threadIdx.x & 63;
+    const int j = kSumRows * t + (lane >> 3), q = lane & 7;
+    const int nr = (int)h.nr;
+    const int lo = j == 0 ? (int)h.g_first : 0, hi = j == nr - 1 ? (int)h.g_end : G;
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+        float v = 0.f;
+        if (j < nr) {
+            const float *p = psum + m * ps + j;
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+            int g = lo + q;
+            for (; g + 24 < hi; g += 32) {
+                a0 += p[g * nr];
+                a1 += p[(g + 8) * nr];
+                a2 += p[(g + 16) * nr];
+                a3 += p[(g + 24) * nr];
+            }
+            for (; g < hi; g += 8)
+                a0 += p[g * nr];
+            v = (a0 + a1) + (a2 + a3);
+        }
+        v += __shfl_xor(v, 4, 8);
+        v += __shfl_xor(v, 2, 8);
+        v += __shfl_xor(v, 1, 8);
+        if (q == 0 && j < nr)
+            ybuf[m * rows + (int)h.ra + j] += v;
+    }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // this workgroup's matrix: the last one whose first workgroup is <= blockIdx.x
+    PMat pm = args.mats[0];
+#pragma unroll
+    for (int i = 1; i < kMaxMats; i++)
+        if (i < args.nmat && (int)blockIdx.x >= args.mats[i].wg0)
+            pm = args.mats[i];
+    const int blk = (int)blockIdx.x - pm.wg0;
+    const int n0 = blk * pm.rows;
+    if (n0 >= pm.N)
+        return;
+    const int R = min(pm.rows, pm.N - n0);
+    const int G = args.G, ps = args.ps, rows = args.rows;
+    const uint32_t tb = (uint32_t)args.tb;
+    const PLayout L = p_layout(MT, G, rows, args.tb, ps);
+    uint32_t *xrec = reinterpret_cast<uint32_t *>(smem + L.x);
+    float *psum = reinterpret_cast<float *>(smem + L.psum);
+    float *ybuf = reinterpret_cast<float *>(smem + L.ybuf);
+    const uint8_t *region = pm.plan + (uint64_t)blk * pm.region;
+    const uint32_t ring = lds_addr(smem + L.ring);
+
+    // ---- tile 0 and the activations, issued together
+    copy_chunks(region, ring, (uint32_t)args.first, wave, kW);
+    {
+        XRegs<MT> xs;
+        x_load<MT>(args.x, args.ldx, G, xs);
+        for (int i = tid; i < MT * R; i += kT)
+            ybuf[(i / R) * rows + i % R] = 0.f;
+        x_store<MT>(G, xs, xrec);
+    }
+    wait_vm0();
+    __syncthreads();
+
+    // ---- tile k sits in ring slot k & 1: wave 0 copies tile k+1 into the
+    // other slot while waves 1.. run the passes of tile k; then all waves sum
+    // the rows of tile k-1 (partials in psum slot (k-1) & 1).
+    Tile prev{};
+    int k = 0;
+    for (;; k++) {
+        const int slot = k & 1;
+        const uint8_t *tile = smem + L.ring + (uint32_t)slot * tb;
+        const Tile h = read_tile(tile);
+        float *ps_k = psum + slot * (MT * ps);
+        if (wave == 0) {
+            if (h.next)
+                copy_chunks(region + (uint64_t)(k + 1) * tb, ring + (uint32_t)(slot ^ 1) * tb, h.next, 0, 1);
+        } else {
+            const int np0 = (int)((h.cnt[0] + 63) >> 6), np1 = (int)((h.cnt[1] + 63) >> 6);
+            const int np2 = (int)((h.cnt[2] + 63) >> 6), np3 = (int)((h.cnt[3] + 63) >> 6);
+            const int pb1 = np0, pb2 = pb1 + np1, pb3 = pb2 + np2, np = pb3 + np3;
+            const uint32_t wb1 = h.cnt[0], wb2 = wb1 + h.cnt[1], wb3 = wb2 + h.cnt[2];
+            const uint32_t off1 = kHdr + 64u * h.cnt[0], off2 = off1 + 32u * h.cnt[1], off3 = off2 + 16u * h.cnt[2];
+            for (int p = wave - 1; p < np; p += kW - 1) {
+                if (p < pb1)
+                    plan_pass<8, MT>(p, h.cnt[0], 0u, kHdr, tile, h, G, ps, xrec, ps_k);
+                else if (p < pb2)
+                    plan_pass<4, MT>(p - pb1, h.cnt[1], wb1, off1, tile, h, G, ps, xrec, ps_k);
+                else if (p < pb3)
+                    plan_pass<2, MT>(p - pb2, h.cnt[2], wb2, off2, tile, h, G, ps, xrec, ps_k);
+                else
+                    plan_pass<1, MT>(p - pb3, h.cnt[3], wb3, off3, tile, h, G, ps, xrec, ps_k);
+            }
+        }
+        if (k > 0) {
+            const int nsum = ((int)prev.nr + kSumRows - 1) / kSumRows;
+            for (int t = (wave + kW - 1) % kW; t < nsum; t += kW) // wave 0, busy copying, takes the last share
+                rowsum_item<MT>(t, prev, G, ps, rows, psum + (slot ^ 1) * (MT * ps), ybuf);
+        }
+        wait_vm0(); // wave 0: the copy of tile k+1
+        __syncthreads();
+        prev = h;
+        if (!h.next)
+            break;
+    }
+    // ---- rows of the last tile (partials in psum slot k & 1)
+    {
+        const int nsum = ((int)prev.nr + kSumRows - 1) / kSumRows;
+        for (int t = wave; t < nsum; t += kW)
+            rowsum_item<MT>(t, prev, G, ps, rows, psum + (k & 1) * (MT * ps), ybuf);
+    }
+    __syncthreads();
+    for (int i = tid; i < MT * R; i += kT) {
+        const int m = i / R, r = i - m * R;
+        const float v = ybuf[m * rows + r];
+        const uint64_t o = (uint64_t)m * pm.ldy + n0 + r;
+        if (args.yt == VBQ_F16)
+            reinterpret_cast<__half *>(pm.y)[o] = __float2half_rn(v);
+        else
+            reinterpret_cast<float *>(pm.y)[o] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+int plan_cus()
+{
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 256;
+    }
+    return cus;
+}
+
+constexpr uint32_t kLdsBudget = 160u * 1024u;
+
+// Partial-sum capacity of a tile: groups (at least 12 bytes each) plus the
+// columns of a first and a last row the tile only partly covers.
+int psum_capacity(int tb, int G) { return (tb - kHdr) / 12 + 2 * G; }
+
+vbq_status check_plan(const vbq_plan *P)
+{
+    if (!P || P->magic != VBQ_PLAN_MAGIC)
+        return VBQ_ERR_LAYOUT;
+    if (P->N < 1 || P->G < 1 || P->G > kMaxG || P->K != 64 * P->G || P->M < 1 || P->M > 2 || P->wgs < 1 ||
+        P->rows < 1 || (int64_t)P->wgs * P->rows < P->N || P->tile_bytes < 4096 || P->tile_bytes > kMaxTb ||
+        P->tile_bytes % 1024 || P->tiles < 1 || P->first_bytes < kHdr || P->first_bytes > P->tile_bytes ||
+        P->region_bytes != (uint64_t)P->tiles * (uint64_t)P->tile_bytes)
+        return VBQ_ERR_LAYOUT;
+    return VBQ_OK;
+}
+
+PrepArgs prep_args(const vbq_layout *L, const void *blob, const vbq_plan *P)
+{
+    PrepArgs a{};
+    a.blob = (const uint8_t *)blob;
+    a.off_row_off = L->off_row_off;
+    a.off_slice_off = L->off_slice_off;
+    a.off_wmap = L->off_wmap;
+    a.off_scales = L->off_scales;
+    a.off_codes = L->off_codes;
+    a.N = (int)L->N;
+    a.G = (int)L->G;
+    a.nS = (int)L->nS;
+    a.rows = P->rows;
+    a.tb = (uint32_t)P->tile_bytes;
+    a.region = P->region_bytes;
+    return a;
+}
+
+template <int MT>
+vbq_status launch_plan(const PArgs &a, int grid, uint32_t lds, hipStream_t stream)
+{
+    static bool configured = false;
+    if (!configured) {
+        VBQ_TRY(hip_status(
+            hipFuncSetAttribute((const void *)k_gemv_plan<MT>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)));
+        configured = true;
+    }
+    hipLaunchKernelGGL(k_gemv_plan<MT>, dim3(grid), dim3(kT), lds, stream, a);
+    return launch_status();
+}
+
+} // namespace
+
+extern "C" {
+
+vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, vbq_plan *P, void *ws,
+                         size_t ws_bytes, hipStream_t stream)
+{
+    if (!blob || !P)
+        return VBQ_ERR_INVALID_ARG;
+    VBQ_TRY(check_layout(L));
+    if (M < 1 || M > 2)
+        return VBQ_ERR_BATCH;
+    if (!ws || ws_bytes < 16)
+        return VBQ_ERR_WORKSPACE;
+    if ((uintptr_t)blob % 256 || (uintptr_t)ws % 4)
+        return VBQ_ERR_ALIGN;
+    const int N = (int)L->N, G = (int)L->G;
+    if (G > kMaxG)
+        return VBQ_ERR_SHAPE;
+    if (wgs <= 0)
+        wgs = plan_cus();
+    const int rows = (N + wgs - 1) / wgs;
+    wgs = (N + rows - 1) / rows;
+    // the largest tile stride (1 KiB steps) whose launch fits the LDS budget
+    int tb = 0;
+    for (int cand = kMaxTb; cand >= 4096; cand -= 1024) {
+        const int ps = psum_capacity(cand, G);
+        if (ps > 65536)
+            continue;
+        if (p_layout(M, G, rows, cand, ps).total <= kLdsBudget) {
+            tb = cand;
+            break;
+        }
+    }
+    if (!tb)
+        return VBQ_ERR_SHAPE;
+    vbq_plan p{};
+    p.magic = VBQ_PLAN_MAGIC;
+    p.N = N;
+    p.K = (int)L->K;
+    p.G = G;
+    p.M = M;
+    p.wgs = wgs;
+    p.rows = rows;
+    p.tile_bytes = tb;
+    p.psum = psum_capacity(tb, G);
+    p.lds_bytes = (int)p_layout(M, G, rows, tb, p.psum).total;
+    // sizing pass: tiles per block region and the largest first tile
+    VBQ_TRY(zero_words(ws, 16, stream));
+    PrepArgs a = prep_args(L, blob, &p);
+    a.plan = nullptr;
+    a.sizes = (uint32_t *)ws;
+    hipLaunchKernelGGL(k_prepare, dim3(wgs), dim3(kT), 0, stream, a);
+    VBQ_TRY(launch_status());
+    uint32_t h[4];
+    VBQ_TRY(hip_status(hipMemcpyAsync(h, ws, 16, hipMemcpyDeviceToHost, stream)));
+    VBQ_TRY(hip_status(hipStreamSynchronize(stream)));
+    if (h[2] || h[0] < 1)
+        return VBQ_ERR_SHAPE; // some block needs more tiles than a plan holds
+    p.tiles = (int)h[0];
+    p.first_bytes = (int)h[1];
+    p.region_bytes = (uint64_t)p.tiles * (uint64_t)tb;
+    p.total_bytes = (uint64_t)wgs * p.region_bytes;
+    *P = p;
+    return VBQ_OK;
+}
+
+vbq_status vbq_prepare(const vbq_plan *P, const vbq_layout *L, const void *blob, void *plan, hipStream_t stream)
+{
+    if (!blob || !plan)
+        return VBQ_ERR_INVALID_ARG;
+    VBQ_TRY(check_layout(L));
+    VBQ_TRY(check_plan(P));
+    if ((int)L->N != P->N || (int)L->K != P->K)
+        return VBQ_ERR_SHAPE;
+    if ((uintptr_t)blob % 256 || (uintptr_t)plan % 256)
+        return VBQ_ERR_ALIGN;
+    PrepArgs a = prep_args(L, blob, P);
+    a.plan = (uint8_t *)plan;
+    a.sizes = nullptr;
+    hipLaunchKernelGGL(k_prepare, dim3(P->wgs), dim3(kT), 0, stream, a);
+    return launch_status();
+}
+
+vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
+                                   vbq_dtype yt, hipStream_t stream)
+{
+    if (!items || n < 1 || n > VBQ_MAX_SHARED || !x)
+        return VBQ_ERR_INVALID_ARG;
+    if (yt != VBQ_F32 && yt != VBQ_F16)
+        return VBQ_ERR_INVALID_ARG;
+    if (M < 1 || M > 2)
+        return VBQ_ERR_BATCH;
+    if ((uintptr_t)x % 2)
+        return VBQ_ERR_ALIGN;
+    PArgs a{};
+    a.x = x;
+    a.ldx = ldx;
+    a.yt = (int)yt;
+    a.nmat = n;
+    int grid = 0;
+    uint32_t lds = 0;
+    for (int i = 0; i < n; i++) {
+        const vbq_planned_item &it = items[i];
+        if (!it.P || !it.plan || !it.y)
+            return VBQ_ERR_INVALID_ARG;
+        VBQ_TRY(check_plan(it.P));
+        const vbq_plan *P = it.P;
+        const vbq_plan *P0 = items[0].P;
+        if (M > P->M)
+            return VBQ_ERR_BATCH;
+        if (P->K != P0->K || ldx < P->K || it.ldy < P->N)
+            return VBQ_ERR_SHAPE;
+        if (P->tile_bytes != P0->tile_bytes || P->psum != P0->psum)
+            return VBQ_ERR_SHAPE; // one launch needs one LDS carve-up
+        if ((uintptr_t)it.plan % 256 || (uintptr_t)it.y % (yt == VBQ_F32 ? 4 : 2))
+            return VBQ_ERR_ALIGN;
+        PMat &m = a.mats[i];
+        m.plan = (const uint8_t *)it.plan;
+        m.y = it.y;
+        m.region = P->region_bytes;
+        m.N = P->N;
+        m.ldy = it.ldy;
+        m.rows = P->rows;
+        m.wg0 = grid;
+        grid += P->wgs;
+        a.first = std::max(a.first, P->first_bytes);
+        a.rows = std::max(a.rows, P->rows); // output staging stride: the plan with the most rows fits
+    }
+    const vbq_plan *P0 = items[0].P;
+    a.G = P0->G;
+    a.tb = P0->tile_bytes;
+    a.ps = P0->psum;
+    lds = p_layout(M, a.G, a.rows, a.tb, a.ps).total;
+    if (lds > kLdsBudget)
+        return VBQ_ERR_SHAPE;
+    return M == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream);
+}
+
+vbq_status vbq_gemv_planned(const vbq_plan *P, const void *plan, int M, const uint16_t *x, int ldx, void *y, int ldy,
+                            vbq_dtype yt, hipStream_t stream)
+{
+    const vbq_planned_item it{P, plan, y, ldy};
+    return vbq_gemv_planned_shared(&it, 1, M, x, ldx, yt, stream);
+}
+
+} // extern "C"

@@ -191,6 +191,96 @@ vbq_status vbq_gemv_shared(const vbq_gemv_item *items /* host */, int n, int M, 
                            vbq_dtype yt, hipStream_t stream);
 
 /*
+ * Prepared plans.  vbq_gemv reads the VBQ1 blob directly and must work out, at
+ * run time and per tile, which groups have which width before a wavefront can
+ * run 64 groups of one width ("Variable Bit-width Quantization", mlsanity.com
+ * page, Abstract: each 64-weight group carries its own width).  A plan does
+ * that once per matrix: a device copy of the blob's codes and scales,
+ * re-ordered for the GEMV kernel of this library on this device.
+ *
+ * Plan buffer: `wgs` row blocks of `rows` rows (the last may have fewer), one
+ * per workgroup of the GEMV launch.  Block b owns bytes [b * region_bytes,
+ * (b + 1) * region_bytes) and stores tiles at a stride of tile_bytes.  Tile t
+ * of a block holds the block's groups (row-major order) whose running sum of
+ * (8*b + 4) bytes starts in [t*C, (t+1)*C), C = tile_bytes - 132.  A tile is:
+ *   64-byte header: u32 groups of width 8, 4, 2, 1; first row (relative to
+ *     the block); rows touched nr; first column of that first row; one past
+ *     the last column of the last row; ceil(2^32 / nr) (0 if nr = 1); bytes
+ *     of the next tile (0 for the last); groups n; offset of the word section;
+ *     this tile's bytes; tile index; tiles in the block; VBQ_PLAN_MAGIC.
+ *   code records of the groups in slot order (width 8, 4, 2, 1; then column;
+ *     then row), copied verbatim from the blob (8*b bytes each);
+ *   u32 per group in slot order: fp16 scale bits | e << 16, where
+ *     e = column * nr + (row - first row).
+ * Bytes past a tile's end up to the next stride are never read.
+ */
+#define VBQ_PLAN_MAGIC 0x4E4C5056u
+
+typedef struct vbq_plan {
+    uint32_t magic;        /* VBQ_PLAN_MAGIC */
+    int32_t N, K, G;       /* matrix shape (G = K / 64 <= 512) */
+    int32_t M;             /* largest token count of its GEMVs (1 or 2) */
+    int32_t wgs, rows;     /* row blocks (workgroups) and rows per block */
+    int32_t tile_bytes;    /* tile stride, multiple of 1024, <= 65536 */
+    int32_t tiles;         /* tiles of the largest block */
+    int32_t first_bytes;   /* bytes of the largest first tile */
+    int32_t psum;          /* partial sums per token a tile may need (LDS sizing) */
+    int32_t lds_bytes;     /* LDS per workgroup of its GEMV launches */
+    uint64_t region_bytes; /* tiles * tile_bytes */
+    uint64_t total_bytes;  /* plan buffer bytes: wgs * region_bytes */
+} vbq_plan;
+
+/*
+ * SYNC.  Fill *P for the matrix (L, blob), GEMVs of up to M tokens (1 or 2)
+ * and `wgs` row blocks (<= 0: one per compute unit of the current device; the
+ * count is reduced so that no block is empty).  Runs one sizing kernel over the
+ * width bit planes (workspace ws: device, >= 16 bytes) and waits for it.
+ * Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_BATCH (M),
+ * VBQ_ERR_WORKSPACE, VBQ_ERR_ALIGN, VBQ_ERR_SHAPE (K > 32768, or the LDS of
+ * the launch cannot hold a tile and the block's outputs), VBQ_ERR_HIP.
+ */
+vbq_status vbq_plan_init(const vbq_layout *L /* host */, const void *blob, int M, int wgs, vbq_plan *P /* host */,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Write the plan of (L, blob) described by *P into `plan` (device,
+ * P->total_bytes, 256-byte aligned).  The blob must be the one *P was sized
+ * for.  Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT (bad *P), VBQ_ERR_SHAPE
+ * (P does not match L), VBQ_ERR_ALIGN.
+ */
+vbq_status vbq_prepare(const vbq_plan *P /* host */, const vbq_layout *L /* host */, const void *blob, void *plan,
+                       hipStream_t stream);
+
+/*
+ * Y = X W^T from a plan, M tokens (1 <= M <= P->M): x fp16 [M][ldx] (ldx >= K),
+ * y [M][ldy] (ldy >= N) in yt.  Same results contract as vbq_gemv_batched
+ * (fp32 accumulation, |y - y_exact| <= 1e-3 * sum_k |w_k||x_k|), and the
+ * result does not depend on timing.  One launch of P->wgs workgroups.
+ * Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_BATCH, VBQ_ERR_SHAPE,
+ * VBQ_ERR_ALIGN (plan not 256-byte aligned, x/y not element aligned).
+ */
+vbq_status vbq_gemv_planned(const vbq_plan *P /* host */, const void *plan, int M, const uint16_t *x, int ldx,
+                            void *y, int ldy, vbq_dtype yt, hipStream_t stream);
+
+/* One matrix of a vbq_gemv_planned_shared call. */
+typedef struct vbq_planned_item {
+    const vbq_plan *P; /* host */
+    const void *plan;  /* device, from vbq_prepare */
+    void *y;           /* device, [M][ldy] in the call's yt */
+    int ldy;           /* >= P->N */
+} vbq_planned_item;
+
+/*
+ * vbq_gemv_planned for n (1..VBQ_MAX_SHARED) matrices that read the same x
+ * (e.g. the gate and up projections of one MLP block), in ONE launch of
+ * sum P_i->wgs workgroups.  The plans must agree on K, tile_bytes and psum
+ * (VBQ_ERR_SHAPE otherwise); prepare them with the same M and with wgs in
+ * proportion to N so that the launch spans the device once.
+ */
+vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items /* host */, int n, int M, const uint16_t *x, int ldx,
+                                   vbq_dtype yt, hipStream_t stream);
+
+/*
  * Dense fp16 control at the same shapes: y[M][ldy] = W16 x with W16 fp16
  * [N][K] row-major (typically vbq_dequant(..., VBQ_F16)), fp32 accumulate.
  * K % 8 == 0, 1 <= M <= 16.

@@ -1,0 +1,230 @@
+"""GPU parity of the prepared-plan GEMV (vbq_plan_init / vbq_prepare /
+vbq_gemv_planned[_shared]) against the CPU oracle, on the same seeded inputs.
+
+* |y - y_ref| <= 1e-3 * sum|w||x| per output, at shapes that span one group,
+  ragged K-slices, rows split across tiles (small row-block counts force many
+  tiles per block) and every width mix.
+* Invariants: x = e_k gives column k of vbq_dequant bit-exactly; repeated runs
+  are bit-identical; a matrix in a shared launch gives the same bits as alone.
+* The plan buffer itself: tile headers read back on the host must describe
+  every group of the matrix exactly once, within the tile stride.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from decode_gemv_vbq_amd import workload as wl
+from tests.gpu_util import upload, within_bound
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def vbq():
+    import decode_gemv_vbq_amd as v
+    v.lib()
+    return v
+
+
+def draw(N, K, mix=None, seed=0, M=1, cluster=1, outliers=0.0):
+    spec = wl.MatrixSpec("t", N, K, mix or wl.MIX_BASE, layer=seed, cluster=cluster)
+    return wl.draw_matrix(spec, 92, M=M, outliers=outliers)
+
+
+def planned(v, q, bits, s, x, M=None, wgs=0, yt="f32"):
+    dq, db, ds, dx = upload(q, bits, s, x, torch)
+    blob, L = v.pack(dq, db, ds)
+    plan, P = v.prepare(L, blob, M=M or dx.shape[0], wgs=wgs)
+    out_dtype = torch.float16 if yt == "f16" else torch.float32
+    y = v.gemv_planned(P, plan, dx, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), (blob, L, plan, P, dx)
+
+
+# (N, K, wgs): one group; G below one slice; ragged slices; rows split across
+# tiles (wgs 1..3 put hundreds of rows in one block); K = 28672 (G = 448)
+CASES = [
+    (1, 64, 0), (3, 128, 0), (768, 768, 0), (37, 2048, 0), (200, 2112, 0), (130, 4096 + 640, 0),
+    (1000, 5632, 0), (300, 4096, 1), (257, 2048, 3), (64, 28672, 0), (9, 28672, 2), (2000, 64, 1),
+]
+
+
+@pytest.mark.parametrize("N,K,wgs", CASES)
+@pytest.mark.parametrize("yt", ["f16", "f32"])
+def test_planned_parity(N, K, wgs, yt):
+    v = vbq()
+    q, bits, s, x = draw(N, K, seed=N + 7)
+    y, _ = planned(v, q, bits, s, x, wgs=wgs, yt=yt)
+    y_ref, bound = oracle.gemv(q, bits, s, x)
+    ok, worst, idx = within_bound(y, y_ref, bound)
+    assert ok, f"N={N} K={K} wgs={wgs} worst err/bound={worst:.3g} at {idx}"
+
+
+@pytest.mark.parametrize("mix", ["u1", "u2", "u4", "u8", "wide", "head"])
+def test_planned_width_mixes_two_tokens(mix):
+    v = vbq()
+    m = {"u1": {1: 1.0}, "u2": {2: 1.0}, "u4": wl.MIX_U4, "u8": wl.MIX_U8, "wide": wl.MIX_WIDE,
+         "head": wl.MIX_HEAD}[mix]
+    q, bits, s, x = draw(300, 2048 + 1024, m, seed=13, M=2, outliers=0.01)
+    for wgs in (0, 2):
+        y, _ = planned(v, q, bits, s, x, wgs=wgs)
+        y_ref, bound = oracle.gemv(q, bits, s, x)
+        ok, worst, idx = within_bound(y, y_ref, bound)
+        assert ok, f"{mix} wgs={wgs} worst err/bound={worst:.3g} at {idx}"
+
+
+def test_planned_special_scales():
+    v = vbq()
+    N, K = 40, 64 * 70
+    q, bits, s, x = draw(N, K, seed=21)
+    s = s.copy()
+    s[0, :] = 0x0000           # +0
+    s[1, :] = 0x8000           # -0
+    s[2, 3] = 0x0001           # smallest subnormal
+    s[3, :] = 0x03FF           # largest subnormal
+    s[4, :] = 0xAC00           # negative
+    s[5, 7] = 0x7C00           # +inf
+    s[6, 40] = 0xFC00          # -inf
+    s[7, 65] = 0x7E00          # NaN
+    s[8, :] = 0x7BFF           # largest finite
+    for yt in ("f32", "f16"):
+        y, _ = planned(v, q, bits, s, x, wgs=3, yt=yt)
+        y_ref, bound = oracle.gemv(q, bits, s, x)
+        if yt == "f16":
+            big = np.abs(y_ref) > 65504
+            bound = np.where(big, np.inf, bound)
+        ok, worst, idx = within_bound(y, y_ref, bound)
+        assert ok, f"{yt}: worst err/bound={worst:.3g} at {idx}"
+        assert np.all(y[0, :2] == 0)
+
+
+def test_planned_unit_vectors_give_dequant_columns():
+    v = vbq()
+    N, K = 97, 64 * 75
+    q, bits, s, _ = draw(N, K, seed=31)
+    dq, db, ds, _ = upload(q, bits, s, np.zeros((1, K), np.uint16), torch)
+    blob, L = v.pack(dq, db, ds)
+    w = v.dequant(L, blob, torch.float32)
+    plan, P = v.prepare(L, blob, M=2, wgs=5)
+    ks = [0, 1, 31, 32, 63, 64, 2047, 2048, 2111, K - 1]
+    for i in range(0, len(ks), 2):
+        X = torch.zeros((2, K), dtype=torch.float16, device="cuda")
+        X[0, ks[i]] = 1.0
+        X[1, ks[i + 1]] = 1.0
+        Y = v.gemv_planned(P, plan, X, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(Y[0], w[:, ks[i]]), f"column {ks[i]}"
+        assert torch.equal(Y[1], w[:, ks[i + 1]]), f"column {ks[i + 1]}"
+
+
+def test_planned_deterministic_strided_and_token_consistent():
+    v = vbq()
+    N, K, M = 333, 64 * 150, 2
+    q, bits, s, x = draw(N, K, seed=41, M=M)
+    dq, db, ds, dx = upload(q, bits, s, x, torch)
+    blob, L = v.pack(dq, db, ds)
+    plan, P = v.prepare(L, blob, M=2)
+    xs = torch.zeros((M, K + 40), dtype=torch.float16, device="cuda")
+    xs[:, :K] = dx
+    out = torch.full((M, N + 10), float("nan"), dtype=torch.float32, device="cuda")
+    v.gemv_planned(P, plan, xs[:, :K], out=out[:, :N])
+    y2 = v.gemv_planned(P, plan, dx, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :N], y2)
+    assert bool(torch.isnan(out[:, N:]).all())  # nothing written past the used part of each row
+    y_ref, bound = oracle.gemv(q, bits, s, x)
+    ok, worst, _ = within_bound(y2.cpu().numpy(), y_ref, bound)
+    assert ok, worst
+    for m in range(M):  # one token alone: the same plan sums in the same order
+        ym = v.gemv_planned(P, plan, dx[m].contiguous(), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(ym, y2[m])
+
+
+@pytest.mark.parametrize("Ns,K,M,yt", [((5632, 5632), 2048, 1, "f16"), ((300, 77, 1000), 4096, 1, "f32"),
+                                        ((640, 33, 200, 129), 2112, 2, "f16")])
+def test_planned_shared_parity_and_equal_to_single(Ns, K, M, yt):
+    v = vbq()
+    out_dtype = torch.float16 if yt == "f16" else torch.float32
+    spec0 = wl.MatrixSpec("t", Ns[0], K, wl.MIX_BASE, layer=K)
+    x = wl.draw_x(spec0, 93, M, outliers=0.01)
+    dx = torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
+    plans, host = [], []
+    rows = -(-max(Ns) // 64)  # about the same rows per block for every matrix
+    for i, N in enumerate(Ns):
+        spec = wl.MatrixSpec("t", N, K, wl.MIX_WIDE if i % 2 else wl.MIX_BASE, layer=i + 3)
+        bits = wl.draw_bits(spec, 93)
+        q = wl.draw_codes(spec, 93, bits)
+        s = wl.draw_scales(spec, 93)
+        dq, db, ds, _ = upload(q, bits, s, x, torch)
+        blob, L = v.pack(dq, db, ds)
+        plan, P = v.prepare(L, blob, M=2, wgs=-(-N // rows))
+        plans.append((P, plan))
+        host.append((q, bits, s))
+    outs = v.gemv_planned_shared(plans, dx, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    for (P, plan), (q, bits, s), y in zip(plans, host, outs):
+        got = y.float().cpu().numpy().astype(np.float64)
+        y_ref, bound = oracle.gemv(q, bits, s, x)
+        ok, worst, where = within_bound(got, y_ref, bound)
+        assert ok, (Ns, P.N, worst, where)
+        alone = v.gemv_planned(P, plan, dx, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(alone, y)
+
+
+@pytest.mark.parametrize("N,K,wgs", [(300, 4096, 1), (1000, 5632, 7), (5, 64, 0), (64, 28672, 3)])
+def test_plan_tiles_cover_every_group_once(N, K, wgs):
+    """Host read-back of the plan: per block, the tile chain covers the block's
+    groups in row-major order exactly once, each tile within the stride, and
+    the per-tile positions and scales match the packed matrix."""
+    v = vbq()
+    q, bits, s, x = draw(N, K, seed=5)
+    _, (blob, L, plan, P, _) = planned(v, q, bits, s, x, wgs=wgs)
+    buf = plan.cpu().numpy()
+    G = K // 64
+    seen = np.zeros((N, G), np.int32)
+    for b in range(P.wgs):
+        n0 = b * P.rows
+        R = min(P.rows, N - n0)
+        base = b * P.region_bytes
+        t, nxt, covered = 0, None, 0
+        while True:
+            off = base + t * P.tile_bytes
+            h = buf[off:off + 64].view(np.uint32)
+            assert h[15] == 0x4E4C5056 and h[13] == t
+            cnt = h[0:4].astype(np.int64)
+            n = int(h[10])
+            assert cnt.sum() == n and n > 0
+            assert int(h[12]) == int(h[11]) + 4 * n <= P.tile_bytes
+            if t == 0:
+                assert int(h[12]) <= P.first_bytes
+            if nxt is not None:
+                assert nxt == int(h[12])
+            ra, nr, gf, ge = int(h[4]), int(h[5]), int(h[6]), int(h[7])
+            words = buf[off + int(h[11]):off + int(h[11]) + 4 * n].view(np.uint32)
+            e = words >> 16
+            col, row = e // nr, e % nr + ra
+            assert np.all(row < R) and np.all(col < G)
+            # groups of this tile: row-major from (ra, gf) to (ra + nr - 1, ge - 1)
+            first, last = ra * G + gf, (ra + nr - 1) * G + ge - 1
+            flat = row * G + col
+            assert flat.min() == first and flat.max() == last and len(np.unique(flat)) == n == last - first + 1
+            assert covered == first
+            covered = last + 1
+            seen[n0 + row, col] += 1
+            np.testing.assert_array_equal((words & 0xFFFF).astype(np.uint16), s[n0 + row, col])
+            # slot order: widths 8,4,2,1, then column, then row
+            widths = bits[n0 + row, col]
+            sec = np.repeat([8, 4, 2, 1], cnt)
+            np.testing.assert_array_equal(widths, sec)
+            key = (np.repeat(np.arange(4), cnt) * G + col) * nr + (row - ra)
+            assert np.all(np.diff(key) > 0)
+            nxt = int(h[9])
+            t += 1
+            if nxt == 0:
+                assert t == int(h[14])
+                break
+        assert covered == R * G
+    assert np.all(seen == 1)
