@@ -5,8 +5,9 @@
 
 One step = every GEMV of one synthetic decoder step (stage order qkv, o,
 gate||up, down per layer, then the LM head; gate and up read the same
-activations and share one launch), M = 1, weights packed in VBQ1 and resident
-in HBM before timing.  Prints ONE JSON line with us/step, the
+activations and share one launch), M = 1, weights packed in VBQ1, prepared
+once into GEMV plans (the default path; --path vbq1 reads the blobs
+directly) and resident in HBM before timing.  Prints ONE JSON line with us/step, the
 achieved algorithmic HBM bandwidth of the GEMV kernel (per-launch duration from
 HIP events around the captured step graph, on the launch stream),
 the on-GPU fp16 dense control and the CPU oracle timed on a bounded sample of
@@ -37,6 +38,8 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode9b", choices=["decode9b", "decode1b", "mlp1b", "linear768"])
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"], help="how the step is launched")
+    ap.add_argument("--path", default="plan", choices=["plan", "vbq1"],
+                    help="GEMVs from prepared plans (default) or straight from the VBQ1 blobs")
     ap.add_argument("--no-control", action="store_true", help="skip the fp16 dense control")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the baseline sample")
@@ -57,29 +60,32 @@ def time_steps(torch, fn, steps):
     return a.elapsed_time(b) / steps  # ms per step
 
 
-KERNEL_SOURCES = ("vbq_stream.hip", "vbq_unpack.h", "vbq_common.h")
+KERNELS = {  # path -> (kernel, entry point, profile name, sources)
+    "plan": ("k_gemv_plan<1>", "vbq_gemv_planned", "k_gemv_plan", ("vbq_plan.hip", "vbq_unpack.h", "vbq_common.h")),
+    "vbq1": ("k_gemv_stream<1>", "vbq_gemv", "k_gemv_stream", ("vbq_stream.hip", "vbq_unpack.h", "vbq_common.h")),
+}
 
 
-def kernel_source_hash():
+def kernel_source_hash(path="plan"):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNELS[path][3]:
         with open(os.path.join(ROOT, "decode_gemv_vbq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, kpath="plan"):
     """HBM bytes per launch of the GEMV kernel from the committed rocprofv3 counter
     summary (FETCH_SIZE x its copy-calibrated factor + WRITE_SIZE), or None when the
     kernel source has changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"k_gemv_stream_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"{KERNELS[kpath][2]}_{workload}.md")
     if not os.path.exists(path):
         return None
     for line in open(path):
         if line.startswith("traffic-json: "):
             t = json.loads(line[len("traffic-json: "):])
-            if t.get("kernel_source_sha") != kernel_source_hash():
+            if t.get("kernel_source_sha") != kernel_source_hash(kpath):
                 return None
             return round(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
     return None
@@ -144,7 +150,7 @@ def main(argv=None):
     v.lib()
     assert torch.cuda.is_available(), "bench needs a GPU"
     log(f"{v.version()} on {torch.cuda.get_device_name(0)}")
-    step = DecodeStep(args.workload, M=1, log=log)
+    step = DecodeStep(args.workload, M=1, log=log, planned=args.path == "plan")
     n_launch = len(step.stages)
     alg = step.alg_bytes()
     log(f"{args.workload}: {len(step.mats)} GEMVs in {n_launch} launches, {step.weights() / 1e9:.3f} B weights, mean {step.mean_bits():.3f} bits, "
@@ -185,7 +191,7 @@ def main(argv=None):
     achieved = alg_per_launch / avg_launch_s
     log(f"kernels: {avg_launch_s * 1e6:.2f} us/launch avg in the step, {achieved / 1e9:.0f} GB/s; per kind (replayed "
         f"alone, {kern_ms * 1e3:.1f} us summed): " + ", ".join(f"{k} {d['us']} us {d['GBps']} GB/s" for k, d in kinds.items()))
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, args.path)
 
     control = None
     if not args.no_control:
@@ -226,7 +232,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": args.workload, "M": 1, "gemvs_per_step": len(step.mats), "launches_per_step": n_launch,
-            "launch": args.mode,
+            "launch": args.mode, "path": args.path,
+            "plan_bytes_per_step": step.plan_bytes() if step.planned else None,
             "weights": step.weights(), "mean_bits": round(step.mean_bits(), 4),
             "alg_bytes_per_step": alg, "layout_bytes_per_step": step.layout_bytes(),
             "GBps_step": round(gbps, 1), "pct_peak_step": round(100 * gbps * 1e9 / PEAK_HBM, 2),
@@ -237,7 +244,7 @@ def main(argv=None):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4), "traffic": traffic,
-            "kernel": "k_gemv_stream<1> (vbq_gemv)", "alg_bytes_per_launch": round(alg_per_launch),
+            "kernel": f"{KERNELS[args.path][0]} ({KERNELS[args.path][1]})", "alg_bytes_per_launch": round(alg_per_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3), "per_matrix": kinds,
             "per_matrix_sum_us": round(kern_ms * 1e3, 1),
         },

@@ -1,12 +1,13 @@
 """One decode step: the stage-ordered VBQ GEMVs of a synthetic decoder, resident in HBM.
 
-Builds every weight matrix of a workload on the device (seeded draw -> vbq_pack),
-keeps the packed blobs, activations, outputs and workspaces, and runs the step
-as back-to-back launches on one stream -- eagerly, or replayed from a captured
-HIP graph (one host launch per step).  A stage is one GEMV, or the gate and up
-projections of a layer, which read the same activations and run as one
-vbq_gemv_shared launch.  The bench times exactly this
-object and the full-size parity test checks exactly this object.
+Builds every weight matrix of a workload on the device (seeded draw -> vbq_pack,
+then, on the default path, vbq_prepare: the one-time plan each GEMV reads),
+keeps the packed blobs, plans, activations, outputs and workspaces, and runs
+the step as back-to-back launches on one stream -- eagerly, or replayed from a
+captured HIP graph (one host launch per step).  A stage is one GEMV, or the
+gate and up projections of a layer, which read the same activations and run as
+one shared launch.  The bench times exactly this object and the full-size
+parity test checks exactly this object.
 """
 from __future__ import annotations
 
@@ -18,10 +19,12 @@ from decode_gemv_vbq_amd import workload as wl
 
 
 class Matrix:
-    __slots__ = ("spec", "L", "blob", "x", "y", "ws", "sample_rows", "sample", "w16", "y16")
+    __slots__ = ("spec", "L", "blob", "x", "y", "ws", "P", "plan", "sample_rows", "sample", "w16", "y16")
 
     def __init__(self, spec, L, blob, x, y, ws):
         self.spec, self.L, self.blob, self.x, self.y, self.ws = spec, L, blob, x, y, ws
+        self.P = None
+        self.plan = None
         self.sample_rows = None
         self.sample = None
         self.w16 = None
@@ -30,9 +33,11 @@ class Matrix:
 
 class DecodeStep:
     def __init__(self, name: str = "decode9b", M: int = 1, variant: str = "clustered", device="cuda",
-                 keep_rows: int = 0, out_dtype=None, log=None):
+                 keep_rows: int = 0, out_dtype=None, log=None, planned: bool = True):
         import torch
         self.torch = torch
+        # prepared plans serve up to two tokens; larger batches read VBQ1 directly
+        self.planned = planned and M <= 2
         self.W = wl.workload(name, M=M, variant=variant)
         self.M = M
         self.device = torch.device(device)
@@ -69,6 +74,40 @@ class DecodeStep:
             if log and (i % 40 == 0 or i == len(self.W.mats) - 1):
                 log(f"built {i + 1}/{len(self.W.mats)} matrices")
         torch.cuda.synchronize()
+        self.shared_ok = [True] * len(self.stages)
+        if self.planned:
+            self.prepare_plans(log)
+
+    def prepare_plans(self, log=None):
+        """One plan per matrix.  The matrices of a shared stage split the
+        device's compute units in proportion to their rows, so that the stage
+        is one launch spanning the device once."""
+        torch = self.torch
+        cus = torch.cuda.get_device_properties(self.device).multi_processor_count
+        for k, st in enumerate(self.stages):
+            ms = [self.mats[i] for i in st]
+            total = sum(m.spec.N for m in ms)
+            for m in ms:
+                wgs = 0 if len(ms) == 1 else max(1, round(cus * m.spec.N / total))
+                m.plan, m.P = v.prepare(m.L, m.blob, M=max(1, self.M), wgs=wgs)
+            if len(ms) > 1:
+                P0 = ms[0].P
+                self.shared_ok[k] = all(m.P.tile_bytes == P0.tile_bytes and m.P.psum == P0.psum for m in ms)
+        torch.cuda.synchronize()
+        if log:
+            log(f"prepared {len(self.mats)} plans, {self.plan_bytes() / 1e6:.1f} MB read per step")
+
+    def plan_bytes(self) -> int:
+        """Bytes the planned kernels read per step: every tile (header, code
+        records, one scale|position word per group) plus the activations."""
+        tot = 0
+        for m in self.mats:
+            if m.P is None:
+                continue
+            groups = m.spec.N * m.spec.G
+            tiles = -(-(int(m.L.code_bytes) + 4 * groups) // (m.P.tile_bytes - 132))
+            tot += int(m.L.code_bytes) + 4 * groups + 64 * max(tiles, m.P.wgs) + 2 * self.M * m.spec.K * m.P.wgs
+        return tot
 
     # ------------------------------------------------------------- the step
     def run(self):
@@ -77,6 +116,17 @@ class DecodeStep:
 
     def run_stage(self, st):
         """Enqueue one stage: a single GEMV, or one launch for matrices sharing x."""
+        if self.planned:
+            ms = [self.mats[i] for i in st]
+            if len(ms) == 1:
+                m = ms[0]
+                v.gemv_planned(m.P, m.plan, m.x, out=m.y)
+            elif self.shared_ok[self.stages.index(st)]:
+                v.gemv_planned_shared([(m.P, m.plan) for m in ms], ms[0].x, outs=[m.y for m in ms])
+            else:
+                for m in ms:
+                    v.gemv_planned(m.P, m.plan, m.x, out=m.y)
+            return
         if len(st) == 1:
             m = self.mats[st[0]]
             if self.M == 1:
