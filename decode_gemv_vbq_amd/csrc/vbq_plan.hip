@@ -24,15 +24,16 @@
 //    the largest first tile, so the kernel issues every copy without first
 //    reading metadata.
 //
-// The GEMV kernel: one 1024-thread workgroup per row block.  Tile 0 is copied
-// into LDS with global_load_lds_dwordx4 as soon as the kernel starts, together
-// with the activations.  Tile k+1 is copied by one wave into the other half of
-// a two-slot ring while the other waves run the passes of tile k; then every
-// wave sums the rows of tile k-1.  One barrier per tile.  A pass is 64 slots
-// of one width: codes are contiguous per lane, x is read per group column
-// (lanes of a column broadcast), partials land at e (contiguous per column).
-// Row sums follow the column order and the tile order, so the result does not
-// depend on timing.
+// The GEMV kernel: one 1024-thread workgroup per row block.  As soon as the
+// kernel starts, half of the workgroup copies tile 0 into LDS with
+// global_load_lds_dwordx4 while the other half stages the activations.  Tile
+// k+1 is copied by two waves into the other half of a two-slot ring while the
+// other waves run the passes of tile k, handed out through an LDS counter;
+// then every wave sums the rows of tile k-1.  One barrier per tile.  A pass is
+// 64 slots of one width: codes are contiguous per lane, x is read per group
+// column (lanes of a column broadcast), partials land at e (contiguous per
+// column).  Row sums follow the column order and the tile order, so the
+// result does not depend on timing.
 #include <algorithm>
 
 #include "vbq_common.h"
@@ -51,6 +52,7 @@ constexpr int kMaxG = 512;  // groups per row the plans support (K <= 32768)
 constexpr int kMaxTiles = 1024; // tiles per row block
 constexpr int kMaxMats = VBQ_MAX_SHARED;
 constexpr int kMaxTb = 64 * 1024; // tile stride bound (16-bit positions)
+constexpr int kCopyWaves = 2;     // waves of the GEMV workgroup that copy the next tile
 
 // Usable bytes per tile before the last group's overhang: a group starting
 // below C ends at most 68 bytes later, and the header takes 64.
@@ -341,7 +343,7 @@ struct PArgs {
 };
 
 struct PLayout {
-    uint32_t x, ring, psum, ybuf, total;
+    uint32_t x, ring, psum, ybuf, ctr, total;
 };
 
 __host__ __device__ inline uint32_t p_take(uint32_t &o, uint32_t bytes)
@@ -360,6 +362,7 @@ __host__ __device__ inline PLayout p_layout(int MT, int G, int rows, int tb, int
     l.ring = p_take(o, 2u * (uint32_t)tb);
     l.psum = p_take(o, 2u * (uint32_t)(MT * ps) * 4u);
     l.ybuf = p_take(o, (uint32_t)(MT * rows) * 4u);
+    l.ctr = p_take(o, 2u * 4u); // pass counters of the two ring slots
     l.total = o;
     return l;
 }
@@ -369,21 +372,23 @@ __host__ __device__ inline PLayout p_layout(int MT, int G, int rows, int tb, int
 // Item = (token, group, quarter q): pairs 4q..4q+3; the 8 items of a group are
 // 8 adjacent lanes.  Loads and stores are separate so the loads go out with
 // the first tile's copy.
+constexpr int kXT = kT / 2; // threads that stage x (the upper half; the lower half copies tile 0)
+
 template <int MT>
 struct XRegs {
-    static constexpr int kPer = (MT * kMaxG * 8 + kT - 1) / kT;
+    static constexpr int kPer = (MT * kMaxG * 8 + kXT - 1) / kXT;
     uint32_t lo0[kPer], lo1[kPer], hi0[kPer], hi1[kPer];
 };
 
 template <int MT>
 __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<MT> &xs)
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x - kXT;
     const int items = MT * G * 8;
     const bool vec = (ldx % 4) == 0 && ((uintptr_t)x % 8) == 0;
 #pragma unroll
     for (int k = 0; k < XRegs<MT>::kPer; k++) {
-        const int i = tid + k * kT;
+        const int i = tid + k * kXT;
         xs.lo0[k] = xs.lo1[k] = xs.hi0[k] = xs.hi1[k] = 0u;
         if (i < items) {
             const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
@@ -408,11 +413,11 @@ __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<
 template <int MT>
 __device__ __forceinline__ void x_store(int G, const XRegs<MT> &xs, uint32_t *xrec)
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x - kXT;
     const int items = MT * G * 8;
 #pragma unroll
     for (int k = 0; k < XRegs<MT>::kPer; k++) {
-        const int i = tid + k * kT;
+        const int i = tid + k * kXT;
         if (i >= items) // whole groups of 8 lanes drop out together
             break;
         const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
@@ -454,11 +459,21 @@ struct Tile {
     uint32_t ra, nr, g_first, g_end, inv_nr, next, n, se_off;
 };
 
+// One lane reads the header (48 bytes instead of 3 KiB of LDS traffic per
+// wave) and the fields are broadcast to the wave.
 __device__ __forceinline__ Tile read_tile(const uint8_t *t)
 {
-    const uint4 a = *reinterpret_cast<const uint4 *>(t);
-    const uint4 b = *reinterpret_cast<const uint4 *>(t + 16);
-    const uint4 c = *reinterpret_cast<const uint4 *>(t + 32);
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a, c = a;
+    if ((threadIdx.x & 63) == 0) {
+        a = *reinterpret_cast<const uint4 *>(t);
+        b = *reinterpret_cast<const uint4 *>(t + 16);
+        c = *reinterpret_cast<const uint4 *>(t + 32);
+    }
+#define VBQ_BCAST(v) v = (uint32_t)__builtin_amdgcn_readfirstlane((int)v)
+    VBQ_BCAST(a.x); VBQ_BCAST(a.y); VBQ_BCAST(a.z); VBQ_BCAST(a.w);
+    VBQ_BCAST(b.x); VBQ_BCAST(b.y); VBQ_BCAST(b.z); VBQ_BCAST(b.w);
+    VBQ_BCAST(c.x); VBQ_BCAST(c.y); VBQ_BCAST(c.z); VBQ_BCAST(c.w);
+#undef VBQ_BCAST
     Tile h;
     h.cnt[0] = a.x;
     h.cnt[1] = a.y;
@@ -501,40 +516,42 @@ __device__ __forceinline__ void plan_pass(int q, uint32_t cnt, uint32_t wb, uint
 #pragma unroll
     for (int m = 0; m < MT; m++) {
         const uint32_t *xr = xrec + ((uint32_t)m * G + xcol) * kXRec;
-        float acc0 = 0.f, acc1 = 0.f; // two chains for instruction-level parallelism
+        float acc[4] = {0.f, 0.f, 0.f, 0.f}; // four chains: pair p goes to chain (p / 4) % 4
 #pragma unroll
-        for (int k = 0; k < 8; k += 2) {
+        for (int k = 0; k < 8; k++) {
             const U4 xa = *reinterpret_cast<const U4 *>(xr + 4 * k);
-            const U4 xb = *reinterpret_cast<const U4 *>(xr + 4 * k + 4);
-            acc0 = dot2(hp[4 * k + 0], xa.v[0], acc0);
-            acc1 = dot2(hp[4 * k + 4], xb.v[0], acc1);
-            acc0 = dot2(hp[4 * k + 1], xa.v[1], acc0);
-            acc1 = dot2(hp[4 * k + 5], xb.v[1], acc1);
-            acc0 = dot2(hp[4 * k + 2], xa.v[2], acc0);
-            acc1 = dot2(hp[4 * k + 6], xb.v[2], acc1);
-            acc0 = dot2(hp[4 * k + 3], xa.v[3], acc0);
-            acc1 = dot2(hp[4 * k + 7], xb.v[3], acc1);
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                acc[k & 3] = dot2(hp[4 * k + t], xa.v[t], acc[k & 3]);
         }
         const float cc = __uint_as_float(xr[32 + C]);
-        psum[m * ps + e] = s * ((acc0 + acc1) - cc);
+        psum[m * ps + e] = s * (((acc[0] + acc[1]) + (acc[2] + acc[3])) - cc);
     }
 }
 
 // Rows per row-sum item (8 lanes per row).
 constexpr int kSumRows = 8;
 
+// Where finished rows go.
+struct YOut {
+    void *y;
+    int ldy, n0, yt;
+};
+
 // Row-sum item t of a tile: rows 8t..8t+7 of the tile.  The partials of row j
 // sit at column * nr + j for the tile's columns of that row; they are summed
-// in column order (four interleaved chains, fixed) and added to ybuf, tiles in
-// order.
+// in column order (four interleaved chains, fixed) and added to the row's sum
+// from earlier tiles (ybuf, tiles in order).  A row that ends in this tile is
+// written to y; only a row that continues into the next tile stays in ybuf.
 template <int MT>
 __device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps, int rows, const float *psum,
-                                            float *ybuf)
+                                            float *ybuf, const YOut &yo)
 {
     const int lane = threadIdx.x & 63;
     const int j = kSumRows * t + (lane >> 3), q = lane & 7;
     const int nr = (int)h.nr;
     const int lo = j == 0 ? (int)h.g_first : 0, hi = j == nr - 1 ? (int)h.g_end : G;
+    const bool done = j < nr - 1 || (int)h.g_end == G || h.next == 0;
 #pragma unroll
     for (int m = 0; m < MT; m++) {
         float v = 0.f;
@@ -555,8 +572,19 @@ __device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps,
         v += __shfl_xor(v, 4, 8);
         v += __shfl_xor(v, 2, 8);
         v += __shfl_xor(v, 1, 8);
-        if (q == 0 && j < nr)
-            ybuf[m * rows + (int)h.ra + j] += v;
+        if (q == 0 && j < nr) {
+            const int r = (int)h.ra + j;
+            const float tot = ybuf[m * rows + r] + v;
+            if (done) {
+                const uint64_t o = (uint64_t)m * yo.ldy + yo.n0 + r;
+                if (yo.yt == VBQ_F16)
+                    reinterpret_cast<__half *>(yo.y)[o] = __float2half_rn(tot);
+                else
+                    reinterpret_cast<float *>(yo.y)[o] = tot;
+            } else {
+                ybuf[m * rows + r] = tot;
+            }
+        }
     }
 }
 
@@ -584,17 +612,24 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
     float *ybuf = reinterpret_cast<float *>(smem + L.ybuf);
     const uint8_t *region = pm.plan + (uint64_t)blk * pm.region;
     const uint32_t ring = lds_addr(smem + L.ring);
+    const YOut yo{pm.y, pm.ldy, n0, args.yt};
 
-    // ---- tile 0 and the activations, issued together
-    copy_chunks(region, ring, (uint32_t)args.first, wave, kW);
-    {
+    // ---- tile 0 (copied by the lower half of the workgroup) and the
+    // activations (staged by the upper half), in flight together; each half
+    // waits only for its own loads
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + L.ctr);
+    if (tid < kXT) {
+        copy_chunks(region, ring, (uint32_t)args.first, wave, kXT / 64);
+        for (int i = tid; i < MT * R; i += kXT)
+            ybuf[(i / R) * rows + i % R] = 0.f;
+        if (tid == 0)
+            cnt[0] = 0u;
+        wait_vm0();
+    } else {
         XRegs<MT> xs;
         x_load<MT>(args.x, args.ldx, G, xs);
-        for (int i = tid; i < MT * R; i += kT)
-            ybuf[(i / R) * rows + i % R] = 0.f;
         x_store<MT>(G, xs, xrec);
     }
-    wait_vm0();
     __syncthreads();
 
     // ---- tile k sits in ring slot k & 1: wave 0 copies tile k+1 into the
@@ -607,16 +642,26 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
         const uint8_t *tile = smem + L.ring + (uint32_t)slot * tb;
         const Tile h = read_tile(tile);
         float *ps_k = psum + slot * (MT * ps);
-        if (wave == 0) {
+        if (wave < kCopyWaves) {
+            if (tid == 0)
+                cnt[slot ^ 1] = 0u; // pass counter of tile k+1 (its last users left tile k-1's phase)
             if (h.next)
-                copy_chunks(region + (uint64_t)(k + 1) * tb, ring + (uint32_t)(slot ^ 1) * tb, h.next, 0, 1);
+                copy_chunks(region + (uint64_t)(k + 1) * tb, ring + (uint32_t)(slot ^ 1) * tb, h.next, wave,
+                            kCopyWaves);
         } else {
             const int np0 = (int)((h.cnt[0] + 63) >> 6), np1 = (int)((h.cnt[1] + 63) >> 6);
             const int np2 = (int)((h.cnt[2] + 63) >> 6), np3 = (int)((h.cnt[3] + 63) >> 6);
             const int pb1 = np0, pb2 = pb1 + np1, pb3 = pb2 + np2, np = pb3 + np3;
             const uint32_t wb1 = h.cnt[0], wb2 = wb1 + h.cnt[1], wb3 = wb2 + h.cnt[2];
             const uint32_t off1 = kHdr + 64u * h.cnt[0], off2 = off1 + 32u * h.cnt[1], off3 = off2 + 16u * h.cnt[2];
-            for (int p = wave - 1; p < np; p += kW - 1) {
+            // worker w runs pass w first; later passes come from an LDS counter,
+            // each asked for before the current pass runs so that the atomic's
+            // latency hides behind it
+            constexpr int nw = kW - kCopyWaves;
+            uint32_t nextp = 0;
+            for (int p = wave - kCopyWaves; p < np; p = __builtin_amdgcn_readfirstlane((int)nextp)) {
+                if ((tid & 63) == 0)
+                    nextp = nw + atomicAdd(cnt + slot, 1u);
                 if (p < pb1)
                     plan_pass<8, MT>(p, h.cnt[0], 0u, kHdr, tile, h, G, ps, xrec, ps_k);
                 else if (p < pb2)
@@ -629,30 +674,20 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
         }
         if (k > 0) {
             const int nsum = ((int)prev.nr + kSumRows - 1) / kSumRows;
-            for (int t = (wave + kW - 1) % kW; t < nsum; t += kW) // wave 0, busy copying, takes the last share
-                rowsum_item<MT>(t, prev, G, ps, rows, psum + (slot ^ 1) * (MT * ps), ybuf);
+            for (int t = (wave + kW - kCopyWaves) % kW; t < nsum; t += kW) // copying waves take the last shares
+                rowsum_item<MT>(t, prev, G, ps, rows, psum + (slot ^ 1) * (MT * ps), ybuf, yo);
         }
-        wait_vm0(); // wave 0: the copy of tile k+1
+        wait_vm0(); // copy waves: the copy of tile k+1
         __syncthreads();
         prev = h;
         if (!h.next)
             break;
     }
-    // ---- rows of the last tile (partials in psum slot k & 1)
+    // ---- rows of the last tile (partials in psum slot k & 1); every row ends here
     {
         const int nsum = ((int)prev.nr + kSumRows - 1) / kSumRows;
         for (int t = wave; t < nsum; t += kW)
-            rowsum_item<MT>(t, prev, G, ps, rows, psum + (k & 1) * (MT * ps), ybuf);
-    }
-    __syncthreads();
-    for (int i = tid; i < MT * R; i += kT) {
-        const int m = i / R, r = i - m * R;
-        const float v = ybuf[m * rows + r];
-        const uint64_t o = (uint64_t)m * pm.ldy + n0 + r;
-        if (args.yt == VBQ_F16)
-            reinterpret_cast<__half *>(pm.y)[o] = __float2half_rn(v);
-        else
-            reinterpret_cast<float *>(pm.y)[o] = v;
+            rowsum_item<MT>(t, prev, G, ps, rows, psum + (k & 1) * (MT * ps), ybuf, yo);
     }
 }
 
