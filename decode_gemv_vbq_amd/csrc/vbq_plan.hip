@@ -460,7 +460,9 @@ struct Tile {
 };
 
 // One lane reads the header (48 bytes instead of 3 KiB of LDS traffic per
-// wave) and the fields are broadcast to the wave.
+// wave) and the fields are broadcast to the wave.  (Reading it from memory
+// through the scalar cache instead would share the lgkmcnt counter with the
+// passes' LDS reads and make them wait for that load.)
 __device__ __forceinline__ Tile read_tile(const uint8_t *t)
 {
     uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a, c = a;
@@ -529,8 +531,12 @@ __device__ __forceinline__ void plan_pass(int q, uint32_t cnt, uint32_t wb, uint
     }
 }
 
-// Rows per row-sum item (8 lanes per row).
-constexpr int kSumRows = 8;
+// Lanes that sum one row: more for longer rows, so that a tile's row sums
+// stay short next to its passes (a row of G partials is G / lanes loads deep).
+__device__ __forceinline__ int sum_lanes(int G) { return G > 256 ? 64 : G > 128 ? 32 : G > 64 ? 16 : 8; }
+
+// Row-sum items of a tile with nr rows.
+__device__ __forceinline__ int sum_items(int nr, int G) { return (nr * sum_lanes(G) + 63) / 64; }
 
 // Where finished rows go.
 struct YOut {
@@ -538,17 +544,20 @@ struct YOut {
     int ldy, n0, yt;
 };
 
-// Row-sum item t of a tile: rows 8t..8t+7 of the tile.  The partials of row j
-// sit at column * nr + j for the tile's columns of that row; they are summed
-// in column order (four interleaved chains, fixed) and added to the row's sum
-// from earlier tiles (ybuf, tiles in order).  A row that ends in this tile is
-// written to y; only a row that continues into the next tile stays in ybuf.
-template <int MT>
-__device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps, int rows, const float *psum,
-                                            float *ybuf, const YOut &yo)
+// Row-sum item t of a tile: rows (64 / L) t .. of the tile, L = sum_lanes(G)
+// lanes per row.  The partials of row j sit at column * nr + j for the tile's
+// columns of that row; lane q sums columns q, q + L, ... (four interleaved
+// chains), the L lanes combine in a fixed butterfly, and the row's sum from
+// earlier tiles (ybuf, tiles in order) is added.  A row that ends in this
+// tile is written to y; only a row that continues into the next tile stays in
+// ybuf.
+template <int MT, int L>
+__device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int ps, int rows, const float *psum,
+                                              float *ybuf, const YOut &yo)
 {
     const int lane = threadIdx.x & 63;
-    const int j = kSumRows * t + (lane >> 3), q = lane & 7;
+    constexpr int per = 64 / L;
+    const int j = per * t + lane / L, q = lane & (L - 1);
     const int nr = (int)h.nr;
     const int lo = j == 0 ? (int)h.g_first : 0, hi = j == nr - 1 ? (int)h.g_end : G;
     const bool done = j < nr - 1 || (int)h.g_end == G || h.next == 0;
@@ -559,19 +568,19 @@ __device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps,
             const float *p = psum + m * ps + j;
             float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
             int g = lo + q;
-            for (; g + 24 < hi; g += 32) {
+            for (; g + 3 * L < hi; g += 4 * L) {
                 a0 += p[g * nr];
-                a1 += p[(g + 8) * nr];
-                a2 += p[(g + 16) * nr];
-                a3 += p[(g + 24) * nr];
+                a1 += p[(g + L) * nr];
+                a2 += p[(g + 2 * L) * nr];
+                a3 += p[(g + 3 * L) * nr];
             }
-            for (; g < hi; g += 8)
+            for (; g < hi; g += L)
                 a0 += p[g * nr];
             v = (a0 + a1) + (a2 + a3);
         }
-        v += __shfl_xor(v, 4, 8);
-        v += __shfl_xor(v, 2, 8);
-        v += __shfl_xor(v, 1, 8);
+#pragma unroll
+        for (int d = L >> 1; d > 0; d >>= 1)
+            v += __shfl_xor(v, d, L);
         if (q == 0 && j < nr) {
             const int r = (int)h.ra + j;
             const float tot = ybuf[m * rows + r] + v;
@@ -585,6 +594,18 @@ __device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps,
                 ybuf[m * rows + r] = tot;
             }
         }
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps, int rows, const float *psum,
+                                            float *ybuf, const YOut &yo)
+{
+    switch (sum_lanes(G)) {
+    case 8: rowsum_item_l<MT, 8>(t, h, G, ps, rows, psum, ybuf, yo); break;
+    case 16: rowsum_item_l<MT, 16>(t, h, G, ps, rows, psum, ybuf, yo); break;
+    case 32: rowsum_item_l<MT, 32>(t, h, G, ps, rows, psum, ybuf, yo); break;
+    default: rowsum_item_l<MT, 64>(t, h, G, ps, rows, psum, ybuf, yo); break;
     }
 }
 
@@ -673,7 +694,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
             }
         }
         if (k > 0) {
-            const int nsum = ((int)prev.nr + kSumRows - 1) / kSumRows;
+            const int nsum = sum_items((int)prev.nr, G);
             for (int t = (wave + kW - kCopyWaves) % kW; t < nsum; t += kW) // copying waves take the last shares
                 rowsum_item<MT>(t, prev, G, ps, rows, psum + (slot ^ 1) * (MT * ps), ybuf, yo);
         }
@@ -685,7 +706,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
     }
     // ---- rows of the last tile (partials in psum slot k & 1); every row ends here
     {
-        const int nsum = ((int)prev.nr + kSumRows - 1) / kSumRows;
+        const int nsum = sum_items((int)prev.nr, G);
         for (int t = wave; t < nsum; t += kW)
             rowsum_item<MT>(t, prev, G, ps, rows, psum + (k & 1) * (MT * ps), ybuf, yo);
     }
@@ -778,16 +799,22 @@ vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, 
         wgs = plan_cus();
     const int rows = (N + wgs - 1) / wgs;
     wgs = (N + rows - 1) / rows;
-    // the largest tile stride (1 KiB steps) whose launch fits the LDS budget
+    // the largest tile stride (1 KiB steps) whose launch fits the LDS budget;
+    // two tokens per launch only while that keeps tiles of 16 KiB or more
+    // (beyond, the x records of two tokens crowd out the tiles)
     int tb = 0;
-    for (int cand = kMaxTb; cand >= 4096; cand -= 1024) {
-        const int ps = psum_capacity(cand, G);
-        if (ps > 65536)
-            continue;
-        if (p_layout(M, G, rows, cand, ps).total <= kLdsBudget) {
-            tb = cand;
-            break;
+    for (;;) {
+        tb = 0;
+        for (int cand = kMaxTb; cand >= 4096 && !tb; cand -= 1024) {
+            const int ps = psum_capacity(cand, G);
+            if (ps <= 65536 && p_layout(M, G, rows, cand, ps).total <= kLdsBudget)
+                tb = cand;
         }
+        if (M > 1 && tb < 16 * 1024) {
+            M--;
+            continue;
+        }
+        break;
     }
     if (!tb)
         return VBQ_ERR_SHAPE;
@@ -839,6 +866,10 @@ vbq_status vbq_prepare(const vbq_plan *P, const vbq_layout *L, const void *blob,
     return launch_status();
 }
 
+// One launch for up to P->M tokens (the plans' LDS carve-up holds that many).
+static vbq_status planned_launch(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
+                                 vbq_dtype yt, int tok0, hipStream_t stream);
+
 vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
                                    vbq_dtype yt, hipStream_t stream)
 {
@@ -846,12 +877,29 @@ vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items, int n, int M, 
         return VBQ_ERR_INVALID_ARG;
     if (yt != VBQ_F32 && yt != VBQ_F16)
         return VBQ_ERR_INVALID_ARG;
-    if (M < 1 || M > 2)
+    if (M < 1 || M > 16)
         return VBQ_ERR_BATCH;
+    int chunk = 2;
+    for (int i = 0; i < n; i++) {
+        if (!items[i].P)
+            return VBQ_ERR_INVALID_ARG;
+        VBQ_TRY(check_plan(items[i].P));
+        chunk = std::min(chunk, (int)items[i].P->M);
+    }
+    // tokens beyond what one launch holds run as further launches over the
+    // same plans; each token's arithmetic is the same in every launch shape
+    for (int t0 = 0; t0 < M; t0 += chunk)
+        VBQ_TRY(planned_launch(items, n, std::min(chunk, M - t0), x, ldx, yt, t0, stream));
+    return VBQ_OK;
+}
+
+static vbq_status planned_launch(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
+                                 vbq_dtype yt, int tok0, hipStream_t stream)
+{
     if ((uintptr_t)x % 2)
         return VBQ_ERR_ALIGN;
     PArgs a{};
-    a.x = x;
+    a.x = x + (uint64_t)tok0 * ldx;
     a.ldx = ldx;
     a.yt = (int)yt;
     a.nmat = n;
@@ -874,7 +922,7 @@ vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items, int n, int M, 
             return VBQ_ERR_ALIGN;
         PMat &m = a.mats[i];
         m.plan = (const uint8_t *)it.plan;
-        m.y = it.y;
+        m.y = (uint8_t *)it.y + (uint64_t)tok0 * it.ldy * (yt == VBQ_F32 ? 4 : 2);
         m.region = P->region_bytes;
         m.N = P->N;
         m.ldy = it.ldy;

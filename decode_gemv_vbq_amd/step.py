@@ -36,8 +36,7 @@ class DecodeStep:
                  keep_rows: int = 0, out_dtype=None, log=None, planned: bool = True):
         import torch
         self.torch = torch
-        # prepared plans serve up to two tokens; larger batches read VBQ1 directly
-        self.planned = planned and M <= 2
+        self.planned = planned
         self.W = wl.workload(name, M=M, variant=variant)
         self.M = M
         self.device = torch.device(device)
@@ -89,7 +88,7 @@ class DecodeStep:
             total = sum(m.spec.N for m in ms)
             for m in ms:
                 wgs = 0 if len(ms) == 1 else max(1, round(cus * m.spec.N / total))
-                m.plan, m.P = v.prepare(m.L, m.blob, M=max(1, self.M), wgs=wgs)
+                m.plan, m.P = v.prepare(m.L, m.blob, M=min(2, self.M), wgs=wgs)
             if len(ms) > 1:
                 P0 = ms[0].P
                 self.shared_ok[k] = all(m.P.tile_bytes == P0.tile_bytes and m.P.psum == P0.psum for m in ms)
@@ -98,15 +97,17 @@ class DecodeStep:
             log(f"prepared {len(self.mats)} plans, {self.plan_bytes() / 1e6:.1f} MB read per step")
 
     def plan_bytes(self) -> int:
-        """Bytes the planned kernels read per step: every tile (header, code
-        records, one scale|position word per group) plus the activations."""
+        """Bytes of the prepared plans the step reads from memory: every tile
+        (header, code records, one scale|position word per group) plus the
+        activations once per matrix (the workgroups of a launch share them
+        through the caches)."""
         tot = 0
         for m in self.mats:
             if m.P is None:
                 continue
             groups = m.spec.N * m.spec.G
             tiles = -(-(int(m.L.code_bytes) + 4 * groups) // (m.P.tile_bytes - 132))
-            tot += int(m.L.code_bytes) + 4 * groups + 64 * max(tiles, m.P.wgs) + 2 * self.M * m.spec.K * m.P.wgs
+            tot += int(m.L.code_bytes) + 4 * groups + 64 * max(tiles, m.P.wgs) + 2 * self.M * m.spec.K
         return tot
 
     # ------------------------------------------------------------- the step

@@ -219,7 +219,7 @@ vbq_status vbq_gemv_shared(const vbq_gemv_item *items /* host */, int n, int M, 
 typedef struct vbq_plan {
     uint32_t magic;        /* VBQ_PLAN_MAGIC */
     int32_t N, K, G;       /* matrix shape (G = K / 64 <= 512) */
-    int32_t M;             /* largest token count of its GEMVs (1 or 2) */
+    int32_t M;             /* tokens per GEMV launch (1 or 2) */
     int32_t wgs, rows;     /* row blocks (workgroups) and rows per block */
     int32_t tile_bytes;    /* tile stride, multiple of 1024, <= 65536 */
     int32_t tiles;         /* tiles of the largest block */
@@ -231,9 +231,11 @@ typedef struct vbq_plan {
 } vbq_plan;
 
 /*
- * SYNC.  Fill *P for the matrix (L, blob), GEMVs of up to M tokens (1 or 2)
- * and `wgs` row blocks (<= 0: one per compute unit of the current device; the
- * count is reduced so that no block is empty).  Runs one sizing kernel over the
+ * SYNC.  Fill *P for the matrix (L, blob), launches of up to M tokens (1 or
+ * 2; P->M may come back as 1 where two tokens' activations would leave tiles
+ * under 16 KiB of LDS) and `wgs` row blocks (<= 0: one per compute unit of the
+ * current device; the count is reduced so that no block is empty).  GEMVs of
+ * more tokens run as several launches over the same plan.  Runs one sizing kernel over the
  * width bit planes (workspace ws: device, >= 16 bytes) and waits for it.
  * Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_BATCH (M),
  * VBQ_ERR_WORKSPACE, VBQ_ERR_ALIGN, VBQ_ERR_SHAPE (K > 32768, or the LDS of
@@ -252,10 +254,11 @@ vbq_status vbq_prepare(const vbq_plan *P /* host */, const vbq_layout *L /* host
                        hipStream_t stream);
 
 /*
- * Y = X W^T from a plan, M tokens (1 <= M <= P->M): x fp16 [M][ldx] (ldx >= K),
+ * Y = X W^T from a plan, M tokens (1 <= M <= 16): x fp16 [M][ldx] (ldx >= K),
  * y [M][ldy] (ldy >= N) in yt.  Same results contract as vbq_gemv_batched
  * (fp32 accumulation, |y - y_exact| <= 1e-3 * sum_k |w_k||x_k|), and the
- * result does not depend on timing.  One launch of P->wgs workgroups.
+ * result does not depend on timing: token m's outputs are bit-identical for
+ * every M.  One launch of P->wgs workgroups per P->M tokens.
  * Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_BATCH, VBQ_ERR_SHAPE,
  * VBQ_ERR_ALIGN (plan not 256-byte aligned, x/y not element aligned).
  */

@@ -142,6 +142,27 @@ def test_planned_deterministic_strided_and_token_consistent():
         assert torch.equal(ym, y2[m])
 
 
+@pytest.mark.parametrize("M,Mp", [(3, 2), (4, 1), (7, 2), (16, 2)])
+def test_planned_many_tokens(M, Mp):
+    """M above what one launch holds: token chunks over the same plan, each
+    token bit-identical to its single-token run and within the bound."""
+    v = vbq()
+    N, K = 150, 4096 + 192
+    q, bits, s, x = draw(N, K, seed=M, M=M, outliers=0.01)
+    dq, db, ds, dx = upload(q, bits, s, x, torch)
+    blob, L = v.pack(dq, db, ds)
+    plan, P = v.prepare(L, blob, M=Mp)
+    y = v.gemv_planned(P, plan, dx, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.gemv(q, bits, s, x)
+    ok, worst, idx = within_bound(y.cpu().numpy(), y_ref, bound)
+    assert ok, f"M={M} worst err/bound={worst:.3g} at {idx}"
+    for m in (0, M - 1):
+        ym = v.gemv_planned(P, plan, dx[m].contiguous(), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(ym, y[m])
+
+
 @pytest.mark.parametrize("Ns,K,M,yt", [((5632, 5632), 2048, 1, "f16"), ((300, 77, 1000), 4096, 1, "f32"),
                                         ((640, 33, 200, 129), 2112, 2, "f16")])
 def test_planned_shared_parity_and_equal_to_single(Ns, K, M, yt):
