@@ -27,7 +27,8 @@ EXPORTS = (
     "vbq_version", "vbq_status_string", "vbq_last_error", "vbq_layout_init", "vbq_layout_from_header",
     "vbq_pack_plan_workspace", "vbq_pack_plan", "vbq_pack", "vbq_status_check", "vbq_dequant",
     "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_shared",
-    "vbq_plan_init", "vbq_prepare", "vbq_gemv_planned", "vbq_gemv_planned_shared", "vbq_dense_f16_gemv",
+    "vbq_plan_init", "vbq_prepare", "vbq_gemv_planned", "vbq_gemv_planned_shared", "vbq_gemv_seq",
+    "vbq_gemv_planned_seq", "vbq_dense_f16_gemv",
 )
 MAX_SHARED = 4
 
@@ -59,6 +60,18 @@ class Plan(ctypes.Structure):
 class PlannedItem(ctypes.Structure):
     """Mirror of ``vbq_planned_item``."""
     _fields_ = [("P", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int)]
+
+
+class SeqItem(ctypes.Structure):
+    """Mirror of ``vbq_seq_item``."""
+    _fields_ = [("L", ctypes.c_void_p), ("blob", ctypes.c_void_p), ("x", ctypes.c_void_p), ("ldx", ctypes.c_int),
+                ("y", ctypes.c_void_p), ("ldy", ctypes.c_int), ("stage", ctypes.c_int)]
+
+
+class PlannedSeqItem(ctypes.Structure):
+    """Mirror of ``vbq_planned_seq_item``."""
+    _fields_ = [("P", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("x", ctypes.c_void_p), ("ldx", ctypes.c_int),
+                ("y", ctypes.c_void_p), ("ldy", ctypes.c_int), ("stage", ctypes.c_int)]
 
 
 class Layout(ctypes.Structure):
@@ -105,6 +118,8 @@ def lib():
         L.vbq_prepare.argtypes = [PP, LP, P, P, P]
         L.vbq_gemv_planned.argtypes = [PP, P, i, P, i, P, i, i, P]
         L.vbq_gemv_planned_shared.argtypes = [ctypes.POINTER(PlannedItem), i, i, P, i, i, P]
+        L.vbq_gemv_seq.argtypes = [ctypes.POINTER(SeqItem), i, i, i, P, sz, P]
+        L.vbq_gemv_planned_seq.argtypes = [ctypes.POINTER(PlannedSeqItem), i, i, i, P]
         L.vbq_dense_f16_gemv.argtypes = [i, i, i, P, P, i, P, i, i, P]
         for f in EXPORTS:
             if f not in ("vbq_version", "vbq_status_string", "vbq_last_error", "vbq_pack_plan_workspace"):
@@ -358,6 +373,64 @@ def gemv_planned_shared(plans, x, outs=None, out_dtype=None):
     _check(lib().vbq_gemv_planned_shared(items, len(plans), M, _ptr(x2), x2.stride(0), yt, _stream()),
            "vbq_gemv_planned_shared")
     return outs
+
+
+# -------------------------------------------------------- step executors
+
+class Seq:
+    """One decode step's GEMVs, in stage order, as one C call.
+
+    ``items`` holds ``(L, blob, x, y, stage)`` (packed blobs, ``planned=False``)
+    or ``(P, plan, x, y, stage)`` (prepared plans, ``planned=True``), with x a
+    [M][K] (or [K]) fp16 device tensor and y a [M][N] (or [N]) device tensor,
+    all outputs of one dtype.  The item array is built once; ``run()``
+    enqueues the whole step on the current stream (vbq_gemv_seq /
+    vbq_gemv_planned_seq), so it can be called inside a graph capture.  The
+    object keeps references to everything the array points at.
+    """
+
+    def __init__(self, items, planned: bool):
+        torch = _torch()
+        items = list(items)
+        if not items:
+            raise ValueError("a step needs at least one GEMV")
+        self.planned = planned
+        self.keep = items
+        Item = PlannedSeqItem if planned else SeqItem
+        self.arr = (Item * len(items))()
+        self.M = None
+        ydt = None
+        for k, (meta, buf, x, y, stage) in enumerate(items):
+            _need_cuda(buf)
+            x2 = x.view(1, -1) if x.dim() == 1 else x
+            y2 = y.view(1, -1) if y.dim() == 1 else y
+            if x2.dim() != 2 or x2.stride(1) != 1 or not x2.is_cuda or x2.dtype != torch.float16:
+                raise ValueError("x must be a fp16 [M][K] device tensor with unit column stride")
+            if y2.stride(1) != 1 or (ydt is not None and y2.dtype != ydt):
+                raise ValueError("outputs must be [M][N] with unit column stride and one dtype")
+            if self.M is not None and x2.shape[0] != self.M:
+                raise ValueError("every GEMV of a step has the same token count M")
+            self.M, ydt = x2.shape[0], y2.dtype
+            self.arr[k] = Item(ctypes.addressof(meta), _ptr(buf), _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0),
+                               int(stage))
+        self.yt = VBQ_F32 if ydt == torch.float32 else VBQ_F16
+        self.n = len(items)
+
+    def run(self):
+        if self.planned:
+            _check(lib().vbq_gemv_planned_seq(self.arr, self.n, self.M, self.yt, _stream()), "vbq_gemv_planned_seq")
+        else:
+            _check(lib().vbq_gemv_seq(self.arr, self.n, self.M, self.yt, None, 0, _stream()), "vbq_gemv_seq")
+
+
+def gemv_seq(items):
+    """Run one step over packed blobs: items of (L, blob, x, y, stage)."""
+    Seq(items, planned=False).run()
+
+
+def gemv_planned_seq(items):
+    """Run one step over prepared plans: items of (P, plan, x, y, stage)."""
+    Seq(items, planned=True).run()
 
 
 def dense_f16_gemv(w16, x, out=None, out_dtype=None):

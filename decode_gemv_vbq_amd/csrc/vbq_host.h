@@ -52,6 +52,11 @@ struct StreamItem {
 bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
                         hipStream_t stream, vbq_status *st);
 
+// Every check vbq_gemv_planned_shared makes, for every launch it would
+// enqueue; launches nothing.
+vbq_status planned_shared_check(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
+                                vbq_dtype yt);
+
 } // namespace vbq
 
 #define VBQ_TRY(expr)                                                                                                 \

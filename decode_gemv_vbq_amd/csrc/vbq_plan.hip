@@ -866,35 +866,14 @@ vbq_status vbq_prepare(const vbq_plan *P, const vbq_layout *L, const void *blob,
     return launch_status();
 }
 
-// One launch for up to P->M tokens (the plans' LDS carve-up holds that many).
-static vbq_status planned_launch(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
-                                 vbq_dtype yt, int tok0, hipStream_t stream);
+} // extern "C"
 
-vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
-                                   vbq_dtype yt, hipStream_t stream)
-{
-    if (!items || n < 1 || n > VBQ_MAX_SHARED || !x)
-        return VBQ_ERR_INVALID_ARG;
-    if (yt != VBQ_F32 && yt != VBQ_F16)
-        return VBQ_ERR_INVALID_ARG;
-    if (M < 1 || M > 16)
-        return VBQ_ERR_BATCH;
-    int chunk = 2;
-    for (int i = 0; i < n; i++) {
-        if (!items[i].P)
-            return VBQ_ERR_INVALID_ARG;
-        VBQ_TRY(check_plan(items[i].P));
-        chunk = std::min(chunk, (int)items[i].P->M);
-    }
-    // tokens beyond what one launch holds run as further launches over the
-    // same plans; each token's arithmetic is the same in every launch shape
-    for (int t0 = 0; t0 < M; t0 += chunk)
-        VBQ_TRY(planned_launch(items, n, std::min(chunk, M - t0), x, ldx, yt, t0, stream));
-    return VBQ_OK;
-}
+namespace {
 
-static vbq_status planned_launch(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
-                                 vbq_dtype yt, int tok0, hipStream_t stream)
+// Checks one launch for up to P->M tokens (the plans' LDS carve-up holds that
+// many) and fills its arguments; launches nothing.
+vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
+                        int tok0, PArgs *out, int *grid_out, uint32_t *lds_out)
 {
     if ((uintptr_t)x % 2)
         return VBQ_ERR_ALIGN;
@@ -939,7 +918,59 @@ static vbq_status planned_launch(const vbq_planned_item *items, int n, int M, co
     lds = p_layout(M, a.G, a.rows, a.tb, a.ps).total;
     if (lds > kLdsBudget)
         return VBQ_ERR_SHAPE;
-    return M == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream);
+    *out = a;
+    *grid_out = grid;
+    *lds_out = lds;
+    return VBQ_OK;
+}
+
+// Tokens beyond what one launch holds run as further launches over the same
+// plans; each token's arithmetic is the same in every launch shape.  Every
+// launch is checked before the first is enqueued; with stream == nullptr and
+// dry set, only the checks run.
+vbq_status planned_shared(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
+                          hipStream_t stream, bool dry)
+{
+    if (!items || n < 1 || n > VBQ_MAX_SHARED || !x)
+        return VBQ_ERR_INVALID_ARG;
+    if (yt != VBQ_F32 && yt != VBQ_F16)
+        return VBQ_ERR_INVALID_ARG;
+    if (M < 1 || M > 16)
+        return VBQ_ERR_BATCH;
+    int chunk = 2;
+    for (int i = 0; i < n; i++) {
+        if (!items[i].P)
+            return VBQ_ERR_INVALID_ARG;
+        VBQ_TRY(check_plan(items[i].P));
+        chunk = std::min(chunk, (int)items[i].P->M);
+    }
+    PArgs a;
+    int grid;
+    uint32_t lds;
+    for (int pass = 0; pass < (dry ? 1 : 2); pass++)
+        for (int t0 = 0; t0 < M; t0 += chunk) {
+            const int m = std::min(chunk, M - t0);
+            VBQ_TRY(planned_args(items, n, m, x, ldx, yt, t0, &a, &grid, &lds));
+            if (pass == 1)
+                VBQ_TRY(m == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream));
+        }
+    return VBQ_OK;
+}
+
+} // namespace
+
+vbq_status vbq::planned_shared_check(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
+                                     vbq_dtype yt)
+{
+    return planned_shared(items, n, M, x, ldx, yt, nullptr, true);
+}
+
+extern "C" {
+
+vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
+                                   vbq_dtype yt, hipStream_t stream)
+{
+    return planned_shared(items, n, M, x, ldx, yt, stream, false);
 }
 
 vbq_status vbq_gemv_planned(const vbq_plan *P, const void *plan, int M, const uint16_t *x, int ldx, void *y, int ldy,

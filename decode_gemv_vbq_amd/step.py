@@ -3,10 +3,10 @@
 Builds every weight matrix of a workload on the device (seeded draw -> vbq_pack,
 then, on the default path, vbq_prepare: the one-time plan each GEMV reads),
 keeps the packed blobs, plans, activations, outputs and workspaces, and runs
-the step as back-to-back launches on one stream -- eagerly, or replayed from a
-captured HIP graph (one host launch per step).  A stage is one GEMV, or the
-gate and up projections of a layer, which read the same activations and run as
-one shared launch.  The bench times exactly this object and the full-size
+the step through the step executor (one C call that enqueues the stage-ordered
+launches on one stream) -- eagerly, or replayed from a captured HIP graph (one
+host launch per step).  A stage is one GEMV, or the gate and up projections of
+a layer, which read the same activations and run as one shared launch.  The bench times exactly this object and the full-size
 parity test checks exactly this object.
 """
 from __future__ import annotations
@@ -44,6 +44,7 @@ class DecodeStep:
         self.mats: list[Matrix] = []
         self.graph = None
         self.graph16 = None
+        self._seq = None
         rng = np.random.default_rng(12345)
         self.stages: list[list[int]] = []
         for i, spec in enumerate(self.W.mats):
@@ -111,9 +112,22 @@ class DecodeStep:
         return tot
 
     # ------------------------------------------------------------- the step
+    def seq(self):
+        """The whole step as one executor call (vbq_gemv_planned_seq or
+        vbq_gemv_seq), built once."""
+        if self._seq is None:
+            items = []
+            for k, st in enumerate(self.stages):
+                for i in st:
+                    m = self.mats[i]
+                    meta, buf = (m.P, m.plan) if self.planned else (m.L, m.blob)
+                    items.append((meta, buf, m.x, m.y, k))
+            self._seq = v.Seq(items, planned=self.planned)
+        return self._seq
+
     def run(self):
         """Enqueue every GEMV of the step, in stage order, on the current stream."""
-        self.run_stages(self.stages)
+        self.seq().run()
 
     def run_stage(self, st):
         """Enqueue one stage: a single GEMV, or one launch for matrices sharing x."""

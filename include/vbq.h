@@ -284,6 +284,56 @@ vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items /* host */, int
                                    vbq_dtype yt, hipStream_t stream);
 
 /*
+ * Decode-step executors.  Autoregressive decode ("Variable Bit-width
+ * Quantization", mlsanity.com page, Abstract) runs a model's projections in a
+ * fixed order, each reading activations the previous stage produced.  A step
+ * is given as an array of GEMVs tagged with a stage number (non-decreasing
+ * along the array, at most 1024 items per stage) and enqueued on `stream` in
+ * that order, so the stream completes every stage before the next starts.
+ * Inside a stage, items that read the same x (same pointer and ldx) with the
+ * same K run as shared launches of up to VBQ_MAX_SHARED matrices; the others
+ * run one launch each.  Every item's y obeys the vbq_gemv error bound and
+ * equals what the single-matrix call gives for it.  Items are host memory read
+ * during the call; every pointer inside is device memory owned by the caller.
+ * Every item is checked before the first launch: a call that returns an error
+ * has launched nothing.  Errors: VBQ_ERR_INVALID_ARG (null pointers, n < 1,
+ * yt, stages decreasing or a stage over 1024 items), VBQ_ERR_BATCH (M outside
+ * [1, 16]), VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE, VBQ_ERR_ALIGN, VBQ_ERR_HIP.
+ * Capturing the call in a HIP graph captures the whole step.
+ */
+typedef struct vbq_seq_item {
+    const vbq_layout *L; /* host */
+    const void *blob;    /* device, 256-byte aligned, from vbq_pack */
+    const uint16_t *x;   /* device, fp16 [M][ldx] */
+    int ldx;             /* >= L->K */
+    void *y;             /* device, [M][ldy] in the call's yt */
+    int ldy;             /* >= L->N */
+    int stage;
+} vbq_seq_item;
+
+/* The step over packed blobs: each launch as vbq_gemv_batched / vbq_gemv_shared
+ * would make it.  ws / ws_bytes are passed to every GEMV (NULL / 0 is valid,
+ * see vbq_workspace_size). */
+vbq_status vbq_gemv_seq(const vbq_seq_item *items /* host */, int n, int M, vbq_dtype yt, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+typedef struct vbq_planned_seq_item {
+    const vbq_plan *P;  /* host */
+    const void *plan;   /* device, from vbq_prepare */
+    const uint16_t *x;  /* device, fp16 [M][ldx] */
+    int ldx;            /* >= P->K */
+    void *y;            /* device, [M][ldy] in the call's yt */
+    int ldy;            /* >= P->N */
+    int stage;
+} vbq_planned_seq_item;
+
+/* The step over prepared plans: each launch as vbq_gemv_planned_shared would
+ * make it.  Items of a stage share a launch when they read the same x and
+ * their plans agree on K, M, tile_bytes and psum. */
+vbq_status vbq_gemv_planned_seq(const vbq_planned_seq_item *items /* host */, int n, int M, vbq_dtype yt,
+                                hipStream_t stream);
+
+/*
  * Dense fp16 control at the same shapes: y[M][ldy] = W16 x with W16 fp16
  * [N][K] row-major (typically vbq_dequant(..., VBQ_F16)), fp32 accumulate.
  * K % 8 == 0, 1 <= M <= 16.

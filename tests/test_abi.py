@@ -148,3 +148,137 @@ def test_gemv_shared_argument_checks_fail_before_launch():
     bad = v.Layout.from_buffer_copy(bytes(L))
     bad.magic = 0
     assert call([L, bad]) == "VBQ_ERR_LAYOUT"
+
+
+def fake_plan(v, N=4, K=4096, M=1, tile_bytes=16384, psum=1024):
+    P = v.Plan()
+    P.magic = 0x4E4C5056
+    P.N, P.K, P.G, P.M = N, K, K // 64, M
+    P.wgs, P.rows = 1, N
+    P.tile_bytes, P.tiles, P.first_bytes, P.psum = tile_bytes, 1, 1024, psum
+    P.region_bytes = P.total_bytes = tile_bytes
+    return P
+
+
+def test_plan_argument_checks_fail_before_launch():
+    v = vbq()
+    lib = v.lib()
+    VP = ctypes.c_void_p
+    fake, null = VP(1 << 20), VP(0)
+    blob = oracle.pack(np.zeros((4, 4096), np.uint8), np.ones((4, 64), np.uint8), np.ones((4, 64), np.uint16))
+    L = v.layout_from_header(blob[:256].tobytes())
+    out = v.Plan()
+
+    def init(M=1, blob=fake, ws=fake, wsb=16, lay=L):
+        return v.STATUS[lib.vbq_plan_init(ctypes.byref(lay), blob, M, 0, ctypes.byref(out), ws, wsb, null)]
+
+    assert init(blob=null) == "VBQ_ERR_INVALID_ARG"
+    assert init(M=0) == "VBQ_ERR_BATCH"
+    assert init(M=3) == "VBQ_ERR_BATCH"
+    assert init(ws=null) == "VBQ_ERR_WORKSPACE"
+    assert init(wsb=8) == "VBQ_ERR_WORKSPACE"
+    assert init(blob=VP((1 << 20) + 64)) == "VBQ_ERR_ALIGN"
+    big = oracle.pack(np.zeros((1, 64 * 513), np.uint8), np.ones((1, 513), np.uint8), np.ones((1, 513), np.uint16))
+    Lbig = v.layout_from_header(big[:256].tobytes())
+    assert init(lay=Lbig) == "VBQ_ERR_SHAPE"  # K > 32768
+    bad = v.Layout.from_buffer_copy(bytes(L))
+    bad.version = 7
+    assert init(lay=bad) == "VBQ_ERR_LAYOUT"
+
+    P = fake_plan(v)
+
+    def gemv(Pl=P, plan=fake, M=1, x=fake, ldx=4096, y=fake, ldy=4, yt=1):
+        return v.STATUS[lib.vbq_gemv_planned(ctypes.byref(Pl), plan, M, x, ldx, y, ldy, yt, null)]
+
+    assert gemv(M=0) == "VBQ_ERR_BATCH"
+    assert gemv(M=17) == "VBQ_ERR_BATCH"
+    assert gemv(plan=null) == "VBQ_ERR_INVALID_ARG"
+    assert gemv(x=null) == "VBQ_ERR_INVALID_ARG"
+    assert gemv(yt=5) == "VBQ_ERR_INVALID_ARG"
+    assert gemv(ldx=4032) == "VBQ_ERR_SHAPE"
+    assert gemv(ldy=3) == "VBQ_ERR_SHAPE"
+    assert gemv(plan=VP((1 << 20) + 128)) == "VBQ_ERR_ALIGN"
+    assert gemv(y=VP((1 << 20) + 2), yt=0) == "VBQ_ERR_ALIGN"  # f32 outputs need 4-byte alignment
+    for field, val in [("magic", 0), ("K", 4032), ("tile_bytes", 5000), ("M", 3), ("first_bytes", 32768),
+                       ("region_bytes", 1024), ("rows", 1)]:
+        bad = fake_plan(v)
+        setattr(bad, field, val)
+        assert gemv(Pl=bad) == "VBQ_ERR_LAYOUT", field
+    # a plan whose LDS carve-up does not fit one workgroup
+    assert gemv(Pl=fake_plan(v, tile_bytes=65536, psum=16384)) == "VBQ_ERR_SHAPE"
+
+    def shared(plans, n=None, x=fake):
+        items = (v.PlannedItem * max(1, len(plans)))()
+        for k, p in enumerate(plans):
+            items[k] = v.PlannedItem(ctypes.addressof(p), fake, fake, 4)
+        return v.STATUS[lib.vbq_gemv_planned_shared(items, len(plans) if n is None else n, 1, x, 4096, 1, null)]
+
+    assert shared([P], n=0) == "VBQ_ERR_INVALID_ARG"
+    assert shared([P] * 5) == "VBQ_ERR_INVALID_ARG"
+    assert shared([P, fake_plan(v, K=2048)]) == "VBQ_ERR_SHAPE"
+    assert shared([P, fake_plan(v, tile_bytes=32768)]) == "VBQ_ERR_SHAPE"
+    assert shared([P, fake_plan(v, psum=2048)]) == "VBQ_ERR_SHAPE"
+    # vbq_prepare: the plan must describe this layout
+    assert v.STATUS[lib.vbq_prepare(ctypes.byref(fake_plan(v, N=8)), ctypes.byref(L), fake, fake, null)] == \
+        "VBQ_ERR_SHAPE"
+    assert v.STATUS[lib.vbq_prepare(ctypes.byref(P), ctypes.byref(L), fake, VP((1 << 20) + 16), null)] == \
+        "VBQ_ERR_ALIGN"
+
+
+def test_seq_argument_checks_fail_before_launch():
+    """Every item of a step is checked before the first launch: a bad item
+    anywhere in the array returns its own error, never the HIP error that a
+    launch of an earlier, valid item would give on a host with no GPU."""
+    v = vbq()
+    lib = v.lib()
+    VP = ctypes.c_void_p
+    fake, null = 1 << 20, VP(0)
+    blob = oracle.pack(np.zeros((4, 4096), np.uint8), np.ones((4, 64), np.uint8), np.ones((4, 64), np.uint16))
+    L = v.layout_from_header(blob[:256].tobytes())
+    bad = v.Layout.from_buffer_copy(bytes(L))
+    bad.magic = 0
+
+    def seq(specs, M=1, yt=1, n=None):
+        items = (v.SeqItem * max(1, len(specs)))()
+        for k, s in enumerate(specs):
+            d = dict(L=L, blob=fake, x=fake, ldx=4096, y=fake, ldy=4, stage=k)
+            d.update(s)
+            items[k] = v.SeqItem(ctypes.addressof(d["L"]), d["blob"], d["x"], d["ldx"], d["y"], d["ldy"], d["stage"])
+        return v.STATUS[lib.vbq_gemv_seq(items, len(specs) if n is None else n, M, yt, null, 0, null)]
+
+    ok = {}
+    assert seq([ok], n=0) == "VBQ_ERR_INVALID_ARG"
+    assert seq([ok], M=0) == "VBQ_ERR_BATCH"
+    assert seq([ok], M=17) == "VBQ_ERR_BATCH"
+    assert seq([ok], yt=4) == "VBQ_ERR_INVALID_ARG"
+    assert seq([ok, ok, dict(blob=0)]) == "VBQ_ERR_INVALID_ARG"
+    assert seq([ok, dict(L=bad)]) == "VBQ_ERR_LAYOUT"
+    assert seq([ok, dict(ldx=64)]) == "VBQ_ERR_SHAPE"
+    assert seq([ok, dict(ldy=1)]) == "VBQ_ERR_SHAPE"
+    assert seq([ok, dict(x=fake + 1)]) == "VBQ_ERR_ALIGN"
+    assert seq([ok, dict(blob=fake + 128)]) == "VBQ_ERR_ALIGN"
+    assert seq([dict(stage=3), dict(stage=2)]) == "VBQ_ERR_INVALID_ARG"  # stages must not decrease
+    assert seq([dict(stage=0)] * 1025) == "VBQ_ERR_INVALID_ARG"  # at most 1024 items per stage
+
+    P = fake_plan(v)
+    P2 = fake_plan(v, tile_bytes=65536, psum=16384)  # checks pass one by one; its LDS does not fit
+    Pbad = fake_plan(v)
+    Pbad.magic = 1
+
+    def pseq(specs, M=1, yt=1):
+        items = (v.PlannedSeqItem * len(specs))()
+        for k, s in enumerate(specs):
+            d = dict(P=P, plan=fake, x=fake, ldx=4096, y=fake, ldy=4, stage=k)
+            d.update(s)
+            items[k] = v.PlannedSeqItem(ctypes.addressof(d["P"]), d["plan"], d["x"], d["ldx"], d["y"], d["ldy"],
+                                        d["stage"])
+        return v.STATUS[lib.vbq_gemv_planned_seq(items, len(specs), M, yt, null)]
+
+    assert pseq([ok], M=0) == "VBQ_ERR_BATCH"
+    assert pseq([ok, dict(plan=0)]) == "VBQ_ERR_INVALID_ARG"
+    assert pseq([ok, dict(P=Pbad)]) == "VBQ_ERR_LAYOUT"
+    assert pseq([ok, dict(ldx=4000)]) == "VBQ_ERR_SHAPE"
+    assert pseq([ok, dict(ldy=2)]) == "VBQ_ERR_SHAPE"
+    assert pseq([ok, dict(plan=fake + 8)]) == "VBQ_ERR_ALIGN"
+    assert pseq([ok, dict(P=P2)]) == "VBQ_ERR_SHAPE"
+    assert pseq([dict(stage=1), dict(stage=0)]) == "VBQ_ERR_INVALID_ARG"
