@@ -57,6 +57,12 @@ bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x
 vbq_status planned_shared_check(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
                                 vbq_dtype yt);
 
+// vbq_gemv_planned_shared whose last launch also fetches, into each
+// workgroup's free ring slot, the first tile that workgroup's counterpart in
+// the following launch (the items `next`, checked plans; null: none) reads.
+vbq_status planned_shared_launch(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
+                                 vbq_dtype yt, hipStream_t stream, const vbq_planned_item *next, int nnext);
+
 } // namespace vbq
 
 #define VBQ_TRY(expr)                                                                                                 \

@@ -316,6 +316,26 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+
+// 64 bytes of the kernel-argument segment at byte offset `off` (a multiple of
+// 64) in one scalar load; the wait is inside the asm block, so no load is
+// left in flight when it ends.
+__device__ __forceinline__ u32x16 kernarg_line(uint32_t off)
+{
+    u32x16 r;
+    asm volatile("s_load_dwordx16 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(r)
+                 : "s"(__builtin_amdgcn_kernarg_segment_ptr()), "s"(off)
+                 : "memory");
+    return r;
+}
+
+__device__ __forceinline__ const void *u64_ptr(uint32_t lo, uint32_t hi)
+{
+    return (const void *)(((uint64_t)hi << 32) | lo);
+}
+
 // Copy `bytes` from global memory to LDS in 1 KiB chunks (16 bytes per lane,
 // the tail masked per 16 bytes): this wave issues chunks first, first + step, ...
 __device__ __forceinline__ void copy_chunks(const uint8_t *src, uint32_t dst, uint32_t bytes, int first, int step)
@@ -328,18 +348,43 @@ __device__ __forceinline__ void copy_chunks(const uint8_t *src, uint32_t dst, ui
     }
 }
 
-struct PMat {
-    const uint8_t *plan;
-    void *y;
-    uint64_t region;
-    int N, ldy, rows, wg0;
+// Kernel arguments.  The argument segment is read from memory at every
+// launch and is not kept in the caches between launches, so each round of
+// dependent argument loads costs a full memory round trip before a workgroup
+// can start.  A workgroup therefore finds everything it needs in ONE 64-byte
+// record, picked by blockIdx.y (the matrix of a shared launch), which it reads
+// with a single scalar load.  Launch-wide fields are repeated in every record.
+struct PRec {
+    const uint8_t *plan;  // this matrix's plan
+    void *y;              // its outputs (this launch's first token)
+    const uint16_t *x;    // activations (this launch's first token)
+    uint32_t region;      // bytes per row block of the plan
+    int32_t N, ldy, rows; // rows per block of this matrix
+    int32_t ldx;
+    uint32_t first;       // bytes of tile 0 to copy (launch-wide maximum)
+    int32_t ps;           // partial sums per token per ring slot (launch-wide)
+    int32_t rows_max;     // output staging stride in LDS (launch-wide)
+    uint32_t g_yt_tb;     // G | yt << 16 | (tile stride / 1 KiB) << 24
+    int32_t wgs;          // row blocks of this matrix (workgroups with blockIdx.x < wgs work)
 };
+static_assert(sizeof(PRec) == 64, "one record is one 64-byte line");
+
+// The launch that follows on the stream: where each of its workgroups starts
+// reading.  Plans do not depend on the activations, so a workgroup of this
+// launch fetches, during its last tile, the first tile of the workgroup with
+// the same linear index there, which then finds it in the caches instead of
+// waiting for HBM.  Read once, late, by the copying waves.
+struct PWarm {
+    const uint8_t *plan[kMaxMats]; // null: no such matrix
+    uint32_t region[kMaxMats];     // bytes per row block
+    uint16_t first16[kMaxMats];    // bytes of tile 0 / 16
+    uint16_t wgs[kMaxMats];        // row blocks
+};
+static_assert(sizeof(PWarm) == 64, "the warming line is one 64-byte line");
 
 struct PArgs {
-    const uint16_t *x;
-    int G, ldx, yt, tb, first, ps, nmat;
-    int rows; // output staging stride in LDS: the most rows per block of any matrix
-    PMat mats[kMaxMats];
+    PRec rec[kMaxMats];
+    PWarm warm;
 };
 
 struct PLayout {
@@ -610,37 +655,42 @@ __device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps,
 }
 
 template <int MT>
-__global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
+__global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_line */)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // this workgroup's matrix: the last one whose first workgroup is <= blockIdx.x
-    PMat pm = args.mats[0];
-#pragma unroll
-    for (int i = 1; i < kMaxMats; i++)
-        if (i < args.nmat && (int)blockIdx.x >= args.mats[i].wg0)
-            pm = args.mats[i];
-    const int blk = (int)blockIdx.x - pm.wg0;
-    const int n0 = blk * pm.rows;
-    if (n0 >= pm.N)
-        return;
-    const int R = min(pm.rows, pm.N - n0);
-    const int G = args.G, ps = args.ps, rows = args.rows;
-    const uint32_t tb = (uint32_t)args.tb;
-    const PLayout L = p_layout(MT, G, rows, args.tb, ps);
+    // this workgroup's record (matrix blockIdx.y of the launch), in one load
+    const u32x16 a = kernarg_line((uint32_t)blockIdx.y * (uint32_t)sizeof(PRec));
+    if ((int)blockIdx.x >= (int)a[15])
+        return; // the launch spans the largest matrix; a smaller one has fewer blocks
+    const uint8_t *plan = (const uint8_t *)u64_ptr(a[0], a[1]);
+    void *const yptr = (void *)u64_ptr(a[2], a[3]);
+    const uint16_t *xptr = (const uint16_t *)u64_ptr(a[4], a[5]);
+    const uint32_t region_bytes = a[6];
+    const int Nm = (int)a[7], ldy = (int)a[8], mrows = (int)a[9], ldx = (int)a[10];
+    const uint32_t first = a[11];
+    const int ps = (int)a[12], rows = (int)a[13];
+    const int G = (int)(a[14] & 0xffffu), yt = (int)((a[14] >> 16) & 0xffu);
+    const uint32_t tb = (a[14] >> 24) * 1024u;
+    const int blk = (int)blockIdx.x;
+    const int n0 = blk * mrows;
+    const int R = min(mrows, Nm - n0);
+    const PLayout L = p_layout(MT, G, rows, (int)tb, ps);
     uint32_t *xrec = reinterpret_cast<uint32_t *>(smem + L.x);
     float *psum = reinterpret_cast<float *>(smem + L.psum);
     float *ybuf = reinterpret_cast<float *>(smem + L.ybuf);
-    const uint8_t *region = pm.plan + (uint64_t)blk * pm.region;
+    const uint8_t *region = plan + (uint64_t)blk * region_bytes;
     const uint32_t ring = lds_addr(smem + L.ring);
-    const YOut yo{pm.y, pm.ldy, n0, args.yt};
+    const YOut yo{yptr, ldy, n0, yt};
+    const uint8_t *warm = nullptr; // set by the copying waves before the last tile's phase
+    uint32_t warm_bytes = 0;
 
     // ---- tile 0 (copied by the lower half of the workgroup) and the
     // activations (staged by the upper half), in flight together; each half
     // waits only for its own loads
     uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + L.ctr);
     if (tid < kXT) {
-        copy_chunks(region, ring, (uint32_t)args.first, wave, kXT / 64);
+        copy_chunks(region, ring, first, wave, kXT / 64);
         for (int i = tid; i < MT * R; i += kXT)
             ybuf[(i / R) * rows + i % R] = 0.f;
         if (tid == 0)
@@ -648,7 +698,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
         wait_vm0();
     } else {
         XRegs<MT> xs;
-        x_load<MT>(args.x, args.ldx, G, xs);
+        x_load<MT>(xptr, ldx, G, xs);
         x_store<MT>(G, xs, xrec);
     }
     __syncthreads();
@@ -666,9 +716,30 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
         if (wave < kCopyWaves) {
             if (tid == 0)
                 cnt[slot ^ 1] = 0u; // pass counter of tile k+1 (its last users left tile k-1's phase)
-            if (h.next)
-                copy_chunks(region + (uint64_t)(k + 1) * tb, ring + (uint32_t)(slot ^ 1) * tb, h.next, wave,
-                            kCopyWaves);
+            if (!h.next) {
+                // last tile: the next launch's workgroup with this linear
+                // index, whose first tile goes into the free slot (awaited at
+                // the very end)
+                const u32x16 w = kernarg_line((uint32_t)(kMaxMats * sizeof(PRec)));
+                uint32_t gx = 0;
+#pragma unroll
+                for (int i = 0; i < kMaxMats; i++)
+                    gx = max(gx, w[14 + i / 2] >> (16 * (i & 1)) & 0xffffu);
+                const uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
+                const uint32_t bx = gx ? lin % gx : 0u, by = gx ? lin / gx : (uint32_t)kMaxMats;
+#pragma unroll
+                for (int i = 0; i < kMaxMats; i++) {
+                    const uint32_t wgs_i = w[14 + i / 2] >> (16 * (i & 1)) & 0xffffu;
+                    const uint32_t first_i = (w[12 + i / 2] >> (16 * (i & 1)) & 0xffffu) * 16u;
+                    const uint8_t *p_i = (const uint8_t *)u64_ptr(w[2 * i], w[2 * i + 1]);
+                    const bool mine = by == (uint32_t)i && bx < wgs_i && p_i != nullptr;
+                    warm = mine ? p_i + (uint64_t)bx * w[8 + i] : warm;
+                    warm_bytes = mine ? min(first_i, tb) : warm_bytes;
+                }
+            }
+            // tile k+1, or after the last tile the warming copy
+            copy_chunks(h.next ? region + (uint64_t)(k + 1) * tb : warm, ring + (uint32_t)(slot ^ 1) * tb,
+                        h.next ? h.next : warm_bytes, wave, kCopyWaves);
         } else {
             const int np0 = (int)((h.cnt[0] + 63) >> 6), np1 = (int)((h.cnt[1] + 63) >> 6);
             const int np2 = (int)((h.cnt[2] + 63) >> 6), np3 = (int)((h.cnt[3] + 63) >> 6);
@@ -698,7 +769,8 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
             for (int t = (wave + kW - kCopyWaves) % kW; t < nsum; t += kW) // copying waves take the last shares
                 rowsum_item<MT>(t, prev, G, ps, rows, psum + (slot ^ 1) * (MT * ps), ybuf, yo);
         }
-        wait_vm0(); // copy waves: the copy of tile k+1
+        if (h.next)
+            wait_vm0(); // copy waves: the copy of tile k+1
         __syncthreads();
         prev = h;
         if (!h.next)
@@ -707,9 +779,13 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs args)
     // ---- rows of the last tile (partials in psum slot k & 1); every row ends here
     {
         const int nsum = sum_items((int)prev.nr, G);
-        for (int t = wave; t < nsum; t += kW)
+        for (int t = (wave + kW - kCopyWaves) % kW; t < nsum; t += kW) // copying waves take the last shares
             rowsum_item<MT>(t, prev, G, ps, rows, psum + (k & 1) * (MT * ps), ybuf, yo);
     }
+    // the warming copy lands in LDS: it must finish before the workgroup's LDS
+    // is released (the other waves leave without waiting for their stores)
+    if (wave < kCopyWaves && warm_bytes)
+        wait_vm0();
 }
 
 // ---------------------------------------------------------------------------
@@ -738,7 +814,8 @@ vbq_status check_plan(const vbq_plan *P)
     if (!P || P->magic != VBQ_PLAN_MAGIC)
         return VBQ_ERR_LAYOUT;
     if (P->N < 1 || P->G < 1 || P->G > kMaxG || P->K != 64 * P->G || P->M < 1 || P->M > 2 || P->wgs < 1 ||
-        P->rows < 1 || (int64_t)P->wgs * P->rows < P->N || P->tile_bytes < 4096 || P->tile_bytes > kMaxTb ||
+        P->rows < 1 || (int64_t)P->wgs * P->rows < P->N || (int64_t)(P->wgs - 1) * P->rows >= P->N ||
+        P->wgs > 65535 || P->tiles > kMaxTiles || P->tile_bytes < 4096 || P->tile_bytes > kMaxTb ||
         P->tile_bytes % 1024 || P->tiles < 1 || P->first_bytes < kHdr || P->first_bytes > P->tile_bytes ||
         P->region_bytes != (uint64_t)P->tiles * (uint64_t)P->tile_bytes)
         return VBQ_ERR_LAYOUT;
@@ -764,7 +841,7 @@ PrepArgs prep_args(const vbq_layout *L, const void *blob, const vbq_plan *P)
 }
 
 template <int MT>
-vbq_status launch_plan(const PArgs &a, int grid, uint32_t lds, hipStream_t stream)
+vbq_status launch_plan(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
     static bool configured = false;
     if (!configured) {
@@ -873,17 +950,13 @@ namespace {
 // Checks one launch for up to P->M tokens (the plans' LDS carve-up holds that
 // many) and fills its arguments; launches nothing.
 vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
-                        int tok0, PArgs *out, int *grid_out, uint32_t *lds_out)
+                        int tok0, PArgs *out, dim3 *grid_out, uint32_t *lds_out)
 {
     if ((uintptr_t)x % 2)
         return VBQ_ERR_ALIGN;
     PArgs a{};
-    a.x = x + (uint64_t)tok0 * ldx;
-    a.ldx = ldx;
-    a.yt = (int)yt;
-    a.nmat = n;
-    int grid = 0;
-    uint32_t lds = 0;
+    int gx = 0, rows_max = 0;
+    uint32_t first = 0;
     for (int i = 0; i < n; i++) {
         const vbq_planned_item &it = items[i];
         if (!it.P || !it.plan || !it.y)
@@ -899,29 +972,48 @@ vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint1
             return VBQ_ERR_SHAPE; // one launch needs one LDS carve-up
         if ((uintptr_t)it.plan % 256 || (uintptr_t)it.y % (yt == VBQ_F32 ? 4 : 2))
             return VBQ_ERR_ALIGN;
-        PMat &m = a.mats[i];
-        m.plan = (const uint8_t *)it.plan;
-        m.y = (uint8_t *)it.y + (uint64_t)tok0 * it.ldy * (yt == VBQ_F32 ? 4 : 2);
-        m.region = P->region_bytes;
-        m.N = P->N;
-        m.ldy = it.ldy;
-        m.rows = P->rows;
-        m.wg0 = grid;
-        grid += P->wgs;
-        a.first = std::max(a.first, P->first_bytes);
-        a.rows = std::max(a.rows, P->rows); // output staging stride: the plan with the most rows fits
+        PRec &r = a.rec[i];
+        r.plan = (const uint8_t *)it.plan;
+        r.y = (uint8_t *)it.y + (uint64_t)tok0 * it.ldy * (yt == VBQ_F32 ? 4 : 2);
+        r.x = x + (uint64_t)tok0 * ldx;
+        r.region = (uint32_t)P->region_bytes;
+        r.N = P->N;
+        r.ldy = it.ldy;
+        r.rows = P->rows;
+        r.ldx = ldx;
+        r.wgs = P->wgs;
+        gx = std::max(gx, P->wgs);
+        first = std::max(first, (uint32_t)P->first_bytes);
+        rows_max = std::max(rows_max, P->rows); // output staging stride: the plan with the most rows fits
     }
     const vbq_plan *P0 = items[0].P;
-    a.G = P0->G;
-    a.tb = P0->tile_bytes;
-    a.ps = P0->psum;
-    lds = p_layout(M, a.G, a.rows, a.tb, a.ps).total;
+    const uint32_t lds = p_layout(M, P0->G, rows_max, P0->tile_bytes, P0->psum).total;
     if (lds > kLdsBudget)
         return VBQ_ERR_SHAPE;
+    for (int i = 0; i < n; i++) {
+        PRec &r = a.rec[i];
+        r.first = first;
+        r.ps = P0->psum;
+        r.rows_max = rows_max;
+        r.g_yt_tb = (uint32_t)P0->G | (uint32_t)yt << 16 | (uint32_t)(P0->tile_bytes / 1024) << 24;
+    }
     *out = a;
-    *grid_out = grid;
+    *grid_out = dim3((unsigned)gx, (unsigned)n);
     *lds_out = lds;
     return VBQ_OK;
+}
+
+// Fills a.warm from the items of the launch that follows (none: no warming).
+void set_next(PArgs &a, const vbq_planned_item *next, int nnext)
+{
+    a.warm = PWarm{};
+    for (int i = 0; next && i < nnext && i < kMaxMats; i++) {
+        const vbq_plan *P = next[i].P;
+        a.warm.plan[i] = (const uint8_t *)next[i].plan;
+        a.warm.region[i] = (uint32_t)P->region_bytes;
+        a.warm.first16[i] = (uint16_t)((P->first_bytes + 15) / 16);
+        a.warm.wgs[i] = (uint16_t)P->wgs;
+    }
 }
 
 // Tokens beyond what one launch holds run as further launches over the same
@@ -929,7 +1021,7 @@ vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint1
 // launch is checked before the first is enqueued; with stream == nullptr and
 // dry set, only the checks run.
 vbq_status planned_shared(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
-                          hipStream_t stream, bool dry)
+                          hipStream_t stream, bool dry, const vbq_planned_item *next = nullptr, int nnext = 0)
 {
     if (!items || n < 1 || n > VBQ_MAX_SHARED || !x)
         return VBQ_ERR_INVALID_ARG;
@@ -945,12 +1037,18 @@ vbq_status planned_shared(const vbq_planned_item *items, int n, int M, const uin
         chunk = std::min(chunk, (int)items[i].P->M);
     }
     PArgs a;
-    int grid;
+    dim3 grid;
     uint32_t lds;
     for (int pass = 0; pass < (dry ? 1 : 2); pass++)
         for (int t0 = 0; t0 < M; t0 += chunk) {
             const int m = std::min(chunk, M - t0);
             VBQ_TRY(planned_args(items, n, m, x, ldx, yt, t0, &a, &grid, &lds));
+            // a further token chunk re-reads the same plans; after the last
+            // chunk comes the caller's next launch
+            if (t0 + chunk < M)
+                set_next(a, items, n);
+            else
+                set_next(a, next, nnext);
             if (pass == 1)
                 VBQ_TRY(m == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream));
         }
@@ -963,6 +1061,12 @@ vbq_status vbq::planned_shared_check(const vbq_planned_item *items, int n, int M
                                      vbq_dtype yt)
 {
     return planned_shared(items, n, M, x, ldx, yt, nullptr, true);
+}
+
+vbq_status vbq::planned_shared_launch(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
+                                      vbq_dtype yt, hipStream_t stream, const vbq_planned_item *next, int nnext)
+{
+    return planned_shared(items, n, M, x, ldx, yt, stream, false, next, nnext);
 }
 
 extern "C" {

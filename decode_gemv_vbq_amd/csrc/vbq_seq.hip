@@ -14,6 +14,8 @@
 // cooperative kernel costs about 5.5 us, against about 1.9 us per kernel node
 // of a replayed HIP graph, so stages stay separate launches and a caller that
 // wants the launch floor captures the step in a graph.
+#include <vector>
+
 #include "vbq_host.h"
 
 using namespace vbq;
@@ -128,23 +130,34 @@ vbq_status vbq_gemv_planned_seq(const vbq_planned_seq_item *items, int n, int M,
         return a.x == b.x && a.ldx == b.ldx && a.P->K == b.P->K && a.P->M == b.P->M &&
                a.P->tile_bytes == b.P->tile_bytes && a.P->psum == b.P->psum;
     };
-    auto group_items = [&](const int *idx, int k, vbq_planned_item *sh) {
+    // the launches in order, every one checked before the first is enqueued
+    struct Launch {
+        vbq_planned_item it[VBQ_MAX_SHARED];
+        int n;
+        const uint16_t *x;
+        int ldx;
+    };
+    std::vector<Launch> launches;
+    VBQ_TRY(for_each_group(items, n, compatible, [&](const int *idx, int k) {
+        Launch l;
+        l.n = k;
+        l.x = items[idx[0]].x;
+        l.ldx = items[idx[0]].ldx;
         for (int j = 0; j < k; j++) {
             const vbq_planned_seq_item &b = items[idx[j]];
-            sh[j] = vbq_planned_item{b.P, b.plan, b.y, b.ldy};
+            l.it[j] = vbq_planned_item{b.P, b.plan, b.y, b.ldy};
         }
-    };
-    // every launch checked first, then enqueued
-    VBQ_TRY(for_each_group(items, n, compatible, [&](const int *idx, int k) {
-        vbq_planned_item sh[VBQ_MAX_SHARED];
-        group_items(idx, k, sh);
-        return planned_shared_check(sh, k, M, items[idx[0]].x, items[idx[0]].ldx, yt);
+        launches.push_back(l);
+        return planned_shared_check(l.it, k, M, l.x, l.ldx, yt);
     }));
-    return for_each_group(items, n, compatible, [&](const int *idx, int k) {
-        vbq_planned_item sh[VBQ_MAX_SHARED];
-        group_items(idx, k, sh);
-        return vbq_gemv_planned_shared(sh, k, M, items[idx[0]].x, items[idx[0]].ldx, yt, stream);
-    });
+    // each launch warms the first tiles of the one after it; the last warms
+    // the first, which a decoder runs again at its next step
+    const int nl = (int)launches.size();
+    for (int i = 0; i < nl; i++) {
+        const Launch &l = launches[i], &nx = launches[(i + 1) % nl];
+        VBQ_TRY(planned_shared_launch(l.it, l.n, M, l.x, l.ldx, yt, stream, nx.it, nx.n));
+    }
+    return VBQ_OK;
 }
 
 } // extern "C"
