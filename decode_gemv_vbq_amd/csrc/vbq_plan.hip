@@ -455,6 +455,34 @@ __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<
     }
 }
 
+// v from another lane of the same DPP row (ctrl: a DPP control code).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum of v over each aligned group of L lanes (L = 8, 16, 32, 64), the same
+// value in every lane of the group, in a fixed order: pairs and quads (DPP
+// quad permutations), then the two quads of each 8 lanes (row_half_mirror:
+// once every lane of a quad holds the quad's sum, the mirrored lane holds the
+// other quad's), then the two halves of each 16-lane row (row_mirror), then
+// across rows.  Lane moves inside a row cost no LDS traffic.
+template <int L>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += dpp_f<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x141>(v); // row_half_mirror
+    if (L >= 16)
+        v += dpp_f<0x140>(v); // row_mirror
+    if (L >= 32)
+        v += __shfl_xor(v, 16, 64);
+    if (L >= 64)
+        v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
 template <int MT>
 __device__ __forceinline__ void x_store(int G, const XRegs<MT> &xs, uint32_t *xrec)
 {
@@ -483,13 +511,11 @@ __device__ __forceinline__ void x_store(int G, const XRegs<MT> &xs, uint32_t *xr
             c2 = fmaf((float)(1 << (10 - pair_pos<2>(t & 7))), sp, c2);
             c4 = fmaf((float)(1 << (10 - pair_pos<4>(t & 3))), sp, c4);
         }
-#pragma unroll
-        for (int d = 1; d < 8; d <<= 1) { // fixed-order tree over the 8 quarters
-            X += __shfl_xor(X, d, 8);
-            c1 += __shfl_xor(c1, d, 8);
-            c2 += __shfl_xor(c2, d, 8);
-            c4 += __shfl_xor(c4, d, 8);
-        }
+        // fixed-order tree over the 8 quarters of the group
+        X = group_sum<8>(X);
+        c1 = group_sum<8>(c1);
+        c2 = group_sum<8>(c2);
+        c4 = group_sum<8>(c4);
         if (q == 0)
             *reinterpret_cast<U4 *>(xr + 32) = U4{{__float_as_uint(fmaf(0.5f, X, c1)),
                                                     __float_as_uint(fmaf(1.5f, X, c2)),
@@ -592,7 +618,7 @@ struct YOut {
 // Row-sum item t of a tile: rows (64 / L) t .. of the tile, L = sum_lanes(G)
 // lanes per row.  The partials of row j sit at column * nr + j for the tile's
 // columns of that row; lane q sums columns q, q + L, ... (four interleaved
-// chains), the L lanes combine in a fixed butterfly, and the row's sum from
+// chains), the L lanes combine in a fixed order (group_sum), and the row's sum from
 // earlier tiles (ybuf, tiles in order) is added.  A row that ends in this
 // tile is written to y; only a row that continues into the next tile stays in
 // ybuf.
@@ -623,9 +649,7 @@ __device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int p
                 a0 += p[g * nr];
             v = (a0 + a1) + (a2 + a3);
         }
-#pragma unroll
-        for (int d = L >> 1; d > 0; d >>= 1)
-            v += __shfl_xor(v, d, L);
+        v = group_sum<L>(v);
         if (q == 0 && j < nr) {
             const int r = (int)h.ra + j;
             const float tot = ybuf[m * rows + r] + v;
