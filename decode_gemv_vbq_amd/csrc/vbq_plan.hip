@@ -417,7 +417,12 @@ __host__ __device__ inline PLayout p_layout(int MT, int G, int rows, int tb, int
 // Item = (token, group, quarter q): pairs 4q..4q+3; the 8 items of a group are
 // 8 adjacent lanes.  Loads and stores are separate so the loads go out with
 // the first tile's copy.
-constexpr int kXT = kT / 2; // threads that stage x (the upper half; the lower half copies tile 0)
+// Prologue split: the first kCT threads copy tile 0 (a few waves issue the
+// whole LDS-DMA copy), the other kXT threads stage x, which is the longer of
+// the two (every workgroup reads the same activations, and each quarter-group
+// item costs about 50 VALU instructions).
+constexpr int kCT = 4 * 64;
+constexpr int kXT = kT - kCT;
 
 template <int MT>
 struct XRegs {
@@ -428,7 +433,7 @@ struct XRegs {
 template <int MT>
 __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<MT> &xs)
 {
-    const int tid = threadIdx.x - kXT;
+    const int tid = threadIdx.x - kCT;
     const int items = MT * G * 8;
     const bool vec = (ldx % 4) == 0 && ((uintptr_t)x % 8) == 0;
 #pragma unroll
@@ -486,7 +491,7 @@ __device__ __forceinline__ float group_sum(float v)
 template <int MT>
 __device__ __forceinline__ void x_store(int G, const XRegs<MT> &xs, uint32_t *xrec)
 {
-    const int tid = threadIdx.x - kXT;
+    const int tid = threadIdx.x - kCT;
     const int items = MT * G * 8;
 #pragma unroll
     for (int k = 0; k < XRegs<MT>::kPer; k++) {
@@ -709,13 +714,13 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     const uint8_t *warm = nullptr; // set by the copying waves before the last tile's phase
     uint32_t warm_bytes = 0;
 
-    // ---- tile 0 (copied by the lower half of the workgroup) and the
-    // activations (staged by the upper half), in flight together; each half
-    // waits only for its own loads
+    // ---- tile 0 (copied by the first kCT threads) and the activations
+    // (staged by the others), in flight together; each side waits only for
+    // its own loads
     uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + L.ctr);
-    if (tid < kXT) {
-        copy_chunks(region, ring, first, wave, kXT / 64);
-        for (int i = tid; i < MT * R; i += kXT)
+    if (tid < kCT) {
+        copy_chunks(region, ring, first, wave, kCT / 64);
+        for (int i = tid; i < MT * R; i += kCT)
             ybuf[(i / R) * rows + i % R] = 0.f;
         if (tid == 0)
             cnt[0] = 0u;
