@@ -47,7 +47,7 @@ namespace {
 constexpr int kT = 1024; // threads per workgroup (prepare and GEMV kernels)
 constexpr int kW = kT / 64;
 constexpr int kHdr = 64;    // tile header bytes
-constexpr int kXRec = 36;   // dwords per x record: 32 pairs (x_p, x_{p+32}) + 4 constants
+constexpr int kXRec = 36;   // dwords of x per group: 32 pairs (x_p, x_{p+32}) + 4 constants
 constexpr int kMaxG = 512;  // groups per row the plans support (K <= 32768)
 constexpr int kMaxTiles = 1024; // tiles per row block
 constexpr int kMaxMats = VBQ_MAX_SHARED;
@@ -412,7 +412,9 @@ __host__ __device__ inline PLayout p_layout(int MT, int G, int rows, int tb, int
     return l;
 }
 
-// x records: fp16 pairs (x_p, x_{p+32}), then per width the correction
+// x records (kXRec dwords per group; the 36-dword stride spreads the records
+// of different columns over the LDS banks): the fp16 pairs (x_p, x_{p+32}),
+// then the negated corrections -C_b for the widths 1, 2, 4, 8, where
 // C_b = sum_p 2^(10-pos_b(p)) (x_p + x_{p+32}) + (2^b-1)/2 sum_j x_j.
 // Item = (token, group, quarter q): pairs 4q..4q+3; the 8 items of a group are
 // 8 adjacent lanes.  Loads and stores are separate so the loads go out with
@@ -522,10 +524,9 @@ __device__ __forceinline__ void x_store(int G, const XRegs<MT> &xs, uint32_t *xr
         c2 = group_sum<8>(c2);
         c4 = group_sum<8>(c4);
         if (q == 0)
-            *reinterpret_cast<U4 *>(xr + 32) = U4{{__float_as_uint(fmaf(0.5f, X, c1)),
-                                                    __float_as_uint(fmaf(1.5f, X, c2)),
-                                                    __float_as_uint(fmaf(7.5f, X, c4)),
-                                                    __float_as_uint(fmaf(127.5f, X, 1024.f * X))}};
+            *reinterpret_cast<U4 *>(xr + 32) =
+                U4{{__float_as_uint(-fmaf(0.5f, X, c1)), __float_as_uint(-fmaf(1.5f, X, c2)),
+                    __float_as_uint(-fmaf(7.5f, X, c4)), __float_as_uint(-fmaf(127.5f, X, 1024.f * X))}};
     }
 }
 
@@ -594,16 +595,20 @@ __device__ __forceinline__ void plan_pass(int q, uint32_t cnt, uint32_t wb, uint
 #pragma unroll
     for (int m = 0; m < MT; m++) {
         const uint32_t *xr = xrec + ((uint32_t)m * G + xcol) * kXRec;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f}; // four chains: pair p goes to chain (p / 4) % 4
+        // two chains, the first starting from -C_b: pairs 0..15, then 16..31
+        float acc0 = __uint_as_float(xr[32 + C]), acc1 = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const U4 xa = *reinterpret_cast<const U4 *>(xr + 4 * k);
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-                acc[k & 3] = dot2(hp[4 * k + t], xa.v[t], acc[k & 3]);
+            for (int t = 0; t < 4; t++) {
+                if (k < 4)
+                    acc0 = dot2(hp[4 * k + t], xa.v[t], acc0);
+                else
+                    acc1 = dot2(hp[4 * k + t], xa.v[t], acc1);
+            }
         }
-        const float cc = __uint_as_float(xr[32 + C]);
-        psum[m * ps + e] = s * (((acc[0] + acc[1]) + (acc[2] + acc[3])) - cc);
+        psum[m * ps + e] = s * (acc0 + acc1);
     }
 }
 
@@ -644,14 +649,16 @@ __device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int p
             const float *p = psum + m * ps + j;
             float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
             int g = lo + q;
-            for (; g + 3 * L < hi; g += 4 * L) {
-                a0 += p[g * nr];
-                a1 += p[(g + L) * nr];
-                a2 += p[(g + 2 * L) * nr];
-                a3 += p[(g + 3 * L) * nr];
+            const int step = L * nr; // column g + L of the row sits L * nr further
+            const float *pg = p + g * nr;
+            for (; g + 3 * L < hi; g += 4 * L, pg += 4 * step) {
+                a0 += pg[0];
+                a1 += pg[step];
+                a2 += pg[2 * step];
+                a3 += pg[3 * step];
             }
-            for (; g < hi; g += L)
-                a0 += p[g * nr];
+            for (; g < hi; g += L, pg += step)
+                a0 += pg[0];
             v = (a0 + a1) + (a2 + a3);
         }
         v = group_sum<L>(v);
