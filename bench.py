@@ -44,6 +44,8 @@ def parse(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the baseline sample")
     ap.add_argument("--kernel-steps", type=int, default=5, help="replays of each per-kind kernel graph")
+    ap.add_argument("--no-kinds", action="store_true",
+                    help="skip the per-kind kernel timing (profiles then see only the step's own launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
     return ap.parse_args(argv)
@@ -173,7 +175,7 @@ def main(argv=None):
     for st in step.stages:
         if step.stage_name(st) not in names:
             names.append(step.stage_name(st))
-    for name in names:
+    for name in ([] if args.no_kinds else names):
         sts = [st for st in step.stages if step.stage_name(st) == name]
         g = step.capture_stages(sts)
         for _ in range(2):
@@ -234,6 +236,7 @@ def main(argv=None):
             "workload": args.workload, "M": 1, "gemvs_per_step": len(step.mats), "launches_per_step": n_launch,
             "launch": args.mode, "path": args.path,
             "plan_bytes_per_step": step.plan_bytes() if step.planned else None,
+            "warm_bytes_per_step": step.warm_bytes() if step.planned else None,
             "weights": step.weights(), "mean_bits": round(step.mean_bits(), 4),
             "alg_bytes_per_step": alg, "layout_bytes_per_step": step.layout_bytes(),
             "GBps_step": round(gbps, 1), "pct_peak_step": round(100 * gbps * 1e9 / PEAK_HBM, 2),
@@ -246,7 +249,7 @@ def main(argv=None):
             "frac": round(achieved / PEAK_HBM, 4), "traffic": traffic,
             "kernel": f"{KERNELS[args.path][0]} ({KERNELS[args.path][1]})", "alg_bytes_per_launch": round(alg_per_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3), "per_matrix": kinds,
-            "per_matrix_sum_us": round(kern_ms * 1e3, 1),
+            "per_matrix_sum_us": round(kern_ms * 1e3, 1) if kinds else None,
         },
         "cpu_baseline": cpu,
     }

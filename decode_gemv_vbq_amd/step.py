@@ -111,6 +111,20 @@ class DecodeStep:
             tot += int(m.L.code_bytes) + 4 * groups + 64 * max(tiles, m.P.wgs) + 2 * self.M * m.spec.K
         return tot
 
+    def warm_bytes(self) -> int:
+        """Bytes the step's launches fetch ahead for the launch after them (the
+        first tile of each of its row blocks, at most one tile stride of the
+        warming launch; the last launch warms the first).  Those bytes are read
+        again by the launch they belong to, from the caches."""
+        tot = 0
+        n = len(self.stages)
+        for k, st in enumerate(self.stages):
+            tb = min(self.mats[i].P.tile_bytes for i in st)
+            for i in self.stages[(k + 1) % n]:
+                P = self.mats[i].P
+                tot += P.wgs * min(-(-P.first_bytes // 16) * 16, tb)
+        return tot
+
     # ------------------------------------------------------------- the step
     def seq(self):
         """The whole step as one executor call (vbq_gemv_planned_seq or
