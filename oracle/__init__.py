@@ -58,6 +58,7 @@ def lib():
         L.vbqo_layout.argtypes = [i, i, P, P]
         L.vbqo_pack.argtypes = [i, i, P, P, P, P, u64]
         L.vbqo_header.argtypes = [P, u64, P]
+        L.vbqo_quantize.argtypes = [i, i, P, i, P, P, P]
         L.vbqo_unpack.argtypes = [P, u64, P, P, P]
         L.vbqo_dequant_f32.argtypes = [i, i, P, P, P, P]
         L.vbqo_dequant_f16.argtypes = [i, i, P, P, P, P]
@@ -130,6 +131,20 @@ def unpack(blob: np.ndarray):
     sc = np.empty((N, G), np.uint16)
     _check(lib().vbqo_unpack(_p(blob), blob.size, _p(q), _p(bits), _p(sc)), "unpack")
     return q, bits, sc
+
+
+def quantize(w, bits):
+    """Round-to-nearest codes and fp16 scales for width map bits u8[N][G] from
+    weights w (fp32 or fp16 values, [N][K]; fp16 is widened exactly) ->
+    (q u8[N][K], scales fp16 bits u16[N][G])."""
+    w = np.asarray(w)
+    w32 = _c(w.astype(np.float32) if w.dtype == np.float16 else w, np.float32)
+    bits = _c(bits, np.uint8)
+    N, K = w32.shape
+    q = np.empty((N, K), np.uint8)
+    s = np.empty((N, K // 64), np.uint16)
+    _check(lib().vbqo_quantize(N, K, _p(w32), K, _p(bits), _p(q), _p(s)), "quantize")
+    return q, s
 
 
 def dequant(q, bits, scales, dtype=np.float32) -> np.ndarray:

@@ -489,3 +489,46 @@ int vbqo_dense_gemv(int N, int K, int M, const uint16_t *w16, const uint16_t *x,
         }
     return VBQO_OK;
 }
+
+/*
+ * Round-to-nearest quantizer for a given width map (the step before packing).
+ * The pages learn the scales during training and give no rule for producing
+ * codes from float weights; the reading fixed here is the plain one: per group
+ * of 64 weights of width b, with c = (2^b - 1) / 2,
+ *   a = max_j |w_j|   (fp32; fmaxf semantics, so a NaN weight is skipped)
+ *   s = fp16_rne(a / c)          (the division in fp32, correctly rounded)
+ *   q_j = min(max(rint(w_j / s + c), 0), 2^b - 1)
+ * with w_j / s and the + c in fp32 (s widened exactly to fp32), rint rounding
+ * half to even, and min/max with fmaxf/fminf semantics (a NaN quotient gives
+ * q = 0).  Every operation is a single IEEE fp32 operation, so a device that
+ * performs the same operations gets the same codes.  w is fp32 [N][ldw].
+ */
+int vbqo_quantize(int N, int K, const float *w, int ldw, const uint8_t *bits, uint8_t *q, uint16_t *scales)
+{
+    if (N < 1 || K < 64 || K % 64 != 0 || ldw < K)
+        return VBQO_ERR_SHAPE;
+    const int G = K / 64;
+    for (int n = 0; n < N; n++)
+        for (int g = 0; g < G; g++) {
+            const int b = bits[(uint64_t)n * G + g];
+            if (b != 1 && b != 2 && b != 4 && b != 8)
+                return VBQO_ERR_BITS;
+            const float c = (float)((1 << b) - 1) / 2.0f;
+            const float top = (float)((1 << b) - 1);
+            const float *wg = w + (uint64_t)n * (uint64_t)ldw + 64u * (uint64_t)g;
+            float a = 0.0f;
+            for (int j = 0; j < 64; j++)
+                a = fmaxf(a, fabsf(wg[j]));
+            const float ratio = a / c;
+            const uint16_t sh = vbqo_f64_to_f16_rne((double)ratio);
+            scales[(uint64_t)n * G + g] = sh;
+            const float s = (float)vbqo_f16_to_f64(sh);
+            for (int j = 0; j < 64; j++) {
+                const float t = wg[j] / s;
+                const float u = t + c;
+                const float r = rintf(u);
+                q[(uint64_t)n * K + 64u * g + j] = (uint8_t)fminf(fmaxf(r, 0.0f), top);
+            }
+        }
+    return VBQO_OK;
+}
