@@ -46,6 +46,9 @@ def parse(argv=None):
     ap.add_argument("--kernel-steps", type=int, default=5, help="replays of each per-kind kernel graph")
     ap.add_argument("--no-kinds", action="store_true",
                     help="skip the per-kind kernel timing (profiles then see only the step's own launches)")
+    ap.add_argument("--op", default="step", choices=["step", "quantize"],
+                    help="step: the decode step (the headline line); quantize: vbq_quantize of the 9B gate "
+                         "projection's fp16 weights (14336x4096) with its width mix")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
     return ap.parse_args(argv)
@@ -129,6 +132,44 @@ def cpu_baseline(step, budget_s):
     }
 
 
+def bench_quantize(torch, v, args):
+    """vbq_quantize on a 14336x4096 fp16 weight matrix with the 9B model's width
+    mix; bytes are the weights read, the widths read, the codes and scales
+    written (an HBM-bound elementwise pass)."""
+    from decode_gemv_vbq_amd import workload as wl
+    N, K = 14336, 4096
+    G = K // 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260703)
+    w = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32).half()
+    widths = sorted(wl.MIX_BASE)
+    p = torch.tensor([wl.MIX_BASE[b] for b in widths], dtype=torch.float32, device="cuda")
+    idx = torch.multinomial(p, N * G, replacement=True, generator=gen).view(N, G)
+    bits = torch.tensor(widths, dtype=torch.uint8, device="cuda")[idx].contiguous()
+    for _ in range(3):
+        v.quantize(w, bits)
+    reps = max(5, args.steps // 2)
+    q = s = None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        q, s = v.quantize(w, bits)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * N * K + N * G + N * K + 2 * N * G
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"vbq_quantize {N}x{K} fp16: {ms * 1e3:.1f} us, {gbps:.0f} GB/s")
+    print(json.dumps({
+        "metric": "us per vbq_quantize call (fp16 weights -> codes + fp16 scales)", "value": round(ms * 1e3, 2),
+        "unit": "us", "n_gpus": 1, "steps": reps, "warmup": 3, "higher_is_better": False, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": "quantize 14336x4096 fp16, 9B width mix", "bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": None, "kernel": "k_quantize (vbq_quantize)"},
+        "cpu_baseline": None}), flush=True)
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -148,6 +189,10 @@ def main(argv=None):
     import decode_gemv_vbq_amd as v
     from decode_gemv_vbq_amd import accounting as acc
     from decode_gemv_vbq_amd.step import DecodeStep
+
+    if args.op == "quantize":
+        bench_quantize(torch, v, args)
+        return
 
     v.lib()
     assert torch.cuda.is_available(), "bench needs a GPU"

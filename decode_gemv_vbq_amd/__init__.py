@@ -16,6 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvbq.so")
 
 VBQ_F32, VBQ_F16 = 0, 1
+#: device status-word bits (include/vbq.h VBQ_STATUS_*)
+STATUS_BITS, STATUS_CODES, STATUS_LAYOUT = 0x1, 0x2, 0x4
 
 STATUS = {
     0: "VBQ_OK", 1: "VBQ_ERR_INVALID_ARG", 2: "VBQ_ERR_SHAPE", 3: "VBQ_ERR_BATCH", 4: "VBQ_ERR_BITS",
@@ -28,7 +30,7 @@ EXPORTS = (
     "vbq_pack_plan_workspace", "vbq_pack_plan", "vbq_pack", "vbq_status_check", "vbq_dequant",
     "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_shared",
     "vbq_plan_init", "vbq_prepare", "vbq_gemv_planned", "vbq_gemv_planned_shared", "vbq_gemv_seq",
-    "vbq_gemv_planned_seq", "vbq_dense_f16_gemv",
+    "vbq_gemv_planned_seq", "vbq_dense_f16_gemv", "vbq_quantize",
 )
 MAX_SHARED = 4
 
@@ -108,6 +110,7 @@ def lib():
         L.vbq_pack.argtypes = [LP, P, P, P, P, P, P]
         L.vbq_status_check.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
         L.vbq_dequant.argtypes = [LP, P, P, i, P]
+        L.vbq_quantize.argtypes = [i, i, P, i, i, P, P, P, P, P]
         L.vbq_workspace_size.argtypes = [LP, i, ctypes.POINTER(sz)]
         L.vbq_workspace_clear.argtypes = [P, sz, P]
         L.vbq_gemv.argtypes = [LP, P, P, P, i, P, sz, P]
@@ -224,6 +227,25 @@ def status_check(status):
 
 
 # ------------------------------------------------------------------ dequant
+
+def quantize(w, bits, status=None):
+    """Round-to-nearest codes and fp16 scales (vbq_quantize) for weights w
+    ([N][K] fp32 or fp16 device tensor, unit column stride) and widths bits
+    (u8 [N][G]) -> (q u8 [N][K], scales int16 view of fp16 bits [N][G]).
+    With ``status`` (a 1-element int32 device tensor) a bad width is flagged
+    there instead of being silent."""
+    torch = _torch()
+    _need_cuda(bits)
+    if w.dim() != 2 or w.stride(1) != 1 or not w.is_cuda or w.dtype not in (torch.float32, torch.float16):
+        raise ValueError("w must be a [N][K] fp32 or fp16 device tensor with unit column stride")
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N, K // 64), dtype=torch.int16, device=w.device)
+    wt = VBQ_F32 if w.dtype == torch.float32 else VBQ_F16
+    _check(lib().vbq_quantize(N, K, _ptr(w), wt, w.stride(0), _ptr(bits), _ptr(q), _ptr(s), _ptr(status),
+                              _stream()), "vbq_quantize")
+    return q, s
+
 
 def dequant(L: Layout, blob, dtype=None):
     torch = _torch()

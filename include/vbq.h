@@ -131,6 +131,26 @@ vbq_status vbq_pack(const vbq_layout *L /* host */, const uint8_t *q, const uint
 vbq_status vbq_status_check(const uint32_t *status_word, uint32_t *raw /* host */, hipStream_t stream);
 
 /*
+ * Round-to-nearest codes and scales for a given width map: the step before
+ * vbq_pack.  "Variable Bit-width Quantization" (mlsanity.com page, Abstract)
+ * gives every group of 64 weights its own width in {1, 2, 4, 8} and learns
+ * its scales in training; the pages give no rule turning float weights into
+ * codes, and this call implements the plain one.  Per group of row n, columns
+ * 64g..64g+63, width b = bits[n][g], c = (2^b - 1) / 2:
+ *   a = max |w| (fp32; NaN weights are skipped),  s = fp16_rne(a / c),
+ *   q = min(max(rint(w / s + c), 0), 2^b - 1)  (fp32 operations, rint ties to
+ *   even; a NaN quotient gives 0, so an all-zero group gets s = 0, q = 0).
+ * w: device [N][ldw] (ldw >= K) of wt (VBQ_F32, or VBQ_F16 widened exactly);
+ * bits: device u8 [N][G]; q: device u8 [N][K] (out, 8-byte aligned); scales:
+ * device fp16 bits [N][G] (out).  A width outside {1, 2, 4, 8} gives that group q = 0 and
+ * s = 0 and sets VBQ_STATUS_BITS in *status_word (device u32, cleared by this
+ * call; may be NULL).  Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_SHAPE (N < 1,
+ * K % 64, ldw < K), VBQ_ERR_ALIGN, VBQ_ERR_HIP.
+ */
+vbq_status vbq_quantize(int N, int K, const void *w, vbq_dtype wt, int ldw, const uint8_t *bits, uint8_t *q,
+                        uint16_t *scales, uint32_t *status_word, hipStream_t stream);
+
+/*
  * Expand a blob to dense weights w[N][K] (row-major): VBQ_F32 gives the exact
  * value of s*(q - (2^b-1)/2); VBQ_F16 gives its round-to-nearest-even fp16.
  */

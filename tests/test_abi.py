@@ -282,3 +282,27 @@ def test_seq_argument_checks_fail_before_launch():
     assert pseq([ok, dict(plan=fake + 8)]) == "VBQ_ERR_ALIGN"
     assert pseq([ok, dict(P=P2)]) == "VBQ_ERR_SHAPE"
     assert pseq([dict(stage=1), dict(stage=0)]) == "VBQ_ERR_INVALID_ARG"
+
+
+def test_quantize_argument_checks_fail_before_launch():
+    v = vbq()
+    lib = v.lib()
+    VP = ctypes.c_void_p
+    fake, null = VP(1 << 20), VP(0)
+
+    def call(N=4, K=128, w=fake, wt=0, ldw=128, bits=fake, q=fake, s=fake, st=null):
+        return v.STATUS[lib.vbq_quantize(N, K, w, wt, ldw, bits, q, s, st, null)]
+
+    assert call(w=null) == "VBQ_ERR_INVALID_ARG"
+    assert call(bits=null) == "VBQ_ERR_INVALID_ARG"
+    assert call(q=null) == "VBQ_ERR_INVALID_ARG"
+    assert call(s=null) == "VBQ_ERR_INVALID_ARG"
+    assert call(wt=2) == "VBQ_ERR_INVALID_ARG"
+    assert call(N=0) == "VBQ_ERR_SHAPE"
+    assert call(K=96, ldw=96) == "VBQ_ERR_SHAPE"
+    assert call(K=32, ldw=32) == "VBQ_ERR_SHAPE"
+    assert call(ldw=100) == "VBQ_ERR_SHAPE"
+    assert call(w=VP((1 << 20) + 2)) == "VBQ_ERR_ALIGN"          # fp32 weights need 4-byte alignment
+    assert call(s=VP((1 << 20) + 1)) == "VBQ_ERR_ALIGN"
+    assert call(q=VP((1 << 20) + 4)) == "VBQ_ERR_ALIGN"
+    assert call(st=VP((1 << 20) + 2)) == "VBQ_ERR_ALIGN"
