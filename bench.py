@@ -46,9 +46,10 @@ def parse(argv=None):
     ap.add_argument("--kernel-steps", type=int, default=5, help="replays of each per-kind kernel graph")
     ap.add_argument("--no-kinds", action="store_true",
                     help="skip the per-kind kernel timing (profiles then see only the step's own launches)")
-    ap.add_argument("--op", default="step", choices=["step", "quantize"],
+    ap.add_argument("--op", default="step", choices=["step", "quantize", "argmax"],
                     help="step: the decode step (the headline line); quantize: vbq_quantize of the 9B gate "
-                         "projection's fp16 weights (14336x4096) with its width mix")
+                         "projection's fp16 weights (14336x4096) with its width mix; argmax: the 9B LM head "
+                         "(128256x4096) as vbq_gemv_planned_argmax against vbq_gemv_planned with fp16 logits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
     return ap.parse_args(argv)
@@ -170,6 +171,58 @@ def bench_quantize(torch, v, args):
         "cpu_baseline": None}), flush=True)
 
 
+def bench_argmax(torch, v, args):
+    """The 9B LM head (128256x4096, head width mix) for one token: greedy
+    argmax epilogue (no logits written) against the plain planned GEMV writing
+    fp16 logits.  Three copies of the matrix are used in turn so that each call
+    streams its weights from HBM (the three exceed the memory-side cache)."""
+    from decode_gemv_vbq_amd import workload as wl
+    from decode_gemv_vbq_amd import accounting as acc
+    spec = wl.MatrixSpec("head", 128256, 4096, wl.MIX_HEAD, layer=0)
+    mats = []
+    for c in range(3):
+        q, bits, s, x = wl.draw_matrix_torch(spec, 94 + c, 1)
+        blob, L = v.pack(q, bits, s.view(torch.float16))
+        del q, bits, s
+        plan, P = v.prepare(L, blob, M=1)
+        mats.append((L, blob, plan, P, x))
+    torch.cuda.synchronize()
+    ws = v.argmax_workspace()
+    ys = [torch.empty((1, spec.N), dtype=torch.float16, device="cuda") for _ in mats]
+
+    def run_argmax():
+        for L, blob, plan, P, x in mats:
+            v.gemv_planned_argmax(P, plan, x, ws=ws)
+
+    def run_logits():
+        for (L, blob, plan, P, x), y in zip(mats, ys):
+            v.gemv_planned(P, plan, x, out=y)
+
+    res = {}
+    for name, fn in (("argmax", run_argmax), ("logits", run_logits)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(3):
+            g.replay()
+        res[name] = time_steps(torch, g.replay, max(10, args.steps // 2)) / len(mats) * 1e3  # us per call
+    alg = acc.vbq_read_bytes(mats[0][0], 1)
+    gbps = alg / (res["argmax"] * 1e-6) / 1e9
+    log(f"LM head 128256x4096: argmax {res['argmax']:.1f} us, logits {res['logits']:.1f} us per call")
+    print(json.dumps({
+        "metric": "us per greedy-decode LM-head call (argmax epilogue, M=1)", "value": round(res["argmax"], 2),
+        "unit": "us", "n_gpus": 1, "steps": max(10, args.steps // 2), "warmup": 3, "higher_is_better": False,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "LM head 128256x4096, head width mix, 3 copies in turn",
+                   "logits_us": round(res["logits"], 2), "alg_bytes": alg},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": None,
+                     "kernel": "k_gemv_plan<1> argmax epilogue (vbq_gemv_planned_argmax)"},
+        "cpu_baseline": None}), flush=True)
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -192,6 +245,9 @@ def main(argv=None):
 
     if args.op == "quantize":
         bench_quantize(torch, v, args)
+        return
+    if args.op == "argmax":
+        bench_argmax(torch, v, args)
         return
 
     v.lib()

@@ -30,7 +30,7 @@ EXPORTS = (
     "vbq_pack_plan_workspace", "vbq_pack_plan", "vbq_pack", "vbq_status_check", "vbq_dequant",
     "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_shared",
     "vbq_plan_init", "vbq_prepare", "vbq_gemv_planned", "vbq_gemv_planned_shared", "vbq_gemv_seq",
-    "vbq_gemv_planned_seq", "vbq_dense_f16_gemv", "vbq_quantize",
+    "vbq_gemv_planned_seq", "vbq_dense_f16_gemv", "vbq_quantize", "vbq_gemv_planned_argmax",
 )
 MAX_SHARED = 4
 
@@ -121,6 +121,7 @@ def lib():
         L.vbq_prepare.argtypes = [PP, LP, P, P, P]
         L.vbq_gemv_planned.argtypes = [PP, P, i, P, i, P, i, i, P]
         L.vbq_gemv_planned_shared.argtypes = [ctypes.POINTER(PlannedItem), i, i, P, i, i, P]
+        L.vbq_gemv_planned_argmax.argtypes = [PP, P, i, P, i, P, P]
         L.vbq_gemv_seq.argtypes = [ctypes.POINTER(SeqItem), i, i, i, P, sz, P]
         L.vbq_gemv_planned_seq.argtypes = [ctypes.POINTER(PlannedSeqItem), i, i, i, P]
         L.vbq_dense_f16_gemv.argtypes = [i, i, i, P, P, i, P, i, i, P]
@@ -374,6 +375,29 @@ def gemv_planned(P: Plan, plan, x, out=None, out_dtype=None):
     _check(lib().vbq_gemv_planned(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), yt,
                                   _stream()), "vbq_gemv_planned")
     return out
+
+
+ARGMAX_WS_BYTES = 8 * 16 + 16 + 4 * 16 + 4 * 16  # sizeof(vbq_argmax_ws)
+
+
+def argmax_workspace(device="cuda"):
+    """A zeroed vbq_argmax_ws (int32 tensor view; index at [36:52], value bits at [52:68])."""
+    torch = _torch()
+    return torch.zeros(ARGMAX_WS_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def gemv_planned_argmax(P: Plan, plan, x, ws=None):
+    """Greedy-decode argmax of W x per token from a plan: -> (index int32[M], value float32[M])
+    device tensors (views into the workspace, valid until its next use)."""
+    torch = _torch()
+    _need_cuda(plan)
+    x2 = _as_2d(x)
+    M = x2.shape[0]
+    if ws is None:
+        ws = argmax_workspace(x.device)
+    _check(lib().vbq_gemv_planned_argmax(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(ws),
+                                         _stream()), "vbq_gemv_planned_argmax")
+    return ws[36:36 + M], ws[52:52 + M].view(torch.float32)
 
 
 def gemv_planned_shared(plans, x, outs=None, out_dtype=None):

@@ -388,7 +388,7 @@ struct PArgs {
 };
 
 struct PLayout {
-    uint32_t x, ring, psum, ybuf, ctr, total;
+    uint32_t x, ring, psum, ybuf, ctr, best, total;
 };
 
 __host__ __device__ inline uint32_t p_take(uint32_t &o, uint32_t bytes)
@@ -408,6 +408,7 @@ __host__ __device__ inline PLayout p_layout(int MT, int G, int rows, int tb, int
     l.psum = p_take(o, 2u * (uint32_t)(MT * ps) * 4u);
     l.ybuf = p_take(o, (uint32_t)(MT * rows) * 4u);
     l.ctr = p_take(o, 2u * 4u); // pass counters of the two ring slots
+    l.best = p_take(o, 2u * 8u); // argmax output: the best (value, row) key per token
     l.total = o;
     return l;
 }
@@ -620,10 +621,26 @@ __device__ __forceinline__ int sum_lanes(int G) { return G > 256 ? 64 : G > 128 
 __device__ __forceinline__ int sum_items(int nr, int G) { return (nr * sum_lanes(G) + 63) / 64; }
 
 // Where finished rows go.
+// Output mode kArgmax: instead of storing rows, keep per token the largest
+// (value, smallest row) as one 64-bit key in LDS (see argmax_key).
+constexpr int kArgmax = 2;
+
 struct YOut {
     void *y;
     int ldy, n0, yt;
+    unsigned long long *best; // LDS, [MT] keys (kArgmax)
 };
+
+// Order-preserving key of (value, row): the fp32 bits mapped so that unsigned
+// order is the IEEE total order (-NaN < -inf < ... < +inf < +NaN), then the
+// complemented row, so that the maximum key is the largest value at its
+// smallest row.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t row)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)ord << 32) | (unsigned long long)(~row);
+}
 
 // Row-sum item t of a tile: rows (64 / L) t .. of the tile, L = sum_lanes(G)
 // lanes per row.  The partials of row j sit at column * nr + j for the tile's
@@ -667,7 +684,9 @@ __device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int p
             const float tot = ybuf[m * rows + r] + v;
             if (done) {
                 const uint64_t o = (uint64_t)m * yo.ldy + yo.n0 + r;
-                if (yo.yt == VBQ_F16)
+                if (yo.yt == kArgmax)
+                    atomicMax(yo.best + m, argmax_key(tot, (uint32_t)(yo.n0 + r)));
+                else if (yo.yt == VBQ_F16)
                     reinterpret_cast<__half *>(yo.y)[o] = __float2half_rn(tot);
                 else
                     reinterpret_cast<float *>(yo.y)[o] = tot;
@@ -688,6 +707,35 @@ __device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps,
     case 32: rowsum_item_l<MT, 32>(t, h, G, ps, rows, psum, ybuf, yo); break;
     default: rowsum_item_l<MT, 64>(t, h, G, ps, rows, psum, ybuf, yo); break;
     }
+}
+
+// Merge this workgroup's keys into the call's (agent-scope atomics on the
+// workspace); the last workgroup of the launch (a ticket counter) decodes the
+// keys of its tokens into index and value and clears keys and counter for the
+// next call.  tok0: the launch's first token.
+template <int MT>
+__device__ void argmax_finish(vbq_argmax_ws *ws, int tok0, const unsigned long long *best)
+{
+#pragma unroll
+    for (int m = 0; m < MT; m++)
+        __hip_atomic_fetch_max(&ws->key[tok0 + m], best[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t total = gridDim.x * gridDim.y;
+    const uint32_t ticket = __hip_atomic_fetch_add(&ws->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (ticket != total - 1)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+        const unsigned long long k =
+            __hip_atomic_load(&ws->key[tok0 + m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t ord = (uint32_t)(k >> 32);
+        const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
+        ws->index[tok0 + m] = (int32_t)(~(uint32_t)k);
+        ws->value[tok0 + m] = __uint_as_float(u);
+        __hip_atomic_store(&ws->key[tok0 + m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __hip_atomic_store(&ws->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int MT>
@@ -717,7 +765,8 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     float *ybuf = reinterpret_cast<float *>(smem + L.ybuf);
     const uint8_t *region = plan + (uint64_t)blk * region_bytes;
     const uint32_t ring = lds_addr(smem + L.ring);
-    const YOut yo{yptr, ldy, n0, yt};
+    unsigned long long *best = reinterpret_cast<unsigned long long *>(smem + L.best);
+    const YOut yo{yptr, ldy, n0, yt, best};
     const uint8_t *warm = nullptr; // set by the copying waves before the last tile's phase
     uint32_t warm_bytes = 0;
 
@@ -731,6 +780,8 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
             ybuf[(i / R) * rows + i % R] = 0.f;
         if (tid == 0)
             cnt[0] = 0u;
+        if (tid < MT)
+            best[tid] = 0ull;
         wait_vm0();
     } else {
         XRegs<MT> xs;
@@ -822,6 +873,11 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     // is released (the other waves leave without waiting for their stores)
     if (wave < kCopyWaves && warm_bytes)
         wait_vm0();
+    if (yt == kArgmax) {
+        __syncthreads(); // every finished row's key is in best[]
+        if (tid == 0)
+            argmax_finish<MT>(reinterpret_cast<vbq_argmax_ws *>(yptr), ldy, best);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1118,6 +1174,37 @@ vbq_status vbq_gemv_planned(const vbq_plan *P, const void *plan, int M, const ui
 {
     const vbq_planned_item it{P, plan, y, ldy};
     return vbq_gemv_planned_shared(&it, 1, M, x, ldx, yt, stream);
+}
+
+vbq_status vbq_gemv_planned_argmax(const vbq_plan *P, const void *plan, int M, const uint16_t *x, int ldx,
+                                   vbq_argmax_ws *ws, hipStream_t stream)
+{
+    if (!P || !plan || !x || !ws)
+        return VBQ_ERR_INVALID_ARG;
+    if (M < 1 || M > 16)
+        return VBQ_ERR_BATCH;
+    VBQ_TRY(check_plan(P));
+    if ((uintptr_t)ws % 8)
+        return VBQ_ERR_ALIGN;
+    const int chunk = P->M;
+    // the same checks and arguments as an fp32 planned GEMV writing to ws, then
+    // the record is switched to the argmax output (y = ws, ldy = first token)
+    const vbq_planned_item it{P, plan, ws, P->N};
+    PArgs a;
+    dim3 grid;
+    uint32_t lds;
+    for (int pass = 0; pass < 2; pass++)
+        for (int t0 = 0; t0 < M; t0 += chunk) {
+            const int m = std::min(chunk, M - t0);
+            VBQ_TRY(planned_args(&it, 1, m, x, ldx, VBQ_F32, t0, &a, &grid, &lds));
+            set_next(a, nullptr, 0);
+            a.rec[0].y = ws;
+            a.rec[0].ldy = t0;
+            a.rec[0].g_yt_tb = (a.rec[0].g_yt_tb & 0xff00ffffu) | ((uint32_t)kArgmax << 16);
+            if (pass == 1)
+                VBQ_TRY(m == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream));
+        }
+    return VBQ_OK;
 }
 
 } // extern "C"

@@ -285,6 +285,34 @@ vbq_status vbq_prepare(const vbq_plan *P /* host */, const vbq_layout *L /* host
 vbq_status vbq_gemv_planned(const vbq_plan *P /* host */, const void *plan, int M, const uint16_t *x, int ldx,
                             void *y, int ldy, vbq_dtype yt, hipStream_t stream);
 
+/*
+ * Greedy-decode epilogue for the LM head ("Variable Bit-width Quantization",
+ * mlsanity.com page, Abstract: the quantized models decode autoregressively;
+ * greedy decoding takes the token of the largest logit).  Workspace of
+ * vbq_gemv_planned_argmax: key/count are internal and must be zero before the
+ * first call (e.g. hipMemset once); every call leaves them zero again.
+ */
+typedef struct vbq_argmax_ws {
+    uint64_t key[16];     /* internal */
+    uint32_t count;       /* internal */
+    uint32_t reserved[3];
+    int32_t index[16];    /* out: token m's row of the largest output */
+    float value[16];      /* out: that output, fp32 */
+} vbq_argmax_ws;
+
+/*
+ * For each token m < M (1..16): the row n of the largest y[m][n] of
+ * Y = X W^T from a plan, without writing Y.  Values are the fp32 outputs of
+ * vbq_gemv_planned (bit for bit), ordered by the IEEE total order
+ * (-NaN < -inf < ... < +inf < +NaN); ties go to the smallest row.  One launch
+ * per P->M tokens; the last workgroup of each launch writes index/value of its
+ * tokens into ws (device, 8-byte aligned).  Calls sharing a workspace must be
+ * ordered (one stream).  Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_BATCH,
+ * VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE, VBQ_ERR_ALIGN.
+ */
+vbq_status vbq_gemv_planned_argmax(const vbq_plan *P /* host */, const void *plan, int M, const uint16_t *x,
+                                   int ldx, vbq_argmax_ws *ws, hipStream_t stream);
+
 /* One matrix of a vbq_gemv_planned_shared call. */
 typedef struct vbq_planned_item {
     const vbq_plan *P; /* host */

@@ -306,3 +306,25 @@ def test_quantize_argument_checks_fail_before_launch():
     assert call(s=VP((1 << 20) + 1)) == "VBQ_ERR_ALIGN"
     assert call(q=VP((1 << 20) + 4)) == "VBQ_ERR_ALIGN"
     assert call(st=VP((1 << 20) + 2)) == "VBQ_ERR_ALIGN"
+
+
+def test_planned_argmax_argument_checks_fail_before_launch():
+    v = vbq()
+    lib = v.lib()
+    VP = ctypes.c_void_p
+    fake, null = VP(1 << 20), VP(0)
+    P = fake_plan(v)
+
+    def call(Pl=P, plan=fake, M=1, x=fake, ldx=4096, ws=fake):
+        return v.STATUS[lib.vbq_gemv_planned_argmax(ctypes.byref(Pl), plan, M, x, ldx, ws, null)]
+
+    assert call(plan=null) == "VBQ_ERR_INVALID_ARG"
+    assert call(x=null) == "VBQ_ERR_INVALID_ARG"
+    assert call(ws=null) == "VBQ_ERR_INVALID_ARG"
+    assert call(M=0) == "VBQ_ERR_BATCH"
+    assert call(M=17) == "VBQ_ERR_BATCH"
+    assert call(ws=VP((1 << 20) + 4)) == "VBQ_ERR_ALIGN"
+    assert call(ldx=100) == "VBQ_ERR_SHAPE"
+    bad = fake_plan(v)
+    bad.magic = 0
+    assert call(Pl=bad) == "VBQ_ERR_LAYOUT"
