@@ -46,10 +46,12 @@ def parse(argv=None):
     ap.add_argument("--kernel-steps", type=int, default=5, help="replays of each per-kind kernel graph")
     ap.add_argument("--no-kinds", action="store_true",
                     help="skip the per-kind kernel timing (profiles then see only the step's own launches)")
-    ap.add_argument("--op", default="step", choices=["step", "quantize", "argmax"],
+    ap.add_argument("--op", default="step", choices=["step", "quantize", "argmax", "swiglu"],
                     help="step: the decode step (the headline line); quantize: vbq_quantize of the 9B gate "
                          "projection's fp16 weights (14336x4096) with its width mix; argmax: the 9B LM head "
-                         "(128256x4096) as vbq_gemv_planned_argmax against vbq_gemv_planned with fp16 logits")
+                         "(128256x4096) as vbq_gemv_planned_argmax against vbq_gemv_planned with fp16 logits; swiglu: "
+                         "the 9B gate and up projections as one interleaved matrix with the SwiGLU epilogue "
+                         "against the shared two-output launch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
     return ap.parse_args(argv)
@@ -171,6 +173,69 @@ def bench_quantize(torch, v, args):
         "cpu_baseline": None}), flush=True)
 
 
+def bench_swiglu(torch, v, args):
+    """The 9B MLP's gate and up projections (2 x 14336x4096) for one token:
+    one interleaved 28672-row matrix with the SwiGLU epilogue (14336 outputs)
+    against the step's shared launch of the two matrices (two 14336-row
+    outputs).  Ten copies are used in turn so each call streams from HBM."""
+    from decode_gemv_vbq_amd import workload as wl
+    from decode_gemv_vbq_amd import accounting as acc
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    copies = []
+    for c in range(10):
+        g = wl.draw_matrix_torch(wl.MatrixSpec("gate", 14336, 4096, wl.MIX_BASE, layer=c), 97, 1)
+        u = wl.draw_matrix_torch(wl.MatrixSpec("up", 14336, 4096, wl.MIX_BASE, layer=c), 98, 1)
+        x = g[3]
+        qi = torch.stack((g[0], u[0]), 1).view(28672, 4096)
+        bi = torch.stack((g[1], u[1]), 1).view(28672, 64)
+        si = torch.stack((g[2], u[2]), 1).view(28672, 64)
+        blob_i, L_i = v.pack(qi, bi, si.view(torch.float16))
+        plan_i, P_i = v.prepare(L_i, blob_i, M=1)
+        sep = []
+        for t in (g, u):
+            blob, L = v.pack(t[0], t[1], t[2].view(torch.float16))
+            plan, P = v.prepare(L, blob, M=1, wgs=cus // 2)
+            sep.append((P, plan, L, blob))
+        del qi, bi, si, g, u
+        copies.append({"x": x, "P": P_i, "plan": plan_i, "L": L_i, "blob": blob_i, "sep": sep,
+                       "h": torch.empty((1, 14336), dtype=torch.float16, device="cuda"),
+                       "yg": torch.empty((1, 14336), dtype=torch.float16, device="cuda"),
+                       "yu": torch.empty((1, 14336), dtype=torch.float16, device="cuda")})
+    torch.cuda.synchronize()
+
+    def run_swiglu():
+        for c in copies:
+            v.gemv_planned_swiglu(c["P"], c["plan"], c["x"], out=c["h"])
+
+    def run_shared():
+        for c in copies:
+            v.gemv_planned_shared([(P, plan) for P, plan, _, _ in c["sep"]], c["x"], outs=[c["yg"], c["yu"]])
+
+    res = {}
+    for name, fn in (("swiglu", run_swiglu), ("shared", run_shared)):
+        fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        for _ in range(2):
+            gr.replay()
+        res[name] = time_steps(torch, gr.replay, max(5, args.steps // 5)) / len(copies) * 1e3
+    alg = acc.vbq_read_bytes(copies[0]["L"], 1)
+    gbps = alg / (res["swiglu"] * 1e-6) / 1e9
+    log(f"gate+up 2x14336x4096: SwiGLU epilogue {res['swiglu']:.1f} us, shared two-output launch {res['shared']:.1f} us")
+    print(json.dumps({
+        "metric": "us per SwiGLU MLP-input call (gate and up GEMVs with the activation fused, M=1)",
+        "value": round(res["swiglu"], 2), "unit": "us", "n_gpus": 1, "steps": max(5, args.steps // 5),
+        "warmup": 2, "higher_is_better": False, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "gate+up 2x14336x4096 interleaved, base width mix, 10 copies in turn",
+                   "shared_two_output_us": round(res["shared"], 2), "alg_bytes": alg},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": None,
+                     "kernel": "k_gemv_plan<1> SwiGLU epilogue (vbq_gemv_planned_swiglu)"},
+        "cpu_baseline": None}), flush=True)
+
+
 def bench_argmax(torch, v, args):
     """The 9B LM head (128256x4096, head width mix) for one token: greedy
     argmax epilogue (no logits written) against the plain planned GEMV writing
@@ -248,6 +313,9 @@ def main(argv=None):
         return
     if args.op == "argmax":
         bench_argmax(torch, v, args)
+        return
+    if args.op == "swiglu":
+        bench_swiglu(torch, v, args)
         return
 
     v.lib()

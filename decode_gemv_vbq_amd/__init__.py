@@ -31,6 +31,7 @@ EXPORTS = (
     "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_shared",
     "vbq_plan_init", "vbq_prepare", "vbq_gemv_planned", "vbq_gemv_planned_shared", "vbq_gemv_seq",
     "vbq_gemv_planned_seq", "vbq_dense_f16_gemv", "vbq_quantize", "vbq_gemv_planned_argmax",
+    "vbq_gemv_planned_swiglu",
 )
 MAX_SHARED = 4
 
@@ -122,6 +123,7 @@ def lib():
         L.vbq_gemv_planned.argtypes = [PP, P, i, P, i, P, i, i, P]
         L.vbq_gemv_planned_shared.argtypes = [ctypes.POINTER(PlannedItem), i, i, P, i, i, P]
         L.vbq_gemv_planned_argmax.argtypes = [PP, P, i, P, i, P, P]
+        L.vbq_gemv_planned_swiglu.argtypes = [PP, P, i, P, i, P, i, i, P]
         L.vbq_gemv_seq.argtypes = [ctypes.POINTER(SeqItem), i, i, i, P, sz, P]
         L.vbq_gemv_planned_seq.argtypes = [ctypes.POINTER(PlannedSeqItem), i, i, i, P]
         L.vbq_dense_f16_gemv.argtypes = [i, i, i, P, P, i, P, i, i, P]
@@ -374,6 +376,23 @@ def gemv_planned(P: Plan, plan, x, out=None, out_dtype=None):
     yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
     _check(lib().vbq_gemv_planned(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), yt,
                                   _stream()), "vbq_gemv_planned")
+    return out
+
+
+def gemv_planned_swiglu(P: Plan, plan, x, out=None, out_dtype=None):
+    """silu(gate) * up per output pair of an interleaved (gate, up) matrix plan
+    -> [M][N/2] (or [N/2] for 1-D x)."""
+    torch = _torch()
+    _need_cuda(plan)
+    x2 = _as_2d(x)
+    M = x2.shape[0]
+    out_dtype = out_dtype or torch.float16
+    if out is None:
+        out = torch.empty((M, P.N // 2), dtype=out_dtype, device=x.device)
+    h2 = out.view(1, -1) if out.dim() == 1 else out
+    ht = VBQ_F32 if h2.dtype == torch.float32 else VBQ_F16
+    _check(lib().vbq_gemv_planned_swiglu(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(h2),
+                                         h2.stride(0), ht, _stream()), "vbq_gemv_planned_swiglu")
     return out
 
 

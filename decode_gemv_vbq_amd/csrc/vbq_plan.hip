@@ -623,7 +623,11 @@ __device__ __forceinline__ int sum_items(int nr, int G) { return (nr * sum_lanes
 // Where finished rows go.
 // Output mode kArgmax: instead of storing rows, keep per token the largest
 // (value, smallest row) as one 64-bit key in LDS (see argmax_key).
+// Output modes kSwiglu | yt: rows 2i and 2i+1 are the gate and up rows of
+// output i; finished rows stay in the LDS staging and the workgroup writes
+// silu(gate) * up for its pairs at the end.
 constexpr int kArgmax = 2;
+constexpr int kSwiglu = 4;
 
 struct YOut {
     void *y;
@@ -686,6 +690,8 @@ __device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int p
                 const uint64_t o = (uint64_t)m * yo.ldy + yo.n0 + r;
                 if (yo.yt == kArgmax)
                     atomicMax(yo.best + m, argmax_key(tot, (uint32_t)(yo.n0 + r)));
+                else if (yo.yt & kSwiglu)
+                    ybuf[m * rows + r] = tot;
                 else if (yo.yt == VBQ_F16)
                     reinterpret_cast<__half *>(yo.y)[o] = __float2half_rn(tot);
                 else
@@ -877,6 +883,19 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
         __syncthreads(); // every finished row's key is in best[]
         if (tid == 0)
             argmax_finish<MT>(reinterpret_cast<vbq_argmax_ws *>(yptr), ldy, best);
+    } else if (yt & kSwiglu) {
+        __syncthreads(); // every row of the block is in ybuf
+        const int pairs = R / 2; // R is even: the block starts at an even row and N is even
+        for (int i = tid; i < MT * pairs; i += kT) {
+            const int m = i / pairs, p = i - m * pairs;
+            const float g = ybuf[m * rows + 2 * p], u = ybuf[m * rows + 2 * p + 1];
+            const float h = g / (1.0f + expf(-g)) * u; // silu(gate) * up
+            const uint64_t o = (uint64_t)m * ldy + n0 / 2 + p;
+            if ((yt & 1) == VBQ_F16)
+                reinterpret_cast<__half *>(yptr)[o] = __float2half_rn(h);
+            else
+                reinterpret_cast<float *>(yptr)[o] = h;
+        }
     }
 }
 
@@ -966,7 +985,11 @@ vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, 
         return VBQ_ERR_SHAPE;
     if (wgs <= 0)
         wgs = plan_cus();
-    const int rows = (N + wgs - 1) / wgs;
+    // an even row count whenever N is even, so that a row block never splits
+    // the (gate, up) pairs of an interleaved SwiGLU matrix
+    int rows = (N + wgs - 1) / wgs;
+    if (N % 2 == 0 && rows % 2)
+        rows++;
     wgs = (N + rows - 1) / rows;
     // the largest tile stride (1 KiB steps) whose launch fits the LDS budget;
     // two tokens per launch only while that keeps tiles of 16 KiB or more
@@ -1174,6 +1197,43 @@ vbq_status vbq_gemv_planned(const vbq_plan *P, const void *plan, int M, const ui
 {
     const vbq_planned_item it{P, plan, y, ldy};
     return vbq_gemv_planned_shared(&it, 1, M, x, ldx, yt, stream);
+}
+
+vbq_status vbq_gemv_planned_swiglu(const vbq_plan *P, const void *plan, int M, const uint16_t *x, int ldx, void *h,
+                                   int ldh, vbq_dtype ht, hipStream_t stream)
+{
+    if (!P || !plan || !x || !h)
+        return VBQ_ERR_INVALID_ARG;
+    if (ht != VBQ_F32 && ht != VBQ_F16)
+        return VBQ_ERR_INVALID_ARG;
+    if (M < 1 || M > 16)
+        return VBQ_ERR_BATCH;
+    VBQ_TRY(check_plan(P));
+    if (P->N % 2 || P->rows % 2 || ldh < P->N / 2)
+        return VBQ_ERR_SHAPE;
+    if ((uintptr_t)h % (ht == VBQ_F32 ? 4 : 2))
+        return VBQ_ERR_ALIGN;
+    const int chunk = P->M;
+    const int esz = ht == VBQ_F32 ? 4 : 2;
+    // an ordinary planned GEMV's checks and arguments (outputs of width N / 2
+    // would fail its ldy >= N check, so it sees ldy = N), then the output
+    // switched to the pairs
+    const vbq_planned_item it{P, plan, h, P->N};
+    PArgs a;
+    dim3 grid;
+    uint32_t lds;
+    for (int pass = 0; pass < 2; pass++)
+        for (int t0 = 0; t0 < M; t0 += chunk) {
+            const int m = std::min(chunk, M - t0);
+            VBQ_TRY(planned_args(&it, 1, m, x, ldx, ht, t0, &a, &grid, &lds));
+            set_next(a, nullptr, 0);
+            a.rec[0].y = (uint8_t *)h + (uint64_t)t0 * (uint64_t)ldh * (uint64_t)esz;
+            a.rec[0].ldy = ldh;
+            a.rec[0].g_yt_tb |= (uint32_t)kSwiglu << 16;
+            if (pass == 1)
+                VBQ_TRY(m == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream));
+        }
+    return VBQ_OK;
 }
 
 vbq_status vbq_gemv_planned_argmax(const vbq_plan *P, const void *plan, int M, const uint16_t *x, int ldx,

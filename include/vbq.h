@@ -254,7 +254,8 @@ typedef struct vbq_plan {
  * SYNC.  Fill *P for the matrix (L, blob), launches of up to M tokens (1 or
  * 2; P->M may come back as 1 where two tokens' activations would leave tiles
  * under 16 KiB of LDS) and `wgs` row blocks (<= 0: one per compute unit of the
- * current device; the count is reduced so that no block is empty).  GEMVs of
+ * current device; the count is reduced so that no block is empty; the rows per
+ * block are even whenever N is even).  GEMVs of
  * more tokens run as several launches over the same plan.  Runs one sizing kernel over the
  * width bit planes (workspace ws: device, >= 16 bytes) and waits for it.
  * Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_BATCH (M),
@@ -312,6 +313,23 @@ typedef struct vbq_argmax_ws {
  */
 vbq_status vbq_gemv_planned_argmax(const vbq_plan *P /* host */, const void *plan, int M, const uint16_t *x,
                                    int ldx, vbq_argmax_ws *ws, hipStream_t stream);
+
+/*
+ * SwiGLU epilogue for the gate and up projections of an MLP block, which read
+ * the same activations (the decode path of "Variable Bit-width Quantization",
+ * mlsanity.com page, Abstract, runs the model's projections as fused
+ * dequantize-and-multiply GEMVs).  The plan is of ONE matrix of 2N rows with
+ * the gate and up rows interleaved (row 2i = gate row i, row 2i+1 = up row i;
+ * the caller packs it so); its plan must have an even row count per block,
+ * which vbq_plan_init gives whenever the row count is even.  Writes, for
+ * tokens m < M (1..16), h[m][i] = silu(g) * u with g, u the fp32 outputs of
+ * rows 2i, 2i+1 (silu(g) = g / (1 + exp(-g)) in fp32), h [M][ldh]
+ * (ldh >= N) in ht, without writing the 2N projections.  Errors:
+ * VBQ_ERR_INVALID_ARG, VBQ_ERR_BATCH, VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE (odd row
+ * count or rows per block, ldh < N), VBQ_ERR_ALIGN.
+ */
+vbq_status vbq_gemv_planned_swiglu(const vbq_plan *P /* host */, const void *plan, int M, const uint16_t *x,
+                                   int ldx, void *h, int ldh, vbq_dtype ht, hipStream_t stream);
 
 /* One matrix of a vbq_gemv_planned_shared call. */
 typedef struct vbq_planned_item {

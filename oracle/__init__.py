@@ -147,6 +147,16 @@ def quantize(w, bits):
     return q, s
 
 
+def swiglu(gate, up):
+    """SwiGLU activation of a gated MLP in fp64: silu(g) * u with
+    silu(g) = g * sigmoid(g) = g / (1 + exp(-g)) (the gate's output through
+    the sigmoid-weighted linear unit, times the up projection's output)."""
+    g = np.asarray(gate, np.float64)
+    u = np.asarray(up, np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
 def dequant(q, bits, scales, dtype=np.float32) -> np.ndarray:
     q = _c(q, np.uint8)
     bits = _c(bits, np.uint8)
