@@ -69,7 +69,7 @@ def time_steps(torch, fn, steps):
 
 
 KERNELS = {  # path -> (kernel, entry point, profile name, sources)
-    "plan": ("k_gemv_plan<1>", "vbq_gemv_planned", "k_gemv_plan", ("vbq_plan.hip", "vbq_unpack.h", "vbq_common.h")),
+    "plan": ("k_gemv_plan<1, 0>", "vbq_gemv_planned", "k_gemv_plan", ("vbq_plan.hip", "vbq_unpack.h", "vbq_common.h")),
     "vbq1": ("k_gemv_stream<1>", "vbq_gemv", "k_gemv_stream", ("vbq_stream.hip", "vbq_unpack.h", "vbq_common.h")),
 }
 
@@ -232,7 +232,7 @@ def bench_swiglu(torch, v, args):
                    "shared_two_output_us": round(res["shared"], 2), "alg_bytes": alg},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": None,
-                     "kernel": "k_gemv_plan<1> SwiGLU epilogue (vbq_gemv_planned_swiglu)"},
+                     "kernel": "k_gemv_plan<1, 2> SwiGLU epilogue (vbq_gemv_planned_swiglu)"},
         "cpu_baseline": None}), flush=True)
 
 
@@ -284,7 +284,7 @@ def bench_argmax(torch, v, args):
                    "logits_us": round(res["logits"], 2), "alg_bytes": alg},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": None,
-                     "kernel": "k_gemv_plan<1> argmax epilogue (vbq_gemv_planned_argmax)"},
+                     "kernel": "k_gemv_plan<1, 1> argmax epilogue (vbq_gemv_planned_argmax)"},
         "cpu_baseline": None}), flush=True)
 
 

@@ -621,13 +621,16 @@ __device__ __forceinline__ int sum_lanes(int G) { return G > 256 ? 64 : G > 128 
 __device__ __forceinline__ int sum_items(int nr, int G) { return (nr * sum_lanes(G) + 63) / 64; }
 
 // Where finished rows go.
-// Output mode kArgmax: instead of storing rows, keep per token the largest
-// (value, smallest row) as one 64-bit key in LDS (see argmax_key).
-// Output modes kSwiglu | yt: rows 2i and 2i+1 are the gate and up rows of
-// output i; finished rows stay in the LDS staging and the workgroup writes
-// silu(gate) * up for its pairs at the end.
-constexpr int kArgmax = 2;
-constexpr int kSwiglu = 4;
+// Output modes, a template parameter of the kernel (a plain GEMV carries no
+// code of the others).  kRows: finished rows are stored as fp32 or fp16 (yt).
+// kArgmax: instead of storing rows, keep per token the largest (value,
+// smallest row) as one 64-bit key in LDS (see argmax_key).  kSwiglu: rows 2i
+// and 2i+1 are the gate and up rows of output i; finished rows stay in the
+// LDS staging and the workgroup writes silu(gate) * up (type yt) for its
+// pairs at the end.
+constexpr int kRows = 0;
+constexpr int kArgmax = 1;
+constexpr int kSwiglu = 2;
 
 struct YOut {
     void *y;
@@ -653,7 +656,7 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t row)
 // earlier tiles (ybuf, tiles in order) is added.  A row that ends in this
 // tile is written to y; only a row that continues into the next tile stays in
 // ybuf.
-template <int MT, int L>
+template <int MT, int OM, int L>
 __device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int ps, int rows, const float *psum,
                                               float *ybuf, const YOut &yo)
 {
@@ -688,9 +691,9 @@ __device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int p
             const float tot = ybuf[m * rows + r] + v;
             if (done) {
                 const uint64_t o = (uint64_t)m * yo.ldy + yo.n0 + r;
-                if (yo.yt == kArgmax)
+                if constexpr (OM == kArgmax)
                     atomicMax(yo.best + m, argmax_key(tot, (uint32_t)(yo.n0 + r)));
-                else if (yo.yt & kSwiglu)
+                else if constexpr (OM == kSwiglu)
                     ybuf[m * rows + r] = tot;
                 else if (yo.yt == VBQ_F16)
                     reinterpret_cast<__half *>(yo.y)[o] = __float2half_rn(tot);
@@ -703,15 +706,15 @@ __device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int p
     }
 }
 
-template <int MT>
+template <int MT, int OM>
 __device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps, int rows, const float *psum,
                                             float *ybuf, const YOut &yo)
 {
     switch (sum_lanes(G)) {
-    case 8: rowsum_item_l<MT, 8>(t, h, G, ps, rows, psum, ybuf, yo); break;
-    case 16: rowsum_item_l<MT, 16>(t, h, G, ps, rows, psum, ybuf, yo); break;
-    case 32: rowsum_item_l<MT, 32>(t, h, G, ps, rows, psum, ybuf, yo); break;
-    default: rowsum_item_l<MT, 64>(t, h, G, ps, rows, psum, ybuf, yo); break;
+    case 8: rowsum_item_l<MT, OM, 8>(t, h, G, ps, rows, psum, ybuf, yo); break;
+    case 16: rowsum_item_l<MT, OM, 16>(t, h, G, ps, rows, psum, ybuf, yo); break;
+    case 32: rowsum_item_l<MT, OM, 32>(t, h, G, ps, rows, psum, ybuf, yo); break;
+    default: rowsum_item_l<MT, OM, 64>(t, h, G, ps, rows, psum, ybuf, yo); break;
     }
 }
 
@@ -744,7 +747,7 @@ __device__ void argmax_finish(vbq_argmax_ws *ws, int tok0, const unsigned long l
     __hip_atomic_store(&ws->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MT>
+template <int MT, int OM>
 __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_line */)
 {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -860,7 +863,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
         if (k > 0) {
             const int nsum = sum_items((int)prev.nr, G);
             for (int t = (wave + kW - kCopyWaves) % kW; t < nsum; t += kW) // copying waves take the last shares
-                rowsum_item<MT>(t, prev, G, ps, rows, psum + (slot ^ 1) * (MT * ps), ybuf, yo);
+                rowsum_item<MT, OM>(t, prev, G, ps, rows, psum + (slot ^ 1) * (MT * ps), ybuf, yo);
         }
         if (h.next)
             wait_vm0(); // copy waves: the copy of tile k+1
@@ -873,17 +876,17 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     {
         const int nsum = sum_items((int)prev.nr, G);
         for (int t = (wave + kW - kCopyWaves) % kW; t < nsum; t += kW) // copying waves take the last shares
-            rowsum_item<MT>(t, prev, G, ps, rows, psum + (k & 1) * (MT * ps), ybuf, yo);
+            rowsum_item<MT, OM>(t, prev, G, ps, rows, psum + (k & 1) * (MT * ps), ybuf, yo);
     }
     // the warming copy lands in LDS: it must finish before the workgroup's LDS
     // is released (the other waves leave without waiting for their stores)
     if (wave < kCopyWaves && warm_bytes)
         wait_vm0();
-    if (yt == kArgmax) {
+    if constexpr (OM == kArgmax) {
         __syncthreads(); // every finished row's key is in best[]
         if (tid == 0)
             argmax_finish<MT>(reinterpret_cast<vbq_argmax_ws *>(yptr), ldy, best);
-    } else if (yt & kSwiglu) {
+    } else if constexpr (OM == kSwiglu) {
         __syncthreads(); // every row of the block is in ybuf
         const int pairs = R / 2; // R is even: the block starts at an even row and N is even
         for (int i = tid; i < MT * pairs; i += kT) {
@@ -891,7 +894,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
             const float g = ybuf[m * rows + 2 * p], u = ybuf[m * rows + 2 * p + 1];
             const float h = g / (1.0f + expf(-g)) * u; // silu(gate) * up
             const uint64_t o = (uint64_t)m * ldy + n0 / 2 + p;
-            if ((yt & 1) == VBQ_F16)
+            if (yt == VBQ_F16)
                 reinterpret_cast<__half *>(yptr)[o] = __float2half_rn(h);
             else
                 reinterpret_cast<float *>(yptr)[o] = h;
@@ -951,17 +954,30 @@ PrepArgs prep_args(const vbq_layout *L, const void *blob, const vbq_plan *P)
     return a;
 }
 
-template <int MT>
-vbq_status launch_plan(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
+template <int MT, int OM>
+vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
     static bool configured = false;
     if (!configured) {
         VBQ_TRY(hip_status(
-            hipFuncSetAttribute((const void *)k_gemv_plan<MT>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)));
+            hipFuncSetAttribute((const void *)k_gemv_plan<MT, OM>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)));
         configured = true;
     }
-    hipLaunchKernelGGL(k_gemv_plan<MT>, dim3(grid), dim3(kT), lds, stream, a);
+    hipLaunchKernelGGL((k_gemv_plan<MT, OM>), dim3(grid), dim3(kT), lds, stream, a);
     return launch_status();
+}
+
+// One launch of m (1 or 2) tokens in output mode om.
+vbq_status launch_plan(int m, int om, const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
+{
+    switch (om * 2 + (m - 1)) {
+    case 0: return launch_plan_t<1, kRows>(a, grid, lds, stream);
+    case 1: return launch_plan_t<2, kRows>(a, grid, lds, stream);
+    case 2: return launch_plan_t<1, kArgmax>(a, grid, lds, stream);
+    case 3: return launch_plan_t<2, kArgmax>(a, grid, lds, stream);
+    case 4: return launch_plan_t<1, kSwiglu>(a, grid, lds, stream);
+    default: return launch_plan_t<2, kSwiglu>(a, grid, lds, stream);
+    }
 }
 
 } // namespace
@@ -1165,7 +1181,7 @@ vbq_status planned_shared(const vbq_planned_item *items, int n, int M, const uin
             else
                 set_next(a, next, nnext);
             if (pass == 1)
-                VBQ_TRY(m == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream));
+                VBQ_TRY(launch_plan(m, kRows, a, grid, lds, stream));
         }
     return VBQ_OK;
 }
@@ -1229,9 +1245,8 @@ vbq_status vbq_gemv_planned_swiglu(const vbq_plan *P, const void *plan, int M, c
             set_next(a, nullptr, 0);
             a.rec[0].y = (uint8_t *)h + (uint64_t)t0 * (uint64_t)ldh * (uint64_t)esz;
             a.rec[0].ldy = ldh;
-            a.rec[0].g_yt_tb |= (uint32_t)kSwiglu << 16;
             if (pass == 1)
-                VBQ_TRY(m == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream));
+                VBQ_TRY(launch_plan(m, kSwiglu, a, grid, lds, stream));
         }
     return VBQ_OK;
 }
@@ -1260,9 +1275,8 @@ vbq_status vbq_gemv_planned_argmax(const vbq_plan *P, const void *plan, int M, c
             set_next(a, nullptr, 0);
             a.rec[0].y = ws;
             a.rec[0].ldy = t0;
-            a.rec[0].g_yt_tb = (a.rec[0].g_yt_tb & 0xff00ffffu) | ((uint32_t)kArgmax << 16);
             if (pass == 1)
-                VBQ_TRY(m == 1 ? launch_plan<1>(a, grid, lds, stream) : launch_plan<2>(a, grid, lds, stream));
+                VBQ_TRY(launch_plan(m, kArgmax, a, grid, lds, stream));
         }
     return VBQ_OK;
 }
