@@ -31,7 +31,7 @@ EXPORTS = (
     "vbq_workspace_size", "vbq_workspace_clear", "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_shared",
     "vbq_plan_init", "vbq_prepare", "vbq_gemv_planned", "vbq_gemv_planned_shared", "vbq_gemv_seq",
     "vbq_gemv_planned_seq", "vbq_dense_f16_gemv", "vbq_quantize", "vbq_gemv_planned_argmax",
-    "vbq_gemv_planned_swiglu",
+    "vbq_gemv_planned_swiglu", "vbq_gemm_plan_init", "vbq_gemm_prepare", "vbq_gemm_workspace", "vbq_gemm",
 )
 MAX_SHARED = 4
 
@@ -75,6 +75,16 @@ class PlannedSeqItem(ctypes.Structure):
     """Mirror of ``vbq_planned_seq_item``."""
     _fields_ = [("P", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("x", ctypes.c_void_p), ("ldx", ctypes.c_int),
                 ("y", ctypes.c_void_p), ("ldy", ctypes.c_int), ("stage", ctypes.c_int)]
+
+
+class GemmPlan(ctypes.Structure):
+    """Mirror of ``vbq_gemm_plan`` (host geometry of a GEMM plan)."""
+    _fields_ = [("magic", ctypes.c_uint32)] + \
+               [(n, ctypes.c_int32) for n in ("N", "K", "G", "nb", "kc", "max_tile", "slot_bytes")] + \
+               [("table_bytes", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 class Layout(ctypes.Structure):
@@ -127,6 +137,11 @@ def lib():
         L.vbq_gemv_seq.argtypes = [ctypes.POINTER(SeqItem), i, i, i, P, sz, P]
         L.vbq_gemv_planned_seq.argtypes = [ctypes.POINTER(PlannedSeqItem), i, i, i, P]
         L.vbq_dense_f16_gemv.argtypes = [i, i, i, P, P, i, P, i, i, P]
+        GP = ctypes.POINTER(GemmPlan)
+        L.vbq_gemm_plan_init.argtypes = [LP, P, GP, P, sz, P]
+        L.vbq_gemm_prepare.argtypes = [GP, LP, P, P, P]
+        L.vbq_gemm_workspace.argtypes = [GP, i, ctypes.POINTER(sz)]
+        L.vbq_gemm.argtypes = [GP, P, i, P, i, P, i, i, P, sz, P]
         for f in EXPORTS:
             if f not in ("vbq_version", "vbq_status_string", "vbq_last_error", "vbq_pack_plan_workspace"):
                 getattr(L, f).restype = i
@@ -496,6 +511,57 @@ def gemv_seq(items):
 def gemv_planned_seq(items):
     """Run one step over prepared plans: items of (P, plan, x, y, stage)."""
     Seq(items, planned=True).run()
+
+
+# -------------------------------------------------------------- prefill GEMM
+
+def gemm_plan_init(L: Layout, blob) -> GemmPlan:
+    """Geometry of the GEMM plan of (L, blob). Synchronizes."""
+    torch = _torch()
+    _need_cuda(blob)
+    ws = torch.empty(16, dtype=torch.uint8, device=blob.device)
+    GP = GemmPlan()
+    _check(lib().vbq_gemm_plan_init(ctypes.byref(L), _ptr(blob), ctypes.byref(GP), _ptr(ws), 16, _stream()),
+           "vbq_gemm_plan_init")
+    return GP
+
+
+def gemm_prepare(L: Layout, blob):
+    """GEMM plan of a packed matrix -> (plan u8 device tensor, GemmPlan)."""
+    GP = gemm_plan_init(L, blob)
+    buf = _empty_aligned(GP.total_bytes, blob.device)
+    _check(lib().vbq_gemm_prepare(ctypes.byref(GP), ctypes.byref(L), _ptr(blob), _ptr(buf), _stream()),
+           "vbq_gemm_prepare")
+    return buf, GP
+
+
+def gemm_workspace_size(GP: GemmPlan, M: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vbq_gemm_workspace(ctypes.byref(GP), M, ctypes.byref(n)), "vbq_gemm_workspace")
+    return n.value
+
+
+def gemm_workspace(GP: GemmPlan, M: int, device="cuda"):
+    """A workspace for vbq_gemm calls of up to M tokens (any contents)."""
+    return _empty_aligned(max(gemm_workspace_size(GP, M), 256), device)
+
+
+def gemm(GP: GemmPlan, buf, x, out=None, out_dtype=None, ws=None):
+    """Y[M][N] = X[M][K] W^T from a GEMM plan (the prefill path, M > 16)."""
+    torch = _torch()
+    _need_cuda(buf)
+    x2 = _as_2d(x)
+    M = x2.shape[0]
+    out_dtype = out_dtype or torch.float16
+    if out is None:
+        out = torch.empty((M, GP.N) if x.dim() == 2 else (GP.N,), dtype=out_dtype, device=x.device)
+    y2 = out.view(1, -1) if out.dim() == 1 else out
+    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    if ws is None:
+        ws = gemm_workspace(GP, M, x.device)
+    _check(lib().vbq_gemm(ctypes.byref(GP), _ptr(buf), M, _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), yt,
+                          _ptr(ws), ws.numel() * ws.element_size(), _stream()), "vbq_gemm")
+    return out
 
 
 def dense_f16_gemv(w16, x, out=None, out_dtype=None):

@@ -400,6 +400,84 @@ vbq_status vbq_gemv_planned_seq(const vbq_planned_seq_item *items /* host */, in
                                 hipStream_t stream);
 
 /*
+ * Prefill GEMM.  With many tokens (M > 16: a prompt's tokens, or a large
+ * batch) Y = X W^T is a dense contraction over K, unlike decode; this path
+ * runs it on the matrix cores.  Each 64-weight group keeps its own width from
+ * {1, 2, 4, 8} ("Variable Bit-width Quantization", mlsanity.com page,
+ * Abstract); a GEMM plan re-orders the blob once per matrix so that tiles of
+ * the weights can be dequantized to fp16 in LDS by wavefronts that each take
+ * groups of one width.
+ *
+ * GEMM plan buffer:
+ *   u32 offset table [nb * kc + 1]: tile (row block i, column chunk j) starts
+ *     at 16 * table[i * kc + j] bytes from the buffer start; entry nb * kc is
+ *     the end of the last tile; zeros up to table_bytes (a multiple of 256).
+ *   tiles, row-block major: rows 128 i .. 128 i + 127 (fewer in the last
+ *     block), columns 128 j .. 128 j + 127 (groups 2 j, 2 j + 1; one in the
+ *     last chunk of an odd G).  A tile is
+ *       16-byte header: u16 groups of width 8, 4, 2, 1; u32 tile bytes; u32
+ *         offset of the word section;
+ *       code records (8*b bytes each, copied verbatim from the blob) in slot
+ *         order: width 8, 4, 2, 1, then column, then row;
+ *       u32 per group in slot order: fp16 scale bits | (column * 128 + row) << 16
+ *         (column and row inside the tile);
+ *       zeros to a multiple of 16 bytes.
+ *   zeros: slot_bytes of padding after the last tile.
+ */
+#define VBQ_GEMM_PLAN_MAGIC 0x4D4D4756u
+
+typedef struct vbq_gemm_plan {
+    uint32_t magic;        /* VBQ_GEMM_PLAN_MAGIC */
+    int32_t N, K, G;       /* matrix shape (K <= 32768) */
+    int32_t nb, kc;        /* row blocks of 128 rows, column chunks of 128 columns */
+    int32_t max_tile;      /* bytes of the largest tile */
+    int32_t slot_bytes;    /* max_tile rounded up to 4 KiB (LDS slot of the GEMM kernel) */
+    uint64_t table_bytes;  /* bytes of the offset table (multiple of 256) */
+    uint64_t total_bytes;  /* plan buffer bytes */
+} vbq_gemm_plan;
+
+/*
+ * SYNC.  Fill *P for the matrix (L, blob): one sizing kernel over the width
+ * bit planes (workspace ws: device, >= 16 bytes, 8-byte aligned), then a wait.
+ * Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_WORKSPACE,
+ * VBQ_ERR_ALIGN (blob not 256-byte aligned), VBQ_ERR_SHAPE (K > 32768),
+ * VBQ_ERR_HIP.
+ */
+vbq_status vbq_gemm_plan_init(const vbq_layout *L /* host */, const void *blob, vbq_gemm_plan *P /* host */,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Write the GEMM plan of (L, blob) described by *P into buf (device,
+ * P->total_bytes, 256-byte aligned); every byte of buf is written.  The blob
+ * must be the one *P was sized for.  Errors: VBQ_ERR_INVALID_ARG,
+ * VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE (P does not match L), VBQ_ERR_ALIGN.
+ */
+vbq_status vbq_gemm_prepare(const vbq_gemm_plan *P /* host */, const vbq_layout *L /* host */, const void *blob,
+                            void *buf, hipStream_t stream);
+
+/* Workspace bytes vbq_gemm needs for M tokens on the current device. */
+vbq_status vbq_gemm_workspace(const vbq_gemm_plan *P /* host */, int M, size_t *bytes /* host */);
+
+/*
+ * Y = X W^T for M tokens (1 <= M <= 2^20; meant for M > 16, where the
+ * product is a dense contraction) from a GEMM plan: x fp16 [M][ldx] (ldx >= K,
+ * ldx % 8 == 0, x 16-byte aligned), y [M][ldy] (ldy >= N) in yt.  Each weight
+ * enters the matrix cores as fp16(s * (q - (2^b-1)/2)) (one rounding to
+ * nearest even), products accumulate in fp32, so
+ * |y - y_exact| <= 1e-3 * sum_k |w_k||x_k| + 2^-24 * sum_k |x_k| per output
+ * (the second term is the fp16 subnormal spacing; weights at or beyond the
+ * fp16 range give non-finite outputs).  The result does not depend on timing.
+ * ws: device, 256-byte aligned, >= vbq_gemm_workspace(P, M) bytes, any
+ * contents (it holds a copy of X and, where the rows alone do not fill the
+ * device, partial sums of K-splits); calls sharing a workspace must be
+ * ordered (one stream).  Two launches.  Errors: VBQ_ERR_INVALID_ARG,
+ * VBQ_ERR_LAYOUT, VBQ_ERR_BATCH, VBQ_ERR_SHAPE, VBQ_ERR_ALIGN,
+ * VBQ_ERR_WORKSPACE.
+ */
+vbq_status vbq_gemm(const vbq_gemm_plan *P /* host */, const void *buf, int M, const uint16_t *x, int ldx, void *y,
+                    int ldy, vbq_dtype yt, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Dense fp16 control at the same shapes: y[M][ldy] = W16 x with W16 fp16
  * [N][K] row-major (typically vbq_dequant(..., VBQ_F16)), fp32 accumulate.
  * K % 8 == 0, 1 <= M <= 16.

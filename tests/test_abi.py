@@ -328,3 +328,68 @@ def test_planned_argmax_argument_checks_fail_before_launch():
     bad = fake_plan(v)
     bad.magic = 0
     assert call(Pl=bad) == "VBQ_ERR_LAYOUT"
+
+
+def fake_gemm_plan(v, N=300, K=4096, max_tile=5000):
+    G = K // 64
+    nb, kc = (N + 127) // 128, (G + 1) // 2
+    table = (4 * (nb * kc + 1) + 255) // 256 * 256
+    slot = (max_tile + 4095) // 4096 * 4096
+    return v.GemmPlan(magic=0x4D4D4756, N=N, K=K, G=G, nb=nb, kc=kc, max_tile=max_tile, slot_bytes=slot,
+                      table_bytes=table, total_bytes=table + 100000 + slot)
+
+
+def test_gemm_argument_checks_fail_before_launch():
+    v = vbq()
+    lib = v.lib()
+    VP = ctypes.c_void_p
+    fake, null = VP(1 << 20), VP(0)
+    blob = oracle.pack(np.zeros((4, 4096), np.uint8), np.ones((4, 64), np.uint8), np.ones((4, 64), np.uint16))
+    L = v.layout_from_header(blob[:256].tobytes())
+    out = v.GemmPlan()
+
+    def init(blob=fake, ws=fake, wsb=16, lay=L):
+        return v.STATUS[lib.vbq_gemm_plan_init(ctypes.byref(lay), blob, ctypes.byref(out), ws, wsb, null)]
+
+    assert init(blob=null) == "VBQ_ERR_INVALID_ARG"
+    assert init(ws=null) == "VBQ_ERR_WORKSPACE"
+    assert init(wsb=8) == "VBQ_ERR_WORKSPACE"
+    assert init(blob=VP((1 << 20) + 64)) == "VBQ_ERR_ALIGN"
+    big = oracle.pack(np.zeros((1, 64 * 513), np.uint8), np.ones((1, 513), np.uint8), np.ones((1, 513), np.uint16))
+    assert init(lay=v.layout_from_header(big[:256].tobytes())) == "VBQ_ERR_SHAPE"  # K > 32768
+    bad = v.Layout.from_buffer_copy(bytes(L))
+    bad.version = 7
+    assert init(lay=bad) == "VBQ_ERR_LAYOUT"
+
+    GP = fake_gemm_plan(v)
+    n = ctypes.c_size_t(0)
+    assert v.STATUS[lib.vbq_gemm_workspace(ctypes.byref(GP), 0, ctypes.byref(n))] == "VBQ_ERR_BATCH"
+    assert v.STATUS[lib.vbq_gemm_workspace(ctypes.byref(GP), 64, ctypes.byref(n))] == "VBQ_OK"
+    # the copy of X in k-slot order at least (64 token rows of K halves)
+    assert n.value >= 64 * 4096 * 2
+    big_ws = n.value
+
+    def gemm(Pl=GP, buf=fake, M=64, x=fake, ldx=4096, y=fake, ldy=300, yt=1, ws=fake, wsb=big_ws):
+        return v.STATUS[lib.vbq_gemm(ctypes.byref(Pl), buf, M, x, ldx, y, ldy, yt, ws, wsb, null)]
+
+    assert gemm(M=0) == "VBQ_ERR_BATCH"
+    assert gemm(M=(1 << 20) + 1) == "VBQ_ERR_BATCH"
+    assert gemm(buf=null) == "VBQ_ERR_INVALID_ARG"
+    assert gemm(x=null) == "VBQ_ERR_INVALID_ARG"
+    assert gemm(ws=null) == "VBQ_ERR_INVALID_ARG"
+    assert gemm(yt=5) == "VBQ_ERR_INVALID_ARG"
+    assert gemm(ldx=4032) == "VBQ_ERR_SHAPE"
+    assert gemm(ldy=299) == "VBQ_ERR_SHAPE"
+    assert gemm(buf=VP((1 << 20) + 128)) == "VBQ_ERR_ALIGN"
+    assert gemm(x=VP((1 << 20) + 8)) == "VBQ_ERR_ALIGN"
+    assert gemm(ldx=4100) == "VBQ_ERR_ALIGN"          # rows of x 16-byte aligned
+    assert gemm(y=VP((1 << 20) + 2), yt=0) == "VBQ_ERR_ALIGN"
+    assert gemm(ws=VP((1 << 20) + 128)) == "VBQ_ERR_ALIGN"
+    assert gemm(wsb=big_ws - 1) == "VBQ_ERR_WORKSPACE"
+    for field, val in [("magic", 0), ("K", 4032), ("nb", 2), ("kc", 33), ("slot_bytes", 6000),
+                       ("slot_bytes", 6 * 4096), ("max_tile", 9000), ("table_bytes", 256), ("total_bytes", 1024)]:
+        badp = fake_gemm_plan(v)
+        setattr(badp, field, val)
+        assert gemm(Pl=badp) == "VBQ_ERR_LAYOUT", field
+    assert v.STATUS[lib.vbq_gemm_prepare(ctypes.byref(fake_gemm_plan(v, N=8)), ctypes.byref(L), fake, fake, null)] \
+        == "VBQ_ERR_SHAPE"
