@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+PEAK_F16 = 2.5e15  # MI355X dense fp16 matrix cores, flop/s
 
 
 def log(msg):
@@ -46,12 +47,17 @@ def parse(argv=None):
     ap.add_argument("--kernel-steps", type=int, default=5, help="replays of each per-kind kernel graph")
     ap.add_argument("--no-kinds", action="store_true",
                     help="skip the per-kind kernel timing (profiles then see only the step's own launches)")
-    ap.add_argument("--op", default="step", choices=["step", "quantize", "argmax", "swiglu"],
+    ap.add_argument("--op", default="step", choices=["step", "quantize", "argmax", "swiglu", "prefill"],
                     help="step: the decode step (the headline line); quantize: vbq_quantize of the 9B gate "
                          "projection's fp16 weights (14336x4096) with its width mix; argmax: the 9B LM head "
                          "(128256x4096) as vbq_gemv_planned_argmax against vbq_gemv_planned with fp16 logits; swiglu: "
                          "the 9B gate and up projections as one interleaved matrix with the SwiGLU epilogue "
-                         "against the shared two-output launch")
+                         "against the shared two-output launch; prefill: vbq_gemm (M > 16 tokens on the "
+                         "matrix cores) on the 28672x8192 up and 8192x28672 down projections of the batched "
+                         "workload against the fp16 GEMM of the dequantized weights")
+    ap.add_argument("--prefill-m", default="32,64,128,256,512,2048",
+                    help="token counts of the prefill sweep (the first of --prefill-head's is the line's value)")
+    ap.add_argument("--prefill-head", type=int, default=256, help="token count the prefill line reports")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
     return ap.parse_args(argv)
@@ -288,6 +294,95 @@ def bench_argmax(torch, v, args):
         "cpu_baseline": None}), flush=True)
 
 
+def bench_prefill(torch, v, args):
+    """Prefill GEMMs: the batched workload's 28672x8192 up and 8192x28672 down
+    projections (clustered widths, 1% outlier channels) for M tokens, as
+    vbq_gemm from GEMM plans against torch's fp16 GEMM (hipBLASLt) of the
+    dequantized weights.  Two copies of each matrix are used in turn so that
+    each call streams its weights from HBM; every path is replayed from a HIP
+    graph.  Roofline per M: the larger of the plan bytes at 8 TB/s and
+    2 M N K flops at the dense fp16 matrix-core peak."""
+    from decode_gemv_vbq_amd import workload as wl
+    from decode_gemv_vbq_amd import accounting as acc
+    wk = wl.workload("batched70b")
+    ms = sorted({int(m) for m in args.prefill_m.split(",")} | {args.prefill_head})
+    mats = []
+    for c in range(2):
+        for spec in wk.mats:
+            q, bits, s, _ = wl.draw_matrix_torch(wl.MatrixSpec(spec.name, spec.N, spec.K, spec.mix, c, spec.proj_id,
+                                                               spec.cluster), wk.wid, 1)
+            blob, L = v.pack(q, bits, s.view(torch.float16))
+            del q, bits, s
+            buf, GP = v.gemm_prepare(L, blob)
+            w16 = v.dequant(L, blob, torch.float16)
+            del blob
+            mats.append({"spec": spec, "L": L, "buf": buf, "GP": GP, "w16": w16})
+    torch.cuda.synchronize()
+    plan_bytes = sum(m["GP"].total_bytes for m in mats[:2])
+    alg_w = sum(acc.vbq_read_bytes(m["L"], 0) for m in mats[:2])
+    log(f"GEMM plans: {plan_bytes / 1e6:.1f} MB for up+down ({alg_w / 1e6:.1f} MB packed), "
+        f"slots {[m['GP'].slot_bytes for m in mats[:2]]}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    rows = []
+    for M in ms:
+        xs = {K: (torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32)).half()
+              for K in {m["spec"].K for m in mats}}
+        ws = v.gemm_workspace(mats[0]["GP"], M)
+        ws2 = v.gemm_workspace(mats[1]["GP"], M)
+        wsz = ws if ws.numel() >= ws2.numel() else ws2
+        outs = [torch.empty((M, m["spec"].N), dtype=torch.float16, device="cuda") for m in mats]
+
+        def run_vbq():
+            for m, o in zip(mats, outs):
+                v.gemm(m["GP"], m["buf"], xs[m["spec"].K], out=o, ws=wsz)
+
+        def run_f16():
+            for m, o in zip(mats, outs):
+                torch.mm(xs[m["spec"].K], m["w16"].t(), out=o)
+
+        res = {}
+        for name, fn in (("vbq", run_vbq), ("f16", run_f16)):
+            fn()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                fn()
+            for _ in range(2):
+                gr.replay()
+            res[name] = time_steps(torch, gr.replay, max(5, args.steps // 5)) / (len(mats) // 2) * 1e3
+        flops = sum(2.0 * M * m["spec"].N * m["spec"].K for m in mats[:2])
+        byts = alg_w + sum(2 * M * m["spec"].K + 2 * M * m["spec"].N for m in mats[:2])
+        t_mfma, t_hbm = flops / PEAK_F16, byts / PEAK_HBM
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        t = res["vbq"] * 1e-6
+        row = {"M": M, "us": round(res["vbq"], 2), "f16_us": round(res["f16"], 2),
+               "speedup_vs_f16": round(res["f16"] / res["vbq"], 3), "bound": bound,
+               "TFLOPs": round(flops / t / 1e12, 1), "GBps": round(byts / t / 1e9, 1),
+               "frac": round(max(t_mfma, t_hbm) / t, 4)}
+        rows.append(row)
+        log(f"M={M}: vbq_gemm {res['vbq']:.1f} us ({row['TFLOPs']} TFLOP/s, {row['GBps']} GB/s, "
+            f"{100 * row['frac']:.1f}% of the {bound} roof), fp16 GEMM {res['f16']:.1f} us, "
+            f"speedup {row['speedup_vs_f16']:.2f}x")
+        del xs, ws, ws2, wsz, outs
+    head = next(r for r in rows if r["M"] == args.prefill_head)
+    if head["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": head["TFLOPs"], "peak": PEAK_F16 / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": head["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof.update({"frac": round(roof["achieved"] / roof["peak"], 4), "traffic": None,
+                 "kernel": "k_xpair + k_gemm<MT> (vbq_gemm), whole calls"})
+    print(json.dumps({
+        "metric": f"us per prefill up+down GEMM pair (M={args.prefill_head} tokens)",
+        "value": head["us"], "unit": "us", "n_gpus": 1, "steps": max(5, args.steps // 5), "warmup": 2,
+        "higher_is_better": False, "dtype": "f16 x f16 -> f32 (matrix cores)", "data": "synthetic",
+        "vs_baseline": None,
+        "config": {"workload": "batched70b up 28672x8192 + down 8192x28672, clustered widths, M tokens",
+                   "M": args.prefill_head, "fp16_gemm_us": head["f16_us"], "speedup_vs_f16": head["speedup_vs_f16"],
+                   "plan_bytes": plan_bytes, "sweep": rows},
+        "roofline": roof, "cpu_baseline": None}), flush=True)
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -316,6 +411,9 @@ def main(argv=None):
         return
     if args.op == "swiglu":
         bench_swiglu(torch, v, args)
+        return
+    if args.op == "prefill":
+        bench_prefill(torch, v, args)
         return
 
     v.lib()

@@ -53,6 +53,39 @@ typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
 typedef _Float16 hf8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (m0 = lds_base, wave-uniform).  Written as asm so the compiler does not tie
+// later LDS reads to it with a vmcnt wait: completion is awaited explicitly
+// (wait_vm / wait_vm0) before the barrier that publishes the data.  The s_nop
+// separates the compiler's m0 write from the LDS-DMA load.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) for a run-time n (clamped: a smaller n only waits longer).
+__device__ __forceinline__ void wait_vm(int n)
+{
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    }
+}
+
 __device__ __forceinline__ uint32_t h2u(hf2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ hf2 u2h(uint32_t v) { return __builtin_bit_cast(hf2, v); }
 

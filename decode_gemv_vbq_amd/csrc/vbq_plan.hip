@@ -299,6 +299,23 @@ __global__ __launch_bounds__(kT) void k_prepare(PrepArgs a)
 // ---------------------------------------------------------------------------
 // The planned GEMV kernel.
 
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (m0 = lds_base, wave-uniform).  Written as asm so the compiler does not tie
+// later LDS reads to it; completion is awaited explicitly (wait_vm0) before the
+// barrier that publishes a tile.  The s_nop separates the m0 write from the load.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 // 64 bytes of the kernel-argument segment at byte offset `off` (a multiple of

@@ -113,6 +113,36 @@ __host__ __device__ inline SLayout s_layout(int MT, int G, int rows, int nS, int
     return l;
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (m0 = lds_base, wave-uniform).  Written as asm so the compiler does not tie
+// every later LDS read to it with a full vmcnt wait: completion is awaited
+// explicitly (wait_vm) before the barrier that publishes a sub-unit.  The
+// leading s_nop separates the compiler's m0 write from the LDS-DMA load.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a run-time n (clamped: a smaller n only waits longer).
+__device__ __forceinline__ void wait_vm(int n)
+{
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    }
+}
+
 // Inclusive prefix sum over the 64 lanes (DPP row shifts and row broadcasts).
 __device__ __forceinline__ int scan64(int v)
 {
