@@ -56,7 +56,7 @@ def parse(argv=None):
                          "matrix cores) on the 28672x8192 up and 8192x28672 down projections of the batched "
                          "workload against the fp16 GEMM of the dequantized weights")
     ap.add_argument("--prefill-m", default="32,64,128,256,512,2048",
-                    help="token counts of the prefill sweep (the first of --prefill-head's is the line's value)")
+                    help="token counts of the prefill sweep (the JSON line reports the one --prefill-head names)")
     ap.add_argument("--prefill-head", type=int, default=256, help="token count the prefill line reports")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
