@@ -503,7 +503,6 @@ def main(argv=None):
             "workload": args.workload, "M": 1, "gemvs_per_step": len(step.mats), "launches_per_step": n_launch,
             "launch": args.mode, "path": args.path,
             "plan_bytes_per_step": step.plan_bytes() if step.planned else None,
-            "warm_bytes_per_step": step.warm_bytes() if step.planned else None,
             "weights": step.weights(), "mean_bits": round(step.mean_bits(), 4),
             "alg_bytes_per_step": alg, "layout_bytes_per_step": step.layout_bytes(),
             "GBps_step": round(gbps, 1), "pct_peak_step": round(100 * gbps * 1e9 / PEAK_HBM, 2),

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libvbq.so")
 
 VBQ_F32, VBQ_F16 = 0, 1
 #: device status-word bits (include/vbq.h VBQ_STATUS_*)
-STATUS_BITS, STATUS_CODES, STATUS_LAYOUT = 0x1, 0x2, 0x4
+STATUS_BITS, STATUS_CODES, STATUS_LAYOUT, STATUS_PLAN = 0x1, 0x2, 0x4, 0x8
 
 STATUS = {
     0: "VBQ_OK", 1: "VBQ_ERR_INVALID_ARG", 2: "VBQ_ERR_SHAPE", 3: "VBQ_ERR_BATCH", 4: "VBQ_ERR_BITS",
@@ -52,8 +52,8 @@ class GemvItem(ctypes.Structure):
 class Plan(ctypes.Structure):
     """Mirror of ``vbq_plan`` (host geometry of a prepared plan)."""
     _fields_ = [("magic", ctypes.c_uint32)] + \
-               [(n, ctypes.c_int32) for n in ("N", "K", "G", "M", "wgs", "rows", "tile_bytes", "tiles", "first_bytes",
-                                               "psum", "lds_bytes")] + \
+               [(n, ctypes.c_int32) for n in ("N", "K", "G", "M", "wgs", "rows", "passes", "per_wave", "psum",
+                                               "lds_bytes", "reserved")] + \
                [("region_bytes", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
 
     def as_dict(self) -> dict:
@@ -129,7 +129,7 @@ def lib():
         L.vbq_gemv_shared.argtypes = [ctypes.POINTER(GemvItem), i, i, P, i, i, P]
         PP = ctypes.POINTER(Plan)
         L.vbq_plan_init.argtypes = [LP, P, i, i, PP, P, sz, P]
-        L.vbq_prepare.argtypes = [PP, LP, P, P, P]
+        L.vbq_prepare.argtypes = [PP, LP, P, P, P, P]
         L.vbq_gemv_planned.argtypes = [PP, P, i, P, i, P, i, i, P]
         L.vbq_gemv_planned_shared.argtypes = [ctypes.POINTER(PlannedItem), i, i, P, i, i, P]
         L.vbq_gemv_planned_argmax.argtypes = [PP, P, i, P, i, P, P]
@@ -363,11 +363,17 @@ def plan_init(L: Layout, blob, M: int = 1, wgs: int = 0) -> Plan:
     return P
 
 
-def prepare(L: Layout, blob, M: int = 1, wgs: int = 0):
-    """Prepared plan of a packed matrix -> (plan u8 device tensor, Plan)."""
+def prepare(L: Layout, blob, M: int = 1, wgs: int = 0, check: bool = True):
+    """Prepared plan of a packed matrix -> (plan u8 device tensor, Plan).
+    With ``check`` the device status word is read back (synchronizes)."""
+    torch = _torch()
     P = plan_init(L, blob, M, wgs)
     plan = _empty_aligned(P.total_bytes, blob.device)
-    _check(lib().vbq_prepare(ctypes.byref(P), ctypes.byref(L), _ptr(blob), _ptr(plan), _stream()), "vbq_prepare")
+    status = torch.empty(1, dtype=torch.int32, device=blob.device)
+    _check(lib().vbq_prepare(ctypes.byref(P), ctypes.byref(L), _ptr(blob), _ptr(plan), _ptr(status), _stream()),
+           "vbq_prepare")
+    if check:
+        status_check(status)
     return plan, P
 
 

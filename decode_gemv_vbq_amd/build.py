@@ -6,6 +6,7 @@
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -26,25 +27,45 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def command(out: str, extra=()):
-    return (["hipcc", "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-             "-Wall", "-Wno-unused-function"] + DEVICE_FLAGS + list(extra) + ["-o", out] + sources())
+OBJDIR = os.path.join(ROOT, "_build")
+
+
+def compile_command(src: str, obj: str, extra=()):
+    return (["hipcc", "-O3", "-std=c++17", "-fPIC", "-c", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+             "-Wall", "-Wno-unused-function"] + DEVICE_FLAGS + list(extra) + ["-o", obj, src])
 
 
 def build(asm_dir: str | None = None, verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+    """Compile every source to an object (in parallel), then link libvbq.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
     extra = []
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
-        extra = ["-save-temps"]
-    cmd = command(tmp, extra)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    cwd = asm_dir or None
-    if asm_dir:
-        # -save-temps writes the intermediates into the working directory
-        cmd = [c for c in cmd]
-    subprocess.check_call(cmd, cwd=cwd)
+        extra = ["-save-temps"]  # writes the intermediates into the working directory
+    jobs = []
+    for src in sources():
+        obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
+        jobs.append((compile_command(src, obj, extra), obj))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        futs = []
+        for cmd, _ in jobs:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            futs.append(ex.submit(subprocess.run, cmd, cwd=asm_dir or None, capture_output=True, text=True))
+        failed = []
+        for (cmd, _), f in zip(jobs, futs):
+            r = f.result()
+            if r.returncode != 0:
+                failed.append(r.stderr)
+            elif verbose and r.stderr:
+                print(r.stderr, file=sys.stderr)
+    if failed:
+        sys.stderr.write("\n".join(failed))
+        raise subprocess.CalledProcessError(1, "hipcc")
+    tmp = LIB + ".tmp"
+    link = ["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + [o for _, o in jobs]
+    subprocess.check_call(link)
     os.replace(tmp, LIB)
     return LIB
 

@@ -360,6 +360,8 @@ vbq_status vbq_status_check(const uint32_t *status_word, uint32_t *raw, hipStrea
         return VBQ_ERR_CODE_RANGE;
     if (v & VBQ_STATUS_LAYOUT)
         return VBQ_ERR_LAYOUT;
+    if (v & VBQ_STATUS_PLAN)
+        return VBQ_ERR_SHAPE;
     return VBQ_OK;
 }
 

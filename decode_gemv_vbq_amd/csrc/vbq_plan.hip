@@ -3,38 +3,39 @@
 //
 // The method ("Variable Bit-width Quantization", mlsanity.com page, Abstract)
 // gives every contiguous group of 64 weights its own width in {1,2,4,8}, and
-// decode multiplies the packed codes without materialising the weights.  The
-// VBQ1 blob stores groups row by row, bucketed by width inside each 32-group
-// slice.  A wavefront must run 64 groups of ONE width at a time, so a kernel
-// reading VBQ1 directly has to plan each tile at run time (find every group
-// of each width, assign it a slot) before it can compute.  A plan moves that
-// work to a preparation step that runs once per matrix:
+// decode, which is bound by memory bandwidth, multiplies the packed codes
+// without materialising the weights.  A wavefront must run groups of ONE
+// width at a time; the VBQ1 blob stores groups row by row, so a kernel that
+// reads it directly has to sort every tile by width at run time.  A plan does
+// that sort once per matrix, and lays the result out so that the GEMV never
+// waits for metadata before it can fetch weights:
 //
-//  * The rows are split into row blocks, one per workgroup of the GEMV launch.
-//    Each block owns a fixed-size region of the plan buffer holding tiles at
-//    a fixed stride.  Tile t takes the groups (row-major order over the
-//    block) whose running byte count starts in [t*C, (t+1)*C), so a row may
-//    continue in the next tile.
-//  * Inside a tile, groups are sorted by (width 8,4,2,1; group column; row).
-//    The tile stores a 64-byte header, the code records in that order
-//    (verbatim 8*b bytes each, so each width section starts aligned to its
-//    record size), and one 32-bit word per group: its fp16 scale and the
-//    group's position e = column * rows_in_tile + row_in_tile.
-//  * Each header carries the byte size of the next tile, and the plan carries
-//    the largest first tile, so the kernel issues every copy without first
-//    reading metadata.
+//  * The rows are split into row blocks, one per workgroup of the GEMV
+//    launch; block b owns a region of the plan buffer at a fixed stride.
+//  * A block's groups are sorted by (width 1,2,4,8; column; row) and cut into
+//    PASSES of 1 KiB of codes: 128 one-bit groups, 64 two-bit, 32 four-bit or
+//    16 eight-bit groups.  Every pass record has the same size (1536 bytes:
+//    the codes, then one 32-bit word per group: fp16 scale | position << 16,
+//    position = column * stride + row), so the address of pass p is
+//    region + 1536 p and a wavefront can issue its loads before it knows
+//    anything else about the pass.
+//  * After the passes, one byte per pass gives its width (0: no pass), laid
+//    out wave-major for the 16 wavefronts of the GEMV workgroup.
 //
-// The GEMV kernel: one 1024-thread workgroup per row block.  As soon as the
-// kernel starts, half of the workgroup copies tile 0 into LDS with
-// global_load_lds_dwordx4 while the other half stages the activations.  Tile
-// k+1 is copied by two waves into the other half of a two-slot ring while the
-// other waves run the passes of tile k, handed out through an LDS counter;
-// then every wave sums the rows of tile k-1.  One barrier per tile.  A pass is
-// 64 slots of one width: codes are contiguous per lane, x is read per group
-// column (lanes of a column broadcast), partials land at e (contiguous per
-// column).  Row sums follow the column order and the tile order, so the
-// result does not depend on timing.
+// The GEMV kernel: one 1024-thread workgroup per row block; wavefront w takes
+// passes w, w+16, w+32, ... and keeps the next three of them in flight from
+// HBM straight into registers while it computes one (16 bytes of codes and 8
+// bytes of words per lane, the same two loads for every width).  Lane l holds
+// groups 2l and 2l+1 of a one-bit pass, group l of a two-bit pass, half of
+// group l/2 of a four-bit pass, a quarter of group l/4 of an eight-bit pass.
+// The activations are staged once per workgroup as records of fp16 pairs
+// (x_p, x_{p+32}) and per-width corrections; each group's dot products land
+// as one fp32 partial at its position in LDS.  Two barriers per launch (the
+// records are ready; every partial is written), then the rows are summed in
+// a fixed order, so the result does not depend on timing.
 #include <algorithm>
+#include <mutex>
+#include <set>
 
 #include "vbq_common.h"
 #include "vbq_host.h"
@@ -46,20 +47,23 @@ namespace {
 
 constexpr int kT = 1024; // threads per workgroup (prepare and GEMV kernels)
 constexpr int kW = kT / 64;
-constexpr int kHdr = 64;    // tile header bytes
-constexpr int kXRec = 36;   // dwords of x per group: 32 pairs (x_p, x_{p+32}) + 4 constants
-constexpr int kMaxG = 512;  // groups per row the plans support (K <= 32768)
-constexpr int kMaxTiles = 1024; // tiles per row block
+constexpr int kPassBytes = 1536; // one pass record
+constexpr int kCodeArea = 1024;  // its code bytes: 16 per lane
+constexpr int kXRec = 36;        // dwords of x per group: 32 pairs (x_p, x_{p+32}) + 4 constants
+constexpr int kMaxG = 512;       // groups per row the plans support (K <= 32768)
+constexpr int kMaxPerWave = 256; // width bytes per wavefront (passes <= 16 * 255)
 constexpr int kMaxMats = VBQ_MAX_SHARED;
-constexpr int kMaxTb = 64 * 1024; // tile stride bound (16-bit positions)
-constexpr int kCopyWaves = 2;     // waves of the GEMV workgroup that copy the next tile
+constexpr uint32_t kLdsBudget = 160u * 1024u;
 
-// Usable bytes per tile before the last group's overhang: a group starting
-// below C ends at most 68 bytes later, and the header takes 64.
-__host__ __device__ constexpr uint32_t tile_cut(uint32_t tb) { return tb - kHdr - 68u; }
+__host__ __device__ constexpr int groups_per_pass(int c) { return 128 >> c; } // c = log2(width)
 
-// Bytes a group of width code c occupies in a tile: code record + scale/position word.
-__device__ __forceinline__ uint32_t group_bytes(int c) { return (8u << c) + 4u; }
+// Position stride of a block: position = column * stride + row.  At least 2,
+// so that the column is always a 32-bit reciprocal multiply away.
+__host__ __device__ constexpr int pos_stride(int rows) { return rows < 2 ? 2 : rows; }
+
+// Partial sums per token in LDS: every position of the widest block plus one
+// slot that the empty places of a partly filled pass write to.
+__host__ __device__ constexpr int psum_stride(int G, int stride) { return (stride * G + 1 + 3) & ~3; }
 
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scan of one value per thread (kT threads).
@@ -103,29 +107,23 @@ struct PrepArgs {
     const uint8_t *blob;
     uint64_t off_row_off, off_slice_off, off_wmap, off_scales, off_codes;
     int N, G, nS, rows;
-    uint32_t tb;     // tile stride
-    uint64_t region; // bytes per block region
-    uint8_t *plan;   // null: sizing only
-    uint32_t *sizes; // sizing: [0] max tiles, [1] max first-tile bytes, [2] blocks over kMaxTiles
+    int passes;       // pass records per block region (fill)
+    int per_wave;     // width bytes per wavefront (fill)
+    uint64_t region;  // bytes per block region
+    uint8_t *plan;    // null: sizing only
+    uint32_t *sizes;  // sizing: [0] the largest block's pass count
+    uint32_t *status; // fill (may be null): VBQ_STATUS_PLAN when a block needs more passes than `passes`
 };
 
-// LDS of the preparation kernel.
-struct PrepShared {
-    uint32_t tmp[kW + 1];
-    uint32_t sizes[kT];                // group sizes of the current chunk
-    uint32_t carry, prev_size, ntiles;
-    uint32_t tstart[kMaxTiles + 1];    // first group of each tile
-    uint32_t tcum[kMaxTiles + 1];      // running byte count at each tile start
-    uint32_t hist[4 * kMaxG];          // per (section, column): count, then first slot
-};
-
-// One workgroup per row block: tile boundaries from a running byte count over
-// the block's groups in row-major order; then (plan != null) each tile is
-// written: groups counted per (width, column), given slots in (width 8,4,2,1;
-// column; row) order, and their code records, scales and positions copied.
+// One workgroup per row block.  Groups are counted per (width, column); an
+// exclusive scan in (width 1,2,4,8; column) order gives each bucket its first
+// slot, and inside a bucket the rows follow in order.  Slot s of width c is
+// group s % groups_per_pass(c) of pass P_c + s / groups_per_pass(c), where
+// the passes of the narrower widths come first.
 __global__ __launch_bounds__(kT) void k_prepare(PrepArgs a)
 {
-    __shared__ PrepShared sh;
+    __shared__ uint32_t tmp[kW + 1];
+    __shared__ uint32_t hist[4 * kMaxG]; // per (width, column): count, then first slot
     const int tid = threadIdx.x;
     const int n0 = (int)blockIdx.x * a.rows;
     if (n0 >= a.N)
@@ -133,190 +131,111 @@ __global__ __launch_bounds__(kT) void k_prepare(PrepArgs a)
     const int R = min(a.rows, a.N - n0);
     const int G = a.G;
     const uint32_t NG = (uint32_t)R * (uint32_t)G;
-    const uint32_t C = tile_cut(a.tb);
     const uint32_t *wmap = reinterpret_cast<const uint32_t *>(a.blob + a.off_wmap);
-    if (tid == 0) {
-        sh.carry = 0;
-        sh.prev_size = 0;
-        sh.ntiles = 0;
+    for (int k = tid; k < 4 * G; k += kT)
+        hist[k] = 0;
+    __syncthreads();
+    for (uint32_t i = (uint32_t)tid; i < NG; i += kT) {
+        const int r = (int)(i / (uint32_t)G), g = (int)(i - (uint32_t)r * G);
+        atomicAdd(&hist[vbq1_width(wmap, a.nS, n0 + r, g) * G + g], 1u);
     }
     __syncthreads();
-    // ---- tile boundaries: group i starts tile t = floor(start_i / C) when the
-    // previous group started in an earlier tile
-    for (uint32_t base = 0; base < NG; base += kT) {
-        const uint32_t i = base + (uint32_t)tid;
-        uint32_t s = 0;
-        if (i < NG) {
-            const int r = (int)(i / (uint32_t)G), g = (int)(i - (uint32_t)r * G);
-            s = group_bytes(vbq1_width(wmap, a.nS, n0 + r, g));
+    {
+        uint32_t carry = 0;
+        for (int base = 0; base < 4 * G; base += kT) {
+            const int k = base + tid;
+            const uint32_t v = k < 4 * G ? hist[k] : 0u;
+            uint32_t tot;
+            const uint32_t ex = block_excl_scan(v, tmp, tot);
+            if (k < 4 * G)
+                hist[k] = carry + ex;
+            carry += tot;
+            __syncthreads();
         }
-        sh.sizes[tid] = s;
-        const uint32_t carry = sh.carry, prev_size = sh.prev_size;
-        uint32_t total;
-        const uint32_t ex = block_excl_scan(s, sh.tmp, total); // (its barriers publish sizes[])
-        if (i < NG) {
-            const uint32_t start = carry + ex;
-            const uint32_t t = start / C;
-            const uint32_t sp = tid ? sh.sizes[tid - 1] : prev_size; // size of group i-1
-            if (i == 0 || (start - sp) / C < t) {
-                if (t < (uint32_t)kMaxTiles) {
-                    sh.tstart[t] = i;
-                    sh.tcum[t] = start;
-                }
-                atomicMax(&sh.ntiles, t + 1);
-            }
-        }
-        __syncthreads();
-        if (tid == 0) {
-            sh.carry = carry + total;
-            const uint32_t last = min(NG - base, (uint32_t)kT) - 1;
-            sh.prev_size = sh.sizes[last];
-        }
-        __syncthreads();
     }
-    const uint32_t total_bytes = sh.carry;
-    const uint32_t ntiles = sh.ntiles;
-    if (ntiles > (uint32_t)kMaxTiles) {
-        if (tid == 0 && a.sizes)
-            atomicAdd(a.sizes + 2, 1u);
-        return;
-    }
-    if (tid == 0) {
-        sh.tstart[ntiles] = NG;
-        sh.tcum[ntiles] = total_bytes;
-    }
-    __syncthreads();
+    uint32_t S[5], P0[5]; // first slot and first pass of each width
+    for (int c = 0; c < 4; c++)
+        S[c] = hist[c * G];
+    S[4] = NG;
+    P0[0] = 0;
+    for (int c = 0; c < 4; c++)
+        P0[c + 1] = P0[c] + (S[c + 1] - S[c] + groups_per_pass(c) - 1) / groups_per_pass(c);
+    const uint32_t npass = P0[4];
     if (!a.plan) {
-        if (tid == 0) {
-            atomicMax(a.sizes, ntiles);
-            atomicMax(a.sizes + 1, (uint32_t)kHdr + sh.tcum[1] - sh.tcum[0]);
-        }
+        if (tid == 0)
+            atomicMax(a.sizes, npass);
         return;
     }
-    // ---- tiles
+    if (npass > (uint32_t)a.passes) { // the plan was sized for other widths: write nothing
+        if (tid == 0 && a.status)
+            atomicOr(a.status, VBQ_STATUS_PLAN);
+        return;
+    }
+    uint8_t *region = a.plan + (uint64_t)blockIdx.x * a.region;
+    const int stride = pos_stride(a.rows);
+    const uint32_t dummy = (uint32_t)(stride * G) << 16; // scale 0 at the spare position
+    // the empty places of each width's last pass: zero codes, the spare position
+    for (int c = 0; c < 4; c++) {
+        const int per = groups_per_pass(c);
+        const int used = (int)((S[c + 1] - S[c]) % (uint32_t)per);
+        if (!used)
+            continue;
+        uint8_t *rec = region + (uint64_t)(P0[c + 1] - 1) * kPassBytes;
+        for (int k = used + tid; k < per; k += kT) {
+            uint32_t *d32 = reinterpret_cast<uint32_t *>(rec + k * (8 << c));
+            for (int d = 0; d < (2 << c); d++)
+                d32[d] = 0u;
+            reinterpret_cast<uint32_t *>(rec + kCodeArea)[k] = dummy;
+        }
+    }
+    // the groups: thread g walks column g's rows, so each bucket's rows follow in order
     const uint32_t *rowoff = reinterpret_cast<const uint32_t *>(a.blob + a.off_row_off);
     const uint32_t *sloff = reinterpret_cast<const uint32_t *>(a.blob + a.off_slice_off);
     const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.blob + a.off_scales);
     const uint8_t *codes = a.blob + a.off_codes;
-    uint8_t *region = a.plan + (uint64_t)blockIdx.x * a.region;
-    for (uint32_t t = 0; t < ntiles; t++) {
-        const uint32_t i0 = sh.tstart[t], i1 = sh.tstart[t + 1];
-        const int ra = (int)(i0 / (uint32_t)G), rb = (int)((i1 - 1) / (uint32_t)G);
-        const int NR = rb - ra + 1;
-        for (int k = tid; k < 4 * G; k += kT)
-            sh.hist[k] = 0;
-        __syncthreads();
-        for (uint32_t i = i0 + (uint32_t)tid; i < i1; i += kT) {
-            const int r = (int)(i / (uint32_t)G), g = (int)(i - (uint32_t)r * G);
-            const int c = vbq1_width(wmap, a.nS, n0 + r, g);
-            atomicAdd(&sh.hist[(3 - c) * G + g], 1u); // sections 8,4,2,1
+    for (int g = tid; g < G; g += kT) {
+        uint32_t run[4] = {0, 0, 0, 0};
+        for (int r = 0; r < R; r++) {
+            const int nn = n0 + r;
+            const uint64_t rs = (uint64_t)nn * a.nS + (g >> 5);
+            const uint32_t p0 = wmap[2 * rs], p1 = wmap[2 * rs + 1];
+            const WidthMasks wm = width_masks(p0, p1, min(32, G - 32 * (g >> 5)));
+            const int c = width_code(p0, p1, g & 31);
+            const uint32_t s = hist[c * G + g] - pick4(S, c) + pick4(run, c);
+            run[0] += c == 0;
+            run[1] += c == 1;
+            run[2] += c == 2;
+            run[3] += c == 3;
+            const uint32_t per = (uint32_t)groups_per_pass(c);
+            uint8_t *rec = region + (uint64_t)(pick4(P0, c) + s / per) * kPassBytes;
+            const uint32_t k = s % per;
+            const uint64_t src = (uint64_t)rowoff[nn] * kRowPad + sloff[rs] + group_offset_in_slice(wm, c, g & 31);
+            const uint32_t *s32 = reinterpret_cast<const uint32_t *>(codes + src);
+            uint32_t *d32 = reinterpret_cast<uint32_t *>(rec + k * (8u << c));
+            for (int d = 0; d < (2 << c); d++)
+                d32[d] = s32[d];
+            const uint32_t e = (uint32_t)g * (uint32_t)stride + (uint32_t)r;
+            reinterpret_cast<uint32_t *>(rec + kCodeArea)[k] = (uint32_t)scales[(uint64_t)nn * G + g] | (e << 16);
         }
-        __syncthreads();
-        // exclusive prefix over (section, column): first slot of each bucket
-        {
-            uint32_t carry = 0;
-            for (int base = 0; base < 4 * G; base += kT) {
-                const int k = base + tid;
-                const uint32_t v = k < 4 * G ? sh.hist[k] : 0u;
-                uint32_t tot;
-                const uint32_t ex = block_excl_scan(v, sh.tmp, tot);
-                if (k < 4 * G)
-                    sh.hist[k] = carry + ex;
-                carry += tot;
-                __syncthreads();
-            }
-        }
-        uint8_t *tile = region + (uint64_t)t * a.tb;
-        const uint32_t n = i1 - i0;
-        uint32_t wb[4]; // first slot of sections 8,4,2,1
-        wb[0] = 0;
-        wb[1] = sh.hist[G];
-        wb[2] = sh.hist[2 * G];
-        wb[3] = sh.hist[3 * G];
-        uint32_t cnt[4];
-        cnt[0] = wb[1];
-        cnt[1] = wb[2] - wb[1];
-        cnt[2] = wb[3] - wb[2];
-        cnt[3] = n - wb[3];
-        uint32_t off[4]; // byte offset of each section's first record
-        off[0] = kHdr;
-        off[1] = off[0] + 64u * cnt[0];
-        off[2] = off[1] + 32u * cnt[1];
-        off[3] = off[2] + 16u * cnt[2];
-        const uint32_t se_off = off[3] + 8u * cnt[3];
-        // thread g walks column g's rows in order: bucket ranks follow the row
-        for (int g = tid; g < G; g += kT) {
-            uint32_t run[4] = {0, 0, 0, 0};
-            for (int r = ra; r <= rb; r++) {
-                const uint32_t i = (uint32_t)r * G + g;
-                if (i < i0 || i >= i1)
-                    continue;
-                const int nn = n0 + r;
-                const uint64_t rs = (uint64_t)nn * a.nS + (g >> 5);
-                const uint32_t p0 = wmap[2 * rs], p1 = wmap[2 * rs + 1];
-                const WidthMasks wm = width_masks(p0, p1, min(32, G - 32 * (g >> 5)));
-                const int c = width_code(p0, p1, g & 31);
-                const int sec = 3 - c;
-                const uint32_t rk = pick4(run, sec);
-                run[0] += sec == 0;
-                run[1] += sec == 1;
-                run[2] += sec == 2;
-                run[3] += sec == 3;
-                const uint32_t slot = sh.hist[sec * G + g] + rk;
-                const uint64_t src = (uint64_t)rowoff[nn] * kRowPad + sloff[rs] + group_offset_in_slice(wm, c, g & 31);
-                const uint32_t dst = pick4(off, sec) + (slot - pick4(wb, sec)) * (8u << c);
-                const uint32_t *s32 = reinterpret_cast<const uint32_t *>(codes + src);
-                uint32_t *d32 = reinterpret_cast<uint32_t *>(tile + dst);
-                for (int d = 0; d < (2 << c); d++)
-                    d32[d] = s32[d];
-                const uint32_t e = (uint32_t)g * (uint32_t)NR + (uint32_t)(r - ra);
-                reinterpret_cast<uint32_t *>(tile + se_off)[slot] = (uint32_t)scales[(uint64_t)nn * G + g] | (e << 16);
-            }
-        }
-        if (tid == 0) {
-            uint32_t *h = reinterpret_cast<uint32_t *>(tile);
-            h[0] = cnt[0];
-            h[1] = cnt[1];
-            h[2] = cnt[2];
-            h[3] = cnt[3];
-            h[4] = (uint32_t)ra;
-            h[5] = (uint32_t)NR;
-            h[6] = i0 - (uint32_t)ra * G;         // first column of row ra in this tile
-            h[7] = i1 - 1 - (uint32_t)rb * G + 1; // one past the last column of row rb
-            h[8] = NR == 1 ? 0u : (uint32_t)((0x100000000ull + (uint64_t)NR - 1) / (uint64_t)NR);
-            h[9] = t + 1 < ntiles ? (uint32_t)kHdr + sh.tcum[t + 2] - sh.tcum[t + 1] : 0u; // next tile's bytes
-            h[10] = n;
-            h[11] = se_off;
-            h[12] = se_off + 4u * n; // this tile's bytes
-            h[13] = t;
-            h[14] = ntiles;
-            h[15] = VBQ_PLAN_MAGIC;
-        }
-        __syncthreads();
+    }
+    // width bytes, wave-major: pass w + 16 j at byte w * per_wave + j
+    uint8_t *meta = region + (uint64_t)a.passes * kPassBytes;
+    for (int i = tid; i < kW * a.per_wave; i += kT) {
+        const int w = i / a.per_wave, j = i - w * a.per_wave;
+        const uint32_t p = (uint32_t)(w + kW * j);
+        uint8_t v = 0;
+        if (p < npass)
+            v = (uint8_t)(1 + (p >= P0[1]) + (p >= P0[2]) + (p >= P0[3]));
+        meta[i] = v;
     }
 }
 
 // ---------------------------------------------------------------------------
 // The planned GEMV kernel.
 
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
-}
-
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
-// (m0 = lds_base, wave-uniform).  Written as asm so the compiler does not tie
-// later LDS reads to it; completion is awaited explicitly (wait_vm0) before the
-// barrier that publishes a tile.  The s_nop separates the m0 write from the load.
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
-{
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
-}
-
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 64 bytes of the kernel-argument segment at byte offset `off` (a multiple of
 // 64) in one scalar load; the wait is inside the asm block, so no load is
@@ -336,18 +255,6 @@ __device__ __forceinline__ const void *u64_ptr(uint32_t lo, uint32_t hi)
     return (const void *)(((uint64_t)hi << 32) | lo);
 }
 
-// Copy `bytes` from global memory to LDS in 1 KiB chunks (16 bytes per lane,
-// the tail masked per 16 bytes): this wave issues chunks first, first + step, ...
-__device__ __forceinline__ void copy_chunks(const uint8_t *src, uint32_t dst, uint32_t bytes, int first, int step)
-{
-    const uint32_t lane16 = (threadIdx.x & 63) * 16u;
-    for (uint32_t j = (uint32_t)first; j * 1024u < bytes; j += (uint32_t)step) {
-        const uint32_t off = j * 1024u + lane16;
-        if (off < bytes)
-            dma16(src + off, dst + j * 1024u);
-    }
-}
-
 // Kernel arguments.  The argument segment is read from memory at every
 // launch and is not kept in the caches between launches, so each round of
 // dependent argument loads costs a full memory round trip before a workgroup
@@ -355,30 +262,30 @@ __device__ __forceinline__ void copy_chunks(const uint8_t *src, uint32_t dst, ui
 // record, picked by blockIdx.y (the matrix of a shared launch), which it reads
 // with a single scalar load.  Launch-wide fields are repeated in every record.
 struct PRec {
-    const uint8_t *plan;  // this matrix's plan
-    void *y;              // its outputs (this launch's first token)
-    const uint16_t *x;    // activations (this launch's first token)
-    uint32_t region;      // bytes per row block of the plan
+    const uint8_t *plan; // this matrix's plan
+    void *y;             // its outputs (this launch's first token)
+    const uint16_t *x;   // activations (this launch's first token)
+    uint32_t region;     // bytes per row block of the plan
     int32_t N, ldy, rows; // rows per block of this matrix
     int32_t ldx;
-    uint32_t first;       // bytes of tile 0 to copy (launch-wide maximum)
-    int32_t ps;           // partial sums per token per ring slot (launch-wide)
-    int32_t rows_max;     // output staging stride in LDS (launch-wide)
-    uint32_t g_yt_tb;     // G | yt << 16 | (tile stride / 1 KiB) << 24
-    int32_t wgs;          // row blocks of this matrix (workgroups with blockIdx.x < wgs work)
+    int32_t passes;      // pass records per block region
+    int32_t per_wave;    // width bytes per wavefront
+    uint32_t g_yt;       // G | yt << 16 (launch-wide)
+    int32_t wgs;         // row blocks of this matrix (workgroups with blockIdx.x < wgs work)
+    int32_t smax;        // largest position stride of the launch's plans (LDS carve-up)
 };
 static_assert(sizeof(PRec) == 64, "one record is one 64-byte line");
 
-// The launch that follows on the stream: where each of its workgroups starts
-// reading.  Plans do not depend on the activations, so a workgroup of this
-// launch fetches, during its last tile, the first tile of the workgroup with
-// the same linear index there, which then finds it in the caches instead of
-// waiting for HBM.  Read once, late, by the copying waves.
+// The launch that follows on the stream.  Plans do not depend on the
+// activations, so wavefront w of a workgroup of this launch fetches pass w of
+// the row block that the workgroup with the same linear index works on in the
+// next launch, which then finds it in the memory-side cache instead of
+// waiting for HBM.  Read once, after the activations are staged.
 struct PWarm {
     const uint8_t *plan[kMaxMats]; // null: no such matrix
     uint32_t region[kMaxMats];     // bytes per row block
-    uint16_t first16[kMaxMats];    // bytes of tile 0 / 16
     uint16_t wgs[kMaxMats];        // row blocks
+    uint16_t passes[kMaxMats];     // pass records per block
 };
 static_assert(sizeof(PWarm) == 64, "the warming line is one 64-byte line");
 
@@ -388,7 +295,7 @@ struct PArgs {
 };
 
 struct PLayout {
-    uint32_t x, ring, psum, ybuf, ctr, best, total;
+    uint32_t x, psum, ybuf, best, warm, total;
 };
 
 __host__ __device__ inline uint32_t p_take(uint32_t &o, uint32_t bytes)
@@ -398,17 +305,18 @@ __host__ __device__ inline uint32_t p_take(uint32_t &o, uint32_t bytes)
     return r;
 }
 
-// LDS carve-up, computed identically on the host (size) and the device.
-__host__ __device__ inline PLayout p_layout(int MT, int G, int rows, int tb, int ps)
+// LDS carve-up, computed identically on the host (size) and the device.  One
+// x record more than the tokens need: the spare position of a partly filled
+// pass decodes to column G and reads it (its result is never used).
+__host__ __device__ inline PLayout p_layout(int MT, int G, int smax)
 {
     PLayout l;
     uint32_t o = 0;
-    l.x = p_take(o, (uint32_t)(MT * G * kXRec * 4));
-    l.ring = p_take(o, 2u * (uint32_t)tb);
-    l.psum = p_take(o, 2u * (uint32_t)(MT * ps) * 4u);
-    l.ybuf = p_take(o, (uint32_t)(MT * rows) * 4u);
-    l.ctr = p_take(o, 2u * 4u); // pass counters of the two ring slots
+    l.x = p_take(o, (uint32_t)((MT * G + 1) * kXRec * 4));
+    l.psum = p_take(o, (uint32_t)(MT * psum_stride(G, smax)) * 4u);
+    l.ybuf = p_take(o, (uint32_t)(MT * smax) * 4u);
     l.best = p_take(o, 2u * 8u); // argmax output: the best (value, row) key per token
+    l.warm = p_take(o, 1024u);   // landing place of the warming copies (never read)
     l.total = o;
     return l;
 }
@@ -418,49 +326,43 @@ __host__ __device__ inline PLayout p_layout(int MT, int G, int rows, int tb, int
 // then the negated corrections -C_b for the widths 1, 2, 4, 8, where
 // C_b = sum_p 2^(10-pos_b(p)) (x_p + x_{p+32}) + (2^b-1)/2 sum_j x_j.
 // Item = (token, group, quarter q): pairs 4q..4q+3; the 8 items of a group are
-// 8 adjacent lanes.  Loads and stores are separate so the loads go out with
-// the first tile's copy.
-// Prologue split: the first kCT threads copy tile 0 (a few waves issue the
-// whole LDS-DMA copy), the other kXT threads stage x, which is the longer of
-// the two (every workgroup reads the same activations, and each quarter-group
-// item costs about 50 VALU instructions).
-constexpr int kCT = 4 * 64;
-constexpr int kXT = kT - kCT;
-
-template <int MT>
+// 8 adjacent lanes.  Loads and stores are separate so that the loads go out
+// before the first passes' loads and the wait for them leaves those in flight.
+// KP items per thread: MT * G * 8 items rounded up to a power of two over the
+// workgroup (chosen per launch, so that no more loads are issued than needed).
+template <int KP>
 struct XRegs {
-    static constexpr int kPer = (MT * kMaxG * 8 + kXT - 1) / kXT;
-    uint32_t lo0[kPer], lo1[kPer], hi0[kPer], hi1[kPer];
+    static constexpr int kPer = KP;
+    uint32_t lo0[KP], lo1[KP], hi0[KP], hi1[KP];
 };
 
-template <int MT>
-__device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<MT> &xs)
+template <int MT, int KP>
+__device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<KP> &xs)
 {
-    const int tid = threadIdx.x - kCT;
+    // x is 8-byte aligned and ldx a multiple of 4 (checked on the host): two
+    // 8-byte buffer loads per item.  Every load is issued (a thread past the
+    // last item re-reads another item and zeroes it), and a compiler barrier
+    // keeps them ahead of the pass loads, so the wait for them is exact and
+    // leaves those in flight.
+    const int tid = threadIdx.x;
     const int items = MT * G * 8;
-    const bool vec = (ldx % 4) == 0 && ((uintptr_t)x % 8) == 0;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)x, 0, (int)(((MT - 1) * (uint32_t)ldx + 64u * (uint32_t)G) * 2u), 0x00020000);
 #pragma unroll
-    for (int k = 0; k < XRegs<MT>::kPer; k++) {
-        const int i = tid + k * kXT;
-        xs.lo0[k] = xs.lo1[k] = xs.hi0[k] = xs.hi1[k] = 0u;
-        if (i < items) {
-            const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
-            const uint16_t *p = x + (uint64_t)m * ldx + 64ull * g + 4 * q;
-            if (vec) {
-                const uint2 va = *reinterpret_cast<const uint2 *>(p);
-                const uint2 vb = *reinterpret_cast<const uint2 *>(p + 32);
-                xs.lo0[k] = va.x;
-                xs.lo1[k] = va.y;
-                xs.hi0[k] = vb.x;
-                xs.hi1[k] = vb.y;
-            } else {
-                xs.lo0[k] = p[0] | ((uint32_t)p[1] << 16);
-                xs.lo1[k] = p[2] | ((uint32_t)p[3] << 16);
-                xs.hi0[k] = p[32] | ((uint32_t)p[33] << 16);
-                xs.hi1[k] = p[34] | ((uint32_t)p[35] << 16);
-            }
-        }
+    for (int k = 0; k < KP; k++) {
+        const int i = tid + k * kT;
+        const bool act = i < items;
+        const int ii = act ? i : i % items;
+        const int q = ii & 7, g = (ii >> 3) % G, m = (ii >> 3) / G;
+        const int off = (m * ldx + 64 * g + 4 * q) * 2;
+        const u32x2 va = __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0);
+        const u32x2 vb = __builtin_amdgcn_raw_buffer_load_b64(xr, off + 64, 0, 0);
+        xs.lo0[k] = act ? va.x : 0u;
+        xs.lo1[k] = act ? va.y : 0u;
+        xs.hi0[k] = act ? vb.x : 0u;
+        xs.hi1[k] = act ? vb.y : 0u;
     }
+    asm volatile("" ::: "memory");
 }
 
 // v from another lane of the same DPP row (ctrl: a DPP control code).
@@ -491,14 +393,14 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
-template <int MT>
-__device__ __forceinline__ void x_store(int G, const XRegs<MT> &xs, uint32_t *xrec)
+template <int MT, int KP>
+__device__ __forceinline__ void x_store(int G, const XRegs<KP> &xs, uint32_t *xrec)
 {
-    const int tid = threadIdx.x - kCT;
+    const int tid = threadIdx.x;
     const int items = MT * G * 8;
 #pragma unroll
-    for (int k = 0; k < XRegs<MT>::kPer; k++) {
-        const int i = tid + k * kXT;
+    for (int k = 0; k < KP; k++) {
+        const int i = tid + k * kT;
         if (i >= items) // whole groups of 8 lanes drop out together
             break;
         const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
@@ -531,110 +433,156 @@ __device__ __forceinline__ void x_store(int G, const XRegs<MT> &xs, uint32_t *xr
     }
 }
 
-// Header fields of one tile, kept in registers.
-struct Tile {
-    uint32_t cnt[4]; // groups per section (widths 8,4,2,1)
-    uint32_t ra, nr, g_first, g_end, inv_nr, next, n, se_off;
+// One pass in flight: this lane's 16 code bytes and 8 word bytes.
+struct PBuf {
+    u32x4 c;
+    u32x2 w;
 };
 
-// One lane reads the header (48 bytes instead of 3 KiB of LDS traffic per
-// wave) and the fields are broadcast to the wave.  (Reading it from memory
-// through the scalar cache instead would share the lgkmcnt counter with the
-// passes' LDS reads and make them wait for that load.)
-__device__ __forceinline__ Tile read_tile(const uint8_t *t)
-{
-    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a, c = a;
-    if ((threadIdx.x & 63) == 0) {
-        a = *reinterpret_cast<const uint4 *>(t);
-        b = *reinterpret_cast<const uint4 *>(t + 16);
-        c = *reinterpret_cast<const uint4 *>(t + 32);
-    }
-#define VBQ_BCAST(v) v = (uint32_t)__builtin_amdgcn_readfirstlane((int)v)
-    VBQ_BCAST(a.x); VBQ_BCAST(a.y); VBQ_BCAST(a.z); VBQ_BCAST(a.w);
-    VBQ_BCAST(b.x); VBQ_BCAST(b.y); VBQ_BCAST(b.z); VBQ_BCAST(b.w);
-    VBQ_BCAST(c.x); VBQ_BCAST(c.y); VBQ_BCAST(c.z); VBQ_BCAST(c.w);
-#undef VBQ_BCAST
-    Tile h;
-    h.cnt[0] = a.x;
-    h.cnt[1] = a.y;
-    h.cnt[2] = a.z;
-    h.cnt[3] = a.w;
-    h.ra = b.x;
-    h.nr = b.y;
-    h.g_first = b.z;
-    h.g_end = b.w;
-    h.inv_nr = c.x;
-    h.next = c.y;
-    h.n = c.z;
-    h.se_off = c.w;
-    return h;
-}
+// What the pass bodies share.
+struct PCtx {
+    const uint32_t *xrec;
+    float *psum;
+    int G, ps;
+    uint32_t inv; // ceil(2^32 / stride): column = umulhi(position, inv)
+};
 
-// One pass: slots j = 64 * q + lane of the section of width B.
-template <int B, int MT>
-__device__ __forceinline__ void plan_pass(int q, uint32_t cnt, uint32_t wb, uint32_t code_off, const uint8_t *tile,
-                                          const Tile &h, int G, int ps, const uint32_t *xrec, float *psum)
+// Dot products of NP pairs of one group (its pairs p0 .. p0 + NP - 1) with
+// every token's x record of column `col`: two fp32 chains, the first starting
+// from the group's -C_b when this lane carries the correction.
+template <int C, int NP, int MT>
+__device__ __forceinline__ void dot_pairs(const uint32_t *hp, int p0, bool corr, uint32_t col, const PCtx &cx,
+                                          float *acc)
 {
-    constexpr int C = B == 1 ? 0 : B == 2 ? 1 : B == 4 ? 2 : 3;
-    const uint32_t j = 64u * (uint32_t)q + (threadIdx.x & 63);
-    if (j >= cnt)
-        return;
-    const uint32_t se = reinterpret_cast<const uint32_t *>(tile + h.se_off)[wb + j];
-    uint32_t w[2 * B];
-    const U2 *src = reinterpret_cast<const U2 *>(tile + code_off + j * (8u * B));
-#pragma unroll
-    for (int k = 0; k < B; k++) {
-        const U2 v = src[k];
-        w[2 * k] = v.v[0];
-        w[2 * k + 1] = v.v[1];
-    }
-    uint32_t hp[32];
-    unpack_pairs<B>(w, hp);
-    const uint32_t e = se >> 16;
-    const uint32_t xcol = h.nr == 1 ? e : __umulhi(e, h.inv_nr);
-    const float s = __half2float(__ushort_as_half((uint16_t)(se & 0xffffu)));
 #pragma unroll
     for (int m = 0; m < MT; m++) {
-        const uint32_t *xr = xrec + ((uint32_t)m * G + xcol) * kXRec;
-        // two chains, the first starting from -C_b: pairs 0..15, then 16..31
-        float acc0 = __uint_as_float(xr[32 + C]), acc1 = 0.f;
+        const uint32_t *xr = cx.xrec + ((uint32_t)m * cx.G + col) * kXRec;
+        const float c0 = __uint_as_float(xr[32 + C]);
+        float a0 = corr ? c0 : 0.f, a1 = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const U4 xa = *reinterpret_cast<const U4 *>(xr + 4 * k);
+        for (int k = 0; k < NP / 4; k++) {
+            const U4 xa = *reinterpret_cast<const U4 *>(xr + p0 + 4 * k);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                if (k < 4)
-                    acc0 = dot2(hp[4 * k + t], xa.v[t], acc0);
+                if (k < NP / 8)
+                    a0 = dot2(hp[4 * k + t], xa.v[t], a0);
                 else
-                    acc1 = dot2(hp[4 * k + t], xa.v[t], acc1);
+                    a1 = dot2(hp[4 * k + t], xa.v[t], a1);
             }
         }
-        psum[m * ps + e] = s * (acc0 + acc1);
+        acc[m] = a0 + a1;
     }
 }
 
-// Lanes that sum one row: more for longer rows, so that a tile's row sums
-// stay short next to its passes (a row of G partials is G / lanes loads deep).
+__device__ __forceinline__ float scale_of(uint32_t se) { return __half2float(__ushort_as_half((uint16_t)(se & 0xffffu))); }
+
+// One-bit pass: this lane's groups 2l and 2l+1 (8 code bytes and one word each).
+template <int MT>
+__device__ __forceinline__ void pass_b1(const PBuf &b, const PCtx &cx)
+{
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const uint32_t w[2] = {b.c[2 * h], b.c[2 * h + 1]};
+        uint32_t hp[32];
+        unpack_pairs<1>(w, hp);
+        const uint32_t se = b.w[h], e = se >> 16;
+        float acc[MT];
+        dot_pairs<0, 32, MT>(hp, 0, true, __umulhi(e, cx.inv), cx, acc);
+        const float s = scale_of(se);
+#pragma unroll
+        for (int m = 0; m < MT; m++)
+            cx.psum[m * cx.ps + e] = s * acc[m];
+    }
+}
+
+// The word of group (lane >> SH) of a pass: lane (lane >> (SH + 1)) loaded
+// words 2i and 2i+1 of the word area.
+template <int SH>
+__device__ __forceinline__ uint32_t word_of(const PBuf &b)
+{
+    const int lane = threadIdx.x & 63;
+    const int src = lane >> (SH + 1);
+    const uint32_t a = (uint32_t)__shfl((int)b.w[0], src, 64), c = (uint32_t)__shfl((int)b.w[1], src, 64);
+    return ((lane >> SH) & 1) ? c : a;
+}
+
+// Two-bit pass: group l (16 code bytes).
+template <int MT>
+__device__ __forceinline__ void pass_b2(const PBuf &b, const PCtx &cx)
+{
+    const uint32_t se = word_of<0>(b), e = se >> 16;
+    const uint32_t w[4] = {b.c[0], b.c[1], b.c[2], b.c[3]};
+    uint32_t hp[32];
+    unpack_pairs<2>(w, hp);
+    float acc[MT];
+    dot_pairs<1, 32, MT>(hp, 0, true, __umulhi(e, cx.inv), cx, acc);
+    const float s = scale_of(se);
+#pragma unroll
+    for (int m = 0; m < MT; m++)
+        cx.psum[m * cx.ps + e] = s * acc[m];
+}
+
+// Four-bit pass: half h = l & 1 of group l >> 1 (its words 4h..4h+3, pairs
+// 16h..16h+15); the two lanes' sums are added, the even lane writes.
+template <int MT>
+__device__ __forceinline__ void pass_b4(const PBuf &b, const PCtx &cx)
+{
+    const int lane = threadIdx.x & 63, h = lane & 1;
+    const uint32_t se = word_of<1>(b), e = se >> 16;
+    const uint32_t w[4] = {b.c[0], b.c[1], b.c[2], b.c[3]};
+    uint32_t hp[16];
+    unpack_words<4, 4>(w, hp);
+    float acc[MT];
+    dot_pairs<2, 16, MT>(hp, 16 * h, h == 0, __umulhi(e, cx.inv), cx, acc);
+    const float s = scale_of(se);
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+        const float v = acc[m] + dpp_f<0xB1>(acc[m]); // quad_perm [1, 0, 3, 2]
+        if (h == 0)
+            cx.psum[m * cx.ps + e] = s * v;
+    }
+}
+
+// Eight-bit pass: quarter q = l & 3 of group l >> 2 (its words 4q..4q+3,
+// pairs 8q..8q+7); the four lanes' sums are added in a fixed order, the first
+// lane writes.
+template <int MT>
+__device__ __forceinline__ void pass_b8(const PBuf &b, const PCtx &cx)
+{
+    const int lane = threadIdx.x & 63, q = lane & 3;
+    const uint32_t se = word_of<2>(b), e = se >> 16;
+    const uint32_t w[4] = {b.c[0], b.c[1], b.c[2], b.c[3]};
+    uint32_t hp[8];
+    unpack_words<8, 4>(w, hp);
+    float acc[MT];
+    dot_pairs<3, 8, MT>(hp, 8 * q, q == 0, __umulhi(e, cx.inv), cx, acc);
+    const float s = scale_of(se);
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+        float v = acc[m] + dpp_f<0xB1>(acc[m]); // quad_perm [1, 0, 3, 2]
+        v += dpp_f<0x4E>(v);                    // quad_perm [2, 3, 0, 1]
+        if (q == 0)
+            cx.psum[m * cx.ps + e] = s * v;
+    }
+}
+
+// Lanes that sum one row: more for longer rows, so that the row sums stay
+// short (a row of G partials is G / lanes loads deep).
 __device__ __forceinline__ int sum_lanes(int G) { return G > 256 ? 64 : G > 128 ? 32 : G > 64 ? 16 : 8; }
 
-// Row-sum items of a tile with nr rows.
-__device__ __forceinline__ int sum_items(int nr, int G) { return (nr * sum_lanes(G) + 63) / 64; }
-
-// Where finished rows go.
 // Output modes, a template parameter of the kernel (a plain GEMV carries no
 // code of the others).  kRows: finished rows are stored as fp32 or fp16 (yt).
 // kArgmax: instead of storing rows, keep per token the largest (value,
 // smallest row) as one 64-bit key in LDS (see argmax_key).  kSwiglu: rows 2i
-// and 2i+1 are the gate and up rows of output i; finished rows stay in the
-// LDS staging and the workgroup writes silu(gate) * up (type yt) for its
-// pairs at the end.
+// and 2i+1 are the gate and up rows of output i; row sums stay in LDS and the
+// workgroup writes silu(gate) * up (type yt) for its pairs at the end.
 constexpr int kRows = 0;
 constexpr int kArgmax = 1;
 constexpr int kSwiglu = 2;
 
 struct YOut {
     void *y;
-    int ldy, n0, yt;
+    int ldy, n0, yt, smax;
     unsigned long long *best; // LDS, [MT] keys (kArgmax)
 };
 
@@ -649,72 +597,60 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t row)
     return ((unsigned long long)ord << 32) | (unsigned long long)(~row);
 }
 
-// Row-sum item t of a tile: rows (64 / L) t .. of the tile, L = sum_lanes(G)
-// lanes per row.  The partials of row j sit at column * nr + j for the tile's
-// columns of that row; lane q sums columns q, q + L, ... (four interleaved
-// chains), the L lanes combine in a fixed order (group_sum), and the row's sum from
-// earlier tiles (ybuf, tiles in order) is added.  A row that ends in this
-// tile is written to y; only a row that continues into the next tile stays in
-// ybuf.
+// Row-sum item t: rows (64 / L) t .. of the block, L lanes per row.  The
+// partials of row j sit at column * stride + j; lane q sums columns q, q + L,
+// ... (four interleaved chains) and the L lanes combine in a fixed order
+// (group_sum).
 template <int MT, int OM, int L>
-__device__ __forceinline__ void rowsum_item_l(int t, const Tile &h, int G, int ps, int rows, const float *psum,
-                                              float *ybuf, const YOut &yo)
+__device__ __forceinline__ void rowsum_item_l(int t, int R, int stride, int G, int ps, const float *psum, float *ybuf,
+                                              const YOut &yo)
 {
     const int lane = threadIdx.x & 63;
     constexpr int per = 64 / L;
     const int j = per * t + lane / L, q = lane & (L - 1);
-    const int nr = (int)h.nr;
-    const int lo = j == 0 ? (int)h.g_first : 0, hi = j == nr - 1 ? (int)h.g_end : G;
-    const bool done = j < nr - 1 || (int)h.g_end == G || h.next == 0;
 #pragma unroll
     for (int m = 0; m < MT; m++) {
         float v = 0.f;
-        if (j < nr) {
+        if (j < R) {
             const float *p = psum + m * ps + j;
             float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-            int g = lo + q;
-            const int step = L * nr; // column g + L of the row sits L * nr further
-            const float *pg = p + g * nr;
-            for (; g + 3 * L < hi; g += 4 * L, pg += 4 * step) {
+            int g = q;
+            const int step = L * stride; // column g + L of the row sits L * stride further
+            const float *pg = p + g * stride;
+            for (; g + 3 * L < G; g += 4 * L, pg += 4 * step) {
                 a0 += pg[0];
                 a1 += pg[step];
                 a2 += pg[2 * step];
                 a3 += pg[3 * step];
             }
-            for (; g < hi; g += L, pg += step)
+            for (; g < G; g += L, pg += step)
                 a0 += pg[0];
             v = (a0 + a1) + (a2 + a3);
         }
         v = group_sum<L>(v);
-        if (q == 0 && j < nr) {
-            const int r = (int)h.ra + j;
-            const float tot = ybuf[m * rows + r] + v;
-            if (done) {
-                const uint64_t o = (uint64_t)m * yo.ldy + yo.n0 + r;
-                if constexpr (OM == kArgmax)
-                    atomicMax(yo.best + m, argmax_key(tot, (uint32_t)(yo.n0 + r)));
-                else if constexpr (OM == kSwiglu)
-                    ybuf[m * rows + r] = tot;
-                else if (yo.yt == VBQ_F16)
-                    reinterpret_cast<__half *>(yo.y)[o] = __float2half_rn(tot);
-                else
-                    reinterpret_cast<float *>(yo.y)[o] = tot;
-            } else {
-                ybuf[m * rows + r] = tot;
-            }
+        if (q == 0 && j < R) {
+            const uint64_t o = (uint64_t)m * yo.ldy + yo.n0 + j;
+            if constexpr (OM == kArgmax)
+                atomicMax(yo.best + m, argmax_key(v, (uint32_t)(yo.n0 + j)));
+            else if constexpr (OM == kSwiglu)
+                ybuf[m * yo.smax + j] = v;
+            else if (yo.yt == VBQ_F16)
+                reinterpret_cast<__half *>(yo.y)[o] = __float2half_rn(v);
+            else
+                reinterpret_cast<float *>(yo.y)[o] = v;
         }
     }
 }
 
 template <int MT, int OM>
-__device__ __forceinline__ void rowsum_item(int t, const Tile &h, int G, int ps, int rows, const float *psum,
-                                            float *ybuf, const YOut &yo)
+__device__ __forceinline__ void rowsum_item(int t, int R, int stride, int G, int ps, const float *psum, float *ybuf,
+                                            const YOut &yo)
 {
     switch (sum_lanes(G)) {
-    case 8: rowsum_item_l<MT, OM, 8>(t, h, G, ps, rows, psum, ybuf, yo); break;
-    case 16: rowsum_item_l<MT, OM, 16>(t, h, G, ps, rows, psum, ybuf, yo); break;
-    case 32: rowsum_item_l<MT, OM, 32>(t, h, G, ps, rows, psum, ybuf, yo); break;
-    default: rowsum_item_l<MT, OM, 64>(t, h, G, ps, rows, psum, ybuf, yo); break;
+    case 8: rowsum_item_l<MT, OM, 8>(t, R, stride, G, ps, psum, ybuf, yo); break;
+    case 16: rowsum_item_l<MT, OM, 16>(t, R, stride, G, ps, psum, ybuf, yo); break;
+    case 32: rowsum_item_l<MT, OM, 32>(t, R, stride, G, ps, psum, ybuf, yo); break;
+    default: rowsum_item_l<MT, OM, 64>(t, R, stride, G, ps, psum, ybuf, yo); break;
     }
 }
 
@@ -747,143 +683,156 @@ __device__ void argmax_finish(vbq_argmax_ws *ws, int tok0, const unsigned long l
     __hip_atomic_store(&ws->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MT, int OM>
+constexpr int kDepth = 3; // passes in flight per wavefront besides the one computed
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (m0 = lds_base, wave-uniform).  Only the warming copy uses it: its data is
+// never read, and its completion is awaited (s_waitcnt vmcnt(0)) before the
+// workgroup's LDS is released.  The s_nop separates the m0 write from the load.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// Wavefront w fetches pass w (or the block's last) of the next launch's
+// counterpart row block: 1 KiB of codes and the 512-byte word area.
+__device__ __forceinline__ void warm_next(int wave, uint32_t lds_base)
+{
+    const u32x16 w = kernarg_line((uint32_t)(kMaxMats * sizeof(PRec)));
+    uint32_t gx = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxMats; i++)
+        gx = max(gx, w[12 + i / 2] >> (16 * (i & 1)) & 0xffffu);
+    if (!gx)
+        return;
+    const uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const uint32_t bx = lin % gx, by = lin / gx;
+    const uint8_t *src = nullptr;
+#pragma unroll
+    for (int i = 0; i < kMaxMats; i++) {
+        const uint32_t wgs_i = w[12 + i / 2] >> (16 * (i & 1)) & 0xffffu;
+        const uint32_t passes_i = w[14 + i / 2] >> (16 * (i & 1)) & 0xffffu;
+        const uint8_t *p_i = (const uint8_t *)u64_ptr(w[2 * i], w[2 * i + 1]);
+        if (by == (uint32_t)i && bx < wgs_i && p_i != nullptr && passes_i > 0)
+            src = p_i + (uint64_t)bx * w[8 + i] + (uint64_t)min((uint32_t)wave, passes_i - 1) * kPassBytes;
+    }
+    if (!src)
+        return;
+    const int lane = threadIdx.x & 63;
+    dma16(src + lane * 16, lds_base);
+    if (lane < 32)
+        dma16(src + kCodeArea + lane * 16, lds_base);
+}
+
+template <int MT, int OM, int KP>
 __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_line */)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // this workgroup's record (matrix blockIdx.y of the launch), in one load
     const u32x16 a = kernarg_line((uint32_t)blockIdx.y * (uint32_t)sizeof(PRec));
-    if ((int)blockIdx.x >= (int)a[15])
+    if ((int)blockIdx.x >= (int)a[14])
         return; // the launch spans the largest matrix; a smaller one has fewer blocks
     const uint8_t *plan = (const uint8_t *)u64_ptr(a[0], a[1]);
     void *const yptr = (void *)u64_ptr(a[2], a[3]);
     const uint16_t *xptr = (const uint16_t *)u64_ptr(a[4], a[5]);
     const uint32_t region_bytes = a[6];
-    const int Nm = (int)a[7], ldy = (int)a[8], mrows = (int)a[9], ldx = (int)a[10];
-    const uint32_t first = a[11];
-    const int ps = (int)a[12], rows = (int)a[13];
-    const int G = (int)(a[14] & 0xffffu), yt = (int)((a[14] >> 16) & 0xffu);
-    const uint32_t tb = (a[14] >> 24) * 1024u;
+    const int Nm = (int)a[7], ldy = (int)a[8], rows = (int)a[9], ldx = (int)a[10];
+    const int passes = (int)a[11], per_wave = (int)a[12];
+    const int G = (int)(a[13] & 0xffffu), yt = (int)(a[13] >> 16);
+    const int smax = (int)a[15];
     const int blk = (int)blockIdx.x;
-    const int n0 = blk * mrows;
-    const int R = min(mrows, Nm - n0);
-    const PLayout L = p_layout(MT, G, rows, (int)tb, ps);
+    const int n0 = blk * rows;
+    const int R = min(rows, Nm - n0);
+    const int stride = pos_stride(rows);
+    const PLayout L = p_layout(MT, G, smax);
+    const int ps = psum_stride(G, smax);
     uint32_t *xrec = reinterpret_cast<uint32_t *>(smem + L.x);
     float *psum = reinterpret_cast<float *>(smem + L.psum);
     float *ybuf = reinterpret_cast<float *>(smem + L.ybuf);
-    const uint8_t *region = plan + (uint64_t)blk * region_bytes;
-    const uint32_t ring = lds_addr(smem + L.ring);
     unsigned long long *best = reinterpret_cast<unsigned long long *>(smem + L.best);
-    const YOut yo{yptr, ldy, n0, yt, best};
-    const uint8_t *warm = nullptr; // set by the copying waves before the last tile's phase
-    uint32_t warm_bytes = 0;
+    const YOut yo{yptr, ldy, n0, yt, smax, best};
+    // the block's region as a buffer resource: pass p's loads are an SGPR
+    // offset (1536 p) away from the same per-lane offsets
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(plan + (uint64_t)blk * region_bytes), 0, (int)region_bytes, 0x00020000);
+    const int voff_c = lane * 16, voff_w = kCodeArea + lane * 8;
+    const int pmax = passes - 1;
 
-    // ---- tile 0 (copied by the first kCT threads) and the activations
-    // (staged by the others), in flight together; each side waits only for
-    // its own loads
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + L.ctr);
-    if (tid < kCT) {
-        copy_chunks(region, ring, first, wave, kCT / 64);
-        for (int i = tid; i < MT * R; i += kCT)
-            ybuf[(i / R) * rows + i % R] = 0.f;
-        if (tid == 0)
-            cnt[0] = 0u;
-        if (tid < MT)
-            best[tid] = 0ull;
-        wait_vm0();
-    } else {
-        XRegs<MT> xs;
-        x_load<MT>(xptr, ldx, G, xs);
-        x_store<MT>(G, xs, xrec);
-    }
+    // width bytes of this wavefront's passes (lane i < per_wave / 4: passes
+    // 4i..4i+3 of the wave; the other lanes hold zeros)
+    const bool own = lane < (per_wave >> 2);
+    const uint32_t meta_raw =
+        __builtin_amdgcn_raw_buffer_load_b32(rs, own ? lane * 4 : 0, passes * kPassBytes + wave * per_wave, 0);
+    const uint32_t meta = own ? meta_raw : 0u;
+    // activations: their loads go out first, so that waiting for them leaves
+    // the pass loads below in flight
+    XRegs<KP> xs;
+    x_load<MT, KP>(xptr, ldx, G, xs);
+    auto issue = [&](PBuf &b, int i) {
+        const int p = min(wave + kW * i, pmax); // past the block's passes: a harmless re-read
+        b.c = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_c, p * kPassBytes, 0);
+        b.w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_w, p * kPassBytes, 0);
+    };
+    // in the order the loop issues them (codes, then words, pass by pass), so
+    // that its waits are the same on the first trip as on every later one
+    PBuf b0, b1, b2, b3;
+    issue(b0, 0);
+    asm volatile("" ::: "memory");
+    issue(b1, 1);
+    asm volatile("" ::: "memory");
+    issue(b2, 2);
+    asm volatile("" ::: "memory");
+    issue(b3, 3);
+    x_store<MT, KP>(G, xs, xrec);
+    if (tid < MT)
+        best[tid] = 0ull;
     __syncthreads();
+    warm_next(wave, lds_addr(smem + L.warm));
 
-    // ---- tile k sits in ring slot k & 1: wave 0 copies tile k+1 into the
-    // other slot while waves 1.. run the passes of tile k; then all waves sum
-    // the rows of tile k-1 (partials in psum slot (k-1) & 1).
-    Tile prev{};
-    int k = 0;
-    for (;; k++) {
-        const int slot = k & 1;
-        const uint8_t *tile = smem + L.ring + (uint32_t)slot * tb;
-        const Tile h = read_tile(tile);
-        float *ps_k = psum + slot * (MT * ps);
-        if (wave < kCopyWaves) {
-            if (tid == 0)
-                cnt[slot ^ 1] = 0u; // pass counter of tile k+1 (its last users left tile k-1's phase)
-            if (!h.next) {
-                // last tile: the next launch's workgroup with this linear
-                // index, whose first tile goes into the free slot (awaited at
-                // the very end)
-                const u32x16 w = kernarg_line((uint32_t)(kMaxMats * sizeof(PRec)));
-                uint32_t gx = 0;
-#pragma unroll
-                for (int i = 0; i < kMaxMats; i++)
-                    gx = max(gx, w[14 + i / 2] >> (16 * (i & 1)) & 0xffffu);
-                const uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
-                const uint32_t bx = gx ? lin % gx : 0u, by = gx ? lin / gx : (uint32_t)kMaxMats;
-#pragma unroll
-                for (int i = 0; i < kMaxMats; i++) {
-                    const uint32_t wgs_i = w[14 + i / 2] >> (16 * (i & 1)) & 0xffffu;
-                    const uint32_t first_i = (w[12 + i / 2] >> (16 * (i & 1)) & 0xffffu) * 16u;
-                    const uint8_t *p_i = (const uint8_t *)u64_ptr(w[2 * i], w[2 * i + 1]);
-                    const bool mine = by == (uint32_t)i && bx < wgs_i && p_i != nullptr;
-                    warm = mine ? p_i + (uint64_t)bx * w[8 + i] : warm;
-                    warm_bytes = mine ? min(first_i, tb) : warm_bytes;
-                }
-            }
-            // tile k+1, or after the last tile the warming copy
-            copy_chunks(h.next ? region + (uint64_t)(k + 1) * tb : warm, ring + (uint32_t)(slot ^ 1) * tb,
-                        h.next ? h.next : warm_bytes, wave, kCopyWaves);
-        } else {
-            const int np0 = (int)((h.cnt[0] + 63) >> 6), np1 = (int)((h.cnt[1] + 63) >> 6);
-            const int np2 = (int)((h.cnt[2] + 63) >> 6), np3 = (int)((h.cnt[3] + 63) >> 6);
-            const int pb1 = np0, pb2 = pb1 + np1, pb3 = pb2 + np2, np = pb3 + np3;
-            const uint32_t wb1 = h.cnt[0], wb2 = wb1 + h.cnt[1], wb3 = wb2 + h.cnt[2];
-            const uint32_t off1 = kHdr + 64u * h.cnt[0], off2 = off1 + 32u * h.cnt[1], off3 = off2 + 16u * h.cnt[2];
-            // worker w runs pass w first; later passes come from an LDS counter,
-            // each asked for before the current pass runs so that the atomic's
-            // latency hides behind it
-            constexpr int nw = kW - kCopyWaves;
-            uint32_t nextp = 0;
-            for (int p = wave - kCopyWaves; p < np; p = __builtin_amdgcn_readfirstlane((int)nextp)) {
-                if ((tid & 63) == 0)
-                    nextp = nw + atomicAdd(cnt + slot, 1u);
-                if (p < pb1)
-                    plan_pass<8, MT>(p, h.cnt[0], 0u, kHdr, tile, h, G, ps, xrec, ps_k);
-                else if (p < pb2)
-                    plan_pass<4, MT>(p - pb1, h.cnt[1], wb1, off1, tile, h, G, ps, xrec, ps_k);
-                else if (p < pb3)
-                    plan_pass<2, MT>(p - pb2, h.cnt[2], wb2, off2, tile, h, G, ps, xrec, ps_k);
-                else
-                    plan_pass<1, MT>(p - pb3, h.cnt[3], wb3, off3, tile, h, G, ps, xrec, ps_k);
+    const PCtx cx{xrec, psum, G, ps, 0xffffffffu / (uint32_t)stride + 1u};
+    // passes of this wavefront: its width bytes are nonzero up to the first 0
+    // (lane i holds bytes 4i..4i+3, and the list ends inside its own lanes),
+    // so full lanes form a prefix
+    const int cl = (meta & 0xffu) ? ((meta & 0xff00u) ? ((meta & 0xff0000u) ? ((meta >> 24) ? 4 : 3) : 2) : 1) : 0;
+    const int nfull = __popcll(__ballot(cl == 4));
+    const int npw = 4 * nfull + __builtin_amdgcn_readlane(cl, nfull);
+    // pass i: the pass body, then (always, so that every step issues the same
+    // loads and the waits stay exact) the loads of pass i + 4 into the same
+    // registers
+    auto step = [&](PBuf &b, int i) {
+        if (i < npw) {
+            const uint32_t mw = (uint32_t)__builtin_amdgcn_readlane((int)meta, i >> 2);
+            switch ((mw >> (8 * (i & 3))) & 0xffu) {
+            case 1: pass_b1<MT>(b, cx); break;
+            case 2: pass_b2<MT>(b, cx); break;
+            case 3: pass_b4<MT>(b, cx); break;
+            default: pass_b8<MT>(b, cx); break;
             }
         }
-        if (k > 0) {
-            const int nsum = sum_items((int)prev.nr, G);
-            for (int t = (wave + kW - kCopyWaves) % kW; t < nsum; t += kW) // copying waves take the last shares
-                rowsum_item<MT, OM>(t, prev, G, ps, rows, psum + (slot ^ 1) * (MT * ps), ybuf, yo);
-        }
-        if (h.next)
-            wait_vm0(); // copy waves: the copy of tile k+1
-        __syncthreads();
-        prev = h;
-        if (!h.next)
-            break;
+        issue(b, i + kDepth + 1);
+    };
+    for (int i = 0; i < npw; i += 4) {
+        step(b0, i);
+        step(b1, i + 1);
+        step(b2, i + 2);
+        step(b3, i + 3);
     }
-    // ---- rows of the last tile (partials in psum slot k & 1); every row ends here
-    {
-        const int nsum = sum_items((int)prev.nr, G);
-        for (int t = (wave + kW - kCopyWaves) % kW; t < nsum; t += kW) // copying waves take the last shares
-            rowsum_item<MT, OM>(t, prev, G, ps, rows, psum + (k & 1) * (MT * ps), ybuf, yo);
-    }
-    // the warming copy lands in LDS: it must finish before the workgroup's LDS
-    // is released (the other waves leave without waiting for their stores)
-    if (wave < kCopyWaves && warm_bytes)
-        wait_vm0();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // the warming copy has landed
+    __syncthreads(); // every partial of the block is in psum
+
+    const int nsum = (R * sum_lanes(G) + 63) / 64;
+    for (int t = wave; t < nsum; t += kW)
+        rowsum_item<MT, OM>(t, R, stride, G, ps, psum, ybuf, yo);
     if constexpr (OM == kArgmax) {
-        __syncthreads(); // every finished row's key is in best[]
+        __syncthreads(); // every row's key is in best[]
         if (tid == 0)
             argmax_finish<MT>(reinterpret_cast<vbq_argmax_ws *>(yptr), ldy, best);
     } else if constexpr (OM == kSwiglu) {
@@ -891,7 +840,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
         const int pairs = R / 2; // R is even: the block starts at an even row and N is even
         for (int i = tid; i < MT * pairs; i += kT) {
             const int m = i / pairs, p = i - m * pairs;
-            const float g = ybuf[m * rows + 2 * p], u = ybuf[m * rows + 2 * p + 1];
+            const float g = ybuf[m * smax + 2 * p], u = ybuf[m * smax + 2 * p + 1];
             const float h = g / (1.0f + expf(-g)) * u; // silu(gate) * up
             const uint64_t o = (uint64_t)m * ldy + n0 / 2 + p;
             if (yt == VBQ_F16)
@@ -905,23 +854,21 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
 // ---------------------------------------------------------------------------
 // Host side.
 
-int plan_cus()
+int device_cus()
 {
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 256;
-    }
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
     return cus;
 }
 
-constexpr uint32_t kLdsBudget = 160u * 1024u;
+uint64_t region_of(int passes, int per_wave)
+{
+    return align_up((uint64_t)passes * kPassBytes + (uint64_t)kW * per_wave, 256);
+}
 
-// Partial-sum capacity of a tile: groups (at least 12 bytes each) plus the
-// columns of a first and a last row the tile only partly covers.
-int psum_capacity(int tb, int G) { return (tb - kHdr) / 12 + 2 * G; }
+int per_wave_of(int passes) { return (int)align_up((uint64_t)((passes + kW - 1) / kW + 1), 4); }
 
 vbq_status check_plan(const vbq_plan *P)
 {
@@ -929,9 +876,10 @@ vbq_status check_plan(const vbq_plan *P)
         return VBQ_ERR_LAYOUT;
     if (P->N < 1 || P->G < 1 || P->G > kMaxG || P->K != 64 * P->G || P->M < 1 || P->M > 2 || P->wgs < 1 ||
         P->rows < 1 || (int64_t)P->wgs * P->rows < P->N || (int64_t)(P->wgs - 1) * P->rows >= P->N ||
-        P->wgs > 65535 || P->tiles > kMaxTiles || P->tile_bytes < 4096 || P->tile_bytes > kMaxTb ||
-        P->tile_bytes % 1024 || P->tiles < 1 || P->first_bytes < kHdr || P->first_bytes > P->tile_bytes ||
-        P->region_bytes != (uint64_t)P->tiles * (uint64_t)P->tile_bytes)
+        P->wgs > 65535 || P->passes < 1 || P->per_wave != per_wave_of(P->passes) || P->per_wave > kMaxPerWave ||
+        (int64_t)pos_stride(P->rows) * P->G + 1 > 65536 || P->psum != psum_stride(P->G, pos_stride(P->rows)) ||
+        P->region_bytes != region_of(P->passes, P->per_wave) ||
+        P->total_bytes != (uint64_t)P->wgs * P->region_bytes)
         return VBQ_ERR_LAYOUT;
     return VBQ_OK;
 }
@@ -949,38 +897,74 @@ PrepArgs prep_args(const vbq_layout *L, const void *blob, const vbq_plan *P)
     a.G = (int)L->G;
     a.nS = (int)L->nS;
     a.rows = P->rows;
-    a.tb = (uint32_t)P->tile_bytes;
+    a.passes = P->passes;
+    a.per_wave = P->per_wave;
     a.region = P->region_bytes;
     return a;
 }
 
-template <int MT, int OM>
+// hipFuncSetAttribute once per kernel and device (thread-safe).
+vbq_status lds_attribute_once(const void *fn)
+{
+    static std::mutex mu;
+    static std::set<std::pair<const void *, int>> done;
+    int dev = 0;
+    VBQ_TRY(hip_status(hipGetDevice(&dev)));
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({fn, dev}))
+        return VBQ_OK;
+    VBQ_TRY(hip_status(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)));
+    done.insert({fn, dev});
+    return VBQ_OK;
+}
+
+template <int MT, int OM, int KP>
 vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
-    static bool configured = false;
-    if (!configured) {
-        VBQ_TRY(hip_status(
-            hipFuncSetAttribute((const void *)k_gemv_plan<MT, OM>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)));
-        configured = true;
-    }
-    hipLaunchKernelGGL((k_gemv_plan<MT, OM>), dim3(grid), dim3(kT), lds, stream, a);
+    VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan<MT, OM, KP>));
+    hipLaunchKernelGGL((k_gemv_plan<MT, OM, KP>), dim3(grid), dim3(kT), lds, stream, a);
     return launch_status();
+}
+
+template <int MT, int OM>
+vbq_status launch_plan_kp(int G, const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
+{
+    const int per = (MT * G * 8 + kT - 1) / kT; // activation items per thread
+    if (per <= 1)
+        return launch_plan_t<MT, OM, 1>(a, grid, lds, stream);
+    if (per <= 2)
+        return launch_plan_t<MT, OM, 2>(a, grid, lds, stream);
+    if (per <= 4)
+        return launch_plan_t<MT, OM, 4>(a, grid, lds, stream);
+    return launch_plan_t<MT, OM, 8>(a, grid, lds, stream);
 }
 
 // One launch of m (1 or 2) tokens in output mode om.
 vbq_status launch_plan(int m, int om, const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
+    const int G = (int)(a.rec[0].g_yt & 0xffffu);
     switch (om * 2 + (m - 1)) {
-    case 0: return launch_plan_t<1, kRows>(a, grid, lds, stream);
-    case 1: return launch_plan_t<2, kRows>(a, grid, lds, stream);
-    case 2: return launch_plan_t<1, kArgmax>(a, grid, lds, stream);
-    case 3: return launch_plan_t<2, kArgmax>(a, grid, lds, stream);
-    case 4: return launch_plan_t<1, kSwiglu>(a, grid, lds, stream);
-    default: return launch_plan_t<2, kSwiglu>(a, grid, lds, stream);
+    case 0: return launch_plan_kp<1, kRows>(G, a, grid, lds, stream);
+    case 1: return launch_plan_kp<2, kRows>(G, a, grid, lds, stream);
+    case 2: return launch_plan_kp<1, kArgmax>(G, a, grid, lds, stream);
+    case 3: return launch_plan_kp<2, kArgmax>(G, a, grid, lds, stream);
+    case 4: return launch_plan_kp<1, kSwiglu>(G, a, grid, lds, stream);
+    default: return launch_plan_kp<2, kSwiglu>(G, a, grid, lds, stream);
     }
 }
 
+bool lds_fits(int M, int G, int rows)
+{
+    return p_layout(M, G, pos_stride(rows)).total <= kLdsBudget && (int64_t)pos_stride(rows) * G + 1 <= 65536;
+}
+
 } // namespace
+
+bool vbq::planned_can_share(const vbq_plan *a, const vbq_plan *b)
+{
+    return a->K == b->K && a->M == b->M &&
+           lds_fits(a->M, a->G, std::max(pos_stride(a->rows), pos_stride(b->rows)));
+}
 
 extern "C" {
 
@@ -999,32 +983,33 @@ vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, 
     const int N = (int)L->N, G = (int)L->G;
     if (G > kMaxG)
         return VBQ_ERR_SHAPE;
+    const int cus = device_cus();
     if (wgs <= 0)
-        wgs = plan_cus();
-    // an even row count whenever N is even, so that a row block never splits
-    // the (gate, up) pairs of an interleaved SwiGLU matrix
-    int rows = (N + wgs - 1) / wgs;
-    if (N % 2 == 0 && rows % 2)
-        rows++;
+        wgs = cus;
+    // rows per block: an even count whenever N is even, so that a row block
+    // never splits the (gate, up) pairs of an interleaved SwiGLU matrix; fewer
+    // rows (more blocks) while a block's partial sums do not fit the LDS
+    auto fit = [&](int m, int &rows_out) {
+        int rows = (N + wgs - 1) / wgs;
+        for (;;) {
+            if (N % 2 == 0 && rows % 2)
+                rows++;
+            if (lds_fits(m, G, rows)) {
+                rows_out = rows;
+                return true;
+            }
+            if (rows <= 1)
+                return false;
+            rows = std::max(1, rows * 3 / 4);
+        }
+    };
+    int rows = 0;
+    if (M == 2 && !(fit(2, rows) && (N + rows - 1) / rows <= 4 * cus))
+        M = 1; // two tokens would need many rounds of small blocks: one token per launch
+    if (M == 1 && !fit(1, rows))
+        return VBQ_ERR_SHAPE;
     wgs = (N + rows - 1) / rows;
-    // the largest tile stride (1 KiB steps) whose launch fits the LDS budget;
-    // two tokens per launch only while that keeps tiles of 16 KiB or more
-    // (beyond, the x records of two tokens crowd out the tiles)
-    int tb = 0;
-    for (;;) {
-        tb = 0;
-        for (int cand = kMaxTb; cand >= 4096 && !tb; cand -= 1024) {
-            const int ps = psum_capacity(cand, G);
-            if (ps <= 65536 && p_layout(M, G, rows, cand, ps).total <= kLdsBudget)
-                tb = cand;
-        }
-        if (M > 1 && tb < 16 * 1024) {
-            M--;
-            continue;
-        }
-        break;
-    }
-    if (!tb)
+    if (wgs > 65535)
         return VBQ_ERR_SHAPE;
     vbq_plan p{};
     p.magic = VBQ_PLAN_MAGIC;
@@ -1034,10 +1019,9 @@ vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, 
     p.M = M;
     p.wgs = wgs;
     p.rows = rows;
-    p.tile_bytes = tb;
-    p.psum = psum_capacity(tb, G);
-    p.lds_bytes = (int)p_layout(M, G, rows, tb, p.psum).total;
-    // sizing pass: tiles per block region and the largest first tile
+    p.psum = psum_stride(G, pos_stride(rows));
+    p.lds_bytes = (int)p_layout(M, G, pos_stride(rows)).total;
+    // sizing pass: the largest block's pass count
     VBQ_TRY(zero_words(ws, 16, stream));
     PrepArgs a = prep_args(L, blob, &p);
     a.plan = nullptr;
@@ -1047,17 +1031,18 @@ vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, 
     uint32_t h[4];
     VBQ_TRY(hip_status(hipMemcpyAsync(h, ws, 16, hipMemcpyDeviceToHost, stream)));
     VBQ_TRY(hip_status(hipStreamSynchronize(stream)));
-    if (h[2] || h[0] < 1)
-        return VBQ_ERR_SHAPE; // some block needs more tiles than a plan holds
-    p.tiles = (int)h[0];
-    p.first_bytes = (int)h[1];
-    p.region_bytes = (uint64_t)p.tiles * (uint64_t)tb;
+    if (h[0] < 1 || h[0] > (uint32_t)kW * (kMaxPerWave - 4))
+        return VBQ_ERR_SHAPE;
+    p.passes = (int)h[0];
+    p.per_wave = per_wave_of(p.passes);
+    p.region_bytes = region_of(p.passes, p.per_wave);
     p.total_bytes = (uint64_t)wgs * p.region_bytes;
     *P = p;
     return VBQ_OK;
 }
 
-vbq_status vbq_prepare(const vbq_plan *P, const vbq_layout *L, const void *blob, void *plan, hipStream_t stream)
+vbq_status vbq_prepare(const vbq_plan *P, const vbq_layout *L, const void *blob, void *plan, uint32_t *status_word,
+                       hipStream_t stream)
 {
     if (!blob || !plan)
         return VBQ_ERR_INVALID_ARG;
@@ -1065,11 +1050,14 @@ vbq_status vbq_prepare(const vbq_plan *P, const vbq_layout *L, const void *blob,
     VBQ_TRY(check_plan(P));
     if ((int)L->N != P->N || (int)L->K != P->K)
         return VBQ_ERR_SHAPE;
-    if ((uintptr_t)blob % 256 || (uintptr_t)plan % 256)
+    if ((uintptr_t)blob % 256 || (uintptr_t)plan % 256 || (uintptr_t)status_word % 4)
         return VBQ_ERR_ALIGN;
+    if (status_word)
+        VBQ_TRY(zero_words(status_word, 4, stream));
     PrepArgs a = prep_args(L, blob, P);
     a.plan = (uint8_t *)plan;
     a.sizes = nullptr;
+    a.status = status_word;
     hipLaunchKernelGGL(k_prepare, dim3(P->wgs), dim3(kT), 0, stream, a);
     return launch_status();
 }
@@ -1078,16 +1066,14 @@ vbq_status vbq_prepare(const vbq_plan *P, const vbq_layout *L, const void *blob,
 
 namespace {
 
-// Checks one launch for up to P->M tokens (the plans' LDS carve-up holds that
-// many) and fills its arguments; launches nothing.
+// Checks one launch for up to P->M tokens and fills its arguments; launches nothing.
 vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
                         int tok0, PArgs *out, dim3 *grid_out, uint32_t *lds_out)
 {
-    if ((uintptr_t)x % 2)
-        return VBQ_ERR_ALIGN;
+    if ((uintptr_t)x % 8 || ldx % 4)
+        return VBQ_ERR_ALIGN; // the activations are read 8 bytes at a time
     PArgs a{};
-    int gx = 0, rows_max = 0;
-    uint32_t first = 0;
+    int gx = 0, smax = 2;
     for (int i = 0; i < n; i++) {
         const vbq_planned_item &it = items[i];
         if (!it.P || !it.plan || !it.y)
@@ -1099,8 +1085,6 @@ vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint1
             return VBQ_ERR_BATCH;
         if (P->K != P0->K || ldx < P->K || it.ldy < P->N)
             return VBQ_ERR_SHAPE;
-        if (P->tile_bytes != P0->tile_bytes || P->psum != P0->psum)
-            return VBQ_ERR_SHAPE; // one launch needs one LDS carve-up
         if ((uintptr_t)it.plan % 256 || (uintptr_t)it.y % (yt == VBQ_F32 ? 4 : 2))
             return VBQ_ERR_ALIGN;
         PRec &r = a.rec[i];
@@ -1112,21 +1096,20 @@ vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint1
         r.ldy = it.ldy;
         r.rows = P->rows;
         r.ldx = ldx;
+        r.passes = P->passes;
+        r.per_wave = P->per_wave;
         r.wgs = P->wgs;
         gx = std::max(gx, P->wgs);
-        first = std::max(first, (uint32_t)P->first_bytes);
-        rows_max = std::max(rows_max, P->rows); // output staging stride: the plan with the most rows fits
+        smax = std::max(smax, pos_stride(P->rows)); // LDS strides: the plan with the most rows fits
     }
-    const vbq_plan *P0 = items[0].P;
-    const uint32_t lds = p_layout(M, P0->G, rows_max, P0->tile_bytes, P0->psum).total;
-    if (lds > kLdsBudget)
+    const int G = items[0].P->G;
+    const uint32_t lds = p_layout(M, G, smax).total;
+    if (lds > kLdsBudget || (int64_t)smax * G + 1 > 65536)
         return VBQ_ERR_SHAPE;
     for (int i = 0; i < n; i++) {
         PRec &r = a.rec[i];
-        r.first = first;
-        r.ps = P0->psum;
-        r.rows_max = rows_max;
-        r.g_yt_tb = (uint32_t)P0->G | (uint32_t)yt << 16 | (uint32_t)(P0->tile_bytes / 1024) << 24;
+        r.g_yt = (uint32_t)G | (uint32_t)yt << 16;
+        r.smax = smax;
     }
     *out = a;
     *grid_out = dim3((unsigned)gx, (unsigned)n);
@@ -1142,15 +1125,15 @@ void set_next(PArgs &a, const vbq_planned_item *next, int nnext)
         const vbq_plan *P = next[i].P;
         a.warm.plan[i] = (const uint8_t *)next[i].plan;
         a.warm.region[i] = (uint32_t)P->region_bytes;
-        a.warm.first16[i] = (uint16_t)((P->first_bytes + 15) / 16);
         a.warm.wgs[i] = (uint16_t)P->wgs;
+        a.warm.passes[i] = (uint16_t)P->passes;
     }
 }
 
 // Tokens beyond what one launch holds run as further launches over the same
 // plans; each token's arithmetic is the same in every launch shape.  Every
-// launch is checked before the first is enqueued; with stream == nullptr and
-// dry set, only the checks run.
+// launch is checked before the first is enqueued; with dry set, only the
+// checks run.
 vbq_status planned_shared(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
                           hipStream_t stream, bool dry, const vbq_planned_item *next = nullptr, int nnext = 0)
 {

@@ -10,10 +10,15 @@
 // with the same K (the gate and up projections of an MLP block) share one
 // launch.  Every item is checked before the first launch.
 //
-// There is no persistent tier: on MI355X a grid-wide barrier inside one
-// cooperative kernel costs about 5.5 us, against about 1.9 us per kernel node
-// of a replayed HIP graph, so stages stay separate launches and a caller that
-// wants the launch floor captures the step in a graph.
+// There is no persistent tier: on MI355X a grid-wide dependency carried
+// through memory inside one cooperative kernel (every workgroup publishes its
+// slice of the outputs, every workgroup waits for all of them and reads the
+// whole vector back) costs 4.4 to 5.2 us per stage however it is signalled
+// (one counter or per-workgroup flags, agent or system scope), and about
+// 60 us with release/acquire fences, which write back and invalidate the L2;
+// a kernel node of a replayed HIP graph costs about 1.9 us.  Stages therefore
+// stay separate launches and a caller that wants the launch floor captures
+// the step in a graph.
 #include <vector>
 
 #include "vbq_host.h"
@@ -127,8 +132,7 @@ vbq_status vbq_gemv_planned_seq(const vbq_planned_seq_item *items, int n, int M,
     VBQ_TRY(check_stages(items, n));
     // two plans share a launch only where one LDS carve-up serves both
     auto compatible = [](const vbq_planned_seq_item &a, const vbq_planned_seq_item &b) {
-        return a.x == b.x && a.ldx == b.ldx && a.P->K == b.P->K && a.P->M == b.P->M &&
-               a.P->tile_bytes == b.P->tile_bytes && a.P->psum == b.P->psum;
+        return a.x == b.x && a.ldx == b.ldx && planned_can_share(a.P, b.P);
     };
     // the launches in order, every one checked before the first is enqueued
     struct Launch {
@@ -150,7 +154,7 @@ vbq_status vbq_gemv_planned_seq(const vbq_planned_seq_item *items, int n, int M,
         launches.push_back(l);
         return planned_shared_check(l.it, k, M, l.x, l.ldx, yt);
     }));
-    // each launch warms the first tiles of the one after it; the last warms
+    // each launch warms the first passes of the one after it; the last warms
     // the first, which a decoder runs again at its next step
     const int nl = (int)launches.size();
     for (int i = 0; i < nl; i++) {

@@ -51,13 +51,16 @@ __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t m
     return r;
 }
 
-// Turn the 2b code words of a b-bit group into 32 fp16 pairs (2^(10-pos)+q).
-template <int B>
-__device__ __forceinline__ void unpack_pairs(const uint32_t *w, uint32_t *h)
+// Turn NW code words of a b-bit group into fp16 pairs (2^(10-pos)+q): word d
+// gives pairs d*(16/b) .. d*(16/b) + 16/b - 1 of the words' run (for b = 8,
+// pairs 2d and 2d+1), so the words of a half or a quarter group give the
+// matching half or quarter of the group's 32 pairs.
+template <int B, int NW>
+__device__ __forceinline__ void unpack_words(const uint32_t *w, uint32_t *h)
 {
     if constexpr (B == 8) {
 #pragma unroll
-        for (int d = 0; d < 16; d++) {
+        for (int d = 0; d < NW; d++) {
             // bytes [b0, 0x64, b2, 0x64] and [b1, 0x64, b3, 0x64]: 1024 + q
             h[2 * d] = __builtin_amdgcn_perm(0x64646464u, w[d], 0x04020400u);
             h[2 * d + 1] = __builtin_amdgcn_perm(0x64646464u, w[d], 0x04030401u);
@@ -66,7 +69,7 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t *w, uint32_t *h)
         constexpr int per = 16 / B;                // pairs per word
         constexpr uint32_t field = (1u << B) - 1u; // one code
 #pragma unroll
-        for (int d = 0; d < 2 * B; d++) {
+        for (int d = 0; d < NW; d++) {
 #pragma unroll
             for (int i = 0; i < per; i++) {
                 const int pos = pair_pos<B>(i);
@@ -76,6 +79,13 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t *w, uint32_t *h)
             }
         }
     }
+}
+
+// The 2b code words of a whole b-bit group -> its 32 pairs.
+template <int B>
+__device__ __forceinline__ void unpack_pairs(const uint32_t *w, uint32_t *h)
+{
+    unpack_words<B, 2 * B>(w, h);
 }
 
 } // namespace vbq

@@ -19,16 +19,32 @@ from decode_gemv_vbq_amd import workload as wl
 
 
 class Matrix:
-    __slots__ = ("spec", "L", "blob", "x", "y", "ws", "P", "plan", "sample_rows", "sample", "w16", "y16")
+    __slots__ = ("spec", "L", "blob", "x", "y", "ws", "P", "plan", "pass_count", "sample_rows", "sample", "w16",
+                 "y16")
 
     def __init__(self, spec, L, blob, x, y, ws):
         self.spec, self.L, self.blob, self.x, self.y, self.ws = spec, L, blob, x, y, ws
         self.P = None
         self.plan = None
+        self.pass_count = 0
         self.sample_rows = None
         self.sample = None
         self.w16 = None
         self.y16 = None
+
+
+def plan_read_bytes(m) -> int:
+    """Bytes one GEMV over m's plan loads: 1536 per pass record of every row
+    block (1 KiB of codes and the 512-byte word area: each lane loads 8 bytes
+    of it whatever the width) and the width bytes of each wavefront."""
+    return int(m.pass_count) * 1536 + int(m.P.wgs) * 16 * int(m.P.per_wave)
+
+
+def count_passes(P, plan) -> int:
+    """Pass records in use over all row blocks of a plan (nonzero width bytes)."""
+    region = plan.view(int(P.wgs), int(P.region_bytes))
+    off = int(P.passes) * 1536
+    return int((region[:, off:off + 16 * int(P.per_wave)] != 0).sum().item())
 
 
 class DecodeStep:
@@ -90,39 +106,25 @@ class DecodeStep:
             for m in ms:
                 wgs = 0 if len(ms) == 1 else max(1, round(cus * m.spec.N / total))
                 m.plan, m.P = v.prepare(m.L, m.blob, M=min(2, self.M), wgs=wgs)
+                m.pass_count = count_passes(m.P, m.plan)
             if len(ms) > 1:
                 P0 = ms[0].P
-                self.shared_ok[k] = all(m.P.tile_bytes == P0.tile_bytes and m.P.psum == P0.psum for m in ms)
+                self.shared_ok[k] = all(m.P.K == P0.K and m.P.M == P0.M for m in ms)
         torch.cuda.synchronize()
         if log:
             log(f"prepared {len(self.mats)} plans, {self.plan_bytes() / 1e6:.1f} MB read per step")
 
     def plan_bytes(self) -> int:
-        """Bytes of the prepared plans the step reads from memory: every tile
-        (header, code records, one scale|position word per group) plus the
-        activations once per matrix (the workgroups of a launch share them
-        through the caches)."""
+        """Bytes the step's GEMVs read from memory: every pass record's code
+        bytes and words as the kernel loads them (16 code bytes and 8 word
+        bytes per lane of each pass, partly filled passes included), the width
+        bytes, plus the activations once per matrix (the workgroups of a
+        launch share them through the caches)."""
         tot = 0
         for m in self.mats:
             if m.P is None:
                 continue
-            groups = m.spec.N * m.spec.G
-            tiles = -(-(int(m.L.code_bytes) + 4 * groups) // (m.P.tile_bytes - 132))
-            tot += int(m.L.code_bytes) + 4 * groups + 64 * max(tiles, m.P.wgs) + 2 * self.M * m.spec.K
-        return tot
-
-    def warm_bytes(self) -> int:
-        """Bytes the step's launches fetch ahead for the launch after them (the
-        first tile of each of its row blocks, at most one tile stride of the
-        warming launch; the last launch warms the first).  Those bytes are read
-        again by the launch they belong to, from the caches."""
-        tot = 0
-        n = len(self.stages)
-        for k, st in enumerate(self.stages):
-            tb = min(self.mats[i].P.tile_bytes for i in st)
-            for i in self.stages[(k + 1) % n]:
-                P = self.mats[i].P
-                tot += P.wgs * min(-(-P.first_bytes // 16) * 16, tb)
+            tot += plan_read_bytes(m) + 2 * self.M * m.spec.K
         return tot
 
     # ------------------------------------------------------------- the step

@@ -74,10 +74,12 @@ typedef struct vbq_layout {
     uint64_t total_bytes, code_bytes, code_bytes_padded;
 } vbq_layout;
 
-/* Device status-word bits set by vbq_pack (read with vbq_status_check). */
+/* Device status-word bits set by vbq_pack, vbq_quantize and vbq_prepare
+ * (read with vbq_status_check). */
 #define VBQ_STATUS_BITS 0x1u   /* some width outside {1,2,4,8} */
 #define VBQ_STATUS_CODES 0x2u  /* some code above 2^b - 1 */
 #define VBQ_STATUS_LAYOUT 0x4u /* widths disagree with the planned layout */
+#define VBQ_STATUS_PLAN 0x8u   /* a row block needs more passes than its plan holds */
 
 /* Library version string, e.g. "vbq 0.1.0 (VBQ1 layout)". */
 const char *vbq_version(void);
@@ -124,9 +126,10 @@ vbq_status vbq_pack(const vbq_layout *L /* host */, const uint8_t *q, const uint
                     void *blob, uint32_t *status_word, hipStream_t stream);
 
 /*
- * SYNC.  Read a status word written by vbq_pack: VBQ_OK, or the first error
- * among VBQ_ERR_BITS, VBQ_ERR_CODE_RANGE, VBQ_ERR_LAYOUT.  *raw (host, may be
- * NULL) receives the word.
+ * SYNC.  Read a status word written by vbq_pack, vbq_quantize or vbq_prepare:
+ * VBQ_OK, or the first error among VBQ_ERR_BITS, VBQ_ERR_CODE_RANGE,
+ * VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE (VBQ_STATUS_PLAN).  *raw (host, may be NULL)
+ * receives the word.
  */
 vbq_status vbq_status_check(const uint32_t *status_word, uint32_t *raw /* host */, hipStream_t stream);
 
@@ -220,47 +223,52 @@ vbq_status vbq_gemv_shared(const vbq_gemv_item *items /* host */, int n, int M, 
  *
  * Plan buffer: `wgs` row blocks of `rows` rows (the last may have fewer), one
  * per workgroup of the GEMV launch.  Block b owns bytes [b * region_bytes,
- * (b + 1) * region_bytes) and stores tiles at a stride of tile_bytes.  Tile t
- * of a block holds the block's groups (row-major order) whose running sum of
- * (8*b + 4) bytes starts in [t*C, (t+1)*C), C = tile_bytes - 132.  A tile is:
- *   64-byte header: u32 groups of width 8, 4, 2, 1; first row (relative to
- *     the block); rows touched nr; first column of that first row; one past
- *     the last column of the last row; ceil(2^32 / nr) (0 if nr = 1); bytes
- *     of the next tile (0 for the last); groups n; offset of the word section;
- *     this tile's bytes; tile index; tiles in the block; VBQ_PLAN_MAGIC.
- *   code records of the groups in slot order (width 8, 4, 2, 1; then column;
- *     then row), copied verbatim from the blob (8*b bytes each);
- *   u32 per group in slot order: fp16 scale bits | e << 16, where
- *     e = column * nr + (row - first row).
- * Bytes past a tile's end up to the next stride are never read.
+ * (b + 1) * region_bytes).  Its groups are sorted by (width 1, 2, 4, 8; then
+ * column; then row) and cut into passes of 1 KiB of codes: 128 one-bit, 64
+ * two-bit, 32 four-bit or 16 eight-bit groups (the last pass of a width may be
+ * partly filled).  Pass p of a block is the 1536-byte record at p * 1536:
+ *   bytes [0, 1024): group k's code record (8*b bytes, copied verbatim from
+ *     the blob) at k * 8*b;
+ *   bytes [1024, 1536): u32 per group k at 1024 + 4k: fp16 scale bits |
+ *     e << 16, e = column * S + (row - first row of the block), S = max(rows, 2);
+ *   an empty place of a partly filled pass has zero codes and the word
+ *     (S * G) << 16 (scale 0 at a position no row uses).
+ * After the `passes` records (at passes * 1536): the width byte of each pass
+ * (log2(b) + 1; 0 after the block's last pass), wave-major for the 16
+ * wavefronts of the GEMV workgroup: pass w + 16 j at byte w * per_wave + j;
+ * per_wave = ceil(passes / 16) + 1 rounded up to a multiple of 4, so every
+ * wavefront's list ends with a 0.  region_bytes = passes * 1536 +
+ * 16 * per_wave rounded up to 256.  Bytes of a region past what its block
+ * uses are never read for arithmetic.
  */
-#define VBQ_PLAN_MAGIC 0x4E4C5056u
+#define VBQ_PLAN_MAGIC 0x32504256u
 
 typedef struct vbq_plan {
     uint32_t magic;        /* VBQ_PLAN_MAGIC */
     int32_t N, K, G;       /* matrix shape (G = K / 64 <= 512) */
     int32_t M;             /* tokens per GEMV launch (1 or 2) */
     int32_t wgs, rows;     /* row blocks (workgroups) and rows per block */
-    int32_t tile_bytes;    /* tile stride, multiple of 1024, <= 65536 */
-    int32_t tiles;         /* tiles of the largest block */
-    int32_t first_bytes;   /* bytes of the largest first tile */
-    int32_t psum;          /* partial sums per token a tile may need (LDS sizing) */
+    int32_t passes;        /* pass records per block region (the largest block's count) */
+    int32_t per_wave;      /* width bytes per wavefront */
+    int32_t psum;          /* partial sums per token a block needs in LDS */
     int32_t lds_bytes;     /* LDS per workgroup of its GEMV launches */
-    uint64_t region_bytes; /* tiles * tile_bytes */
+    int32_t reserved;
+    uint64_t region_bytes; /* bytes per block region */
     uint64_t total_bytes;  /* plan buffer bytes: wgs * region_bytes */
 } vbq_plan;
 
 /*
- * SYNC.  Fill *P for the matrix (L, blob), launches of up to M tokens (1 or
- * 2; P->M may come back as 1 where two tokens' activations would leave tiles
- * under 16 KiB of LDS) and `wgs` row blocks (<= 0: one per compute unit of the
- * current device; the count is reduced so that no block is empty; the rows per
- * block are even whenever N is even).  GEMVs of
- * more tokens run as several launches over the same plan.  Runs one sizing kernel over the
- * width bit planes (workspace ws: device, >= 16 bytes) and waits for it.
- * Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_BATCH (M),
- * VBQ_ERR_WORKSPACE, VBQ_ERR_ALIGN, VBQ_ERR_SHAPE (K > 32768, or the LDS of
- * the launch cannot hold a tile and the block's outputs), VBQ_ERR_HIP.
+ * SYNC.  Fill *P for the matrix (L, blob) and launches of up to M tokens (1
+ * or 2).  `wgs` row blocks (<= 0: one per compute unit of the current
+ * device); the rows per block are even whenever N is even, and the block
+ * count grows where a block's partial sums would not fit the LDS of one
+ * workgroup (P->M comes back as 1 when two tokens would need more than four
+ * blocks per compute unit).  GEMVs of more tokens run as several launches
+ * over the same plan.  Runs one sizing kernel over the width bit planes
+ * (workspace ws: device, >= 16 bytes) and waits for it.  Errors:
+ * VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_BATCH (M), VBQ_ERR_WORKSPACE,
+ * VBQ_ERR_ALIGN, VBQ_ERR_SHAPE (K > 32768, or no block size fits the LDS),
+ * VBQ_ERR_HIP.
  */
 vbq_status vbq_plan_init(const vbq_layout *L /* host */, const void *blob, int M, int wgs, vbq_plan *P /* host */,
                          void *ws, size_t ws_bytes, hipStream_t stream);
@@ -268,11 +276,13 @@ vbq_status vbq_plan_init(const vbq_layout *L /* host */, const void *blob, int M
 /*
  * Write the plan of (L, blob) described by *P into `plan` (device,
  * P->total_bytes, 256-byte aligned).  The blob must be the one *P was sized
- * for.  Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT (bad *P), VBQ_ERR_SHAPE
- * (P does not match L), VBQ_ERR_ALIGN.
+ * for: a row block that would need more passes than P->passes is not written
+ * and sets VBQ_STATUS_PLAN in *status_word (device u32, 4-byte aligned,
+ * cleared by this call; may be NULL).  Errors: VBQ_ERR_INVALID_ARG,
+ * VBQ_ERR_LAYOUT (bad *P), VBQ_ERR_SHAPE (P does not match L), VBQ_ERR_ALIGN.
  */
 vbq_status vbq_prepare(const vbq_plan *P /* host */, const vbq_layout *L /* host */, const void *blob, void *plan,
-                       hipStream_t stream);
+                       uint32_t *status_word, hipStream_t stream);
 
 /*
  * Y = X W^T from a plan, M tokens (1 <= M <= 16): x fp16 [M][ldx] (ldx >= K),
@@ -342,9 +352,10 @@ typedef struct vbq_planned_item {
 /*
  * vbq_gemv_planned for n (1..VBQ_MAX_SHARED) matrices that read the same x
  * (e.g. the gate and up projections of one MLP block), in ONE launch of
- * sum P_i->wgs workgroups.  The plans must agree on K, tile_bytes and psum
- * (VBQ_ERR_SHAPE otherwise); prepare them with the same M and with wgs in
- * proportion to N so that the launch spans the device once.
+ * max P_i->wgs x n workgroups.  The plans must agree on K, and the partial
+ * sums of the largest block must fit one workgroup's LDS (VBQ_ERR_SHAPE
+ * otherwise); prepare them with the same M and with wgs in proportion to N
+ * so that the launch spans the device once.
  */
 vbq_status vbq_gemv_planned_shared(const vbq_planned_item *items /* host */, int n, int M, const uint16_t *x, int ldx,
                                    vbq_dtype yt, hipStream_t stream);
@@ -394,8 +405,9 @@ typedef struct vbq_planned_seq_item {
 } vbq_planned_seq_item;
 
 /* The step over prepared plans: each launch as vbq_gemv_planned_shared would
- * make it.  Items of a stage share a launch when they read the same x and
- * their plans agree on K, M, tile_bytes and psum. */
+ * make it.  Items of a stage share a launch when they read the same x, their
+ * plans agree on K and M, and one workgroup's LDS holds the partial sums of
+ * the largest of their blocks. */
 vbq_status vbq_gemv_planned_seq(const vbq_planned_seq_item *items /* host */, int n, int M, vbq_dtype yt,
                                 hipStream_t stream);
 

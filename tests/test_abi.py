@@ -150,13 +150,16 @@ def test_gemv_shared_argument_checks_fail_before_launch():
     assert call([L, bad]) == "VBQ_ERR_LAYOUT"
 
 
-def fake_plan(v, N=4, K=4096, M=1, tile_bytes=16384, psum=1024):
+def fake_plan(v, N=4, K=4096, M=1, passes=1):
+    """A plan struct that passes the host checks (one row block of N rows)."""
     P = v.Plan()
-    P.magic = 0x4E4C5056
+    P.magic = 0x32504256
     P.N, P.K, P.G, P.M = N, K, K // 64, M
     P.wgs, P.rows = 1, N
-    P.tile_bytes, P.tiles, P.first_bytes, P.psum = tile_bytes, 1, 1024, psum
-    P.region_bytes = P.total_bytes = tile_bytes
+    P.passes = passes
+    P.per_wave = (-(-passes // 16) + 1 + 3) // 4 * 4
+    P.psum = (max(N, 2) * (K // 64) + 1 + 3) // 4 * 4
+    P.region_bytes = P.total_bytes = (passes * 1536 + 16 * P.per_wave + 255) // 256 * 256
     return P
 
 
@@ -199,13 +202,14 @@ def test_plan_argument_checks_fail_before_launch():
     assert gemv(ldy=3) == "VBQ_ERR_SHAPE"
     assert gemv(plan=VP((1 << 20) + 128)) == "VBQ_ERR_ALIGN"
     assert gemv(y=VP((1 << 20) + 2), yt=0) == "VBQ_ERR_ALIGN"  # f32 outputs need 4-byte alignment
-    for field, val in [("magic", 0), ("K", 4032), ("tile_bytes", 5000), ("M", 3), ("first_bytes", 32768),
-                       ("region_bytes", 1024), ("rows", 1)]:
+    for field, val in [("magic", 0), ("K", 4032), ("M", 3), ("passes", 0), ("per_wave", 8), ("psum", 5),
+                       ("region_bytes", 1024), ("total_bytes", 2048), ("rows", 1)]:
         bad = fake_plan(v)
         setattr(bad, field, val)
         assert gemv(Pl=bad) == "VBQ_ERR_LAYOUT", field
-    # a plan whose LDS carve-up does not fit one workgroup
-    assert gemv(Pl=fake_plan(v, tile_bytes=65536, psum=16384)) == "VBQ_ERR_SHAPE"
+    # a plan whose partial sums do not fit one workgroup's LDS
+    big = fake_plan(v, N=1000)
+    assert gemv(Pl=big, ldy=1000) == "VBQ_ERR_SHAPE"
 
     def shared(plans, n=None, x=fake):
         items = (v.PlannedItem * max(1, len(plans)))()
@@ -216,12 +220,13 @@ def test_plan_argument_checks_fail_before_launch():
     assert shared([P], n=0) == "VBQ_ERR_INVALID_ARG"
     assert shared([P] * 5) == "VBQ_ERR_INVALID_ARG"
     assert shared([P, fake_plan(v, K=2048)]) == "VBQ_ERR_SHAPE"
-    assert shared([P, fake_plan(v, tile_bytes=32768)]) == "VBQ_ERR_SHAPE"
-    assert shared([P, fake_plan(v, psum=2048)]) == "VBQ_ERR_SHAPE"
+    assert shared([P, fake_plan(v, N=1000)]) == "VBQ_ERR_SHAPE"  # the larger block's partial sums do not fit
     # vbq_prepare: the plan must describe this layout
-    assert v.STATUS[lib.vbq_prepare(ctypes.byref(fake_plan(v, N=8)), ctypes.byref(L), fake, fake, null)] == \
+    assert v.STATUS[lib.vbq_prepare(ctypes.byref(fake_plan(v, N=8)), ctypes.byref(L), fake, fake, null, null)] == \
         "VBQ_ERR_SHAPE"
-    assert v.STATUS[lib.vbq_prepare(ctypes.byref(P), ctypes.byref(L), fake, VP((1 << 20) + 16), null)] == \
+    assert v.STATUS[lib.vbq_prepare(ctypes.byref(P), ctypes.byref(L), fake, VP((1 << 20) + 16), null, null)] == \
+        "VBQ_ERR_ALIGN"
+    assert v.STATUS[lib.vbq_prepare(ctypes.byref(P), ctypes.byref(L), fake, fake, VP((1 << 20) + 2), null)] == \
         "VBQ_ERR_ALIGN"
 
 
@@ -261,7 +266,7 @@ def test_seq_argument_checks_fail_before_launch():
     assert seq([dict(stage=0)] * 1025) == "VBQ_ERR_INVALID_ARG"  # at most 1024 items per stage
 
     P = fake_plan(v)
-    P2 = fake_plan(v, tile_bytes=65536, psum=16384)  # checks pass one by one; its LDS does not fit
+    P2 = fake_plan(v, N=1000)  # its layout checks pass; its partial sums do not fit the LDS
     Pbad = fake_plan(v)
     Pbad.magic = 1
 
@@ -280,7 +285,7 @@ def test_seq_argument_checks_fail_before_launch():
     assert pseq([ok, dict(ldx=4000)]) == "VBQ_ERR_SHAPE"
     assert pseq([ok, dict(ldy=2)]) == "VBQ_ERR_SHAPE"
     assert pseq([ok, dict(plan=fake + 8)]) == "VBQ_ERR_ALIGN"
-    assert pseq([ok, dict(P=P2)]) == "VBQ_ERR_SHAPE"
+    assert pseq([ok, dict(P=P2, ldy=1000)]) == "VBQ_ERR_SHAPE"
     assert pseq([dict(stage=1), dict(stage=0)]) == "VBQ_ERR_INVALID_ARG"
 
 

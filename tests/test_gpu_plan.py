@@ -2,18 +2,19 @@
 vbq_gemv_planned[_shared]) against the CPU oracle, on the same seeded inputs.
 
 * |y - y_ref| <= 1e-3 * sum|w||x| per output, at shapes that span one group,
-  ragged K-slices, rows split across tiles (small row-block counts force many
-  tiles per block) and every width mix.
+  ragged K-slices, large row blocks (small block counts, up to the LDS limit)
+  and every width mix.
 * Invariants: x = e_k gives column k of vbq_dequant bit-exactly; repeated runs
   are bit-identical; a matrix in a shared launch gives the same bits as alone.
-* The plan buffer itself: tile headers read back on the host must describe
-  every group of the matrix exactly once, within the tile stride.
+* The plan buffer itself: pass records and width bytes read back on the host
+  must hold every group of the matrix exactly once, in the documented order.
 """
 import numpy as np
 import pytest
 
 import oracle
 from decode_gemv_vbq_amd import workload as wl
+from tests import mini_oracle
 from tests.gpu_util import upload, within_bound
 
 pytestmark = pytest.mark.gpu
@@ -42,8 +43,9 @@ def planned(v, q, bits, s, x, M=None, wgs=0, yt="f32"):
     return y.float().cpu().numpy().astype(np.float64), (blob, L, plan, P, dx)
 
 
-# (N, K, wgs): one group; G below one slice; ragged slices; rows split across
-# tiles (wgs 1..3 put hundreds of rows in one block); K = 28672 (G = 448)
+# (N, K, wgs): one group; G below one slice; ragged slices; large blocks (wgs
+# 1..3 put hundreds of rows in one block, up to the LDS limit, beyond which the
+# block count grows); K = 28672 (G = 448)
 CASES = [
     (1, 64, 0), (3, 128, 0), (768, 768, 0), (37, 2048, 0), (200, 2112, 0), (130, 4096 + 640, 0),
     (1000, 5632, 0), (300, 4096, 1), (257, 2048, 3), (64, 28672, 0), (9, 28672, 2), (2000, 64, 1),
@@ -195,57 +197,54 @@ def test_planned_shared_parity_and_equal_to_single(Ns, K, M, yt):
         assert torch.equal(alone, y)
 
 
-@pytest.mark.parametrize("N,K,wgs", [(300, 4096, 1), (1000, 5632, 7), (5, 64, 0), (64, 28672, 3)])
-def test_plan_tiles_cover_every_group_once(N, K, wgs):
-    """Host read-back of the plan: per block, the tile chain covers the block's
-    groups in row-major order exactly once, each tile within the stride, and
-    the per-tile positions and scales match the packed matrix."""
+@pytest.mark.parametrize("N,K,wgs", [(300, 4096, 1), (1000, 5632, 7), (5, 64, 0), (64, 28672, 3), (1, 128, 0)])
+def test_plan_passes_cover_every_group_once(N, K, wgs):
+    """Host read-back of the plan: per block, the width bytes list the passes
+    (widths 1, 2, 4, 8 in order) for each wavefront; every group of the block
+    sits in exactly one pass of its width, with the blob's code record (the
+    independent numpy packer's bytes for its codes), its scale and its
+    position; (column, row) ascend within a width; empty places hold zero
+    codes, scale 0 and the spare position."""
     v = vbq()
     q, bits, s, x = draw(N, K, seed=5)
     _, (blob, L, plan, P, _) = planned(v, q, bits, s, x, wgs=wgs)
     buf = plan.cpu().numpy()
     G = K // 64
+    S = max(P.rows, 2)
     seen = np.zeros((N, G), np.int32)
+    assert P.region_bytes == (P.passes * 1536 + 16 * P.per_wave + 255) // 256 * 256
     for b in range(P.wgs):
         n0 = b * P.rows
         R = min(P.rows, N - n0)
         base = b * P.region_bytes
-        t, nxt, covered = 0, None, 0
-        while True:
-            off = base + t * P.tile_bytes
-            h = buf[off:off + 64].view(np.uint32)
-            assert h[15] == 0x4E4C5056 and h[13] == t
-            cnt = h[0:4].astype(np.int64)
-            n = int(h[10])
-            assert cnt.sum() == n and n > 0
-            assert int(h[12]) == int(h[11]) + 4 * n <= P.tile_bytes
-            if t == 0:
-                assert int(h[12]) <= P.first_bytes
-            if nxt is not None:
-                assert nxt == int(h[12])
-            ra, nr, gf, ge = int(h[4]), int(h[5]), int(h[6]), int(h[7])
-            words = buf[off + int(h[11]):off + int(h[11]) + 4 * n].view(np.uint32)
-            e = words >> 16
-            col, row = e // nr, e % nr + ra
-            assert np.all(row < R) and np.all(col < G)
-            # groups of this tile: row-major from (ra, gf) to (ra + nr - 1, ge - 1)
-            first, last = ra * G + gf, (ra + nr - 1) * G + ge - 1
-            flat = row * G + col
-            assert flat.min() == first and flat.max() == last and len(np.unique(flat)) == n == last - first + 1
-            assert covered == first
-            covered = last + 1
-            seen[n0 + row, col] += 1
-            np.testing.assert_array_equal((words & 0xFFFF).astype(np.uint16), s[n0 + row, col])
-            # slot order: widths 8,4,2,1, then column, then row
-            widths = bits[n0 + row, col]
-            sec = np.repeat([8, 4, 2, 1], cnt)
-            np.testing.assert_array_equal(widths, sec)
-            key = (np.repeat(np.arange(4), cnt) * G + col) * nr + (row - ra)
-            assert np.all(np.diff(key) > 0)
-            nxt = int(h[9])
-            t += 1
-            if nxt == 0:
-                assert t == int(h[14])
-                break
-        assert covered == R * G
+        meta = buf[base + P.passes * 1536:base + P.passes * 1536 + 16 * P.per_wave].reshape(16, P.per_wave)
+        width_byte = np.zeros(16 * P.per_wave, np.uint8)
+        for w in range(16):
+            for j in range(P.per_wave):
+                width_byte[w + 16 * j] = meta[w, j]
+        npass = int(np.argmin(width_byte != 0))
+        assert npass >= 1 and not width_byte[npass:].any() and npass <= P.passes
+        assert np.all(np.diff(width_byte[:npass].astype(int)) >= 0)  # widths 1, 2, 4, 8 in order
+        last = {}
+        for p in range(npass):
+            c = int(width_byte[p]) - 1
+            wbits, per = 1 << c, 128 >> c
+            rec = buf[base + p * 1536:base + (p + 1) * 1536]
+            words = rec[1024:1024 + 4 * per].view(np.uint32)
+            for k in range(per):
+                e = int(words[k]) >> 16
+                code = rec[k * 8 * wbits:(k + 1) * 8 * wbits]
+                if e == S * G:  # an empty place
+                    assert int(words[k]) & 0xFFFF == 0 and not code.any()
+                    continue
+                col, row = e // S, e % S
+                assert row < R and col < G
+                n = n0 + row
+                assert int(bits[n, col]) == wbits
+                assert int(words[k]) & 0xFFFF == int(s[n, col])
+                assert code.tobytes() == mini_oracle.group_bytes(q[n, 64 * col:64 * col + 64], wbits)
+                key = (col, row)
+                assert last.get(c, (-1, -1)) < key  # (column, row) ascend within a width
+                last[c] = key
+                seen[n, col] += 1
     assert np.all(seen == 1)
