@@ -57,12 +57,6 @@ bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x
 vbq_status planned_shared_check(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
                                 vbq_dtype yt);
 
-// vbq_gemv_planned_shared whose last launch also fetches, for each workgroup,
-// the first passes of its counterpart in the following launch (the items
-// `next`, checked plans; null: none).
-vbq_status planned_shared_launch(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
-                                 vbq_dtype yt, hipStream_t stream, const vbq_planned_item *next, int nnext);
-
 // Whether two plans can share one launch (same K and M, and one LDS carve-up
 // holds both blocks' partial sums).
 bool planned_can_share(const vbq_plan *a, const vbq_plan *b);

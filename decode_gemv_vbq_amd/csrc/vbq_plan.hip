@@ -276,26 +276,12 @@ struct PRec {
 };
 static_assert(sizeof(PRec) == 64, "one record is one 64-byte line");
 
-// The launch that follows on the stream.  Plans do not depend on the
-// activations, so wavefront w of a workgroup of this launch fetches pass w of
-// the row block that the workgroup with the same linear index works on in the
-// next launch, which then finds it in the memory-side cache instead of
-// waiting for HBM.  Read once, after the activations are staged.
-struct PWarm {
-    const uint8_t *plan[kMaxMats]; // null: no such matrix
-    uint32_t region[kMaxMats];     // bytes per row block
-    uint16_t wgs[kMaxMats];        // row blocks
-    uint16_t passes[kMaxMats];     // pass records per block
-};
-static_assert(sizeof(PWarm) == 64, "the warming line is one 64-byte line");
-
 struct PArgs {
     PRec rec[kMaxMats];
-    PWarm warm;
 };
 
 struct PLayout {
-    uint32_t x, psum, ybuf, best, warm, total;
+    uint32_t x, psum, ybuf, best, total;
 };
 
 __host__ __device__ inline uint32_t p_take(uint32_t &o, uint32_t bytes)
@@ -316,7 +302,6 @@ __host__ __device__ inline PLayout p_layout(int MT, int G, int smax)
     l.psum = p_take(o, (uint32_t)(MT * psum_stride(G, smax)) * 4u);
     l.ybuf = p_take(o, (uint32_t)(MT * smax) * 4u);
     l.best = p_take(o, 2u * 8u); // argmax output: the best (value, row) key per token
-    l.warm = p_take(o, 1024u);   // landing place of the warming copies (never read)
     l.total = o;
     return l;
 }
@@ -340,27 +325,26 @@ template <int MT, int KP>
 __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<KP> &xs)
 {
     // x is 8-byte aligned and ldx a multiple of 4 (checked on the host): two
-    // 8-byte buffer loads per item.  Every load is issued (a thread past the
-    // last item re-reads another item and zeroes it), and a compiler barrier
-    // keeps them ahead of the pass loads, so the wait for them is exact and
-    // leaves those in flight.
+    // 8-byte buffer loads per item.  Every load is issued (so that the wait
+    // for them is exact), and a compiler barrier keeps them ahead of the pass
+    // loads, so that this wait leaves those in flight.
     const int tid = threadIdx.x;
     const int items = MT * G * 8;
-    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)x, 0, (int)(((MT - 1) * (uint32_t)ldx + 64u * (uint32_t)G) * 2u), 0x00020000);
+    const int nrec = (int)(((MT - 1) * (uint32_t)ldx + 64u * (uint32_t)G) * 2u); // < 2^31: checked on the host
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, nrec, 0x00020000);
 #pragma unroll
     for (int k = 0; k < KP; k++) {
         const int i = tid + k * kT;
-        const bool act = i < items;
-        const int ii = act ? i : i % items;
-        const int q = ii & 7, g = (ii >> 3) % G, m = (ii >> 3) / G;
-        const int off = (m * ldx + 64 * g + 4 * q) * 2;
+        // a lane past the last item gets an offset past the buffer: the load
+        // returns zeros without a memory access
+        const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
+        const int off = i < items ? (m * ldx + 64 * g + 4 * q) * 2 : nrec;
         const u32x2 va = __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0);
         const u32x2 vb = __builtin_amdgcn_raw_buffer_load_b64(xr, off + 64, 0, 0);
-        xs.lo0[k] = act ? va.x : 0u;
-        xs.lo1[k] = act ? va.y : 0u;
-        xs.hi0[k] = act ? vb.x : 0u;
-        xs.hi1[k] = act ? vb.y : 0u;
+        xs.lo0[k] = va.x;
+        xs.lo1[k] = va.y;
+        xs.hi0[k] = vb.x;
+        xs.hi1[k] = vb.y;
     }
     asm volatile("" ::: "memory");
 }
@@ -685,51 +669,6 @@ __device__ void argmax_finish(vbq_argmax_ws *ws, int tok0, const unsigned long l
 
 constexpr int kDepth = 3; // passes in flight per wavefront besides the one computed
 
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
-}
-
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
-// (m0 = lds_base, wave-uniform).  Only the warming copy uses it: its data is
-// never read, and its completion is awaited (s_waitcnt vmcnt(0)) before the
-// workgroup's LDS is released.  The s_nop separates the m0 write from the load.
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
-{
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
-}
-
-// Wavefront w fetches pass w (or the block's last) of the next launch's
-// counterpart row block: 1 KiB of codes and the 512-byte word area.
-__device__ __forceinline__ void warm_next(int wave, uint32_t lds_base)
-{
-    const u32x16 w = kernarg_line((uint32_t)(kMaxMats * sizeof(PRec)));
-    uint32_t gx = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxMats; i++)
-        gx = max(gx, w[12 + i / 2] >> (16 * (i & 1)) & 0xffffu);
-    if (!gx)
-        return;
-    const uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
-    const uint32_t bx = lin % gx, by = lin / gx;
-    const uint8_t *src = nullptr;
-#pragma unroll
-    for (int i = 0; i < kMaxMats; i++) {
-        const uint32_t wgs_i = w[12 + i / 2] >> (16 * (i & 1)) & 0xffffu;
-        const uint32_t passes_i = w[14 + i / 2] >> (16 * (i & 1)) & 0xffffu;
-        const uint8_t *p_i = (const uint8_t *)u64_ptr(w[2 * i], w[2 * i + 1]);
-        if (by == (uint32_t)i && bx < wgs_i && p_i != nullptr && passes_i > 0)
-            src = p_i + (uint64_t)bx * w[8 + i] + (uint64_t)min((uint32_t)wave, passes_i - 1) * kPassBytes;
-    }
-    if (!src)
-        return;
-    const int lane = threadIdx.x & 63;
-    dma16(src + lane * 16, lds_base);
-    if (lane < 32)
-        dma16(src + kCodeArea + lane * 16, lds_base);
-}
-
 template <int MT, int OM, int KP>
 __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_line */)
 {
@@ -764,8 +703,11 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(plan + (uint64_t)blk * region_bytes), 0, (int)region_bytes, 0x00020000);
     const int voff_c = lane * 16, voff_w = kCodeArea + lane * 8;
-    const int pmax = passes - 1;
-
+    // Loads past this wavefront's last pass (the pipeline runs kDepth + 1
+    // passes ahead; before the width bytes are in, past the plan's pass count)
+    // go through an empty resource: they are issued, so every wait stays
+    // exact, and return zeros without a memory access.
+    const __amdgpu_buffer_rsrc_t r0 = __builtin_amdgcn_make_buffer_rsrc((void *)plan, 0, 0, 0x00020000);
     // width bytes of this wavefront's passes (lane i < per_wave / 4: passes
     // 4i..4i+3 of the wave; the other lanes hold zeros)
     const bool own = lane < (per_wave >> 2);
@@ -776,10 +718,13 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     // the pass loads below in flight
     XRegs<KP> xs;
     x_load<MT, KP>(xptr, ldx, G, xs);
+    int npw = (passes - wave + kW - 1) / kW; // this wavefront's pass count (an upper bound until its width bytes are in)
     auto issue = [&](PBuf &b, int i) {
-        const int p = min(wave + kW * i, pmax); // past the block's passes: a harmless re-read
-        b.c = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_c, p * kPassBytes, 0);
-        b.w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_w, p * kPassBytes, 0);
+        const bool own = i < npw;
+        const __amdgpu_buffer_rsrc_t r = own ? rs : r0;
+        const int p = own ? wave + kW * i : 0;
+        b.c = __builtin_amdgcn_raw_buffer_load_b128(r, voff_c, p * kPassBytes, 0);
+        b.w = __builtin_amdgcn_raw_buffer_load_b64(r, voff_w, p * kPassBytes, 0);
     };
     // in the order the loop issues them (codes, then words, pass by pass), so
     // that its waits are the same on the first trip as on every later one
@@ -795,7 +740,6 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     if (tid < MT)
         best[tid] = 0ull;
     __syncthreads();
-    warm_next(wave, lds_addr(smem + L.warm));
 
     const PCtx cx{xrec, psum, G, ps, 0xffffffffu / (uint32_t)stride + 1u};
     // passes of this wavefront: its width bytes are nonzero up to the first 0
@@ -803,7 +747,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     // so full lanes form a prefix
     const int cl = (meta & 0xffu) ? ((meta & 0xff00u) ? ((meta & 0xff0000u) ? ((meta >> 24) ? 4 : 3) : 2) : 1) : 0;
     const int nfull = __popcll(__ballot(cl == 4));
-    const int npw = 4 * nfull + __builtin_amdgcn_readlane(cl, nfull);
+    npw = 4 * nfull + __builtin_amdgcn_readlane(cl, nfull);
     // pass i: the pass body, then (always, so that every step issues the same
     // loads and the waits stay exact) the loads of pass i + 4 into the same
     // registers
@@ -825,7 +769,6 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
         step(b2, i + 2);
         step(b3, i + 3);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // the warming copy has landed
     __syncthreads(); // every partial of the block is in psum
 
     const int nsum = (R * sum_lanes(G) + 63) / 64;
@@ -1072,6 +1015,8 @@ vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint1
 {
     if ((uintptr_t)x % 8 || ldx % 4)
         return VBQ_ERR_ALIGN; // the activations are read 8 bytes at a time
+    if ((int64_t)(M - 1) * ldx + items[0].P->K >= (int64_t)1 << 30)
+        return VBQ_ERR_SHAPE; // one launch's activations are addressed with 32-bit byte offsets
     PArgs a{};
     int gx = 0, smax = 2;
     for (int i = 0; i < n; i++) {
@@ -1117,25 +1062,12 @@ vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint1
     return VBQ_OK;
 }
 
-// Fills a.warm from the items of the launch that follows (none: no warming).
-void set_next(PArgs &a, const vbq_planned_item *next, int nnext)
-{
-    a.warm = PWarm{};
-    for (int i = 0; next && i < nnext && i < kMaxMats; i++) {
-        const vbq_plan *P = next[i].P;
-        a.warm.plan[i] = (const uint8_t *)next[i].plan;
-        a.warm.region[i] = (uint32_t)P->region_bytes;
-        a.warm.wgs[i] = (uint16_t)P->wgs;
-        a.warm.passes[i] = (uint16_t)P->passes;
-    }
-}
-
 // Tokens beyond what one launch holds run as further launches over the same
 // plans; each token's arithmetic is the same in every launch shape.  Every
 // launch is checked before the first is enqueued; with dry set, only the
 // checks run.
 vbq_status planned_shared(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
-                          hipStream_t stream, bool dry, const vbq_planned_item *next = nullptr, int nnext = 0)
+                          hipStream_t stream, bool dry)
 {
     if (!items || n < 1 || n > VBQ_MAX_SHARED || !x)
         return VBQ_ERR_INVALID_ARG;
@@ -1157,12 +1089,6 @@ vbq_status planned_shared(const vbq_planned_item *items, int n, int M, const uin
         for (int t0 = 0; t0 < M; t0 += chunk) {
             const int m = std::min(chunk, M - t0);
             VBQ_TRY(planned_args(items, n, m, x, ldx, yt, t0, &a, &grid, &lds));
-            // a further token chunk re-reads the same plans; after the last
-            // chunk comes the caller's next launch
-            if (t0 + chunk < M)
-                set_next(a, items, n);
-            else
-                set_next(a, next, nnext);
             if (pass == 1)
                 VBQ_TRY(launch_plan(m, kRows, a, grid, lds, stream));
         }
@@ -1175,12 +1101,6 @@ vbq_status vbq::planned_shared_check(const vbq_planned_item *items, int n, int M
                                      vbq_dtype yt)
 {
     return planned_shared(items, n, M, x, ldx, yt, nullptr, true);
-}
-
-vbq_status vbq::planned_shared_launch(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
-                                      vbq_dtype yt, hipStream_t stream, const vbq_planned_item *next, int nnext)
-{
-    return planned_shared(items, n, M, x, ldx, yt, stream, false, next, nnext);
 }
 
 extern "C" {
@@ -1225,7 +1145,6 @@ vbq_status vbq_gemv_planned_swiglu(const vbq_plan *P, const void *plan, int M, c
         for (int t0 = 0; t0 < M; t0 += chunk) {
             const int m = std::min(chunk, M - t0);
             VBQ_TRY(planned_args(&it, 1, m, x, ldx, ht, t0, &a, &grid, &lds));
-            set_next(a, nullptr, 0);
             a.rec[0].y = (uint8_t *)h + (uint64_t)t0 * (uint64_t)ldh * (uint64_t)esz;
             a.rec[0].ldy = ldh;
             if (pass == 1)
@@ -1255,7 +1174,6 @@ vbq_status vbq_gemv_planned_argmax(const vbq_plan *P, const void *plan, int M, c
         for (int t0 = 0; t0 < M; t0 += chunk) {
             const int m = std::min(chunk, M - t0);
             VBQ_TRY(planned_args(&it, 1, m, x, ldx, VBQ_F32, t0, &a, &grid, &lds));
-            set_next(a, nullptr, 0);
             a.rec[0].y = ws;
             a.rec[0].ldy = t0;
             if (pass == 1)

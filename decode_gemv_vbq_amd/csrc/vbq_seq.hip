@@ -154,13 +154,8 @@ vbq_status vbq_gemv_planned_seq(const vbq_planned_seq_item *items, int n, int M,
         launches.push_back(l);
         return planned_shared_check(l.it, k, M, l.x, l.ldx, yt);
     }));
-    // each launch warms the first passes of the one after it; the last warms
-    // the first, which a decoder runs again at its next step
-    const int nl = (int)launches.size();
-    for (int i = 0; i < nl; i++) {
-        const Launch &l = launches[i], &nx = launches[(i + 1) % nl];
-        VBQ_TRY(planned_shared_launch(l.it, l.n, M, l.x, l.ldx, yt, stream, nx.it, nx.n));
-    }
+    for (const Launch &l : launches)
+        VBQ_TRY(vbq_gemv_planned_shared(l.it, l.n, M, l.x, l.ldx, yt, stream));
     return VBQ_OK;
 }
 
