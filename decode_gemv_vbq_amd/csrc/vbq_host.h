@@ -57,6 +57,14 @@ bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x
 vbq_status planned_shared_check(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,
                                 vbq_dtype yt);
 
+// The argmax launches of vbq_gemv_planned_argmax for M (1..16) tokens of a
+// checked plan: keys and the ticket counter at `state` (16 u64 keys, then a
+// u32 counter; zero before the call, left zero after it), results to
+// index[M] and value[M].  Checks plan, x and M-dependent shapes; launches
+// nothing on error.
+vbq_status planned_argmax(const vbq_plan *P, const void *plan, int M, const uint16_t *x, int ldx, void *state,
+                          int32_t *index, float *value, hipStream_t stream);
+
 // Whether two plans can share one launch (same K and M, and one LDS carve-up
 // holds both blocks' partial sums).
 bool planned_can_share(const vbq_plan *a, const vbq_plan *b);

@@ -639,32 +639,32 @@ __device__ __forceinline__ void rowsum_item(int t, int R, int stride, int G, int
 }
 
 // Merge this workgroup's keys into the call's (agent-scope atomics on the
-// workspace); the last workgroup of the launch (a ticket counter) decodes the
-// keys of its tokens into index and value and clears keys and counter for the
-// next call.  tok0: the launch's first token.
+// keys of the argmax state); the last workgroup of the launch (a ticket
+// counter) decodes the keys of its tokens into index and value and clears
+// keys and counter for the next call.  tok0: the launch's first token.
 template <int MT>
-__device__ void argmax_finish(vbq_argmax_ws *ws, int tok0, const unsigned long long *best)
+__device__ void argmax_finish(unsigned long long *key, uint32_t *count, int32_t *index, float *value, int tok0,
+                              const unsigned long long *best)
 {
 #pragma unroll
     for (int m = 0; m < MT; m++)
-        __hip_atomic_fetch_max(&ws->key[tok0 + m], best[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max(&key[tok0 + m], best[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t total = gridDim.x * gridDim.y;
-    const uint32_t ticket = __hip_atomic_fetch_add(&ws->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ticket = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (ticket != total - 1)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
     for (int m = 0; m < MT; m++) {
-        const unsigned long long k =
-            __hip_atomic_load(&ws->key[tok0 + m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long k = __hip_atomic_load(&key[tok0 + m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t ord = (uint32_t)(k >> 32);
         const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
-        ws->index[tok0 + m] = (int32_t)(~(uint32_t)k);
-        ws->value[tok0 + m] = __uint_as_float(u);
-        __hip_atomic_store(&ws->key[tok0 + m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        index[tok0 + m] = (int32_t)(~(uint32_t)k);
+        value[tok0 + m] = __uint_as_float(u);
+        __hip_atomic_store(&key[tok0 + m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __hip_atomic_store(&ws->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kDepth = 3; // passes in flight per wavefront besides the one computed
@@ -776,8 +776,14 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
         rowsum_item<MT, OM>(t, R, stride, G, ps, psum, ybuf, yo);
     if constexpr (OM == kArgmax) {
         __syncthreads(); // every row's key is in best[]
-        if (tid == 0)
-            argmax_finish<MT>(reinterpret_cast<vbq_argmax_ws *>(yptr), ldy, best);
+        if (tid == 0) {
+            // argmax launches: y is the state (16 keys, then the counter);
+            // the second record holds the index and value outputs
+            const u32x16 o = kernarg_line((uint32_t)sizeof(PRec));
+            unsigned long long *key = reinterpret_cast<unsigned long long *>(yptr);
+            argmax_finish<MT>(key, reinterpret_cast<uint32_t *>(key + 16), (int32_t *)u64_ptr(o[0], o[1]),
+                              (float *)u64_ptr(o[2], o[3]), ldy, best);
+        }
     } else if constexpr (OM == kSwiglu) {
         __syncthreads(); // every row of the block is in ybuf
         const int pairs = R / 2; // R is even: the block starts at an even row and N is even
@@ -1153,6 +1159,35 @@ vbq_status vbq_gemv_planned_swiglu(const vbq_plan *P, const void *plan, int M, c
     return VBQ_OK;
 }
 
+} // extern "C"
+
+vbq_status vbq::planned_argmax(const vbq_plan *P, const void *plan, int M, const uint16_t *x, int ldx, void *state,
+                               int32_t *index, float *value, hipStream_t stream)
+{
+    const int chunk = P->M;
+    // the same checks and arguments as an fp32 planned GEMV writing to the
+    // state, then the record is switched to the argmax output (y = state,
+    // ldy = first token, outputs in the second record)
+    const vbq_planned_item it{P, plan, state, P->N};
+    PArgs a;
+    dim3 grid;
+    uint32_t lds;
+    for (int pass = 0; pass < 2; pass++)
+        for (int t0 = 0; t0 < M; t0 += chunk) {
+            const int m = std::min(chunk, M - t0);
+            VBQ_TRY(planned_args(&it, 1, m, x, ldx, VBQ_F32, t0, &a, &grid, &lds));
+            a.rec[0].y = state;
+            a.rec[0].ldy = t0;
+            a.rec[1].plan = (const uint8_t *)index;
+            a.rec[1].y = value;
+            if (pass == 1)
+                VBQ_TRY(launch_plan(m, kArgmax, a, grid, lds, stream));
+        }
+    return VBQ_OK;
+}
+
+extern "C" {
+
 vbq_status vbq_gemv_planned_argmax(const vbq_plan *P, const void *plan, int M, const uint16_t *x, int ldx,
                                    vbq_argmax_ws *ws, hipStream_t stream)
 {
@@ -1163,23 +1198,7 @@ vbq_status vbq_gemv_planned_argmax(const vbq_plan *P, const void *plan, int M, c
     VBQ_TRY(check_plan(P));
     if ((uintptr_t)ws % 8)
         return VBQ_ERR_ALIGN;
-    const int chunk = P->M;
-    // the same checks and arguments as an fp32 planned GEMV writing to ws, then
-    // the record is switched to the argmax output (y = ws, ldy = first token)
-    const vbq_planned_item it{P, plan, ws, P->N};
-    PArgs a;
-    dim3 grid;
-    uint32_t lds;
-    for (int pass = 0; pass < 2; pass++)
-        for (int t0 = 0; t0 < M; t0 += chunk) {
-            const int m = std::min(chunk, M - t0);
-            VBQ_TRY(planned_args(&it, 1, m, x, ldx, VBQ_F32, t0, &a, &grid, &lds));
-            a.rec[0].y = ws;
-            a.rec[0].ldy = t0;
-            if (pass == 1)
-                VBQ_TRY(launch_plan(m, kArgmax, a, grid, lds, stream));
-        }
-    return VBQ_OK;
+    return planned_argmax(P, plan, M, x, ldx, ws, ws->index, ws->value, stream);
 }
 
 } // extern "C"
