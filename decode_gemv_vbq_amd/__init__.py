@@ -32,6 +32,7 @@ EXPORTS = (
     "vbq_plan_init", "vbq_prepare", "vbq_gemv_planned", "vbq_gemv_planned_shared", "vbq_gemv_seq",
     "vbq_gemv_planned_seq", "vbq_dense_f16_gemv", "vbq_quantize", "vbq_gemv_planned_argmax",
     "vbq_gemv_planned_swiglu", "vbq_gemm_plan_init", "vbq_gemm_prepare", "vbq_gemm_workspace", "vbq_gemm",
+    "vbq_gemv_planned_argmax_noalloc",
 )
 MAX_SHARED = 4
 
@@ -133,6 +134,7 @@ def lib():
         L.vbq_gemv_planned.argtypes = [PP, P, i, P, i, P, i, i, P]
         L.vbq_gemv_planned_shared.argtypes = [ctypes.POINTER(PlannedItem), i, i, P, i, i, P]
         L.vbq_gemv_planned_argmax.argtypes = [PP, P, i, P, i, P, P]
+        L.vbq_gemv_planned_argmax_noalloc.argtypes = [PP, P, i, P, i, P, P, P]
         L.vbq_gemv_planned_swiglu.argtypes = [PP, P, i, P, i, P, i, i, P]
         L.vbq_gemv_seq.argtypes = [ctypes.POINTER(SeqItem), i, i, i, P, sz, P]
         L.vbq_gemv_planned_seq.argtypes = [ctypes.POINTER(PlannedSeqItem), i, i, i, P]
@@ -438,6 +440,26 @@ def gemv_planned_argmax(P: Plan, plan, x, ws=None):
     _check(lib().vbq_gemv_planned_argmax(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(ws),
                                          _stream()), "vbq_gemv_planned_argmax")
     return ws[36:36 + M], ws[52:52 + M].view(torch.float32)
+
+
+def gemv_planned_argmax_noalloc(P: Plan, plan, x, index=None, value=None):
+    """vbq_gemv_planned_argmax without a workspace (the library's own device
+    array holds the keys): -> (index int32[M], value float32[M])."""
+    torch = _torch()
+    _need_cuda(plan)
+    x2 = _as_2d(x)
+    M = x2.shape[0]
+    if index is None:
+        index = torch.empty(M, dtype=torch.int32, device=x.device)
+    if value is None:
+        value = torch.empty(M, dtype=torch.float32, device=x.device)
+    _need_cuda(index, value)
+    if index.dtype != torch.int32 or value.dtype != torch.float32 or index.numel() < M or value.numel() < M:
+        raise ValueError("index must be int32 and value float32 device tensors of M entries")
+    _check(lib().vbq_gemv_planned_argmax_noalloc(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0),
+                                                 _ptr(index), _ptr(value), _stream()),
+           "vbq_gemv_planned_argmax_noalloc")
+    return index, value
 
 
 def gemv_planned_shared(plans, x, outs=None, out_dtype=None):

@@ -325,6 +325,23 @@ vbq_status vbq_gemv_planned_argmax(const vbq_plan *P /* host */, const void *pla
                                    int ldx, vbq_argmax_ws *ws, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc): the result of
+ * vbq_gemv_planned_argmax (the same launches, bit for bit) with no workspace
+ * argument.  The keys and the ticket counter live in a 256-byte device array
+ * of the library (one per device, held until the process ends, cleared by
+ * the first call on each device, left cleared by every call); token m's row
+ * of the largest output goes to index[m] and that output to value[m] (device,
+ * 4-byte aligned, M entries each).  Calls on one device share the array:
+ * calls that overlap on a device (different streams) race and must be
+ * ordered by the caller.  No device memory is allocated.  Errors:
+ * VBQ_ERR_INVALID_ARG, VBQ_ERR_BATCH (M outside [1, 16], the array's
+ * limit), VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE, VBQ_ERR_ALIGN, VBQ_ERR_HIP.
+ */
+vbq_status vbq_gemv_planned_argmax_noalloc(const vbq_plan *P /* host */, const void *plan, int M, const uint16_t *x,
+                                           int ldx, int32_t *index, float *value, hipStream_t stream);
+
+/*
  * SwiGLU epilogue for the gate and up projections of an MLP block, which read
  * the same activations (the decode path of "Variable Bit-width Quantization",
  * mlsanity.com page, Abstract, runs the model's projections as fused
