@@ -37,13 +37,16 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode9b", choices=["decode9b", "decode1b", "mlp1b", "linear768"])
+    ap.add_argument("--workload", default="decode9b", choices=["decode9b", "decode1b", "mlp1b", "linear768", "batched70b"],
+                    help="decode steps (M = 1), or batched70b: the 28672x8192 up and 8192x28672 down projections "
+                         "for M in {1, 4, 8, 16} tokens, clustered / uniform 4-bit / all-8-bit widths")
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"], help="how the step is launched")
     ap.add_argument("--path", default="plan", choices=["plan", "vbq1"],
                     help="GEMVs from prepared plans (default) or straight from the VBQ1 blobs")
     ap.add_argument("--no-control", action="store_true", help="skip the fp16 dense control")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU work budget of the baseline: each of its single-thread runs takes about a quarter")
     ap.add_argument("--kernel-steps", type=int, default=5, help="replays of each per-kind kernel graph")
     ap.add_argument("--no-kinds", action="store_true",
                     help="skip the per-kind kernel timing (profiles then see only the step's own launches)")
@@ -63,6 +66,22 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
+def step_percentiles(torch, fn, steps):
+    """Per-step durations (events between consecutive steps on the launch
+    stream): median, p10 and p90 in us."""
+    import numpy as np
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)])
+    return {"median": round(float(np.median(d)), 2), "p10": round(float(np.percentile(d, 10)), 2),
+            "p90": round(float(np.percentile(d, 90)), 2)}
+
+
 def time_steps(torch, fn, steps):
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -75,7 +94,7 @@ def time_steps(torch, fn, steps):
 
 
 KERNELS = {  # path -> (kernel, entry point, profile name, sources)
-    "plan": ("k_gemv_plan<1, 0>", "vbq_gemv_planned", "k_gemv_plan", ("vbq_plan.hip", "vbq_unpack.h", "vbq_common.h")),
+    "plan": ("k_gemv_plan<1, 0, KP>", "vbq_gemv_planned", "k_gemv_plan", ("vbq_plan.hip", "vbq_unpack.h", "vbq_common.h")),
     "vbq1": ("k_gemv_stream<1>", "vbq_gemv", "k_gemv_stream", ("vbq_stream.hip", "vbq_unpack.h", "vbq_common.h")),
 }
 
@@ -105,40 +124,202 @@ def measured_traffic(workload, kpath="plan"):
     return None
 
 
-def cpu_baseline(step, budget_s):
-    """The oracle (plain C, one thread) on a bounded row sample of every matrix of
-    the step, scaled by N / rows to a whole step."""
+def cpu_info():
+    """(CPU model string, host threads this process may run on, capped at 16)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, max(1, min(avail, 16))
+
+
+def oracle_rate():
+    """Seconds per weight of the oracle GEMV (one thread, M = 1), measured on a
+    small host draw: sizes the CPU baseline's row sample before the step is built."""
+    import oracle
+    from decode_gemv_vbq_amd import workload as wl
+    spec = wl.MatrixSpec("calib", 16, 4096, wl.MIX_BASE)
+    q, b, s, x = wl.draw_matrix(spec, 99, M=1)
+    oracle.gemv(q, b, s, x)
+    t0 = time.perf_counter()
+    oracle.gemv(q, b, s, x)
+    return (time.perf_counter() - t0) / (16 * 4096)
+
+
+def cpu_baseline(step, reps=3):
+    """The oracle (plain C, fp64) timed on the host on the step's sampled rows:
+    the same device draws the GPU multiplies, copied back when the step was
+    built.  One thread, then every host thread (the sampled rows of each matrix
+    split into slices run by a thread pool; ctypes releases the GIL, the oracle
+    itself is unchanged), median of `reps` each, scaled by the step's weights
+    over the sampled weights."""
+    import concurrent.futures
+
     import numpy as np
 
     import oracle
-    from decode_gemv_vbq_amd import workload as wl
+    model, threads = cpu_info()
+    mats = [m for m in step.mats if m.sample is not None]
+    sampled = sum(m.sample[0].shape[0] * m.spec.K for m in mats)
+    total = step.weights()
 
-    W = step.W
-    # calibrate: time a small slice of the largest-K matrix
-    spec0 = max(W.mats, key=lambda s: s.K)
-    q, b, s, x = wl.draw_matrix(spec0, W.wid, M=step.M, outliers=W.outliers, N=8)
-    t0 = time.perf_counter()
-    oracle.gemv(q, b, s, x)
-    per_weight = (time.perf_counter() - t0) / (8 * spec0.K)
-    total_weights = sum(sp.N * sp.K for sp in W.mats)
-    frac = min(1.0, budget_s / max(per_weight * total_weights, 1e-9))
-    est_total = 0.0
-    sampled_rows = 0
-    spent = 0.0
-    for sp in W.mats:
-        rows = max(1, int(round(sp.N * frac)))
-        q, b, s, x = wl.draw_matrix(sp, W.wid, M=step.M, outliers=W.outliers, N=rows)
+    def run(nthr):
         t0 = time.perf_counter()
-        oracle.gemv(q, b, s, x)
-        dt = time.perf_counter() - t0
-        spent += dt
-        est_total += dt * sp.N / rows
-        sampled_rows += rows
+        with concurrent.futures.ThreadPoolExecutor(nthr) as ex:
+            futs = []
+            for m in mats:
+                q, bits, sc, x = m.sample
+                for sl in np.array_split(np.arange(q.shape[0]), min(nthr, q.shape[0])):
+                    futs.append(ex.submit(oracle.gemv, q[sl], bits[sl], sc[sl], x))
+            for f in futs:
+                f.result()
+        return time.perf_counter() - t0
+
+    one = sorted(run(1) for _ in range(reps))[reps // 2]
+    many = sorted(run(threads) for _ in range(reps))[reps // 2]
+    scale = total / sampled
     return {
-        "value": est_total * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
-        "sample": f"{sampled_rows} rows ({frac:.4f} of every matrix's rows, seeded host draw of the same "
-                  f"distributions), {spent:.1f} s measured, scaled by N/rows per matrix",
+        "value": round(many * scale * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+        "single_thread_us_per_step": round(one * scale * 1e6, 1), "cpu_model": model,
+        "sample": f"{sum(m.sample[0].shape[0] for m in mats)} rows of the step's own device draws "
+                  f"({sampled / total:.4f} of its weights), median of {reps} runs: {one:.2f} s on 1 thread, "
+                  f"{many:.2f} s on {threads} threads, scaled by weights / sampled weights",
     }
+
+
+PEAK_VALU = 256 * 64 * 2.4e9  # MI355X lane-instructions/s: 256 CUs x 64 lanes per clock x 2.4 GHz
+
+
+def valu_lane_instr(weights, M):
+    """Estimated VALU lane-instructions of a mixed-bit GEMV over `weights` for M
+    tokens: about 1.2 per weight for the unpack and bookkeeping, M / 2 dot2 per
+    weight (two products each) and M / 8 for the per-group epilogue."""
+    return weights * (1.2 + M / 2 + M / 8)
+
+
+def bench_batched(torch, v, args):
+    """The batched decode workload: the 28672x8192 up and 8192x28672 down
+    projections for M in {1, 4, 8, 16} tokens (1% outlier channels), width
+    variants clustered (runs of 8 groups from the base mix), uniform 4-bit and
+    all-8-bit.  Per (variant, M), one up+down pair through the prepared plans
+    (vbq_gemv_planned) and straight from the blobs (vbq_gemv_batched), with
+    enough weight copies in turn that a round streams at least 1 GB (so each
+    call reads from HBM), replayed from a HIP graph; the hand-written dense fp16
+    GEMV and torch.matmul on the dequantized weights of one copy at the same
+    shapes.  Rooflines: HBM (algorithmic bytes at 8 TB/s) and VALU (estimated
+    lane instructions at 39.3 T/s); the larger bounds."""
+    import numpy as np
+
+    from decode_gemv_vbq_amd import accounting as acc
+    from decode_gemv_vbq_amd import workload as wl
+    Ms = (1, 4, 8, 16)
+    rows = []
+    for variant in ("clustered", "u4", "u8"):
+        W = wl.workload("batched70b", variant=variant)
+        copies = []
+        alg1 = None
+        c = 0
+        while True:
+            pair = []
+            for spec in W.mats:
+                sp = wl.MatrixSpec(spec.name, spec.N, spec.K, spec.mix, c, spec.proj_id, spec.cluster)
+                q, bits, sc, _ = wl.draw_matrix_torch(sp, W.wid, 1)
+                blob, L = v.pack(q, bits, sc.view(torch.float16))
+                del q, bits, sc
+                plan, P = v.prepare(L, blob, M=2)
+                pair.append({"spec": spec, "L": L, "blob": blob, "plan": plan, "P": P})
+            copies.append(pair)
+            alg1 = sum(acc.vbq_read_bytes(m["L"], 0) for m in pair)
+            c += 1
+            if c * alg1 >= 1e9:
+                break
+        torch.cuda.synchronize()
+        weights = sum(m["spec"].N * m["spec"].K for m in copies[0])
+        xs_host = {spec.K: wl.draw_x(spec, W.wid, 16, outliers=W.outliers) for spec in W.mats}
+        xs = {K: torch.from_numpy(xh.view(np.int16)).cuda().view(torch.float16) for K, xh in xs_host.items()}
+        w16 = [v.dequant(m["L"], m["blob"], torch.float16) for m in copies[0]]
+        log(f"batched70b {variant}: {len(copies)} copies of up+down ({alg1 / 1e6:.1f} MB algorithmic each)")
+        for M in Ms:
+            outs = [[torch.empty((M, m["spec"].N), dtype=torch.float16, device="cuda") for m in pair]
+                    for pair in copies]
+            xm = {K: xv[:M] for K, xv in xs.items()}
+
+            def planned():
+                for pair, o in zip(copies, outs):
+                    for m, y in zip(pair, o):
+                        v.gemv_planned(m["P"], m["plan"], xm[m["spec"].K], out=y)
+
+            def blobs():
+                for pair, o in zip(copies, outs):
+                    for m, y in zip(pair, o):
+                        v.gemv_batched(m["L"], m["blob"], xm[m["spec"].K], out=y)
+
+            def dense():
+                for m, w, y in zip(copies[0], w16, outs[0]):
+                    v.dense_f16_gemv(w, xm[m["spec"].K], out=y)
+
+            def tmm():
+                for m, w, y in zip(copies[0], w16, outs[0]):
+                    torch.mm(xm[m["spec"].K], w.t(), out=y)
+
+            res = {}
+            for name, fn, n in (("planned", planned, len(copies)), ("vbq_gemv_batched", blobs, len(copies)),
+                                ("dense_f16", dense, 1), ("torch_matmul", tmm, 1)):
+                fn()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn()
+                for _ in range(2):
+                    g.replay()
+                res[name] = time_steps(torch, g.replay, max(3, args.steps // 10)) / n * 1e3  # us per pair
+                del g
+            alg = sum(acc.vbq_read_bytes(m["L"], M) for m in copies[0])
+            t_hbm = alg / PEAK_HBM
+            t_valu = valu_lane_instr(weights, M) / PEAK_VALU
+            best = min(res["planned"], res["vbq_gemv_batched"])
+            row = {"variant": variant, "M": M, **{f"{k}_us": round(t, 2) for k, t in res.items()},
+                   "alg_bytes": alg, "GBps": round(alg / (best * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(t_hbm / (best * 1e-6), 4), "valu_frac": round(t_valu / (best * 1e-6), 4),
+                   "bound": "alu" if t_valu > t_hbm else "hbm",
+                   "speedup_vs_dense_f16": round(res["dense_f16"] / best, 3),
+                   "speedup_vs_torch_matmul": round(res["torch_matmul"] / best, 3)}
+            rows.append(row)
+            log(f"  M={M:2d}: planned {res['planned']:.1f} us, vbq_gemv_batched {res['vbq_gemv_batched']:.1f} us, "
+                f"dense fp16 {res['dense_f16']:.1f} us, torch.matmul {res['torch_matmul']:.1f} us; "
+                f"{row['GBps']} GB/s, {100 * row['hbm_frac']:.1f}% of HBM, {100 * row['valu_frac']:.1f}% of VALU")
+            del outs
+        del copies, w16, xs
+        torch.cuda.empty_cache()
+    head = next(r for r in rows if r["variant"] == "clustered" and r["M"] == 16)
+    t = min(head["planned_us"], head["vbq_gemv_batched_us"]) * 1e-6
+    if head["bound"] == "alu":
+        w = sum(sp.N * sp.K for sp in wl.workload("batched70b").mats)
+        ach = valu_lane_instr(w, 16) / t
+        roof = {"bound": "alu", "achieved": round(ach / 1e12, 2), "peak": round(PEAK_VALU / 1e12, 2),
+                "unit": "T lane-instr/s", "frac": round(ach / PEAK_VALU, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": head["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": head["hbm_frac"]}
+    roof.update({"traffic": None, "kernel": "k_gemv_plan<2, 0> (vbq_gemv_planned, 8 launches of 2 tokens)"})
+    print(json.dumps({
+        "metric": "us per batched decode up+down GEMV pair (28672x8192 + 8192x28672, M=16 tokens)",
+        "value": min(head["planned_us"], head["vbq_gemv_batched_us"]), "unit": "us", "n_gpus": 1,
+        "steps": max(3, args.steps // 10), "warmup": 2, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "batched70b: up 28672x8192 + down 8192x28672, M in {1,4,8,16}, clustered / u4 / u8 "
+                               "widths, 1% outlier channels; weight copies in turn, >= 1 GB per round",
+                   "M": 16, "variant": "clustered", "sweep": rows},
+        "roofline": roof, "cpu_baseline": None}), flush=True)
 
 
 def bench_quantize(torch, v, args):
@@ -419,7 +600,16 @@ def main(argv=None):
     v.lib()
     assert torch.cuda.is_available(), "bench needs a GPU"
     log(f"{v.version()} on {torch.cuda.get_device_name(0)}")
-    step = DecodeStep(args.workload, M=1, log=log, planned=args.path == "plan")
+    if args.workload == "batched70b":
+        bench_batched(torch, v, args)
+        return
+    frac = 0.0
+    if not args.no_cpu:
+        # the CPU baseline's row sample: about cpu_seconds / 4 per single-thread run
+        from decode_gemv_vbq_amd import workload as wl
+        total_w = sum(sp.N * sp.K for sp in wl.workload(args.workload).mats)
+        frac = min(1.0, args.cpu_seconds / 4 / (oracle_rate() * total_w))
+    step = DecodeStep(args.workload, M=1, log=log, planned=args.path == "plan", sample_frac=frac)
     n_launch = len(step.stages)
     alg = step.alg_bytes()
     log(f"{args.workload}: {len(step.mats)} GEMVs in {n_launch} launches, {step.weights() / 1e9:.3f} B weights, mean {step.mean_bits():.3f} bits, "
@@ -432,7 +622,9 @@ def main(argv=None):
     for _ in range(args.warmup):
         fn()
     ms = time_steps(torch, fn, args.steps)
-    log(f"step: {ms * 1e3:.1f} us ({args.mode}), {alg / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
+    dist = step_percentiles(torch, fn, args.steps)
+    log(f"step: {ms * 1e3:.1f} us ({args.mode}), {alg / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic; per step "
+        f"median {dist['median']} us, p10 {dist['p10']}, p90 {dist['p90']}")
 
     # per-launch kernel durations: for each stage kind, that kind's launches of
     # one step captured back to back in a graph (events on the launch stream)
@@ -476,14 +668,26 @@ def main(argv=None):
         control = {"us_per_step": cms * 1e3, "GBps": dense / (cms * 1e-3) / 1e9, "bytes": dense,
                    "speedup_vbq": cms / ms}
         log(f"fp16 control: {cms * 1e3:.1f} us/step, {control['GBps']:.0f} GB/s, VBQ speedup {cms / ms:.2f}x")
+        # the library's fp16 GEMV (torch.matmul: rocBLAS / hipBLASLt) at the same shapes
+        tfn = step.run_torch_control
+        if args.mode == "graph":
+            tfn = step.capture_torch_control().replay
+        for _ in range(max(1, args.warmup // 2)):
+            tfn()
+        tms = time_steps(torch, tfn, max(3, args.steps // 5))
+        control.update({"torch_matmul_us_per_step": tms * 1e3, "torch_matmul_GBps": dense / (tms * 1e-3) / 1e9,
+                        "speedup_vbq_vs_torch_matmul": tms / ms})
+        log(f"torch.matmul fp16: {tms * 1e3:.1f} us/step, {dense / (tms * 1e-3) / 1e9:.0f} GB/s, "
+            f"VBQ speedup {tms / ms:.2f}x")
         step.free_control()
         torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
         log("CPU oracle baseline ...")
-        cpu = cpu_baseline(step, args.cpu_seconds)
-        log(f"CPU oracle: {cpu['value'] / 1e6:.1f} s/step (scaled), {cpu['sample']}")
+        cpu = cpu_baseline(step)
+        log(f"CPU oracle: {cpu['value'] / 1e6:.2f} s/step on {cpu['cores']} threads "
+            f"({cpu['single_thread_us_per_step'] / 1e6:.2f} s on one), {cpu['cpu_model']}; {cpu['sample']}")
 
     gbps = alg / (ms * 1e-3) / 1e9
     out = {
@@ -506,6 +710,7 @@ def main(argv=None):
             "weights": step.weights(), "mean_bits": round(step.mean_bits(), 4),
             "alg_bytes_per_step": alg, "layout_bytes_per_step": step.layout_bytes(),
             "GBps_step": round(gbps, 1), "pct_peak_step": round(100 * gbps * 1e9 / PEAK_HBM, 2),
+            "us_per_step_median": dist["median"], "us_per_step_p10": dist["p10"], "us_per_step_p90": dist["p90"],
             "fp16_control": None if control is None else {k: round(x, 3) if isinstance(x, float) else x
                                                           for k, x in control.items()},
             "arith": "fp16 codes x fp16 activations, fp32 accumulate",

@@ -49,7 +49,7 @@ def count_passes(P, plan) -> int:
 
 class DecodeStep:
     def __init__(self, name: str = "decode9b", M: int = 1, variant: str = "clustered", device="cuda",
-                 keep_rows: int = 0, out_dtype=None, log=None, planned: bool = True):
+                 keep_rows: int = 0, out_dtype=None, log=None, planned: bool = True, sample_frac: float = 0.0):
         import torch
         self.torch = torch
         self.planned = planned
@@ -60,9 +60,12 @@ class DecodeStep:
         self.mats: list[Matrix] = []
         self.graph = None
         self.graph16 = None
+        self.graph16t = None
         self._seq = None
         rng = np.random.default_rng(12345)
         self.stages: list[list[int]] = []
+        # sample_frac keeps that fraction of every matrix's rows (the device
+        # draws copied back), the inputs a CPU timing of the oracle runs on
         for i, spec in enumerate(self.W.mats):
             q, bits, s, x = wl.draw_matrix_torch(spec, self.W.wid, M, self.W.outliers, device=self.device)
             # the up projection reads the same activations as the gate projection
@@ -78,8 +81,10 @@ class DecodeStep:
             y = torch.empty((M, spec.N), dtype=self.out_dtype, device=self.device)
             ws = v.workspace(L, M, self.device)
             m = Matrix(spec, L, blob, x, y, ws)
-            if keep_rows:
-                rows = np.unique(np.concatenate([[0, spec.N - 1], rng.choice(spec.N, size=keep_rows, replace=False)]))
+            n_keep = max(keep_rows, int(round(sample_frac * spec.N)))
+            if n_keep:
+                n_keep = min(n_keep, spec.N)
+                rows = np.unique(np.concatenate([[0, spec.N - 1], rng.choice(spec.N, size=n_keep, replace=False)]))
                 idx = torch.from_numpy(rows).to(self.device)
                 m.sample_rows = rows
                 m.sample = (q.index_select(0, idx).cpu().numpy(), bits.index_select(0, idx).cpu().numpy(),
@@ -223,11 +228,28 @@ class DecodeStep:
         self.graph16 = g
         return g
 
+    def run_torch_control(self):
+        """The same dense fp16 weights through torch.matmul (the vendor GEMV/GEMM)."""
+        for m in self.mats:
+            self.torch.mm(m.x, m.w16.t(), out=m.y16)
+
+    def capture_torch_control(self):
+        torch = self.torch
+        self.run_torch_control()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_torch_control()
+        torch.cuda.synchronize()
+        self.graph16t = g
+        return g
+
     def free_control(self):
         for m in self.mats:
             m.w16 = None
             m.y16 = None
         self.graph16 = None
+        self.graph16t = None
 
     # ----------------------------------------------------------- accounting
     def alg_bytes(self) -> int:

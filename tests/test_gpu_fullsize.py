@@ -1,6 +1,9 @@
 """Full-size parity: the decode steps exactly as bench.py times them (the same
 DecodeStep object, HIP-graph replay, M = 1), checked against the oracle on
-sampled output rows of every matrix, plus graph-replay consistency."""
+sampled output rows of every matrix, plus graph-replay consistency; and the
+batched workload's full matrices (28672x8192 up, 8192x28672 down) at M = 16
+through both the prepared plans and vbq_gemv_batched, sampled rows against the
+oracle, with each token of the plan path equal to its own single-token run."""
 import numpy as np
 import pytest
 
@@ -50,3 +53,21 @@ def test_decode_step_sampled_parity(name, rows):
     torch.cuda.synchronize()
     for m, r in zip(step.mats, ref):
         assert torch.equal(m.y, r)
+
+
+@pytest.mark.parametrize("variant,planned", [("clustered", True), ("clustered", False), ("u4", True), ("u8", True)])
+def test_batched70b_m16_sampled_parity(variant, planned):
+    from decode_gemv_vbq_amd.step import DecodeStep
+    step = DecodeStep("batched70b", M=16, variant=variant, keep_rows=6, planned=planned)
+    step.run()
+    torch.cuda.synchronize()
+    bad, worst = check_step(step)
+    assert not bad, f"{variant} planned={planned}: {bad}"
+    print(f"batched70b {variant} planned={planned} M=16: worst err/bound {worst:.2e}")
+    if planned:
+        import decode_gemv_vbq_amd as v
+        for m in step.mats:
+            for t in (0, 15):  # a token's bits do not depend on the batch it runs in
+                yt = v.gemv_planned(m.P, m.plan, m.x[t].contiguous(), out_dtype=m.y.dtype)
+                torch.cuda.synchronize()
+                assert torch.equal(yt, m.y[t]), (m.spec.name, t)
