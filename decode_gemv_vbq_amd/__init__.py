@@ -182,6 +182,47 @@ def _need_cuda(*ts):
             raise ValueError("expected contiguous device tensors")
 
 
+def _x2(x, K: int, what: str = "x"):
+    """x as a [M][K] view: a float16 tensor [K] (one token) or [M][K], unit
+    column stride.  The device is checked by _on_device after every dtype and
+    shape check, so that each rejection can be exercised without one."""
+    torch = _torch()
+    if x.dtype != torch.float16:
+        raise ValueError(f"{what} must be float16, got {x.dtype}")
+    if x.dim() not in (1, 2) or x.shape[-1] != K:
+        raise ValueError(f"{what} must be [K] or [M][K] with K = {K}, got {tuple(x.shape)}")
+    x2 = x.view(1, -1) if x.dim() == 1 else x
+    if x2.stride(1) != 1:
+        raise ValueError(f"{what} needs unit column stride")
+    return x2
+
+
+def _y2(out, M: int, N: int, one: bool, what: str = "out"):
+    """out as a [M][N] view: float16 or float32, shape (M, N), or (N,) /
+    (1, N) for a one-token [K] input, unit column stride."""
+    torch = _torch()
+    if out.dtype not in (torch.float16, torch.float32):
+        raise ValueError(f"{what} must be float16 or float32, got {out.dtype}")
+    shape = tuple(out.shape)
+    if not (shape == (M, N) or (one and shape == (N,))):
+        want = f"({N},)" if one else f"({M}, {N})"
+        raise ValueError(f"{what} must have shape {want}, got {shape}")
+    y2 = out.view(1, -1) if out.dim() == 1 else out
+    if y2.stride(1) != 1:
+        raise ValueError(f"{what} needs unit column stride")
+    return y2
+
+
+def _on_device(**ts):
+    for name, t in ts.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+def _yt(out):
+    return VBQ_F32 if out.dtype == _torch().float32 else VBQ_F16
+
+
 def _empty_aligned(nbytes: int, device, align: int = 256):
     """A uint8 device buffer whose data pointer is `align`-byte aligned."""
     torch = _torch()
@@ -297,11 +338,18 @@ def workspace(L: Layout, M: int = 16, device="cuda"):
 def gemv(L: Layout, blob, x, out=None, out_dtype=None, ws=None):
     """y[N] = W x for x fp16[K]."""
     torch = _torch()
-    _need_cuda(blob, x)
+    x2 = _x2(x, L.K)
+    if x2.shape[0] != 1 or not x.is_contiguous():
+        raise ValueError("x must be one contiguous token, [K] or [1][K]")
     out_dtype = out_dtype or torch.float16
     if out is None:
         out = torch.empty(L.N, dtype=out_dtype, device=x.device)
-    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    _y2(out, 1, L.N, True)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    _on_device(x=x, out=out)
+    _need_cuda(blob)
+    yt = _yt(out)
     if ws is None:
         ws = workspace(L, 1, x.device)
     _check(lib().vbq_gemv(ctypes.byref(L), _ptr(blob), _ptr(x), _ptr(out), yt, _ptr(ws),
@@ -312,13 +360,17 @@ def gemv(L: Layout, blob, x, out=None, out_dtype=None, ws=None):
 def gemv_batched(L: Layout, blob, x, out=None, out_dtype=None, ws=None):
     """Y[M][N] = X[M][K] W^T for 1 <= M <= 16 (x fp16, rows may be strided)."""
     torch = _torch()
-    if x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
-        raise ValueError("x must be a [M][K] device tensor with unit column stride")
+    if x.dim() != 2:
+        raise ValueError("x must be [M][K]")
+    x = _x2(x, L.K)
     M = x.shape[0]
     out_dtype = out_dtype or torch.float16
     if out is None:
         out = torch.empty((M, L.N), dtype=out_dtype, device=x.device)
-    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    _y2(out, M, L.N, False)
+    _on_device(x=x, out=out)
+    _need_cuda(blob)
+    yt = _yt(out)
     if ws is None:
         ws = workspace(L, M, x.device)
     _check(lib().vbq_gemv_batched(ctypes.byref(L), _ptr(blob), M, _ptr(x), x.stride(0), _ptr(out), out.stride(0), yt,
@@ -330,24 +382,29 @@ def gemv_shared(mats, x, outs=None, out_dtype=None):
     """[W_i x for (L_i, blob_i) in mats] in one launch where possible: the
     matrices share K and the activations x ([M][K], or [K] for one token)."""
     torch = _torch()
+    if not mats:
+        raise ValueError("no matrices")
     one = x.dim() == 1
-    x2 = x.view(1, -1) if one else x
-    if x2.dim() != 2 or x2.stride(1) != 1 or not x2.is_cuda:
-        raise ValueError("x must be a [M][K] device tensor with unit column stride")
+    x2 = _x2(x, mats[0][0].K)
     M = x2.shape[0]
     out_dtype = out_dtype or torch.float16
     if outs is None:
         outs = [torch.empty((M, L.N), dtype=out_dtype, device=x.device) for L, _ in mats]
-    items = (GemvItem * len(mats))()
+    if len(outs) != len(mats):
+        raise ValueError("one output per matrix")
     ys = []
     for k, ((L, blob), out) in enumerate(zip(mats, outs)):
+        if L.K != mats[0][0].K:
+            raise ValueError("the matrices of a shared launch have one K")
+        ys.append(_y2(out, M, L.N, one, f"outs[{k}]"))
+        if out.dtype != outs[0].dtype:
+            raise ValueError("outputs have one dtype")
+    items = (GemvItem * len(mats))()
+    for k, ((L, blob), y2) in enumerate(zip(mats, ys)):
+        _on_device(x=x2, out=y2)
         _need_cuda(blob)
-        y2 = out.view(1, -1) if out.dim() == 1 else out
-        if y2.stride(1) != 1 or y2.dtype != outs[0].dtype:
-            raise ValueError("outputs must be [M][N] with unit column stride and one dtype")
         items[k] = GemvItem(ctypes.addressof(L), _ptr(blob), _ptr(y2), y2.stride(0))
-        ys.append(y2)
-    yt = VBQ_F32 if outs[0].dtype == torch.float32 else VBQ_F16
+    yt = _yt(outs[0])
     _check(lib().vbq_gemv_shared(items, len(mats), M, _ptr(x2), x2.stride(0), yt, _stream()), "vbq_gemv_shared")
     return outs
 
@@ -379,24 +436,18 @@ def prepare(L: Layout, blob, M: int = 1, wgs: int = 0, check: bool = True):
     return plan, P
 
 
-def _as_2d(x):
-    x2 = x.view(1, -1) if x.dim() == 1 else x
-    if x2.dim() != 2 or x2.stride(1) != 1 or not x2.is_cuda:
-        raise ValueError("x must be a [M][K] (or [K]) device tensor with unit column stride")
-    return x2
-
-
 def gemv_planned(P: Plan, plan, x, out=None, out_dtype=None):
     """Y[M][N] = X[M][K] W^T from a prepared plan (y[N] for 1-D x)."""
     torch = _torch()
-    _need_cuda(plan)
-    x2 = _as_2d(x)
+    x2 = _x2(x, P.K)
     M = x2.shape[0]
     out_dtype = out_dtype or torch.float16
     if out is None:
         out = torch.empty((M, P.N) if x.dim() == 2 else (P.N,), dtype=out_dtype, device=x.device)
-    y2 = out.view(1, -1) if out.dim() == 1 else out
-    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    y2 = _y2(out, M, P.N, x.dim() == 1)
+    _on_device(x=x2, out=y2)
+    _need_cuda(plan)
+    yt = _yt(out)
     _check(lib().vbq_gemv_planned(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), yt,
                                   _stream()), "vbq_gemv_planned")
     return out
@@ -406,14 +457,15 @@ def gemv_planned_swiglu(P: Plan, plan, x, out=None, out_dtype=None):
     """silu(gate) * up per output pair of an interleaved (gate, up) matrix plan
     -> [M][N/2] (or [N/2] for 1-D x)."""
     torch = _torch()
-    _need_cuda(plan)
-    x2 = _as_2d(x)
+    x2 = _x2(x, P.K)
     M = x2.shape[0]
     out_dtype = out_dtype or torch.float16
     if out is None:
-        out = torch.empty((M, P.N // 2), dtype=out_dtype, device=x.device)
-    h2 = out.view(1, -1) if out.dim() == 1 else out
-    ht = VBQ_F32 if h2.dtype == torch.float32 else VBQ_F16
+        out = torch.empty((M, P.N // 2) if x.dim() == 2 else (P.N // 2,), dtype=out_dtype, device=x.device)
+    h2 = _y2(out, M, P.N // 2, x.dim() == 1)
+    _on_device(x=x2, out=h2)
+    _need_cuda(plan)
+    ht = _yt(out)
     _check(lib().vbq_gemv_planned_swiglu(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(h2),
                                          h2.stride(0), ht, _stream()), "vbq_gemv_planned_swiglu")
     return out
@@ -432,11 +484,15 @@ def gemv_planned_argmax(P: Plan, plan, x, ws=None):
     """Greedy-decode argmax of W x per token from a plan: -> (index int32[M], value float32[M])
     device tensors (views into the workspace, valid until its next use)."""
     torch = _torch()
-    _need_cuda(plan)
-    x2 = _as_2d(x)
+    x2 = _x2(x, P.K)
     M = x2.shape[0]
+    _on_device(x=x2)
+    _need_cuda(plan)
     if ws is None:
         ws = argmax_workspace(x.device)
+    if ws.dtype != torch.int32 or ws.numel() * 4 < ARGMAX_WS_BYTES:
+        raise ValueError(f"ws must be an int32 tensor of {ARGMAX_WS_BYTES // 4} entries")
+    _need_cuda(ws)
     _check(lib().vbq_gemv_planned_argmax(ctypes.byref(P), _ptr(plan), M, _ptr(x2), x2.stride(0), _ptr(ws),
                                          _stream()), "vbq_gemv_planned_argmax")
     return ws[36:36 + M], ws[52:52 + M].view(torch.float32)
@@ -446,9 +502,10 @@ def gemv_planned_argmax_noalloc(P: Plan, plan, x, index=None, value=None):
     """vbq_gemv_planned_argmax without a workspace (the library's own device
     array holds the keys): -> (index int32[M], value float32[M])."""
     torch = _torch()
-    _need_cuda(plan)
-    x2 = _as_2d(x)
+    x2 = _x2(x, P.K)
     M = x2.shape[0]
+    _on_device(x=x2)
+    _need_cuda(plan)
     if index is None:
         index = torch.empty(M, dtype=torch.int32, device=x.device)
     if value is None:
@@ -465,19 +522,29 @@ def gemv_planned_argmax_noalloc(P: Plan, plan, x, index=None, value=None):
 def gemv_planned_shared(plans, x, outs=None, out_dtype=None):
     """[W_i x for (P_i, plan_i) in plans] in one launch (shared activations x)."""
     torch = _torch()
-    x2 = _as_2d(x)
+    if not plans:
+        raise ValueError("no plans")
+    one = x.dim() == 1
+    x2 = _x2(x, plans[0][0].K)
     M = x2.shape[0]
     out_dtype = out_dtype or torch.float16
     if outs is None:
         outs = [torch.empty((M, P.N), dtype=out_dtype, device=x.device) for P, _ in plans]
-    items = (PlannedItem * len(plans))()
+    if len(outs) != len(plans):
+        raise ValueError("one output per plan")
+    ys = []
     for k, ((P, plan), out) in enumerate(zip(plans, outs)):
+        if P.K != plans[0][0].K:
+            raise ValueError("the plans of a shared launch have one K")
+        ys.append(_y2(out, M, P.N, one, f"outs[{k}]"))
+        if out.dtype != outs[0].dtype:
+            raise ValueError("outputs have one dtype")
+    items = (PlannedItem * len(plans))()
+    for k, ((P, plan), y2) in enumerate(zip(plans, ys)):
+        _on_device(x=x2, out=y2)
         _need_cuda(plan)
-        y2 = out.view(1, -1) if out.dim() == 1 else out
-        if y2.stride(1) != 1 or y2.dtype != outs[0].dtype:
-            raise ValueError("outputs must be [M][N] with unit column stride and one dtype")
         items[k] = PlannedItem(ctypes.addressof(P), _ptr(plan), _ptr(y2), y2.stride(0))
-    yt = VBQ_F32 if outs[0].dtype == torch.float32 else VBQ_F16
+    yt = _yt(outs[0])
     _check(lib().vbq_gemv_planned_shared(items, len(plans), M, _ptr(x2), x2.stride(0), yt, _stream()),
            "vbq_gemv_planned_shared")
     return outs
@@ -508,17 +575,19 @@ class Seq:
         self.arr = (Item * len(items))()
         self.M = None
         ydt = None
+        views = []
         for k, (meta, buf, x, y, stage) in enumerate(items):
-            _need_cuda(buf)
-            x2 = x.view(1, -1) if x.dim() == 1 else x
-            y2 = y.view(1, -1) if y.dim() == 1 else y
-            if x2.dim() != 2 or x2.stride(1) != 1 or not x2.is_cuda or x2.dtype != torch.float16:
-                raise ValueError("x must be a fp16 [M][K] device tensor with unit column stride")
-            if y2.stride(1) != 1 or (ydt is not None and y2.dtype != ydt):
-                raise ValueError("outputs must be [M][N] with unit column stride and one dtype")
+            x2 = _x2(x, meta.K, f"items[{k}] x")
             if self.M is not None and x2.shape[0] != self.M:
                 raise ValueError("every GEMV of a step has the same token count M")
+            y2 = _y2(y, x2.shape[0], meta.N, x.dim() == 1, f"items[{k}] y")
+            if ydt is not None and y2.dtype != ydt:
+                raise ValueError("the outputs of a step have one dtype")
             self.M, ydt = x2.shape[0], y2.dtype
+            views.append((x2, y2))
+        for k, ((meta, buf, x, y, stage), (x2, y2)) in enumerate(zip(items, views)):
+            _on_device(x=x2, y=y2)
+            _need_cuda(buf)
             self.arr[k] = Item(ctypes.addressof(meta), _ptr(buf), _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0),
                                int(stage))
         self.yt = VBQ_F32 if ydt == torch.float32 else VBQ_F16
@@ -577,14 +646,15 @@ def gemm_workspace(GP: GemmPlan, M: int, device="cuda"):
 def gemm(GP: GemmPlan, buf, x, out=None, out_dtype=None, ws=None):
     """Y[M][N] = X[M][K] W^T from a GEMM plan (the prefill path, M > 16)."""
     torch = _torch()
-    _need_cuda(buf)
-    x2 = _as_2d(x)
+    x2 = _x2(x, GP.K)
     M = x2.shape[0]
     out_dtype = out_dtype or torch.float16
     if out is None:
         out = torch.empty((M, GP.N) if x.dim() == 2 else (GP.N,), dtype=out_dtype, device=x.device)
-    y2 = out.view(1, -1) if out.dim() == 1 else out
-    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
+    y2 = _y2(out, M, GP.N, x.dim() == 1)
+    _on_device(x=x2, out=y2)
+    _need_cuda(buf)
+    yt = _yt(out)
     if ws is None:
         ws = gemm_workspace(GP, M, x.device)
     _check(lib().vbq_gemm(ctypes.byref(GP), _ptr(buf), M, _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), yt,
@@ -595,15 +665,19 @@ def gemm(GP: GemmPlan, buf, x, out=None, out_dtype=None, ws=None):
 def dense_f16_gemv(w16, x, out=None, out_dtype=None):
     """Dense fp16 control: y[M][N] = x[M][K] W16^T (or y[N] for 1-D x)."""
     torch = _torch()
-    _need_cuda(w16)
-    one = x.dim() == 1
-    x2 = x.view(1, -1) if one else x
-    M = x2.shape[0]
+    if w16.dtype != torch.float16 or w16.dim() != 2:
+        raise ValueError("w16 must be a float16 [N][K] tensor")
     N, K = w16.shape
+    one = x.dim() == 1
+    x2 = _x2(x, K)
+    M = x2.shape[0]
     out_dtype = out_dtype or torch.float16
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    yt = VBQ_F32 if out.dtype == torch.float32 else VBQ_F16
-    _check(lib().vbq_dense_f16_gemv(N, K, M, _ptr(w16), _ptr(x2), x2.stride(0), _ptr(out), out.stride(0), yt,
+        out = torch.empty((N,) if one else (M, N), dtype=out_dtype, device=x.device)
+    y2 = _y2(out, M, N, one)
+    _on_device(x=x2, out=y2)
+    _need_cuda(w16)
+    yt = _yt(out)
+    _check(lib().vbq_dense_f16_gemv(N, K, M, _ptr(w16), _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), yt,
                                     _stream()), "vbq_dense_f16_gemv")
-    return out[0] if one else out
+    return out

@@ -3,6 +3,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+
 #include "vbq_common.h"
 #include "vbq_host.h"
 
@@ -119,6 +122,30 @@ __global__ void k_zero_u32(uint32_t *p, uint64_t nwords)
 } // namespace
 
 namespace vbq {
+
+int current_device_cus()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    return cus;
+}
+
+vbq_status dynamic_lds_once(const void *fn, int bytes)
+{
+    static std::mutex mu;
+    static std::map<std::pair<const void *, int>, int> done;  // (kernel, device) -> bytes set
+    int dev = 0;
+    VBQ_TRY(hip_status(hipGetDevice(&dev)));
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = done.find({fn, dev});
+    if (it != done.end() && it->second >= bytes)
+        return VBQ_OK;
+    VBQ_TRY(hip_status(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)));
+    done[{fn, dev}] = bytes;
+    return VBQ_OK;
+}
 
 vbq_status zero_words(void *p, uint64_t bytes, hipStream_t stream)
 {

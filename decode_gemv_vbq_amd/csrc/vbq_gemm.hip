@@ -607,17 +607,7 @@ uint32_t lds_need(int MT, int F)
     return 2u * kWBytes + 2u * (32u * (uint32_t)MT) * kLdw * 2u + (uint32_t)kRing * 4096u * (uint32_t)F;
 }
 
-int gemm_cus()
-{
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 256;
-    }
-    return cus;
-}
+int gemm_cus() { return current_device_cus(); }
 
 vbq_status check_gemm_plan(const vbq_gemm_plan *P)
 {
@@ -694,12 +684,7 @@ GWs ws_layout(const vbq_gemm_plan *P, const GShape &s)
 template <int MT>
 vbq_status launch_gemm(const GArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
-    static bool configured = false;
-    if (!configured) {
-        VBQ_TRY(hip_status(hipFuncSetAttribute((const void *)k_gemm<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               kGLds)));
-        configured = true;
-    }
+    VBQ_TRY(dynamic_lds_once((const void *)k_gemm<MT>, kGLds));
     hipLaunchKernelGGL(k_gemm<MT>, grid, dim3(kGT), lds, stream, a);
     return launch_status();
 }

@@ -1000,16 +1000,8 @@ Plan make_plan(const vbq_layout *L, int MT)
 template <int MT>
 vbq_status launch(GemvArgs a, const Plan &p, hipStream_t stream)
 {
-    static int configured = 0;
-    static int cus = 0;
-    if (!configured) {
-        VBQ_TRY(hip_status(hipFuncSetAttribute((const void *)k_gemv<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               96 * 1024)));
-        int dev = 0;
-        VBQ_TRY(hip_status(hipGetDevice(&dev)));
-        VBQ_TRY(hip_status(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)));
-        configured = 1;
-    }
+    VBQ_TRY(dynamic_lds_once((const void *)k_gemv<MT>, 96 * 1024));
+    const int cus = current_device_cus();
     int per_cu = 0;
     VBQ_TRY(hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv<MT>, kThreads,
                                                                      p.smem)));
@@ -1029,12 +1021,7 @@ vbq_status launch(GemvArgs a, const Plan &p, hipStream_t stream)
 template <int MT>
 vbq_status launch_wave(GemvArgs a, const WavePlan &p, int cus, hipStream_t stream)
 {
-    static int configured = 0;
-    if (!configured) {
-        VBQ_TRY(hip_status(hipFuncSetAttribute((const void *)k_gemv_wave<MT>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)));
-        configured = 1;
-    }
+    VBQ_TRY(dynamic_lds_once((const void *)k_gemv_wave<MT>, 160 * 1024));
     int per_cu = 0;
     VBQ_TRY(hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv_wave<MT>,
                                                                      kWThreads, p.smem)));
@@ -1050,16 +1037,6 @@ vbq_status launch_wave(GemvArgs a, const WavePlan &p, int cus, hipStream_t strea
     return launch_status();
 }
 
-int device_cus()
-{
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 256;
-    }
-    return cus;
-}
 
 } // namespace
 
@@ -1099,7 +1076,7 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
             return st;
     }
     int MT = tokens_template(M);
-    const int cus = device_cus();
+    const int cus = current_device_cus();
     WavePlan wp = make_wave_plan(L, MT, cus);
     Plan p = make_plan(L, MT);
     GemvArgs a;

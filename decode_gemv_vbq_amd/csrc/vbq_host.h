@@ -22,6 +22,14 @@ vbq_status zero_words(void *p, uint64_t bytes, hipStream_t stream);
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
+// Compute units of the current device, queried on every call (so a process
+// that drives several devices gets each one's count); 256 if the query fails.
+int current_device_cus();
+
+// hipFuncSetAttribute(fn, MaxDynamicSharedMemorySize, bytes) once per kernel
+// and device; thread-safe.
+vbq_status dynamic_lds_once(const void *fn, int bytes);
+
 // One GEMV request after host-side validation.
 struct GemvCall {
     const vbq_layout *L;

@@ -34,8 +34,6 @@
 // records are ready; every partial is written), then the rows are summed in
 // a fixed order, so the result does not depend on timing.
 #include <algorithm>
-#include <mutex>
-#include <set>
 
 #include "vbq_common.h"
 #include "vbq_host.h"
@@ -803,15 +801,6 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
 // ---------------------------------------------------------------------------
 // Host side.
 
-int device_cus()
-{
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        cus = 256;
-    return cus;
-}
-
 uint64_t region_of(int passes, int per_wave)
 {
     return align_up((uint64_t)passes * kPassBytes + (uint64_t)kW * per_wave, 256);
@@ -852,20 +841,7 @@ PrepArgs prep_args(const vbq_layout *L, const void *blob, const vbq_plan *P)
     return a;
 }
 
-// hipFuncSetAttribute once per kernel and device (thread-safe).
-vbq_status lds_attribute_once(const void *fn)
-{
-    static std::mutex mu;
-    static std::set<std::pair<const void *, int>> done;
-    int dev = 0;
-    VBQ_TRY(hip_status(hipGetDevice(&dev)));
-    std::lock_guard<std::mutex> lock(mu);
-    if (done.count({fn, dev}))
-        return VBQ_OK;
-    VBQ_TRY(hip_status(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget)));
-    done.insert({fn, dev});
-    return VBQ_OK;
-}
+vbq_status lds_attribute_once(const void *fn) { return dynamic_lds_once(fn, kLdsBudget); }
 
 template <int MT, int OM, int KP>
 vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
@@ -932,7 +908,7 @@ vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, 
     const int N = (int)L->N, G = (int)L->G;
     if (G > kMaxG)
         return VBQ_ERR_SHAPE;
-    const int cus = device_cus();
+    const int cus = current_device_cus();
     if (wgs <= 0)
         wgs = cus;
     // rows per block: an even count whenever N is even, so that a row block

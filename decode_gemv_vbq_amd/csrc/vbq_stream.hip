@@ -803,27 +803,10 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs args)
     }
 }
 
-int device_cus()
-{
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 256;
-    }
-    return cus;
-}
-
 template <int MT>
 vbq_status launch_stream(const SArgs &a, int grid, size_t smem, hipStream_t stream)
 {
-    static bool configured = false;
-    if (!configured) {
-        VBQ_TRY(hip_status(hipFuncSetAttribute((const void *)k_gemv_stream<MT>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)));
-        configured = true;
-    }
+    VBQ_TRY(dynamic_lds_once((const void *)k_gemv_stream<MT>, 160 * 1024));
     hipLaunchKernelGGL(k_gemv_stream<MT>, dim3(grid), dim3(kT), smem, stream, a);
     return launch_status();
 }
@@ -844,7 +827,7 @@ bool make_plan(const StreamItem *items, int n, int M, Plan &p)
     int64_t total = 0;
     for (int i = 0; i < n; i++)
         total += items[i].L->N;
-    const int wgs = device_cus();
+    const int wgs = current_device_cus();
     int rows = (int)((total + wgs - 1) / wgs);
     rows = std::max(1, std::min(rows, kMetaRS / nS));
     const uint32_t budget = 160u * 1024u;

@@ -31,8 +31,13 @@
  *
  * Conventions for every call below:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
- *     memory (blob, q, bits, scales, x, y, w, workspaces, status words); the
- *     library never allocates device memory and keeps no global state.
+ *     memory (blob, q, bits, scales, x, y, w, workspaces, status words).  The
+ *     library allocates no device memory at run time; its only global state
+ *     is (a) a per-(kernel, device) record that the dynamic-LDS attribute has
+ *     been set (mutex-guarded, set on a kernel's first launch on a device),
+ *     (b) vbq_last_error()'s thread-local text, and (c) the 256-byte device
+ *     array of vbq_gemv_planned_argmax_noalloc, one per device that calls it.
+ *     The compute-unit count is read from the current device on every call.
  *   - Calls are asynchronous on `stream` unless marked SYNC.  Argument checks
  *     run on the host before any launch; a call that returns an error has
  *     launched nothing.  VBQ_ERR_HIP carries the HIP error text in
@@ -115,6 +120,10 @@ vbq_status vbq_pack_plan(int N, int K, const uint8_t *bits, vbq_layout *L /* hos
                          hipStream_t stream);
 
 /*
+ * Storage of the frozen allocation: "Variable Bit-width Quantization"
+ * (mlsanity.com page, Abstract) keeps each 64-weight group at its own width
+ * in {1, 2, 4, 8} and stores the model as packed low-bit codes; the VBQ1
+ * layout above is this library's packing of them.
  * Pack q[N][K] (u8 codes), bits[N][G] (u8 widths), scales[N][G] (fp16 bits)
  * into blob (L->total_bytes bytes, 256-byte aligned, any prior contents).
  * Every blob byte is written; the result is the unique VBQ1 byte string.
@@ -154,6 +163,9 @@ vbq_status vbq_quantize(int N, int K, const void *w, vbq_dtype wt, int ldw, cons
                         uint16_t *scales, uint32_t *status_word, hipStream_t stream);
 
 /*
+ * The dequantize half of the fused dequantize-and-multiply kernels of
+ * "Variable Bit-width Quantization" (mlsanity.com page, Abstract), on its own:
+ * the group rule w = s * (q - (2^b - 1)/2) stated at the top of this file.
  * Expand a blob to dense weights w[N][K] (row-major): VBQ_F32 gives the exact
  * value of s*(q - (2^b-1)/2); VBQ_F16 gives its round-to-nearest-even fp16.
  */
@@ -171,6 +183,10 @@ vbq_status vbq_workspace_size(const vbq_layout *L /* host */, int M, size_t *byt
 vbq_status vbq_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The decode GEMV: "Variable Bit-width Quantization" (mlsanity.com page,
+ * Abstract) decodes autoregressively, bound by memory bandwidth, with fused
+ * dequantize-and-multiply kernels over the packed mixed-width codes; this is
+ * that product for one token, read straight from a VBQ1 blob.
  * y = W x for one token: x fp16[K], y[N] in yt (VBQ_F16 rounds to nearest
  * even).  Accumulation is fp32; |y - y_exact| <= 1e-3 * sum_k |w_k||x_k| per
  * output.  Outputs that meet a non-finite weight (inf/NaN scale) with a
@@ -180,6 +196,8 @@ vbq_status vbq_gemv(const vbq_layout *L /* host */, const void *blob, const uint
                     void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The same fused dequantize-and-multiply product ("Variable Bit-width
+ * Quantization", mlsanity.com page, Abstract) for a decode batch of M tokens.
  * Y = X W^T for M tokens (1 <= M <= 16): x fp16 [M][ldx] (ldx >= K),
  * y [M][ldy] (ldy >= N).  Each packed code is unpacked once per call and
  * reused for all M tokens.  Error bound as vbq_gemv, per token and output.
