@@ -236,7 +236,7 @@ def bench_batched(torch, v, args):
                 blob, L = v.pack(q, bits, sc.view(torch.float16))
                 del q, bits, sc
                 plan, P = v.prepare(L, blob, M=2)
-                pair.append({"spec": spec, "L": L, "blob": blob, "plan": plan, "P": P})
+                pair.append({"spec": spec, "L": L, "blob": blob, "plan": plan, "P": P, "ws": v.workspace(L, 16)})
             copies.append(pair)
             alg1 = sum(acc.vbq_read_bytes(m["L"], 0) for m in pair)
             c += 1
@@ -261,7 +261,7 @@ def bench_batched(torch, v, args):
             def blobs():
                 for pair, o in zip(copies, outs):
                     for m, y in zip(pair, o):
-                        v.gemv_batched(m["L"], m["blob"], xm[m["spec"].K], out=y)
+                        v.gemv_batched(m["L"], m["blob"], xm[m["spec"].K], out=y, ws=m["ws"])
 
             def dense():
                 for m, w, y in zip(copies[0], w16, outs[0]):

@@ -1049,15 +1049,13 @@ vbq_status vbq_workspace_size(const vbq_layout *L, int M, size_t *bytes)
     VBQ_TRY(check_layout(L));
     if (M < 1 || M > 16)
         return VBQ_ERR_BATCH;
-    *bytes = 0; // rows are never split across workgroups
+    *bytes = M >= kMfmaMinTokens ? mfma_workspace(L, M) : 0;
     return VBQ_OK;
 }
 
 vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const uint16_t *x, int ldx, void *y, int ldy,
                             vbq_dtype yt, void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     if (!blob || !x || !y)
         return VBQ_ERR_INVALID_ARG;
     if (yt != VBQ_F32 && yt != VBQ_F16)
@@ -1071,6 +1069,8 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
         return VBQ_ERR_ALIGN;
     {
         GemvCall call{L, blob, M, x, ldx, y, ldy, yt, stream};
+        if (mfma_applies(L, M, x, ldx))
+            return mfma_gemv(call, ws, ws_bytes);
         vbq_status st;
         if (stream_gemv(call, &st))
             return st;

@@ -60,6 +60,16 @@ struct StreamItem {
 bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
                         hipStream_t stream, vbq_status *st);
 
+// The matrix-core batched GEMV (vbq_mfma.hip): used for M >= kMfmaMinTokens
+// when x is 16-byte aligned, ldx % 8 == 0 and the blob and x fit 32-bit
+// buffer offsets.
+constexpr int kMfmaMinTokens = 3;
+bool mfma_applies(const vbq_layout *L, int M, const uint16_t *x, int ldx);
+// Workspace bytes for the K split the current device would use at M tokens.
+size_t mfma_workspace(const vbq_layout *L, int M);
+// Launch on g.stream; splits K only when ws (4-byte aligned) holds the partial sums.
+vbq_status mfma_gemv(const GemvCall &g, void *ws, size_t ws_bytes);
+
 // Every check vbq_gemv_planned_shared makes, for every launch it would
 // enqueue; launches nothing.
 vbq_status planned_shared_check(const vbq_planned_item *items, int n, int M, const uint16_t *x, int ldx,

@@ -88,9 +88,14 @@ def test_gemv_argument_checks_fail_before_launch():
     null = P(0)
     ref = ctypes.byref(L)
     sz = ctypes.c_size_t(0)
-    assert lib.vbq_workspace_size(ref, 16, ctypes.byref(sz)) == 0
-    need = sz.value  # rows are never split across workgroups: no workspace
-    assert need == 0
+    # the workspace holds the fp32 partial sums of a K split: none for M <= 2,
+    # else a whole number (at most 16) of [M][N] planes
+    for M in (1, 2):
+        assert lib.vbq_workspace_size(ref, M, ctypes.byref(sz)) == 0 and sz.value == 0
+    for M in (3, 16):
+        assert lib.vbq_workspace_size(ref, M, ctypes.byref(sz)) == 0
+        assert sz.value % (4 * M * 4) == 0 and sz.value <= 16 * 4 * M * 4
+    need = sz.value
 
     def call(M=1, blob=fake, x=fake, ldx=4096, y=fake, ldy=4, yt=1, ws=fake, wsb=None):
         return v.STATUS[lib.vbq_gemv_batched(ref, blob, M, x, ldx, y, ldy, yt, ws, need if wsb is None else wsb, null)]
