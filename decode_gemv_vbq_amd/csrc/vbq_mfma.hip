@@ -25,14 +25,15 @@
 // low 16 bits, half 1 in the high 16 bits).  A and B use the same order, and
 // the contraction does not depend on it.
 //
-// Workgroup: 8 wavefronts = 128 rows x a K range of whole 8-group chunks.  Per
-// chunk, in one of three LDS buffers: the 8 groups' activations as fp16 pairs
-// (wavefront w stages group w), their offset constants, and per wavefront the
-// byte offset, width and scale of each of its rows' 8 groups.  While chunk c is
-// computed, chunk c+2 is staged and its code words are loaded into registers
-// (three register sets), and the inputs of chunk c+5 (activations, width
-// planes, slice offsets, scales) are loaded: every load has two to three
-// chunks of work to arrive in.
+// Workgroup: 4 wavefronts = 64 rows x a K range of whole 4-group chunks, at
+// most 128 registers per lane so that four workgroups share a compute unit
+// (four wavefronts per SIMD hide each other's LDS, matrix-core and memory
+// latencies).  Per chunk, in one of two LDS buffers: the 4 groups' activations
+// as fp16 pairs (wavefront w stages group w), their offset constants, and per
+// wavefront the byte offset, width and scale of its 16 rows' 4 groups (lane
+// (q, n) works out group q of row n).  While chunk c is computed, chunk c+1 is
+// staged and its code words are loaded into registers, and the inputs of chunk
+// c+3 (activations, width planes, slice offset, scale) are loaded.
 //
 // K segments.  A matrix with too few row blocks to fill the device has its
 // chunks cut into segments (from the shape and the device's compute units
@@ -50,10 +51,11 @@ using namespace vbq;
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 16 * kWaves;
-constexpr int kChunk = 8;              // groups per chunk: wavefront w stages group w
+constexpr int kChunk = 4;              // groups per chunk: wavefront w stages group w, lane (q, n) plans group q
+constexpr int kBlocksPerCu = 4;
 constexpr int kTok = 144;              // LDS bytes per token of a staged group (128 + 16 against bank conflicts)
 constexpr int kXGroup = 16 * kTok;     // one staged group, 16 tokens
 constexpr int kXBytes = kChunk * kXGroup;
@@ -62,8 +64,9 @@ constexpr int kCBytes = kChunk * kCGroup;
 constexpr int kMWave = kChunk * 16 * 8; // one wavefront's metadata: [group][row] {offset | code, scale}
 constexpr int kMBytes = kWaves * kMWave;
 constexpr int kBufBytes = kXBytes + kCBytes + kMBytes;
-constexpr int kBufs = 3;
-constexpr int kLdsBytes = kBufs * kBufBytes;
+constexpr int kBufs = 2;
+constexpr int kTabBytes = 5 * 48;      // B operands of the offset constants: [width code, or 4 = zero][Bm0 Bm1 Bo]
+constexpr int kLdsBytes = kBufs * kBufBytes + kTabBytes;
 constexpr int kMaxSplits = 16;
 constexpr uint32_t kNone = 0xffffffffu; // a buffer offset past every buffer: the load returns 0 and reads nothing
 
@@ -156,15 +159,15 @@ __device__ __forceinline__ void unpack_quarter(const u32x4 &w, uint32_t rot, uin
     }
 }
 
-// Per-chunk inputs a lane loads one chunk before they are staged.
+// Per-chunk inputs a lane loads two chunks before they are staged.
 struct ChunkIn {
     u32x4 xa, xb;    // activations: token n, columns 64g+8q..+7 and 64g+32+8q..+7 of the staged group
-    uint32_t p0, p1; // width-code bit planes of this lane's row, its slice
+    uint32_t p0, p1; // width-code bit planes of this lane's row in the slice of its planned group
     uint32_t so;     // slice offset in the row record
-    uint32_t s0, s1; // scales of groups 8c+2q, 8c+2q+1 (fp16 bits)
+    uint32_t sc;     // scale of the planned group (fp16 bits)
 };
 
-__global__ __launch_bounds__(kThreads) void k_gemv_mfma(MArgs a)
+__global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -176,22 +179,21 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(MArgs a)
     const int c1 = min(nch, c0 + a.chunks_per_split);
     const __amdgpu_buffer_rsrc_t rb = rsrc(a.blob, a.blob_bytes);
     const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
+    uint8_t *tab = smem + kBufs * kBufBytes;
 
-    // B operands of the offset constants: column n < 4 is width code n
-    uint32_t bm0[4], bm1[4], bo[4];
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-        bm0[v] = n < 4 ? neg_magic_pair(mpos(n, v)) : 0u;
-        bm1[v] = n < 4 ? neg_magic_pair(mpos(n, 4 + v)) : 0u;
-        bo[v] = n < 4 ? neg_offset_pair(n) : 0u;
+    // table of the offset constants' B operands: entry c < 4 is column width
+    // code c (k-slot pairs 0..3, 4..7, then the (2^b - 1)/2 part), entry 4 zero
+    if (threadIdx.x < 60) {
+        const int c = threadIdx.x / 12, k = threadIdx.x % 12, v = k & 3;
+        const uint32_t val = c == 4 ? 0u : k < 4 ? neg_magic_pair(mpos(c, v)) : k < 8 ? neg_magic_pair(mpos(c, 4 + v))
+                                                                                      : neg_offset_pair(c);
+        reinterpret_cast<uint32_t *>(tab)[threadIdx.x] = val;
     }
-    const hf8 Bm0 = as_hf8(bm0[0], bm0[1], bm0[2], bm0[3]), Bm1 = as_hf8(bm1[0], bm1[1], bm1[2], bm1[3]);
-    const hf8 Bo = as_hf8(bo[0], bo[1], bo[2], bo[3]);
 
     const uint32_t row_off = __builtin_amdgcn_raw_buffer_load_b32(rb, live ? a.off_row_off + 4u * row : kNone, 0, 0);
     const uint32_t row_base = a.off_codes + 128u * row_off;
 
-    // inputs of chunk ch (all offsets kNone past the K range: zeros, no reads)
+    // inputs of chunk ch (offsets kNone past the K range: zeros, no reads)
     auto load_in = [&](int ch, ChunkIn &in) {
         const bool on = ch < c1;
         const int g = ch * kChunk + wave;
@@ -199,16 +201,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(MArgs a)
         const uint32_t xo = 2u * ((uint32_t)n * (uint32_t)a.ldx + 64u * (uint32_t)g + 8u * q);
         in.xa = __builtin_amdgcn_raw_buffer_load_b128(rx, xon ? xo : kNone, 0, 0);
         in.xb = __builtin_amdgcn_raw_buffer_load_b128(rx, xon ? xo + 64u : kNone, 0, 0);
-        const int gi = ch * kChunk + 2 * q, sl = gi >> 5;
+        const int gi = ch * kChunk + q;
         const bool mon = on && live && gi < a.G;
-        const uint32_t rs = (uint32_t)row * (uint32_t)a.nS + (uint32_t)sl;
+        const uint32_t rs = (uint32_t)row * (uint32_t)a.nS + (uint32_t)(gi >> 5);
         const u32x2 wm = __builtin_amdgcn_raw_buffer_load_b64(rb, mon ? a.off_wmap + 8u * rs : kNone, 0, 0);
         in.p0 = wm.x;
         in.p1 = wm.y;
         in.so = __builtin_amdgcn_raw_buffer_load_b32(rb, mon ? a.off_slice_off + 4u * rs : kNone, 0, 0);
-        const uint32_t so = a.off_scales + 2u * ((uint32_t)row * (uint32_t)a.G + (uint32_t)gi);
-        in.s0 = __builtin_amdgcn_raw_buffer_load_b16(rb, mon ? so : kNone, 0, 0);
-        in.s1 = __builtin_amdgcn_raw_buffer_load_b16(rb, mon && gi + 1 < a.G ? so + 2u : kNone, 0, 0);
+        in.sc = __builtin_amdgcn_raw_buffer_load_b16(
+            rb, mon ? a.off_scales + 2u * ((uint32_t)row * (uint32_t)a.G + (uint32_t)gi) : kNone, 0, 0);
     };
 
     // stage chunk ch into buffer bi: activations, offset constants, this
@@ -224,34 +225,31 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(MArgs a)
         u32x4 *xs = reinterpret_cast<u32x4 *>(buf + wave * kXGroup + n * kTok + 32 * q);
         xs[0] = u32x4{p[0], p[1], p[2], p[3]};
         xs[1] = u32x4{p[4], p[5], p[6], p[7]};
+        const u32x4 *tb = reinterpret_cast<const u32x4 *>(tab + 48 * (n < 4 ? n : 4));
+        const u32x4 bm0 = tb[0], bm1 = tb[1], bo = tb[2];
         const hf8 A0 = as_hf8(p[0], p[1], p[2], p[3]), A1 = as_hf8(p[4], p[5], p[6], p[7]);
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mfma(A0, Bm0, d);
-        d = mfma(A1, Bm1, d);
-        d = mfma(A0, Bo, d);
-        d = mfma(A1, Bo, d);
+        d = mfma(A0, as_hf8(bm0.x, bm0.y, bm0.z, bm0.w), d);
+        d = mfma(A1, as_hf8(bm1.x, bm1.y, bm1.z, bm1.w), d);
+        d = mfma(A0, as_hf8(bo.x, bo.y, bo.z, bo.w), d);
+        d = mfma(A1, as_hf8(bo.x, bo.y, bo.z, bo.w), d);
         if (n < 4)
             *reinterpret_cast<f32x4 *>(buf + kXBytes + wave * kCGroup + n * 64 + 16 * q) = d;
 
-        const int gi = ch * kChunk + 2 * q, sl = gi >> 5, i0 = gi & 31;
+        const int gi = ch * kChunk + q, sl = gi >> 5, i = gi & 31;
         const int ng = min(32, a.G - 32 * sl);
         const WidthMasks wm = width_masks(in.p0, in.p1, ng);
-        uint32_t st[4];
-        st[0] = 0u;
-        st[1] = 8u * (uint32_t)__popc(wm.m[0]);
-        st[2] = st[1] + 16u * (uint32_t)__popc(wm.m[1]);
-        st[3] = st[2] + 32u * (uint32_t)__popc(wm.m[2]);
-        uint8_t *mb = buf + kXBytes + kCBytes + wave * kMWave;
+        const int c = (int)(((in.p0 >> i) & 1u) | (((in.p1 >> i) & 1u) << 1));
+        uint32_t start = 0u;
 #pragma unroll
-        for (int e = 0; e < 2; e++) {
-            const int i = i0 + e;
-            const int c = (int)(((in.p0 >> i) & 1u) | (((in.p1 >> i) & 1u) << 1));
-            const uint32_t rank = (uint32_t)__popc(pick4(wm.m, c) & ((1u << i) - 1u));
-            const uint32_t off = row_base + in.so + pick4(st, c) + (rank << (3 + c));
-            const bool ok = live && ch < c1 && gi + e < a.G;
-            *reinterpret_cast<u32x2 *>(mb + (2 * q + e) * 128 + n * 8) =
-                u32x2{ok ? off | (uint32_t)c : 0u, ok ? (e ? in.s1 : in.s0) : 0u};
-        }
+        for (int cc = 0; cc < 3; cc++)
+            if (cc < c)
+                start += (uint32_t)__popc(wm.m[cc]) << (3 + cc);
+        const uint32_t rank = (uint32_t)__popc(pick4(wm.m, c) & ((1u << i) - 1u));
+        const uint32_t off = row_base + in.so + start + (rank << (3 + c));
+        const bool ok = live && ch < c1 && gi < a.G;
+        *reinterpret_cast<u32x2 *>(buf + kXBytes + kCBytes + wave * kMWave + q * 128 + n * 8) =
+            u32x2{ok ? off | (uint32_t)c : 0u, ok ? in.sc : 0u};
     };
 
     // code words of the staged chunk in buffer bi, this lane's quarter (byte
@@ -308,40 +306,32 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(MArgs a)
         }
     };
 
-    // ---- prologue: chunks c0 and c0+1 staged (buffers 0, 1), their codes in
-    // flight, the inputs of c0+2 .. c0+4 in flight
-    ChunkIn in0, in1, in2;
-    u32x4 cw0[kChunk], cw1[kChunk], cw2[kChunk];
+    // ---- prologue: chunk c0 staged (buffer 0), its codes and the inputs of
+    // chunks c0+1, c0+2 in flight
+    ChunkIn in0, in1;
+    u32x4 cw0[kChunk], cw1[kChunk];
     load_in(c0, in0);
     load_in(c0 + 1, in1);
-    load_in(c0 + 2, in2);
+    __syncthreads(); // the constant table
     stage(c0, 0, in0);
     load_codes(0, cw0);
-    load_in(c0 + 3, in0);
-    stage(c0 + 1, 1, in1);
-    load_codes(1, cw1);
-    load_in(c0 + 4, in1);
+    load_in(c0 + 2, in0);
     __syncthreads();
 
-    // step for chunk ch (buffer and register set ch % 3): stage chunk ch+2,
-    // issue its codes and the inputs of ch+5, compute chunk ch.  The loads are
+    // step for chunk ch (buffer and register set ch % 2): stage chunk ch+1,
+    // issue its codes and the inputs of ch+3, compute chunk ch.  The loads are
     // issued whether or not their chunk exists (past the range they read
     // nothing or a few bytes of the blob), so the waits stay exact counts.
-    for (int ch = c0; ch < c1; ch += 3) {
-        stage(ch + 2, 2, in2);
-        load_codes(2, cw2);
-        load_in(ch + 5, in2);
+    for (int ch = c0; ch < c1; ch += 2) {
+        stage(ch + 1, 1, in1);
+        load_codes(1, cw1);
+        load_in(ch + 3, in1);
         compute(ch, 0, cw0);
         __syncthreads();
-        stage(ch + 3, 0, in0);
+        stage(ch + 2, 0, in0);
         load_codes(0, cw0);
-        load_in(ch + 6, in0);
+        load_in(ch + 4, in0);
         compute(ch + 1, 1, cw1);
-        __syncthreads();
-        stage(ch + 4, 1, in1);
-        load_codes(1, cw1);
-        load_in(ch + 7, in1);
-        compute(ch + 2, 2, cw2);
         __syncthreads();
     }
 
@@ -386,9 +376,9 @@ struct MfmaGeom {
     size_t ws; // workspace bytes the segments need as separate workgroups
 };
 
-// Row blocks x K segments: the segment count that minimizes (rounds of one
-// workgroup per compute unit) x (chunks per segment + the start-up of a
-// workgroup, about two chunks of latency), fewer segments on ties.
+// Row blocks x K segments: the segment count that minimizes (rounds of
+// kBlocksPerCu workgroups per compute unit) x (chunks per segment + the
+// start-up of a workgroup, about two chunks of latency), fewer segments on ties.
 // The segments depend on the shape and the compute units only; they run as
 // separate workgroups (splits) when ws_bytes holds their M*N fp32 partial sums
 // each, else in one workgroup per row block.
@@ -400,12 +390,13 @@ MfmaGeom mfma_geom(const vbq_layout *L, int M, int cus, size_t ws_bytes)
     int nseg = 1;
     g.seg = nch;
     constexpr int kStart = 2;
-    long best = (long)((g.blocks + cus - 1) / cus) * (nch + kStart);
+    const long slots = (long)cus * kBlocksPerCu;
+    long best = (long)((g.blocks + slots - 1) / slots) * (nch + kStart);
     for (int s = 2; s <= std::min(kMaxSplits, nch); s++) {
         const int cps = (nch + s - 1) / s;
         if ((nch + cps - 1) / cps != s)
             continue; // s segments of cps chunks would leave one empty
-        const long cost = (long)(((long)g.blocks * s + cus - 1) / cus) * (cps + kStart);
+        const long cost = (long)(((long)g.blocks * s + slots - 1) / slots) * (cps + kStart);
         if (cost < best) {
             best = cost;
             nseg = s;
