@@ -61,6 +61,8 @@ def parse(argv=None):
     ap.add_argument("--prefill-m", default="32,64,128,256,512,2048",
                     help="token counts of the prefill sweep (the JSON line reports the one --prefill-head names)")
     ap.add_argument("--prefill-head", type=int, default=256, help="token count the prefill line reports")
+    ap.add_argument("--batched-m", default="1,4,8,16", help="token counts of the batched workload")
+    ap.add_argument("--variants", default="clustered,u4,u8", help="width variants of the batched workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
     return ap.parse_args(argv)
@@ -96,6 +98,7 @@ def time_steps(torch, fn, steps):
 KERNELS = {  # path -> (kernel, entry point, profile name, sources)
     "plan": ("k_gemv_plan<1, 0, KP>", "vbq_gemv_planned", "k_gemv_plan", ("vbq_plan.hip", "vbq_unpack.h", "vbq_common.h")),
     "vbq1": ("k_gemv_stream<1>", "vbq_gemv", "k_gemv_stream", ("vbq_stream.hip", "vbq_unpack.h", "vbq_common.h")),
+    "mfma": ("k_gemv_mfma", "vbq_gemv_batched", "k_gemv_mfma", ("vbq_mfma.hip", "vbq_unpack.h", "vbq_common.h")),
 }
 
 
@@ -112,15 +115,22 @@ def measured_traffic(workload, kpath="plan"):
     """HBM bytes per launch of the GEMV kernel from the committed rocprofv3 counter
     summary (FETCH_SIZE x its copy-calibrated factor + WRITE_SIZE), or None when the
     kernel source has changed since the counters were taken."""
+    t = profile_json(workload, kpath, "traffic")
+    if t is None:
+        return None
+    return round(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+
+
+def profile_json(workload, kpath, key):
+    """The `key-json:` line of profiles/<kernel>_<workload>.md, or None when it
+    is missing or the kernel source has changed since it was measured."""
     path = os.path.join(ROOT, "profiles", f"{KERNELS[kpath][2]}_{workload}.md")
     if not os.path.exists(path):
         return None
     for line in open(path):
-        if line.startswith("traffic-json: "):
-            t = json.loads(line[len("traffic-json: "):])
-            if t.get("kernel_source_sha") != kernel_source_hash(kpath):
-                return None
-            return round(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+        if line.startswith(key + "-json: "):
+            t = json.loads(line[len(key) + 7:])
+            return t if t.get("kernel_source_sha") == kernel_source_hash(kpath) else None
     return None
 
 
@@ -221,9 +231,10 @@ def bench_batched(torch, v, args):
 
     from decode_gemv_vbq_amd import accounting as acc
     from decode_gemv_vbq_amd import workload as wl
-    Ms = (1, 4, 8, 16)
+    Ms = tuple(int(m) for m in args.batched_m.split(","))
+    mf_valu = profile_json("batched70b", "mfma", "valu")
     rows = []
-    for variant in ("clustered", "u4", "u8"):
+    for variant in args.variants.split(","):
         W = wl.workload("batched70b", variant=variant)
         copies = []
         alg1 = None
@@ -285,32 +296,47 @@ def bench_batched(torch, v, args):
                 del g
             alg = sum(acc.vbq_read_bytes(m["L"], M) for m in copies[0])
             t_hbm = alg / PEAK_HBM
-            t_valu = valu_lane_instr(weights, M) / PEAK_VALU
             best = min(res["planned"], res["vbq_gemv_batched"])
+            mf = M >= 3 and res["vbq_gemv_batched"] <= res["planned"]
+            if mf:  # the matrix-core kernel: lane instructions per weight measured by counters
+                lipw = (mf_valu or {}).get("lane_instr_per_weight", {}).get(variant)
+                lane = None if lipw is None else lipw * weights
+            else:
+                lane = valu_lane_instr(weights, M)
+            t_valu = None if lane is None else lane / PEAK_VALU
             row = {"variant": variant, "M": M, **{f"{k}_us": round(t, 2) for k, t in res.items()},
                    "alg_bytes": alg, "GBps": round(alg / (best * 1e-6) / 1e9, 1),
-                   "hbm_frac": round(t_hbm / (best * 1e-6), 4), "valu_frac": round(t_valu / (best * 1e-6), 4),
-                   "bound": "alu" if t_valu > t_hbm else "hbm",
+                   "kernel": "k_gemv_mfma" if mf else "k_gemv_plan",
+                   "valu_lane_instr": lane,
+                   "hbm_frac": round(t_hbm / (best * 1e-6), 4),
+                   "valu_frac": None if t_valu is None else round(t_valu / (best * 1e-6), 4),
+                   "bound": "hbm" if t_valu is None or t_valu <= t_hbm else "alu",
                    "speedup_vs_dense_f16": round(res["dense_f16"] / best, 3),
                    "speedup_vs_torch_matmul": round(res["torch_matmul"] / best, 3)}
             rows.append(row)
             log(f"  M={M:2d}: planned {res['planned']:.1f} us, vbq_gemv_batched {res['vbq_gemv_batched']:.1f} us, "
                 f"dense fp16 {res['dense_f16']:.1f} us, torch.matmul {res['torch_matmul']:.1f} us; "
-                f"{row['GBps']} GB/s, {100 * row['hbm_frac']:.1f}% of HBM, {100 * row['valu_frac']:.1f}% of VALU")
+                f"{row['GBps']} GB/s, {100 * row['hbm_frac']:.1f}% of HBM, "
+                + ("VALU model unmeasured" if row["valu_frac"] is None else f"{100 * row['valu_frac']:.1f}% of VALU")
+                + f" ({row['kernel']})")
             del outs
         del copies, w16, xs
         torch.cuda.empty_cache()
-    head = next(r for r in rows if r["variant"] == "clustered" and r["M"] == 16)
+    head = next((r for r in rows if r["variant"] == "clustered" and r["M"] == 16), rows[-1])
     t = min(head["planned_us"], head["vbq_gemv_batched_us"]) * 1e-6
+    mf = head["kernel"] == "k_gemv_mfma"
     if head["bound"] == "alu":
-        w = sum(sp.N * sp.K for sp in wl.workload("batched70b").mats)
-        ach = valu_lane_instr(w, 16) / t
+        ach = head["valu_lane_instr"] / t
         roof = {"bound": "alu", "achieved": round(ach / 1e12, 2), "peak": round(PEAK_VALU / 1e12, 2),
                 "unit": "T lane-instr/s", "frac": round(ach / PEAK_VALU, 4)}
     else:
         roof = {"bound": "hbm", "achieved": head["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": head["hbm_frac"]}
-    roof.update({"traffic": None, "kernel": "k_gemv_plan<2, 0> (vbq_gemv_planned, 8 launches of 2 tokens)"})
+    roof.update({"traffic": None,
+                 "kernel": ("k_gemv_mfma (vbq_gemv_batched, 64-row workgroups, K split when the workspace allows)"
+                            if mf else "k_gemv_plan<2, 0> (vbq_gemv_planned, launches of 2 tokens)"),
+                 "valu_model": ("lane instructions per weight from the committed SQ_INSTS_VALU counters"
+                                if mf else "1.2 + M/2 + M/8 lane instructions per weight")})
     print(json.dumps({
         "metric": "us per batched decode up+down GEMV pair (28672x8192 + 8192x28672, M=16 tokens)",
         "value": min(head["planned_us"], head["vbq_gemv_batched_us"]), "unit": "us", "n_gpus": 1,
