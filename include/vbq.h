@@ -172,10 +172,14 @@ vbq_status vbq_quantize(int N, int K, const void *w, vbq_dtype wt, int ldw, cons
 vbq_status vbq_dequant(const vbq_layout *L /* host */, const void *blob, void *w, vbq_dtype wt, hipStream_t stream);
 
 /*
- * Workspace bytes vbq_gemv / vbq_gemv_batched need for layout L and M tokens.
- * This version never splits a row across workgroups and needs none (0): the
- * ws arguments of the GEMV calls may be NULL / 0.  The query and the clear
- * call stay so that callers are ready for shapes that would need one.
+ * Workspace bytes vbq_gemv / vbq_gemv_batched can use for layout L and M
+ * tokens on the current device: 0 for M <= 2; for M >= 3, the fp32 partial
+ * sums ([segments][M][N]) of the K segments the matrix-core kernel cuts a
+ * matrix with few row blocks into (0 when it cuts none).  The workspace is
+ * optional: with at least this many bytes (4-byte aligned) each segment runs as
+ * its own workgroups and a second kernel adds the partial sums; with less, or
+ * NULL, one workgroup per row block runs all segments and adds their sums in
+ * the same order, so the result is the same bit for bit, only slower.
  */
 vbq_status vbq_workspace_size(const vbq_layout *L /* host */, int M, size_t *bytes /* host */);
 
@@ -201,6 +205,11 @@ vbq_status vbq_gemv(const vbq_layout *L /* host */, const void *blob, const uint
  * Y = X W^T for M tokens (1 <= M <= 16): x fp16 [M][ldx] (ldx >= K),
  * y [M][ldy] (ldy >= N).  Each packed code is unpacked once per call and
  * reused for all M tokens.  Error bound as vbq_gemv, per token and output.
+ * For 3 <= M <= 16 with x 16-byte aligned and ldx % 8 == 0 the product runs on
+ * the matrix cores (fp16 operands exact, fp32 accumulation); a token's outputs
+ * then do not depend on the other tokens of the batch or on M, bit for bit.
+ * ws / ws_bytes: optional, see vbq_workspace_size (results do not depend on
+ * it); calls sharing a workspace must be ordered.
  */
 vbq_status vbq_gemv_batched(const vbq_layout *L /* host */, const void *blob, int M, const uint16_t *x, int ldx,
                             void *y, int ldy, vbq_dtype yt, void *ws, size_t ws_bytes, hipStream_t stream);
