@@ -141,7 +141,7 @@ def lib():
         L.vbq_dense_f16_gemv.argtypes = [i, i, i, P, P, i, P, i, i, P]
         GP = ctypes.POINTER(GemmPlan)
         L.vbq_gemm_plan_init.argtypes = [LP, P, GP, P, sz, P]
-        L.vbq_gemm_prepare.argtypes = [GP, LP, P, P, P]
+        L.vbq_gemm_prepare.argtypes = [GP, LP, P, P, P, P]
         L.vbq_gemm_workspace.argtypes = [GP, i, ctypes.POINTER(sz)]
         L.vbq_gemm.argtypes = [GP, P, i, P, i, P, i, i, P, sz, P]
         for f in EXPORTS:
@@ -623,12 +623,17 @@ def gemm_plan_init(L: Layout, blob) -> GemmPlan:
     return GP
 
 
-def gemm_prepare(L: Layout, blob):
-    """GEMM plan of a packed matrix -> (plan u8 device tensor, GemmPlan)."""
+def gemm_prepare(L: Layout, blob, check: bool = True):
+    """GEMM plan of a packed matrix -> (plan u8 device tensor, GemmPlan).
+    With ``check`` the device status word is read back (synchronizes)."""
+    torch = _torch()
     GP = gemm_plan_init(L, blob)
     buf = _empty_aligned(GP.total_bytes, blob.device)
-    _check(lib().vbq_gemm_prepare(ctypes.byref(GP), ctypes.byref(L), _ptr(blob), _ptr(buf), _stream()),
-           "vbq_gemm_prepare")
+    status = torch.empty(1, dtype=torch.int32, device=blob.device)
+    _check(lib().vbq_gemm_prepare(ctypes.byref(GP), ctypes.byref(L), _ptr(blob), _ptr(buf), _ptr(status),
+                                  _stream()), "vbq_gemm_prepare")
+    if check:
+        status_check(status)
     return buf, GP
 
 

@@ -99,6 +99,8 @@ struct GPrep {
     uint8_t *buf;       // plan buffer (fill), null for sizing
     uint32_t *table;    // buf's offset table (size pass with a buffer, scan, fill)
     uint32_t *stats;    // sizing without a buffer: [0] largest tile, [2..3] u64 sum of tiles in 16-byte units
+    uint32_t *status;   // fill: VBQ_STATUS_PLAN when the blob does not fit the plan (may be null)
+    uint32_t max_tile;  // fill: the largest tile the plan was sized for
 };
 
 // The cell of thread u of a tile's workgroup: column gl = u / 128 of the
@@ -182,8 +184,12 @@ __global__ __launch_bounds__(kGT) void k_gsize(GPrep a)
 
 // Exclusive scan of the tile sizes into offsets (16-byte units from the plan
 // start; the tiles start at `base`), entry nt = the end of the last tile.
-// One workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void k_gscan(uint32_t *table, uint32_t nt, uint32_t base)
+// If the tiles end past `cap` (16-byte units; a blob other than the one the
+// plan was sized for), VBQ_STATUS_PLAN goes to *status and every entry is set
+// to `base`, so nothing reads or writes past the buffer.  One workgroup of
+// 1024 threads.
+__global__ __launch_bounds__(1024) void k_gscan(uint32_t *table, uint32_t nt, uint32_t base, uint32_t cap,
+                                                uint32_t *status)
 {
     __shared__ uint32_t ws[16];
     __shared__ uint32_t carry;
@@ -214,8 +220,15 @@ __global__ __launch_bounds__(1024) void k_gscan(uint32_t *table, uint32_t nt, ui
             carry = before + inc;
         __syncthreads();
     }
-    if (tid == 0)
-        table[nt] = carry;
+    if (carry <= cap) {
+        if (tid == 0)
+            table[nt] = carry;
+        return;
+    }
+    if (tid == 0 && status)
+        atomicOr(status, VBQ_STATUS_PLAN);
+    for (uint32_t i = tid; i <= nt; i += 1024)
+        table[i] = base;
 }
 
 // One workgroup per tile: header, code records bucketed by width (8, 4, 2, 1;
@@ -227,6 +240,13 @@ __global__ __launch_bounds__(kGT) void k_gfill(GPrep a)
     const Cell e = tile_cell(a, nbi, kci, u);
     uint32_t cnt[4];
     const uint32_t rank = width_counts(e.c, wc, cnt);
+    // a tile larger than the plan's largest, or a plan whose tiles did not fit
+    // (the scan pointed them all at the first): write nothing (uniform)
+    if (tile_bytes(cnt) > a.max_tile || (a.status && (*a.status & VBQ_STATUS_PLAN))) {
+        if (u == 0 && a.status)
+            atomicOr(a.status, VBQ_STATUS_PLAN);
+        return;
+    }
     uint8_t *t = a.buf + 16ull * a.table[(uint64_t)nbi * a.kc + kci];
     // buckets in the order 8, 4, 2, 1 bits
     uint32_t code_off[4], slot0[4];
@@ -734,7 +754,7 @@ vbq_status vbq_gemm_plan_init(const vbq_layout *L, const void *blob, vbq_gemm_pl
 }
 
 vbq_status vbq_gemm_prepare(const vbq_gemm_plan *P, const vbq_layout *L, const void *blob, void *buf,
-                            hipStream_t stream)
+                            uint32_t *status_word, hipStream_t stream)
 {
     if (!blob || !buf)
         return VBQ_ERR_INVALID_ARG;
@@ -742,16 +762,21 @@ vbq_status vbq_gemm_prepare(const vbq_gemm_plan *P, const vbq_layout *L, const v
     VBQ_TRY(check_gemm_plan(P));
     if ((int)L->N != P->N || (int)L->K != P->K)
         return VBQ_ERR_SHAPE;
-    if ((uintptr_t)blob % 256 || (uintptr_t)buf % 256)
+    if ((uintptr_t)blob % 256 || (uintptr_t)buf % 256 || (uintptr_t)status_word % 4)
         return VBQ_ERR_ALIGN;
     VBQ_TRY(zero_words(buf, P->total_bytes, stream));
+    if (status_word)
+        VBQ_TRY(zero_words(status_word, 4, stream));
     GPrep a = gprep(L, blob, P->kc);
     a.buf = (uint8_t *)buf;
     a.table = (uint32_t *)buf;
+    a.status = status_word;
+    a.max_tile = (uint32_t)P->max_tile;
     const uint32_t nt = (uint32_t)P->nb * (uint32_t)P->kc;
     hipLaunchKernelGGL(k_gsize, dim3(P->kc, P->nb), dim3(kGT), 0, stream, a);
     VBQ_TRY(launch_status());
-    hipLaunchKernelGGL(k_gscan, dim3(1), dim3(1024), 0, stream, a.table, nt, (uint32_t)(P->table_bytes / 16));
+    hipLaunchKernelGGL(k_gscan, dim3(1), dim3(1024), 0, stream, a.table, nt, (uint32_t)(P->table_bytes / 16),
+                       (uint32_t)((P->total_bytes - (uint64_t)P->slot_bytes) / 16), status_word);
     VBQ_TRY(launch_status());
     hipLaunchKernelGGL(k_gfill, dim3(P->kc, P->nb), dim3(kGT), 0, stream, a);
     return launch_status();

@@ -33,7 +33,7 @@
 // wavefront the byte offset, width and scale of its 16 rows' 4 groups (lane
 // (q, n) works out group q of row n).  While chunk c is computed, chunk c+1 is
 // staged and its code words are loaded into registers, and the inputs of chunk
-// c+3 (activations, width planes, slice offset, scale) are loaded.
+// c+2 (activations, width planes, slice offset, scale) are loaded.
 //
 // K segments.  A matrix with too few row blocks to fill the device has its
 // chunks cut into segments (from the shape and the device's compute units
@@ -159,7 +159,7 @@ __device__ __forceinline__ void unpack_quarter(const u32x4 &w, uint32_t rot, uin
     }
 }
 
-// Per-chunk inputs a lane loads two chunks before they are staged.
+// Per-chunk inputs a lane loads one chunk before they are staged.
 struct ChunkIn {
     u32x4 xa, xb;    // activations: token n, columns 64g+8q..+7 and 64g+32+8q..+7 of the staged group
     uint32_t p0, p1; // width-code bit planes of this lane's row in the slice of its planned group
@@ -306,31 +306,29 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
         }
     };
 
-    // ---- prologue: chunk c0 staged (buffer 0), its codes and the inputs of
-    // chunks c0+1, c0+2 in flight
-    ChunkIn in0, in1;
+    // ---- prologue: chunk c0 staged (buffer 0); its codes and the inputs of
+    // chunk c0 + 1 in flight.  Then per step for chunk ch (buffer and register
+    // set ch % 2): stage chunk ch+1, issue its codes and the inputs of ch+2,
+    // compute chunk ch.  The loads are issued whether or not their chunk exists
+    // (past the range they read nothing or a few bytes of the blob), so the
+    // waits stay exact counts.
+    ChunkIn in;
     u32x4 cw0[kChunk], cw1[kChunk];
-    load_in(c0, in0);
-    load_in(c0 + 1, in1);
+    load_in(c0, in);
     __syncthreads(); // the constant table
-    stage(c0, 0, in0);
+    stage(c0, 0, in);
     load_codes(0, cw0);
-    load_in(c0 + 2, in0);
+    load_in(c0 + 1, in);
     __syncthreads();
-
-    // step for chunk ch (buffer and register set ch % 2): stage chunk ch+1,
-    // issue its codes and the inputs of ch+3, compute chunk ch.  The loads are
-    // issued whether or not their chunk exists (past the range they read
-    // nothing or a few bytes of the blob), so the waits stay exact counts.
     for (int ch = c0; ch < c1; ch += 2) {
-        stage(ch + 1, 1, in1);
+        stage(ch + 1, 1, in);
         load_codes(1, cw1);
-        load_in(ch + 3, in1);
+        load_in(ch + 2, in);
         compute(ch, 0, cw0);
         __syncthreads();
-        stage(ch + 2, 0, in0);
+        stage(ch + 2, 0, in);
         load_codes(0, cw0);
-        load_in(ch + 4, in0);
+        load_in(ch + 3, in);
         compute(ch + 1, 1, cw1);
         __syncthreads();
     }

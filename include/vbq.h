@@ -505,11 +505,15 @@ vbq_status vbq_gemm_plan_init(const vbq_layout *L /* host */, const void *blob, 
 /*
  * Write the GEMM plan of (L, blob) described by *P into buf (device,
  * P->total_bytes, 256-byte aligned); every byte of buf is written.  The blob
- * must be the one *P was sized for.  Errors: VBQ_ERR_INVALID_ARG,
- * VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE (P does not match L), VBQ_ERR_ALIGN.
+ * must be the one *P was sized for: if its tiles do not fit (a tile larger
+ * than P->max_tile, or more tile bytes than the buffer holds), no tile is
+ * written past the buffer, the plan is unusable and VBQ_STATUS_PLAN is set in
+ * *status_word (device u32, 4-byte aligned, cleared by this call; may be
+ * NULL).  Errors: VBQ_ERR_INVALID_ARG, VBQ_ERR_LAYOUT, VBQ_ERR_SHAPE (P does
+ * not match L), VBQ_ERR_ALIGN.
  */
 vbq_status vbq_gemm_prepare(const vbq_gemm_plan *P /* host */, const vbq_layout *L /* host */, const void *blob,
-                            void *buf, hipStream_t stream);
+                            void *buf, uint32_t *status_word, hipStream_t stream);
 
 /* Workspace bytes vbq_gemm needs for M tokens on the current device. */
 vbq_status vbq_gemm_workspace(const vbq_gemm_plan *P /* host */, int M, size_t *bytes /* host */);

@@ -401,5 +401,7 @@ def test_gemm_argument_checks_fail_before_launch():
         badp = fake_gemm_plan(v)
         setattr(badp, field, val)
         assert gemm(Pl=badp) == "VBQ_ERR_LAYOUT", field
-    assert v.STATUS[lib.vbq_gemm_prepare(ctypes.byref(fake_gemm_plan(v, N=8)), ctypes.byref(L), fake, fake, null)] \
-        == "VBQ_ERR_SHAPE"
+    assert v.STATUS[lib.vbq_gemm_prepare(ctypes.byref(fake_gemm_plan(v, N=8)), ctypes.byref(L), fake, fake, null,
+                                         null)] == "VBQ_ERR_SHAPE"
+    assert v.STATUS[lib.vbq_gemm_prepare(ctypes.byref(fake_gemm_plan(v, N=4)), ctypes.byref(L), fake, fake,
+                                         VP((1 << 20) + 2), null)] == "VBQ_ERR_ALIGN"  # status word alignment
