@@ -49,11 +49,21 @@ def count_passes(P, plan) -> int:
 
 class DecodeStep:
     def __init__(self, name: str = "decode9b", M: int = 1, variant: str = "clustered", device="cuda",
-                 keep_rows: int = 0, out_dtype=None, log=None, planned: bool = True, sample_frac: float = 0.0):
+                 keep_rows: int = 0, out_dtype=None, log=None, planned: bool = True, sample_frac: float = 0.0,
+                 copies: int = 1):
+        import dataclasses
+
         import torch
         self.torch = torch
         self.planned = planned
         self.W = wl.workload(name, M=M, variant=variant)
+        # `copies` repeats the workload's matrices with fresh draws (other
+        # layer ids), stage after stage, so that a small workload streams its
+        # weights from HBM instead of the memory-side cache
+        self.copies = copies
+        if copies > 1:
+            self.W.mats = [dataclasses.replace(sp, layer=sp.layer + 1000 * c) for c in range(copies)
+                           for sp in self.W.mats]
         self.M = M
         self.device = torch.device(device)
         self.out_dtype = out_dtype or torch.float16
@@ -64,8 +74,11 @@ class DecodeStep:
         self._seq = None
         rng = np.random.default_rng(12345)
         self.stages: list[list[int]] = []
-        # sample_frac keeps that fraction of every matrix's rows (the device
-        # draws copied back), the inputs a CPU timing of the oracle runs on
+        # sample_frac keeps that fraction of the rows of every matrix of the
+        # first copy (the device draws copied back), the inputs a CPU timing of
+        # the oracle runs on
+        n_one = len(self.W.mats) // copies
+        every = max(40, len(self.W.mats) // 10)
         for i, spec in enumerate(self.W.mats):
             q, bits, s, x = wl.draw_matrix_torch(spec, self.W.wid, M, self.W.outliers, device=self.device)
             # the up projection reads the same activations as the gate projection
@@ -81,7 +94,7 @@ class DecodeStep:
             y = torch.empty((M, spec.N), dtype=self.out_dtype, device=self.device)
             ws = v.workspace(L, M, self.device)
             m = Matrix(spec, L, blob, x, y, ws)
-            n_keep = max(keep_rows, int(round(sample_frac * spec.N)))
+            n_keep = max(keep_rows, int(round(sample_frac * spec.N))) if i < n_one else 0
             if n_keep:
                 n_keep = min(n_keep, spec.N)
                 rows = np.unique(np.concatenate([[0, spec.N - 1], rng.choice(spec.N, size=n_keep, replace=False)]))
@@ -92,7 +105,7 @@ class DecodeStep:
                             x.cpu().numpy().view(np.uint16))
             del q, bits, s
             self.mats.append(m)
-            if log and (i % 40 == 0 or i == len(self.W.mats) - 1):
+            if log and (i % every == 0 or i == len(self.W.mats) - 1):
                 log(f"built {i + 1}/{len(self.W.mats)} matrices")
         torch.cuda.synchronize()
         self.shared_ok = [True] * len(self.stages)
