@@ -61,7 +61,7 @@ def parse(argv=None):
     ap.add_argument("--prefill-m", default="32,64,128,256,512,2048",
                     help="token counts of the prefill sweep (the JSON line reports the one --prefill-head names)")
     ap.add_argument("--prefill-head", type=int, default=256, help="token count the prefill line reports")
-    ap.add_argument("--batched-m", default="1,4,8,16", help="token counts of the batched workload")
+    ap.add_argument("--batched-m", default="1,4,8,16,32", help="token counts of the batched workload")
     ap.add_argument("--variants", default="clustered,u4,u8", help="width variants of the batched workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales HBM counters) and exit")
@@ -219,10 +219,11 @@ def valu_lane_instr(weights, M):
 
 def bench_batched(torch, v, args):
     """The batched decode workload: the 28672x8192 up and 8192x28672 down
-    projections for M in {1, 4, 8, 16} tokens (1% outlier channels), width
-    variants clustered (runs of 8 groups from the base mix), uniform 4-bit and
-    all-8-bit.  Per (variant, M), one up+down pair through the prepared plans
-    (vbq_gemv_planned) and straight from the blobs (vbq_gemv_batched), with
+    projections for M in {1, 4, 8, 16} tokens (and 32, which only the blob path
+    and torch.matmul take) (1% outlier channels), width variants clustered (runs
+    of 8 groups from the base mix), uniform 4-bit and all-8-bit.  Per (variant,
+    M), one up+down pair through the prepared plans (vbq_gemv_planned) and
+    straight from the blobs (vbq_gemv_batched), with
     enough weight copies in turn that a round streams at least 1 GB (so each
     call reads from HBM), replayed from a HIP graph; the hand-written dense fp16
     GEMV and torch.matmul on the dequantized weights of one copy at the same
@@ -248,7 +249,8 @@ def bench_batched(torch, v, args):
                 blob, L = v.pack(q, bits, sc.view(torch.float16))
                 del q, bits, sc
                 plan, P = v.prepare(L, blob, M=2)
-                pair.append({"spec": spec, "L": L, "blob": blob, "plan": plan, "P": P, "ws": v.workspace(L, 16)})
+                pair.append({"spec": spec, "L": L, "blob": blob, "plan": plan, "P": P,
+                             "ws": v.workspace(L, max(Ms))})
             copies.append(pair)
             alg1 = sum(acc.vbq_read_bytes(m["L"], 0) for m in pair)
             c += 1
@@ -256,7 +258,7 @@ def bench_batched(torch, v, args):
                 break
         torch.cuda.synchronize()
         weights = sum(m["spec"].N * m["spec"].K for m in copies[0])
-        xs_host = {spec.K: wl.draw_x(spec, W.wid, 16, outliers=W.outliers) for spec in W.mats}
+        xs_host = {spec.K: wl.draw_x(spec, W.wid, max(16, max(Ms)), outliers=W.outliers) for spec in W.mats}
         xs = {K: torch.from_numpy(xh.view(np.int16)).cuda().view(torch.float16) for K, xh in xs_host.items()}
         w16 = [v.dequant(m["L"], m["blob"], torch.float16) for m in copies[0]]
         log(f"batched70b {variant}: {len(copies)} copies of up+down ({alg1 / 1e6:.1f} MB algorithmic each)")
@@ -286,6 +288,9 @@ def bench_batched(torch, v, args):
             res = {}
             for name, fn, n in (("planned", planned, len(copies)), ("vbq_gemv_batched", blobs, len(copies)),
                                 ("dense_f16", dense, 1), ("torch_matmul", tmm, 1)):
+                if M > 16 and name in ("planned", "dense_f16"):  # these take at most 16 tokens
+                    res[name] = float("inf")
+                    continue
                 fn()
                 torch.cuda.synchronize()
                 g = torch.cuda.CUDAGraph()
@@ -299,25 +304,26 @@ def bench_batched(torch, v, args):
             t_hbm = alg / PEAK_HBM
             best = min(res["planned"], res["vbq_gemv_batched"])
             mf = M >= 3 and res["vbq_gemv_batched"] <= res["planned"]
-            if mf:  # the matrix-core kernel: lane instructions per weight measured by counters
+            if mf:  # the matrix-core kernel: lane instructions per weight measured by counters (at 16 tokens)
                 lipw = (mf_valu or {}).get("lane_instr_per_weight", {}).get(variant)
-                lane = None if lipw is None else lipw * weights
+                lane = None if lipw is None or M > 16 else lipw * weights
             else:
                 lane = valu_lane_instr(weights, M)
             t_valu = None if lane is None else lane / PEAK_VALU
-            row = {"variant": variant, "M": M, **{f"{k}_us": round(t, 2) for k, t in res.items()},
+            row = {"variant": variant, "M": M,
+                   **{f"{k}_us": None if t == float("inf") else round(t, 2) for k, t in res.items()},
                    "alg_bytes": alg, "GBps": round(alg / (best * 1e-6) / 1e9, 1),
                    "kernel": "k_gemv_mfma" if mf else "k_gemv_plan",
                    "valu_lane_instr": lane,
                    "hbm_frac": round(t_hbm / (best * 1e-6), 4),
                    "valu_frac": None if t_valu is None else round(t_valu / (best * 1e-6), 4),
                    "bound": "hbm" if t_valu is None or t_valu <= t_hbm else "alu",
-                   "speedup_vs_dense_f16": round(res["dense_f16"] / best, 3),
+                   "speedup_vs_dense_f16": None if res["dense_f16"] == float("inf") else round(res["dense_f16"] / best, 3),
                    "speedup_vs_torch_matmul": round(res["torch_matmul"] / best, 3)}
             rows.append(row)
-            log(f"  M={M:2d}: planned {res['planned']:.1f} us, vbq_gemv_batched {res['vbq_gemv_batched']:.1f} us, "
-                f"dense fp16 {res['dense_f16']:.1f} us, torch.matmul {res['torch_matmul']:.1f} us; "
-                f"{row['GBps']} GB/s, {100 * row['hbm_frac']:.1f}% of HBM, "
+            log((f"  M={M:2d}: planned {res['planned']:.1f} us, vbq_gemv_batched {res['vbq_gemv_batched']:.1f} us, "
+                 f"dense fp16 {res['dense_f16']:.1f} us, torch.matmul {res['torch_matmul']:.1f} us; ").replace("inf us", "n/a")
+                + f"{row['GBps']} GB/s, {100 * row['hbm_frac']:.1f}% of HBM, "
                 + ("VALU model unmeasured" if row["valu_frac"] is None else f"{100 * row['valu_frac']:.1f}% of VALU")
                 + f" ({row['kernel']})")
             del outs
@@ -506,7 +512,8 @@ def bench_prefill(torch, v, args):
     """Prefill GEMMs: the batched workload's 28672x8192 up and 8192x28672 down
     projections (clustered widths, 1% outlier channels) for M tokens, as
     vbq_gemm from GEMM plans against torch's fp16 GEMM (hipBLASLt) of the
-    dequantized weights.  Two copies of each matrix are used in turn so that
+    dequantized weights, and for up to 32 tokens vbq_gemv_batched straight from
+    the blobs (the matrix-core GEMV).  Two copies of each matrix are used in turn so that
     each call streams its weights from HBM; every path is replayed from a HIP
     graph.  Roofline per M: the larger of the plan bytes at 8 TB/s and
     2 M N K flops at the dense fp16 matrix-core peak."""
@@ -523,8 +530,8 @@ def bench_prefill(torch, v, args):
             del q, bits, s
             buf, GP = v.gemm_prepare(L, blob)
             w16 = v.dequant(L, blob, torch.float16)
-            del blob
-            mats.append({"spec": spec, "L": L, "buf": buf, "GP": GP, "w16": w16})
+            mats.append({"spec": spec, "L": L, "buf": buf, "GP": GP, "w16": w16, "blob": blob,
+                         "ws_b": v.workspace(L, 32)})
     torch.cuda.synchronize()
     plan_bytes = sum(m["GP"].total_bytes for m in mats[:2])
     alg_w = sum(acc.vbq_read_bytes(m["L"], 0) for m in mats[:2])
@@ -549,8 +556,13 @@ def bench_prefill(torch, v, args):
             for m, o in zip(mats, outs):
                 torch.mm(xs[m["spec"].K], m["w16"].t(), out=o)
 
+        def run_batched():  # up to 32 tokens: the matrix-core GEMV straight from the blobs
+            for m, o in zip(mats, outs):
+                v.gemv_batched(m["L"], m["blob"], xs[m["spec"].K], out=o, ws=m["ws_b"])
+
         res = {}
-        for name, fn in (("vbq", run_vbq), ("f16", run_f16)):
+        paths = (("vbq", run_vbq), ("f16", run_f16)) + ((("batched", run_batched),) if M <= 32 else ())
+        for name, fn in paths:
             fn()
             torch.cuda.synchronize()
             gr = torch.cuda.CUDAGraph()
@@ -566,12 +578,16 @@ def bench_prefill(torch, v, args):
         t = res["vbq"] * 1e-6
         row = {"M": M, "us": round(res["vbq"], 2), "f16_us": round(res["f16"], 2),
                "speedup_vs_f16": round(res["f16"] / res["vbq"], 3), "bound": bound,
+               "vbq_gemv_batched_us": round(res["batched"], 2) if "batched" in res else None,
+               "speedup_batched_vs_f16": round(res["f16"] / res["batched"], 3) if "batched" in res else None,
                "TFLOPs": round(flops / t / 1e12, 1), "GBps": round(byts / t / 1e9, 1),
                "frac": round(max(t_mfma, t_hbm) / t, 4)}
         rows.append(row)
         log(f"M={M}: vbq_gemm {res['vbq']:.1f} us ({row['TFLOPs']} TFLOP/s, {row['GBps']} GB/s, "
             f"{100 * row['frac']:.1f}% of the {bound} roof), fp16 GEMM {res['f16']:.1f} us, "
-            f"speedup {row['speedup_vs_f16']:.2f}x")
+            f"speedup {row['speedup_vs_f16']:.2f}x"
+            + (f"; vbq_gemv_batched {res['batched']:.1f} us ({row['speedup_batched_vs_f16']:.2f}x)" if "batched" in res
+               else ""))
         del xs, ws, ws2, wsz, outs
     head = next(r for r in rows if r["M"] == args.prefill_head)
     if head["bound"] == "mfma":

@@ -358,7 +358,8 @@ def gemv(L: Layout, blob, x, out=None, out_dtype=None, ws=None):
 
 
 def gemv_batched(L: Layout, blob, x, out=None, out_dtype=None, ws=None):
-    """Y[M][N] = X[M][K] W^T for 1 <= M <= 16 (x fp16, rows may be strided)."""
+    """Y[M][N] = X[M][K] W^T for 1 <= M <= 32 (x fp16, rows may be strided; M > 16
+    needs x 16-byte aligned and a row stride that is a multiple of 8)."""
     torch = _torch()
     if x.dim() != 2:
         raise ValueError("x must be [M][K]")

@@ -1047,7 +1047,7 @@ vbq_status vbq_workspace_size(const vbq_layout *L, int M, size_t *bytes)
     if (!bytes)
         return VBQ_ERR_INVALID_ARG;
     VBQ_TRY(check_layout(L));
-    if (M < 1 || M > 16)
+    if (M < 1 || M > kMaxBatch)
         return VBQ_ERR_BATCH;
     *bytes = M >= kMfmaMinTokens ? mfma_workspace(L, M) : 0;
     return VBQ_OK;
@@ -1061,7 +1061,7 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
     if (yt != VBQ_F32 && yt != VBQ_F16)
         return VBQ_ERR_INVALID_ARG;
     VBQ_TRY(check_layout(L));
-    if (M < 1 || M > 16)
+    if (M < 1 || M > kMaxBatch)
         return VBQ_ERR_BATCH;
     if (ldx < (int)L->K || ldy < (int)L->N)
         return VBQ_ERR_SHAPE;
@@ -1071,6 +1071,8 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
         GemvCall call{L, blob, M, x, ldx, y, ldy, yt, stream};
         if (mfma_applies(L, M, x, ldx))
             return mfma_gemv(call, ws, ws_bytes);
+        if (M > 16) // only the matrix cores take more than 16 tokens
+            return (uintptr_t)x % 16 || ldx % 8 ? VBQ_ERR_ALIGN : VBQ_ERR_SHAPE;
         vbq_status st;
         if (stream_gemv(call, &st))
             return st;

@@ -64,6 +64,7 @@ bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x
 // when x is 16-byte aligned, ldx % 8 == 0 and the blob and x fit 32-bit
 // buffer offsets.
 constexpr int kMfmaMinTokens = 3;
+constexpr int kMaxBatch = 32; // vbq_gemv_batched: more than 16 tokens only on the matrix cores
 bool mfma_applies(const vbq_layout *L, int M, const uint16_t *x, int ldx);
 // Workspace bytes for the K split the current device would use at M tokens.
 size_t mfma_workspace(const vbq_layout *L, int M);

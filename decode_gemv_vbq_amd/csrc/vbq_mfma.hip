@@ -1,5 +1,5 @@
-// Batched decode GEMV on the matrix cores: Y[M][N] = X[M][K] W^T for up to 16
-// tokens, read straight from a VBQ1 blob.
+// Batched decode GEMV on the matrix cores: Y[M][N] = X[M][K] W^T for up to 32
+// tokens (one or two tiles of 16), read straight from a VBQ1 blob.
 //
 // "Variable Bit-width Quantization" (mlsanity.com page, Abstract) gives every
 // 64-weight group its own width in {1, 2, 4, 8} and decodes with fused
@@ -9,8 +9,9 @@
 // on v_mfma_f32_16x16x32_f16.  A wavefront owns 16 weight rows; for each group
 // column its 64 lanes unpack the 16 rows' groups into the B operand (row
 // n = lane % 16, quarter q = lane / 16 of the group's 32 code pairs), while the
-// A operand holds the 16 tokens' activations of that group.  Lane (q, n) then
-// holds the outputs of row n for tokens 4q..4q+3.
+// A operand holds 16 tokens' activations of that group.  Lane (q, n) then
+// holds the outputs of row n for tokens 4q..4q+3 of the tile; a second tile of
+// 16 tokens reuses the same unpacked B operand with its own A and accumulator.
 //
 // Exactness.  An unpacked half is 2^(10-pos) + code exactly (the code lifted
 // into the mantissa of a power of two) and the MFMA accumulates in fp32.  The
@@ -26,7 +27,8 @@
 // the contraction does not depend on it.
 //
 // Workgroup: 4 wavefronts = 64 rows x a K range of whole 4-group chunks, at
-// most 128 registers per lane so that four workgroups share a compute unit
+// most 128 registers per lane so that four workgroups (three with two token
+// tiles, for the LDS) share a compute unit
 // (four wavefronts per SIMD hide each other's LDS, matrix-core and memory
 // latencies).  Per chunk, in one of two LDS buffers: the 4 groups' activations
 // as fp16 pairs (wavefront w stages group w), their offset constants, and per
@@ -55,19 +57,29 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 16 * kWaves;
 constexpr int kChunk = 4;              // groups per chunk: wavefront w stages group w, lane (q, n) plans group q
-constexpr int kBlocksPerCu = 4;
 constexpr int kTok = 144;              // LDS bytes per token of a staged group (128 + 16 against bank conflicts)
-constexpr int kXGroup = 16 * kTok;     // one staged group, 16 tokens
-constexpr int kXBytes = kChunk * kXGroup;
-constexpr int kCGroup = 4 * 16 * 4;    // offset constants of one group: [width code][token] fp32
-constexpr int kCBytes = kChunk * kCGroup;
+constexpr int kXGroup = 16 * kTok;     // one staged group, one tile of 16 tokens
+constexpr int kCGroup = 4 * 16 * 4;    // offset constants of one group and tile: [width code][token] fp32
 constexpr int kMWave = kChunk * 16 * 8; // one wavefront's metadata: [group][row] {offset | code, scale}
 constexpr int kMBytes = kWaves * kMWave;
-constexpr int kBufBytes = kXBytes + kCBytes + kMBytes;
 constexpr int kBufs = 2;
 constexpr int kTabBytes = 5 * 48;      // B operands of the offset constants: [width code, or 4 = zero][Bm0 Bm1 Bo]
-constexpr int kLdsBytes = kBufs * kBufBytes + kTabBytes;
 constexpr int kMaxSplits = 16;
+constexpr int kMaxTiles = 2;           // token tiles of 16 per call
+
+// Per token-tile count T (a call of up to 16 T tokens): one LDS buffer holds
+// the chunk's activations [group][tile][token] and offset constants
+// [group][tile][width][token], then the wavefronts' metadata.  One tile leaves
+// room for four workgroups per compute unit, two tiles for three.
+template <int T>
+struct Geo {
+    static constexpr int kXBytes = kChunk * T * kXGroup;
+    static constexpr int kCBytes = kChunk * T * kCGroup;
+    static constexpr int kBufBytes = kXBytes + kCBytes + kMBytes;
+    static constexpr int kLdsBytes = kBufs * kBufBytes + kTabBytes;
+    static constexpr int kBlocksPerCu = T == 1 ? 4 : 3;
+};
+static_assert(Geo<kMaxTiles>::kLdsBytes * Geo<kMaxTiles>::kBlocksPerCu <= 160 * 1024, "LDS of the resident workgroups");
 constexpr uint32_t kNone = 0xffffffffu; // a buffer offset past every buffer: the load returns 0 and reads nothing
 
 typedef _Float16 hf8 __attribute__((ext_vector_type(8)));
@@ -160,15 +172,18 @@ __device__ __forceinline__ void unpack_quarter(const u32x4 &w, uint32_t rot, uin
 }
 
 // Per-chunk inputs a lane loads one chunk before they are staged.
+template <int T>
 struct ChunkIn {
-    u32x4 xa, xb;    // activations: token n, columns 64g+8q..+7 and 64g+32+8q..+7 of the staged group
-    uint32_t p0, p1; // width-code bit planes of this lane's row in the slice of its planned group
-    uint32_t so;     // slice offset in the row record
-    uint32_t sc;     // scale of the planned group (fp16 bits)
+    u32x4 xa[T], xb[T]; // activations: token n + 16 t, columns 64g+8q..+7 and 64g+32+8q..+7 of the staged group
+    uint32_t p0, p1;    // width-code bit planes of this lane's row in the slice of its planned group
+    uint32_t so;        // slice offset in the row record
+    uint32_t sc;        // scale of the planned group (fp16 bits)
 };
 
-__global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
+template <int T>
+__global__ __launch_bounds__(kThreads, Geo<T>::kBlocksPerCu) void k_gemv_mfma(MArgs a)
 {
+    constexpr int kXBytes = Geo<T>::kXBytes, kCBytes = Geo<T>::kCBytes, kBufBytes = Geo<T>::kBufBytes;
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, q = lane >> 4;
@@ -194,13 +209,17 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
     const uint32_t row_base = a.off_codes + 128u * row_off;
 
     // inputs of chunk ch (offsets kNone past the K range: zeros, no reads)
-    auto load_in = [&](int ch, ChunkIn &in) {
+    auto load_in = [&](int ch, ChunkIn<T> &in) {
         const bool on = ch < c1;
         const int g = ch * kChunk + wave;
-        const bool xon = on && g < a.G && n < a.M;
-        const uint32_t xo = 2u * ((uint32_t)n * (uint32_t)a.ldx + 64u * (uint32_t)g + 8u * q);
-        in.xa = __builtin_amdgcn_raw_buffer_load_b128(rx, xon ? xo : kNone, 0, 0);
-        in.xb = __builtin_amdgcn_raw_buffer_load_b128(rx, xon ? xo + 64u : kNone, 0, 0);
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+            const int tok = n + 16 * t;
+            const bool xon = on && g < a.G && tok < a.M;
+            const uint32_t xo = 2u * ((uint32_t)tok * (uint32_t)a.ldx + 64u * (uint32_t)g + 8u * q);
+            in.xa[t] = __builtin_amdgcn_raw_buffer_load_b128(rx, xon ? xo : kNone, 0, 0);
+            in.xb[t] = __builtin_amdgcn_raw_buffer_load_b128(rx, xon ? xo + 64u : kNone, 0, 0);
+        }
         const int gi = ch * kChunk + q;
         const bool mon = on && live && gi < a.G;
         const uint32_t rs = (uint32_t)row * (uint32_t)a.nS + (uint32_t)(gi >> 5);
@@ -214,27 +233,30 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
 
     // stage chunk ch into buffer bi: activations, offset constants, this
     // wavefront's metadata
-    auto stage = [&](int ch, int bi, const ChunkIn &in) {
+    auto stage = [&](int ch, int bi, const ChunkIn<T> &in) {
         uint8_t *buf = smem + bi * kBufBytes;
-        uint32_t p[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint32_t lo = in.xa[j >> 1], hi = in.xb[j >> 1];
-            p[j] = __builtin_amdgcn_perm(hi, lo, (j & 1) ? 0x07060302u : 0x05040100u);
-        }
-        u32x4 *xs = reinterpret_cast<u32x4 *>(buf + wave * kXGroup + n * kTok + 32 * q);
-        xs[0] = u32x4{p[0], p[1], p[2], p[3]};
-        xs[1] = u32x4{p[4], p[5], p[6], p[7]};
         const u32x4 *tb = reinterpret_cast<const u32x4 *>(tab + 48 * (n < 4 ? n : 4));
         const u32x4 bm0 = tb[0], bm1 = tb[1], bo = tb[2];
-        const hf8 A0 = as_hf8(p[0], p[1], p[2], p[3]), A1 = as_hf8(p[4], p[5], p[6], p[7]);
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mfma(A0, as_hf8(bm0.x, bm0.y, bm0.z, bm0.w), d);
-        d = mfma(A1, as_hf8(bm1.x, bm1.y, bm1.z, bm1.w), d);
-        d = mfma(A0, as_hf8(bo.x, bo.y, bo.z, bo.w), d);
-        d = mfma(A1, as_hf8(bo.x, bo.y, bo.z, bo.w), d);
-        if (n < 4)
-            *reinterpret_cast<f32x4 *>(buf + kXBytes + wave * kCGroup + n * 64 + 16 * q) = d;
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+            uint32_t p[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint32_t lo = in.xa[t][j >> 1], hi = in.xb[t][j >> 1];
+                p[j] = __builtin_amdgcn_perm(hi, lo, (j & 1) ? 0x07060302u : 0x05040100u);
+            }
+            u32x4 *xs = reinterpret_cast<u32x4 *>(buf + (wave * T + t) * kXGroup + n * kTok + 32 * q);
+            xs[0] = u32x4{p[0], p[1], p[2], p[3]};
+            xs[1] = u32x4{p[4], p[5], p[6], p[7]};
+            const hf8 A0 = as_hf8(p[0], p[1], p[2], p[3]), A1 = as_hf8(p[4], p[5], p[6], p[7]);
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            d = mfma(A0, as_hf8(bm0.x, bm0.y, bm0.z, bm0.w), d);
+            d = mfma(A1, as_hf8(bm1.x, bm1.y, bm1.z, bm1.w), d);
+            d = mfma(A0, as_hf8(bo.x, bo.y, bo.z, bo.w), d);
+            d = mfma(A1, as_hf8(bo.x, bo.y, bo.z, bo.w), d);
+            if (n < 4)
+                *reinterpret_cast<f32x4 *>(buf + kXBytes + (wave * T + t) * kCGroup + n * 64 + 16 * q) = d;
+        }
 
         const int gi = ch * kChunk + q, sl = gi >> 5, i = gi & 31;
         const int ng = min(32, a.G - 32 * sl);
@@ -268,7 +290,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
         }
     };
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, total = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[T], total[T];
+#pragma unroll
+    for (int t = 0; t < T; t++)
+        acc[t] = total[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t rot = 8u * (uint32_t)(q & 1);
 
     auto compute = [&](int ch, int bi, const u32x4 *cw) {
@@ -279,9 +304,19 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
             if (ch < c1 && ch * kChunk + gl < a.G) { // uniform
                 const u32x2 e = *reinterpret_cast<const u32x2 *>(mb + gl * 128 + n * 8);
                 const int c = (int)(e.x & 3u);
-                const u32x4 *xs = reinterpret_cast<const u32x4 *>(buf + gl * kXGroup + n * kTok + 32 * q);
-                const u32x4 x0 = xs[0], x1 = xs[1];
-                const f32x4 cinit = *reinterpret_cast<const f32x4 *>(buf + kXBytes + gl * kCGroup + c * 64 + 16 * q);
+                // the tiles' activations and offset constants first, so that
+                // their LDS latency overlaps the unpack
+                u32x4 x0[T], x1[T];
+                f32x4 cinit[T];
+#pragma unroll
+                for (int t = 0; t < T; t++) {
+                    const u32x4 *xs =
+                        reinterpret_cast<const u32x4 *>(buf + (gl * T + t) * kXGroup + n * kTok + 32 * q);
+                    x0[t] = xs[0];
+                    x1[t] = xs[1];
+                    cinit[t] =
+                        *reinterpret_cast<const f32x4 *>(buf + kXBytes + (gl * T + t) * kCGroup + c * 64 + 16 * q);
+                }
                 uint32_t h[8];
                 switch (c) {
                 case 0: unpack_quarter<0>(cw[gl], rot, h); break;
@@ -289,20 +324,26 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
                 case 2: unpack_quarter<2>(cw[gl], rot, h); break;
                 default: unpack_quarter<3>(cw[gl], rot, h); break;
                 }
-                f32x4 d = mfma(as_hf8(x0.x, x0.y, x0.z, x0.w), as_hf8(h[0], h[1], h[2], h[3]), cinit);
-                d = mfma(as_hf8(x1.x, x1.y, x1.z, x1.w), as_hf8(h[4], h[5], h[6], h[7]), d);
                 const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)e.y);
+                const hf8 B0 = as_hf8(h[0], h[1], h[2], h[3]), B1 = as_hf8(h[4], h[5], h[6], h[7]);
 #pragma unroll
-                for (int r = 0; r < 4; r++)
-                    acc[r] = __builtin_fmaf(s, d[r], acc[r]);
+                for (int t = 0; t < T; t++) {
+                    f32x4 d = mfma(as_hf8(x0[t].x, x0[t].y, x0[t].z, x0[t].w), B0, cinit[t]);
+                    d = mfma(as_hf8(x1[t].x, x1[t].y, x1[t].z, x1[t].w), B1, d);
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[t][r] = __builtin_fmaf(s, d[r], acc[t][r]);
+                }
             }
         }
         if (ch < c1 && (ch + 1 - c0) % a.seg == 0) { // end of a K segment (uniform)
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                total[r] += acc[r];
-                acc[r] = 0.f;
-            }
+            for (int t = 0; t < T; t++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    total[t][r] += acc[t][r];
+                    acc[t][r] = 0.f;
+                }
         }
     };
 
@@ -312,7 +353,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
     // compute chunk ch.  The loads are issued whether or not their chunk exists
     // (past the range they read nothing or a few bytes of the blob), so the
     // waits stay exact counts.
-    ChunkIn in;
+    ChunkIn<T> in;
     u32x4 cw0[kChunk], cw1[kChunk];
     load_in(c0, in);
     __syncthreads(); // the constant table
@@ -336,19 +377,21 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void k_gemv_mfma(MArgs a)
     if (!live)
         return;
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const int t = 4 * q + r;
-        if (t >= a.M)
-            continue;
-        const float v = total[r] + acc[r]; // acc is zero here unless the last segment is partial
-        if (a.splits > 1) {
-            a.part[((size_t)blockIdx.y * a.M + t) * a.N + row] = v;
-        } else if (a.yt == VBQ_F32) {
-            reinterpret_cast<float *>(a.y)[(size_t)t * a.ldy + row] = v;
-        } else {
-            reinterpret_cast<__half *>(a.y)[(size_t)t * a.ldy + row] = __float2half_rn(v);
+    for (int tt = 0; tt < T; tt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int t = 16 * tt + 4 * q + r;
+            if (t >= a.M)
+                continue;
+            const float v = total[tt][r] + acc[tt][r]; // acc is zero here unless the last segment is partial
+            if (a.splits > 1) {
+                a.part[((size_t)blockIdx.y * a.M + t) * a.N + row] = v;
+            } else if (a.yt == VBQ_F32) {
+                reinterpret_cast<float *>(a.y)[(size_t)t * a.ldy + row] = v;
+            } else {
+                reinterpret_cast<__half *>(a.y)[(size_t)t * a.ldy + row] = __float2half_rn(v);
+            }
         }
-    }
 }
 
 // y[t][n] = 0 + part[0][t][n] + part[1][t][n] + ..., left to right: the
@@ -380,8 +423,11 @@ struct MfmaGeom {
 // The segments depend on the shape and the compute units only; they run as
 // separate workgroups (splits) when ws_bytes holds their M*N fp32 partial sums
 // each, else in one workgroup per row block.
+int mfma_tiles(int M) { return M > 16 ? 2 : 1; }
+
 MfmaGeom mfma_geom(const vbq_layout *L, int M, int cus, size_t ws_bytes)
 {
+    const int kBlocksPerCu = mfma_tiles(M) == 1 ? Geo<1>::kBlocksPerCu : Geo<2>::kBlocksPerCu;
     MfmaGeom g{};
     const int nch = ((int)L->G + kChunk - 1) / kChunk;
     g.blocks = ((int)L->N + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -414,7 +460,7 @@ namespace vbq {
 
 bool mfma_applies(const vbq_layout *L, int M, const uint16_t *x, int ldx)
 {
-    return M >= kMfmaMinTokens && M <= 16 && L->total_bytes < (1ull << 32) && (uintptr_t)x % 16 == 0 &&
+    return M >= kMfmaMinTokens && M <= 16 * kMaxTiles && L->total_bytes < (1ull << 32) && (uintptr_t)x % 16 == 0 &&
            ldx % 8 == 0 && (uint64_t)(M - 1) * ldx * 2 + 2ull * L->K < (1ull << 32);
 }
 
@@ -449,8 +495,15 @@ vbq_status mfma_gemv(const GemvCall &g, void *ws, size_t ws_bytes)
     a.splits = geo.splits;
     a.chunks_per_split = geo.cps;
     a.seg = geo.seg;
-    VBQ_TRY(dynamic_lds_once((const void *)k_gemv_mfma, kLdsBytes));
-    hipLaunchKernelGGL(k_gemv_mfma, dim3(geo.blocks, geo.splits), dim3(kThreads), kLdsBytes, g.stream, a);
+    if (mfma_tiles(g.M) == 1) {
+        VBQ_TRY(dynamic_lds_once((const void *)k_gemv_mfma<1>, Geo<1>::kLdsBytes));
+        hipLaunchKernelGGL(k_gemv_mfma<1>, dim3(geo.blocks, geo.splits), dim3(kThreads), Geo<1>::kLdsBytes, g.stream,
+                           a);
+    } else {
+        VBQ_TRY(dynamic_lds_once((const void *)k_gemv_mfma<2>, Geo<2>::kLdsBytes));
+        hipLaunchKernelGGL(k_gemv_mfma<2>, dim3(geo.blocks, geo.splits), dim3(kThreads), Geo<2>::kLdsBytes, g.stream,
+                           a);
+    }
     VBQ_TRY(launch_status());
     if (geo.splits > 1) {
         const int total = g.M * (int)L->N;

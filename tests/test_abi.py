@@ -92,16 +92,20 @@ def test_gemv_argument_checks_fail_before_launch():
     # else a whole number (at most 16) of [M][N] planes
     for M in (1, 2):
         assert lib.vbq_workspace_size(ref, M, ctypes.byref(sz)) == 0 and sz.value == 0
-    for M in (3, 16):
+    for M in (3, 17, 32, 16):
         assert lib.vbq_workspace_size(ref, M, ctypes.byref(sz)) == 0
         assert sz.value % (4 * M * 4) == 0 and sz.value <= 16 * 4 * M * 4
     need = sz.value
+    assert v.STATUS[lib.vbq_workspace_size(ref, 33, ctypes.byref(sz))] == "VBQ_ERR_BATCH"
 
     def call(M=1, blob=fake, x=fake, ldx=4096, y=fake, ldy=4, yt=1, ws=fake, wsb=None):
         return v.STATUS[lib.vbq_gemv_batched(ref, blob, M, x, ldx, y, ldy, yt, ws, need if wsb is None else wsb, null)]
 
     assert call(M=0) == "VBQ_ERR_BATCH"
-    assert call(M=17) == "VBQ_ERR_BATCH"
+    assert call(M=33) == "VBQ_ERR_BATCH"
+    # more than 16 tokens only on the matrix cores: x 16-byte aligned, ldx % 8 == 0
+    assert call(M=17, x=odd) == "VBQ_ERR_ALIGN"
+    assert call(M=32, ldx=4100) == "VBQ_ERR_ALIGN"
     assert call(blob=null) == "VBQ_ERR_INVALID_ARG"
     assert call(x=null) == "VBQ_ERR_INVALID_ARG"
     assert call(yt=7) == "VBQ_ERR_INVALID_ARG"

@@ -1,5 +1,5 @@
-"""GPU parity of the matrix-core batched GEMV (vbq_gemv_batched with 3 <= M <= 16,
-x 16-byte aligned, ldx % 8 == 0) against the CPU oracle.
+"""GPU parity of the matrix-core batched GEMV (vbq_gemv_batched with 3 <= M <= 32,
+x 16-byte aligned, ldx % 8 == 0; one or two token tiles of 16) against the CPU oracle.
 
 * |y - y_ref| <= 1e-3 * sum|w||x| per output over ragged shapes (N not a
   multiple of the 16-row tile or the 128-row block, G not a multiple of the
@@ -50,7 +50,7 @@ SHAPES = [(1, 64), (17, 128), (129, 64 * 13), (130, 2112), (333, 64 * 150), (100
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
-@pytest.mark.parametrize("M", [3, 16])
+@pytest.mark.parametrize("M", [3, 16, 17, 32])
 def test_mfma_parity_shapes(N, K, M):
     v = vbq()
     q, bits, s, x = draw(N, K, seed=N + M, M=M, outliers=0.01)
@@ -62,18 +62,19 @@ def test_mfma_parity_shapes(N, K, M):
 
 
 @pytest.mark.parametrize("mix", ["u1", "u2", "u4", "u8", "wide", "head"])
-def test_mfma_width_mixes(mix):
+@pytest.mark.parametrize("M", [8, 24])
+def test_mfma_width_mixes(mix, M):
     v = vbq()
     m = {"u1": {1: 1.0}, "u2": {2: 1.0}, "u4": wl.MIX_U4, "u8": wl.MIX_U8, "wide": wl.MIX_WIDE,
          "head": wl.MIX_HEAD}[mix]
-    q, bits, s, x = draw(300, 64 * 45, m, seed=12, M=8, outliers=0.01)
+    q, bits, s, x = draw(300, 64 * 45, m, seed=12, M=M, outliers=0.01)
     blob, L, dx = packed(v, q, bits, s, x)
     y = v.gemv_batched(L, blob, dx, out_dtype=torch.float32)
     torch.cuda.synchronize()
     check(y, q, bits, s, x, mix)
 
 
-@pytest.mark.parametrize("M", list(range(3, 17)))
+@pytest.mark.parametrize("M", list(range(3, 33)))
 def test_mfma_every_batch_size(M):
     v = vbq()
     q, bits, s, x = draw(200, 64 * 70, seed=100 + M, M=M, cluster=8, outliers=0.01)
@@ -83,33 +84,39 @@ def test_mfma_every_batch_size(M):
     check(y, q, bits, s, x, f"M={M}")
 
 
-def test_mfma_split_k_and_determinism():
+@pytest.mark.parametrize("M", [16, 32])
+def test_mfma_split_k_and_determinism(M):
     """A matrix with few row blocks and a long K splits K when the workspace
     allows it; split and unsplit results both meet the bound, and each is
     bit-identical across calls."""
     v = vbq()
-    N, K, M = 200, 64 * 300, 16
+    N, K = 200, 64 * 300
     q, bits, s, x = draw(N, K, seed=61, M=M, outliers=0.01)
     blob, L, dx = packed(v, q, bits, s, x)
     ws = v.workspace(L, M)
     assert ws is not None and v.workspace_size(L, M) >= 2 * M * N * 4  # this shape splits
     ys = v.gemv_batched(L, blob, dx, out_dtype=torch.float32, ws=ws)
     ys2 = v.gemv_batched(L, blob, dx, out_dtype=torch.float32, ws=ws)
-    y1 = v.gemv_batched(L, blob, dx, out_dtype=torch.float32)
-    y12 = v.gemv_batched(L, blob, dx, out_dtype=torch.float32)
+    small = torch.zeros(16, dtype=torch.uint8, device="cuda")  # too small for the partial sums: one workgroup per row block
+    y1 = v.gemv_batched(L, blob, dx, out_dtype=torch.float32, ws=small)
+    y12 = v.gemv_batched(L, blob, dx, out_dtype=torch.float32, ws=small)
     torch.cuda.synchronize()
     assert torch.equal(ys, ys2) and torch.equal(y1, y12)
+    assert torch.equal(ys, y1)  # the K segments are added in the same order either way
     check(ys, q, bits, s, x, "split")
     check(y1, q, bits, s, x, "unsplit")
 
 
 def test_mfma_token_independent_of_batch():
+    """A token's outputs are the same bit for bit in a batch of 32 (two tiles),
+    of 16 or of 3, wherever it sits in the batch."""
     v = vbq()
     N, K = 150, 64 * 67
-    q, bits, s, x = draw(N, K, seed=71, M=16, outliers=0.01)
+    q, bits, s, x = draw(N, K, seed=71, M=32, outliers=0.01)
     blob, L, dx = packed(v, q, bits, s, x)
     y16 = v.gemv_batched(L, blob, dx, out_dtype=torch.float32)
-    for lo, hi in ((0, 3), (5, 9), (13, 16)):
+    check(y16, q, bits, s, x, "M=32")
+    for lo, hi in ((0, 3), (5, 9), (13, 16), (14, 20), (16, 32), (3, 29), (0, 17)):
         part = torch.empty((hi - lo, K), dtype=torch.float16, device="cuda")
         part.copy_(dx[lo:hi])
         yp = v.gemv_batched(L, blob, part, out_dtype=torch.float32)
@@ -124,8 +131,8 @@ def test_mfma_unit_vectors_give_dequant_columns():
     blob, L, _ = packed(v, q, bits, s, np.zeros((1, K), np.uint16))
     w = v.dequant(L, blob, torch.float32)
     ks = list(range(64)) + [64, 100, 2047, 2048, 2111, 4000, K - 1]
-    for i0 in range(0, len(ks), 16):
-        kk = ks[i0:i0 + 16]
+    for i0 in range(0, len(ks), 32):
+        kk = ks[i0:i0 + 32]
         if len(kk) < 3:
             kk = kk + ks[:3 - len(kk)]
         X = torch.zeros((len(kk), K), dtype=torch.float16, device="cuda")
@@ -163,14 +170,21 @@ def test_mfma_special_scales():
         assert bool((y[:, :2] == 0).all())
 
 
-def test_mfma_strided_rows():
+@pytest.mark.parametrize("M", [5, 20])
+def test_mfma_strided_rows(M):
     """Row strides: ldx % 8 == 0 takes the matrix cores, other strides the
-    vector kernels; both give in-bound results and write only [M][N]."""
+    vector kernels (M <= 16; more tokens are refused); results are in bound and
+    only [M][N] is written."""
     v = vbq()
-    N, K, M = 70, 2048 + 64, 5
+    N, K = 70, 2048 + 64
     q, bits, s, x = draw(N, K, seed=52, M=M)
     blob, L, dx = packed(v, q, bits, s, x)
     for pad in (64, 40, 3):
+        if M > 16 and pad % 8:
+            xs = torch.zeros((M, K + pad), dtype=torch.float16, device="cuda")
+            with pytest.raises(v.VbqError, match="ALIGN"):
+                v.gemv_batched(L, blob, xs[:, :K])
+            continue
         xs = torch.zeros((M, K + pad), dtype=torch.float16, device="cuda")
         xs[:, :K] = dx
         out = torch.full((M, N + 10), float("nan"), dtype=torch.float32, device="cuda")
