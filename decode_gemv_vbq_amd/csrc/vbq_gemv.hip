@@ -1049,7 +1049,9 @@ vbq_status vbq_workspace_size(const vbq_layout *L, int M, size_t *bytes)
     VBQ_TRY(check_layout(L));
     if (M < 1 || M > kMaxBatch)
         return VBQ_ERR_BATCH;
-    *bytes = M >= kMfmaMinTokens ? mfma_workspace(L, M) : 0;
+    // the matrix cores take 3 or more tokens, and fewer where the streaming
+    // kernel does not apply
+    *bytes = M >= kMfmaMinTokens || !stream_applies(L, M) ? mfma_workspace(L, M) : 0;
     return VBQ_OK;
 }
 
@@ -1069,13 +1071,18 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
         return VBQ_ERR_ALIGN;
     {
         GemvCall call{L, blob, M, x, ldx, y, ldy, yt, stream};
-        if (mfma_applies(L, M, x, ldx))
+        const bool mfma = mfma_applies(L, M, x, ldx);
+        if (mfma && M >= kMfmaMinTokens)
             return mfma_gemv(call, ws, ws_bytes);
         if (M > 16) // only the matrix cores take more than 16 tokens
             return (uintptr_t)x % 16 || ldx % 8 ? VBQ_ERR_ALIGN : VBQ_ERR_SHAPE;
         vbq_status st;
         if (stream_gemv(call, &st))
             return st;
+        // one or two tokens on a matrix the streaming kernel does not take
+        // (K > 16256): the matrix cores, which unpack each code once all the same
+        if (mfma)
+            return mfma_gemv(call, ws, ws_bytes);
     }
     int MT = tokens_template(M);
     const int cus = current_device_cus();

@@ -46,6 +46,8 @@ struct GemvCall {
 // Launches the streaming kernel when it applies (M <= 2 and every row record
 // fits one LDS sub-unit); returns false, launching nothing, when it does not.
 bool stream_gemv(const GemvCall &g, vbq_status *st);
+// Whether the streaming kernel takes a matrix of layout L at M tokens (host only).
+bool stream_applies(const vbq_layout *L, int M);
 
 // One matrix of a shared-activation launch.
 struct StreamItem {
@@ -60,9 +62,10 @@ struct StreamItem {
 bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x, int ldx, vbq_dtype yt,
                         hipStream_t stream, vbq_status *st);
 
-// The matrix-core batched GEMV (vbq_mfma.hip): used for M >= kMfmaMinTokens
-// when x is 16-byte aligned, ldx % 8 == 0 and the blob and x fit 32-bit
-// buffer offsets.
+// The matrix-core batched GEMV (vbq_mfma.hip): used for M >= kMfmaMinTokens,
+// and for M <= 2 where the streaming kernel does not apply, when x is 16-byte
+// aligned, ldx % 8 == 0 and the blob and x fit 32-bit buffer offsets
+// (mfma_applies checks those conditions for any 1 <= M <= kMaxBatch).
 constexpr int kMfmaMinTokens = 3;
 constexpr int kMaxBatch = 32; // vbq_gemv_batched: more than 16 tokens only on the matrix cores
 bool mfma_applies(const vbq_layout *L, int M, const uint16_t *x, int ldx);

@@ -460,7 +460,7 @@ namespace vbq {
 
 bool mfma_applies(const vbq_layout *L, int M, const uint16_t *x, int ldx)
 {
-    return M >= kMfmaMinTokens && M <= 16 * kMaxTiles && L->total_bytes < (1ull << 32) && (uintptr_t)x % 16 == 0 &&
+    return M >= 1 && M <= 16 * kMaxTiles && L->total_bytes < (1ull << 32) && (uintptr_t)x % 16 == 0 &&
            ldx % 8 == 0 && (uint64_t)(M - 1) * ldx * 2 + 2ull * L->K < (1ull << 32);
 }
 

@@ -906,6 +906,15 @@ bool stream_gemv_shared(const StreamItem *items, int n, int M, const uint16_t *x
     return true;
 }
 
+bool stream_applies(const vbq_layout *L, int M)
+{
+    if (M < 1 || M > 2)
+        return false;
+    const StreamItem it{L, nullptr, nullptr, 0};
+    Plan p;
+    return make_plan(&it, 1, M, p);
+}
+
 bool stream_gemv(const GemvCall &g, vbq_status *st)
 {
     const StreamItem it{g.L, g.blob, g.y, g.ldy};

@@ -173,7 +173,8 @@ vbq_status vbq_dequant(const vbq_layout *L /* host */, const void *blob, void *w
 
 /*
  * Workspace bytes vbq_gemv / vbq_gemv_batched can use for layout L and M
- * tokens (1 <= M <= 32) on the current device: 0 for M <= 2; for M >= 3, the fp32 partial
+ * tokens (1 <= M <= 32) on the current device: 0 for M <= 2 when K <= 16256
+ * (the streaming kernel); otherwise the fp32 partial
  * sums ([segments][M][N]) of the K segments the matrix-core kernel cuts a
  * matrix with few row blocks into (0 when it cuts none).  The workspace is
  * optional: with at least this many bytes (4-byte aligned) each segment runs as
@@ -208,7 +209,9 @@ vbq_status vbq_gemv(const vbq_layout *L /* host */, const void *blob, const uint
  * For 3 <= M <= 32 with x 16-byte aligned and ldx % 8 == 0 the product runs on
  * the matrix cores (fp16 operands exact, fp32 accumulation, one or two tiles
  * of 16 tokens per call); a token's outputs then do not depend on the other
- * tokens of the batch or on M, bit for bit.  M > 16 runs only there:
+ * tokens of the batch or on M, bit for bit.  M <= 2 runs on the vector units
+ * (one streaming kernel) when K <= 16256, else also on the matrix cores when x
+ * and ldx allow it.  M > 16 runs only there:
  * VBQ_ERR_ALIGN when x or ldx does not meet those conditions, VBQ_ERR_SHAPE
  * when the blob or the span of x exceeds 4 GiB.
  * ws / ws_bytes: optional, see vbq_workspace_size (results do not depend on

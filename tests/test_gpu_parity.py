@@ -301,3 +301,34 @@ def test_gemv_shared_parity_and_equal_to_single(Ns, K, M, yt):
         alone = v.gemv_batched(L, blob, dx, out_dtype=out_dtype)
         torch.cuda.synchronize()
         assert torch.equal(alone, y)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("align", [True, False])
+def test_gemv_long_k_one_or_two_tokens(M, align):
+    """K above what the streaming kernel stages (16256): one or two tokens run
+    on the matrix cores when x is 16-byte aligned (with or without a
+    workspace, the same bits), else on the vector fallback; both in bound."""
+    v = vbq()
+    N, K = 150, 64 * 448
+    q, bits, s, x = draw(N, K, seed=90 + M, M=M, outliers=0.01)
+    dq, db, ds, dx = upload(q, bits, s, x, torch)
+    blob, L = v.pack(dq, db, ds)
+    if not align:  # rows at an odd 8-byte offset: not 16-byte aligned
+        xs = torch.zeros(M * K + 4, dtype=torch.float16, device="cuda")
+        xs[4:].view(M, K).copy_(dx)
+        dx = xs[4:].view(M, K)
+    assert (dx.data_ptr() % 16 == 0) == align
+    ws = v.workspace(L, M)
+    assert ws is not None  # a long K on few row blocks: the matrix cores' K split wants partial sums
+    ys = []
+    for w in (ws, torch.zeros(16, dtype=torch.uint8, device="cuda")):
+        if M == 1 and align:
+            ys.append(v.gemv(L, blob, dx[0], out_dtype=torch.float32, ws=w)[None])
+        else:
+            ys.append(v.gemv_batched(L, blob, dx, out_dtype=torch.float32, ws=w))
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    y_ref, bound = oracle.gemv(q, bits, s, x)
+    ok, worst, idx = within_bound(ys[0].cpu().numpy().astype(np.float64), y_ref, bound)
+    assert ok, f"M={M} align={align} worst err/bound={worst:.3g} at {idx}"
