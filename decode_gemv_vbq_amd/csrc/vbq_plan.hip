@@ -668,15 +668,11 @@ __device__ void argmax_finish(unsigned long long *key, uint32_t *count, int32_t 
 constexpr int kDepth = 3; // passes in flight per wavefront besides the one computed
 
 template <int MT, int OM, int KP>
-__global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_line */)
+__device__ __forceinline__ void plan_body(const u32x16 a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // this workgroup's record (matrix blockIdx.y of the launch), in one load
-    const u32x16 a = kernarg_line((uint32_t)blockIdx.y * (uint32_t)sizeof(PRec));
-    if ((int)blockIdx.x >= (int)a[14])
-        return; // the launch spans the largest matrix; a smaller one has fewer blocks
     const uint8_t *plan = (const uint8_t *)u64_ptr(a[0], a[1]);
     void *const yptr = (void *)u64_ptr(a[2], a[3]);
     const uint16_t *xptr = (const uint16_t *)u64_ptr(a[4], a[5]);
@@ -803,6 +799,43 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     }
 }
 
+template <int MT, int OM, int KP>
+__global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_line */)
+{
+    // this workgroup's record (matrix blockIdx.y of the launch), in one load
+    const u32x16 a = kernarg_line((uint32_t)blockIdx.y * (uint32_t)sizeof(PRec));
+    if ((int)blockIdx.x >= (int)a[14])
+        return; // the launch spans the largest matrix; a smaller one has fewer blocks
+    plan_body<MT, OM, KP>(a);
+}
+
+// One matrix, one token, plain rows: the record's fields as scalar arguments,
+// which the dispatch preloads into SGPRs, so no wavefront waits for a load of
+// its arguments.
+template <int KP>
+__global__ __launch_bounds__(kT) void k_gemv_plan1(const uint8_t *plan, void *y, const uint16_t *x, uint32_t region,
+                                                   int N, int rows, int passes, int per_wave, uint32_t g_yt, int smax)
+{
+    u32x16 a;
+    a[0] = (uint32_t)(uintptr_t)plan;
+    a[1] = (uint32_t)((uintptr_t)plan >> 32);
+    a[2] = (uint32_t)(uintptr_t)y;
+    a[3] = (uint32_t)((uintptr_t)y >> 32);
+    a[4] = (uint32_t)(uintptr_t)x;
+    a[5] = (uint32_t)((uintptr_t)x >> 32);
+    a[6] = region;
+    a[7] = (uint32_t)N;
+    a[8] = 0u; // ldy: one token
+    a[9] = (uint32_t)rows;
+    a[10] = 0u; // ldx: one token
+    a[11] = (uint32_t)passes;
+    a[12] = (uint32_t)per_wave;
+    a[13] = g_yt;
+    a[14] = 0x7fffffffu;
+    a[15] = (uint32_t)smax;
+    plan_body<1, kRows, KP>(a);
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 
@@ -851,6 +884,15 @@ vbq_status lds_attribute_once(const void *fn) { return dynamic_lds_once(fn, kLds
 template <int MT, int OM, int KP>
 vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
+    if constexpr (MT == 1 && OM == kRows) {
+        if (grid.y == 1) {
+            const PRec &r = a.rec[0];
+            VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan1<KP>));
+            hipLaunchKernelGGL((k_gemv_plan1<KP>), dim3(grid), dim3(kT), lds, stream, r.plan, r.y, r.x, r.region, r.N,
+                               r.rows, r.passes, r.per_wave, r.g_yt, r.smax);
+            return launch_status();
+        }
+    }
     VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan<MT, OM, KP>));
     hipLaunchKernelGGL((k_gemv_plan<MT, OM, KP>), dim3(grid), dim3(kT), lds, stream, a);
     return launch_status();
