@@ -56,8 +56,17 @@ constexpr uint32_t kLdsBudget = 160u * 1024u;
 __host__ __device__ constexpr int groups_per_pass(int c) { return 128 >> c; } // c = log2(width)
 
 // Position stride of a block: position = column * stride + row.  At least 2,
-// so that the column is always a 32-bit reciprocal multiply away.
-__host__ __device__ constexpr int pos_stride(int rows) { return rows < 2 ? 2 : rows; }
+// so that the column is always a 32-bit reciprocal multiply away.  From 32
+// rows on it is padded to 64 / L modulo 32 (L lanes sum a row at the end, L
+// by G as in sum_lanes), so that the L lanes of a row and the 64 / L rows of a
+// wavefront read the partial sums from distinct LDS banks (two lanes per bank,
+// the least for 64 lanes): 2% on a 9B decode step.
+__host__ __device__ constexpr int sum_lanes_of(int G) { return G > 256 ? 64 : G > 128 ? 32 : G > 64 ? 16 : 8; }
+__host__ __device__ constexpr int pos_stride(int rows, int G)
+{
+    const int r = rows < 2 ? 2 : rows, want = 64 / sum_lanes_of(G);
+    return r < 32 ? r : r + ((want - r) % 32 + 32) % 32;
+}
 
 // Partial sums per token in LDS: every position of the widest block plus one
 // slot that the empty places of a partly filled pass write to.
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(kT) void k_prepare(PrepArgs a)
         return;
     }
     uint8_t *region = a.plan + (uint64_t)blockIdx.x * a.region;
-    const int stride = pos_stride(a.rows);
+    const int stride = pos_stride(a.rows, a.G);
     const uint32_t dummy = (uint32_t)(stride * G) << 16; // scale 0 at the spare position
     // the empty places of each width's last pass: zero codes, the spare position
     for (int c = 0; c < 4; c++) {
@@ -550,7 +559,7 @@ __device__ __forceinline__ void pass_b8(const PBuf &b, const PCtx &cx)
 
 // Lanes that sum one row: more for longer rows, so that the row sums stay
 // short (a row of G partials is G / lanes loads deep).
-__device__ __forceinline__ int sum_lanes(int G) { return G > 256 ? 64 : G > 128 ? 32 : G > 64 ? 16 : 8; }
+__device__ __forceinline__ int sum_lanes(int G) { return sum_lanes_of(G); }
 
 // Output modes, a template parameter of the kernel (a plain GEMV carries no
 // code of the others).  kRows: finished rows are stored as fp32 or fp16 (yt).
@@ -684,7 +693,7 @@ __device__ __forceinline__ void plan_body(const u32x16 a)
     const int blk = (int)blockIdx.x;
     const int n0 = blk * rows;
     const int R = min(rows, Nm - n0);
-    const int stride = pos_stride(rows);
+    const int stride = pos_stride(rows, G);
     const PLayout L = p_layout(MT, G, smax);
     const int ps = psum_stride(G, smax);
     uint32_t *xrec = reinterpret_cast<uint32_t *>(smem + L.x);
@@ -853,7 +862,8 @@ vbq_status check_plan(const vbq_plan *P)
     if (P->N < 1 || P->G < 1 || P->G > kMaxG || P->K != 64 * P->G || P->M < 1 || P->M > 2 || P->wgs < 1 ||
         P->rows < 1 || (int64_t)P->wgs * P->rows < P->N || (int64_t)(P->wgs - 1) * P->rows >= P->N ||
         P->wgs > 65535 || P->passes < 1 || P->per_wave != per_wave_of(P->passes) || P->per_wave > kMaxPerWave ||
-        (int64_t)pos_stride(P->rows) * P->G + 1 > 65536 || P->psum != psum_stride(P->G, pos_stride(P->rows)) ||
+        (int64_t)pos_stride(P->rows, P->G) * P->G + 1 > 65536 ||
+        P->psum != psum_stride(P->G, pos_stride(P->rows, P->G)) ||
         P->region_bytes != region_of(P->passes, P->per_wave) ||
         P->total_bytes != (uint64_t)P->wgs * P->region_bytes)
         return VBQ_ERR_LAYOUT;
@@ -927,7 +937,7 @@ vbq_status launch_plan(int m, int om, const PArgs &a, dim3 grid, uint32_t lds, h
 
 bool lds_fits(int M, int G, int rows)
 {
-    return p_layout(M, G, pos_stride(rows)).total <= kLdsBudget && (int64_t)pos_stride(rows) * G + 1 <= 65536;
+    return p_layout(M, G, pos_stride(rows, G)).total <= kLdsBudget && (int64_t)pos_stride(rows, G) * G + 1 <= 65536;
 }
 
 } // namespace
@@ -935,7 +945,7 @@ bool lds_fits(int M, int G, int rows)
 bool vbq::planned_can_share(const vbq_plan *a, const vbq_plan *b)
 {
     return a->K == b->K && a->M == b->M &&
-           lds_fits(a->M, a->G, std::max(pos_stride(a->rows), pos_stride(b->rows)));
+           lds_fits(a->M, a->G, std::max(pos_stride(a->rows, a->G), pos_stride(b->rows, b->G)));
 }
 
 extern "C" {
@@ -962,17 +972,18 @@ vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, 
     // never splits the (gate, up) pairs of an interleaved SwiGLU matrix; fewer
     // rows (more blocks) while a block's partial sums do not fit the LDS
     auto fit = [&](int m, int &rows_out) {
+        const int step = N % 2 == 0 ? 2 : 1; // an even N keeps even blocks
         int rows = (N + wgs - 1) / wgs;
+        rows += rows % step;
         for (;;) {
-            if (N % 2 == 0 && rows % 2)
-                rows++;
             if (lds_fits(m, G, rows)) {
                 rows_out = rows;
                 return true;
             }
-            if (rows <= 1)
+            if (rows <= step)
                 return false;
-            rows = std::max(1, rows * 3 / 4);
+            // about 3/4 as many rows, a multiple of step, and strictly fewer
+            rows = std::max(step, std::min(rows - step, rows * 3 / 4 / step * step));
         }
     };
     int rows = 0;
@@ -991,8 +1002,8 @@ vbq_status vbq_plan_init(const vbq_layout *L, const void *blob, int M, int wgs, 
     p.M = M;
     p.wgs = wgs;
     p.rows = rows;
-    p.psum = psum_stride(G, pos_stride(rows));
-    p.lds_bytes = (int)p_layout(M, G, pos_stride(rows)).total;
+    p.psum = psum_stride(G, pos_stride(rows, G));
+    p.lds_bytes = (int)p_layout(M, G, pos_stride(rows, G)).total;
     // sizing pass: the largest block's pass count
     VBQ_TRY(zero_words(ws, 16, stream));
     PrepArgs a = prep_args(L, blob, &p);
@@ -1074,7 +1085,7 @@ vbq_status planned_args(const vbq_planned_item *items, int n, int M, const uint1
         r.per_wave = P->per_wave;
         r.wgs = P->wgs;
         gx = std::max(gx, P->wgs);
-        smax = std::max(smax, pos_stride(P->rows)); // LDS strides: the plan with the most rows fits
+        smax = std::max(smax, pos_stride(P->rows, P->G)); // LDS strides: the plan with the most rows fits
     }
     const int G = items[0].P->G;
     const uint32_t lds = p_layout(M, G, smax).total;

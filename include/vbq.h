@@ -263,7 +263,10 @@ vbq_status vbq_gemv_shared(const vbq_gemv_item *items /* host */, int n, int M, 
  *   bytes [0, 1024): group k's code record (8*b bytes, copied verbatim from
  *     the blob) at k * 8*b;
  *   bytes [1024, 1536): u32 per group k at 1024 + 4k: fp16 scale bits |
- *     e << 16, e = column * S + (row - first row of the block), S = max(rows, 2);
+ *     e << 16, e = column * S + (row - first row of the block); the position
+ *     stride S = max(rows, 2) below 32 rows, else the smallest S >= rows with
+ *     S = 64 / L (mod 32), L = 8, 16, 32 or 64 for G <= 64, <= 128, <= 256 or
+ *     more;
  *   an empty place of a partly filled pass has zero codes and the word
  *     (S * G) << 16 (scale 0 at a position no row uses).
  * After the `passes` records (at passes * 1536): the width byte of each pass

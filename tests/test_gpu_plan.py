@@ -210,7 +210,10 @@ def test_plan_passes_cover_every_group_once(N, K, wgs):
     _, (blob, L, plan, P, _) = planned(v, q, bits, s, x, wgs=wgs)
     buf = plan.cpu().numpy()
     G = K // 64
-    S = max(P.rows, 2)
+    # the documented position stride: from 32 rows on, padded to 64 / L mod 32
+    L = 64 if G > 256 else 32 if G > 128 else 16 if G > 64 else 8
+    S = max(P.rows, 2) if P.rows < 32 else P.rows + (64 // L - P.rows) % 32
+    assert P.psum == (S * G + 1 + 3) // 4 * 4
     seen = np.zeros((N, G), np.int32)
     assert P.region_bytes == (P.passes * 1536 + 16 * P.per_wave + 255) // 256 * 256
     for b in range(P.wgs):
