@@ -55,6 +55,14 @@ constexpr uint32_t kLdsBudget = 160u * 1024u;
 
 __host__ __device__ constexpr int groups_per_pass(int c) { return 128 >> c; } // c = log2(width)
 
+// Width bytes per wavefront for a region of `passes` pass records (every
+// wavefront's list ends with a 0; a multiple of 4), and the region's bytes.
+__host__ __device__ constexpr int per_wave_for(int passes) { return ((passes + kW - 1) / kW + 1 + 3) & ~3; }
+__host__ __device__ constexpr uint32_t region_for(int passes, int per_wave)
+{
+    return ((uint32_t)passes * kPassBytes + (uint32_t)kW * per_wave + 255u) & ~255u;
+}
+
 // Position stride of a block: position = column * stride + row.  At least 2,
 // so that the column is always a 32-bit reciprocal multiply away.  From 32
 // rows on it is padded to 64 / L modulo 32 (L lanes sum a row at the end, L
@@ -845,15 +853,46 @@ __global__ __launch_bounds__(kT) void k_gemv_plan1(const uint8_t *plan, void *y,
     plan_body<1, kRows, KP>(a);
 }
 
+// Two matrices of one shape that share x (a layer's gate and up projections),
+// one token, plain rows: both records in 13 preloaded scalar arguments
+// (n_rows = N | rows << 20, passes = passes of matrix 0 | of matrix 1 << 16;
+// per-wave bytes, region and position stride follow from them); blockIdx.y
+// picks the matrix.
+template <int KP>
+__global__ __launch_bounds__(kT) void k_gemv_plan2(const uint8_t *plan0, const uint8_t *plan1, void *y0, void *y1,
+                                                   const uint16_t *x, uint32_t n_rows, uint32_t passes01, uint32_t g_yt)
+{
+    const bool second = blockIdx.y != 0;
+    const uint8_t *plan = second ? plan1 : plan0;
+    void *y = second ? y1 : y0;
+    const int passes = (int)(second ? passes01 >> 16 : passes01 & 0xffffu);
+    const int per_wave = per_wave_for(passes), rows = (int)(n_rows >> 20);
+    u32x16 a;
+    a[0] = (uint32_t)(uintptr_t)plan;
+    a[1] = (uint32_t)((uintptr_t)plan >> 32);
+    a[2] = (uint32_t)(uintptr_t)y;
+    a[3] = (uint32_t)((uintptr_t)y >> 32);
+    a[4] = (uint32_t)(uintptr_t)x;
+    a[5] = (uint32_t)((uintptr_t)x >> 32);
+    a[6] = region_for(passes, per_wave);
+    a[7] = n_rows & 0xfffffu;
+    a[8] = 0u; // ldy: one token
+    a[9] = (uint32_t)rows;
+    a[10] = 0u; // ldx: one token
+    a[11] = (uint32_t)passes;
+    a[12] = (uint32_t)per_wave;
+    a[13] = g_yt;
+    a[14] = 0x7fffffffu; // both matrices have the launch's block count
+    a[15] = (uint32_t)pos_stride(rows, (int)(g_yt & 0xffffu));
+    plan_body<1, kRows, KP>(a);
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 
-uint64_t region_of(int passes, int per_wave)
-{
-    return align_up((uint64_t)passes * kPassBytes + (uint64_t)kW * per_wave, 256);
-}
+uint64_t region_of(int passes, int per_wave) { return region_for(passes, per_wave); }
 
-int per_wave_of(int passes) { return (int)align_up((uint64_t)((passes + kW - 1) / kW + 1), 4); }
+int per_wave_of(int passes) { return per_wave_for(passes); }
 
 vbq_status check_plan(const vbq_plan *P)
 {
@@ -900,6 +939,18 @@ vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t st
             VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan1<KP>));
             hipLaunchKernelGGL((k_gemv_plan1<KP>), dim3(grid), dim3(kT), lds, stream, r.plan, r.y, r.x, r.region, r.N,
                                r.rows, r.passes, r.per_wave, r.g_yt, r.smax);
+            return launch_status();
+        }
+        const PRec &r0 = a.rec[0], &r1 = a.rec[1];
+        const int G = (int)(r0.g_yt & 0xffffu);
+        if (grid.y == 2 && r0.x == r1.x && r0.g_yt == r1.g_yt && r0.N == r1.N && r0.rows == r1.rows &&
+            r0.wgs == (int)grid.x && r1.wgs == (int)grid.x && r0.N < (1 << 20) && r0.rows < (1 << 12) &&
+            r0.passes < (1 << 16) && r1.passes < (1 << 16) && r0.smax == pos_stride(r0.rows, G) &&
+            r0.smax == r1.smax) {
+            VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan2<KP>));
+            hipLaunchKernelGGL((k_gemv_plan2<KP>), dim3(grid), dim3(kT), lds, stream, r0.plan, r1.plan, r0.y, r1.y,
+                               r0.x, (uint32_t)r0.N | ((uint32_t)r0.rows << 20),
+                               (uint32_t)r0.passes | ((uint32_t)r1.passes << 16), r0.g_yt);
             return launch_status();
         }
     }
