@@ -166,7 +166,10 @@ def test_planned_many_tokens(M, Mp):
 
 
 @pytest.mark.parametrize("Ns,K,M,yt", [((5632, 5632), 2048, 1, "f16"), ((300, 77, 1000), 4096, 1, "f32"),
-                                        ((640, 33, 200, 129), 2112, 2, "f16")])
+                                        ((640, 33, 200, 129), 2112, 2, "f16"),
+                                        # two same-shape matrices, one token: the preloaded two-record kernel;
+                                        # two shapes: the argument records
+                                        ((3000, 3000), 4096 + 640, 1, "f32"), ((1000, 998), 4096, 1, "f32")])
 def test_planned_shared_parity_and_equal_to_single(Ns, K, M, yt):
     v = vbq()
     out_dtype = torch.float16 if yt == "f16" else torch.float32
