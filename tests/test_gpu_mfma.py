@@ -192,3 +192,31 @@ def test_mfma_strided_rows(M):
         torch.cuda.synchronize()
         check(out[:, :N], q, bits, s, x, f"ldx={K + pad}")
         assert bool(torch.isnan(out[:, N:]).all())
+
+
+@pytest.mark.parametrize("M", [16, 32])
+def test_mfma_graph_replays_match_eager(M):
+    """The split launch and its partial-sum kernel captured in a HIP graph:
+    every replay (with eager work and synchronisation between replays) gives
+    the eager result bit for bit."""
+    v = vbq()
+    N, K = 200, 64 * 300
+    q, bits, s, x = draw(N, K, seed=33 + M, M=M, outliers=0.01)
+    blob, L, dx = packed(v, q, bits, s, x)
+    ws = v.workspace(L, M)
+    assert ws is not None
+    eager = v.gemv_batched(L, blob, dx, out_dtype=torch.float32, ws=ws)
+    out = torch.empty_like(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        v.gemv_batched(L, blob, dx, out=out, ws=ws)
+    for r in range(3):
+        out.fill_(float("nan"))
+        other = v.gemv_batched(L, blob, dx[:3].contiguous(), out_dtype=torch.float32, ws=ws)  # eager work between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
+        assert torch.equal(other, eager[:3])
+    check(eager, q, bits, s, x, f"M={M}")
