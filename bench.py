@@ -222,8 +222,9 @@ def bench_batched(torch, v, args):
     projections for M in {1, 4, 8, 16} tokens (and 32, which only the blob path
     and torch.matmul take) (1% outlier channels), width variants clustered (runs
     of 8 groups from the base mix), uniform 4-bit and all-8-bit.  Per (variant,
-    M), one up+down pair through the prepared plans (vbq_gemv_planned) and
-    straight from the blobs (vbq_gemv_batched), with
+    M), one up+down pair through the prepared plans (vbq_gemv_planned: plans made
+    for one-token launches at M = 1, for token pairs otherwise) and straight
+    from the blobs (vbq_gemv_batched), with
     enough weight copies in turn that a round streams at least 1 GB (so each
     call reads from HBM), replayed from a HIP graph; the hand-written dense fp16
     GEMV and torch.matmul on the dequantized weights of one copy at the same
@@ -249,7 +250,8 @@ def bench_batched(torch, v, args):
                 blob, L = v.pack(q, bits, sc.view(torch.float16))
                 del q, bits, sc
                 plan, P = v.prepare(L, blob, M=2)
-                pair.append({"spec": spec, "L": L, "blob": blob, "plan": plan, "P": P,
+                plan1, P1 = v.prepare(L, blob, M=1) if 1 in Ms else (None, None)  # one-token launches
+                pair.append({"spec": spec, "L": L, "blob": blob, "plan": plan, "P": P, "plan1": plan1, "P1": P1,
                              "ws": v.workspace(L, max(Ms))})
             copies.append(pair)
             alg1 = sum(acc.vbq_read_bytes(m["L"], 0) for m in pair)
@@ -270,7 +272,10 @@ def bench_batched(torch, v, args):
             def planned():
                 for pair, o in zip(copies, outs):
                     for m, y in zip(pair, o):
-                        v.gemv_planned(m["P"], m["plan"], xm[m["spec"].K], out=y)
+                        if M == 1:  # the plan made for one-token launches
+                            v.gemv_planned(m["P1"], m["plan1"], xm[m["spec"].K], out=y)
+                        else:
+                            v.gemv_planned(m["P"], m["plan"], xm[m["spec"].K], out=y)
 
             def blobs():
                 for pair, o in zip(copies, outs):
