@@ -96,7 +96,8 @@ def time_steps(torch, fn, steps):
 
 
 KERNELS = {  # path -> (kernel, entry point, profile name, sources)
-    "plan": ("k_gemv_plan<1, 0, KP>", "vbq_gemv_planned", "k_gemv_plan", ("vbq_plan.hip", "vbq_unpack.h", "vbq_common.h")),
+    "plan": ("k_gemv_plan1<KP> / k_gemv_plan2<KP> (the k_gemv_plan body, one token, preloaded arguments)",
+             "vbq_gemv_planned", "k_gemv_plan", ("vbq_plan.hip", "vbq_unpack.h", "vbq_common.h")),
     "vbq1": ("k_gemv_stream<1>", "vbq_gemv", "k_gemv_stream", ("vbq_stream.hip", "vbq_unpack.h", "vbq_common.h")),
     "mfma": ("k_gemv_mfma", "vbq_gemv_batched", "k_gemv_mfma", ("vbq_mfma.hip", "vbq_unpack.h", "vbq_common.h")),
 }
