@@ -166,6 +166,15 @@ def oracle_rate():
     return (time.perf_counter() - t0) / (16 * 4096)
 
 
+def cold_copies(W) -> int:
+    """Copies of workload W that a timed step runs in turn: 1 when its weights
+    (estimated from the width mix) exceed the 256 MB memory-side cache, else
+    enough fresh copies to stream at least 512 MB per step, so that every GEMV
+    reads its weights from HBM as it would between other layers."""
+    alg_one = sum(sp.N * sp.K * sum(b * f for b, f in sp.mix.items()) / 8 + sp.N * sp.G * 2 for sp in W.mats)
+    return 1 if alg_one >= 256e6 else int(-(-512e6 // alg_one))
+
+
 def cpu_baseline(step, reps=3, copies=1):
     """The oracle (plain C, fp64) timed on the host on the step's sampled rows:
     the same device draws the GPU multiplies, copied back when the step was
@@ -653,12 +662,8 @@ def main(argv=None):
         bench_batched(torch, v, args)
         return
     from decode_gemv_vbq_amd import workload as wl
-    # a workload that fits the 256 MB memory-side cache runs as several copies
-    # in turn (fresh draws, at least 512 MB of weights per round), reported per
-    # copy, so that its weights come from HBM as they would between other layers
     one = wl.workload(args.workload)
-    alg_one = sum(sp.N * sp.K * sum(b * f for b, f in sp.mix.items()) / 8 + sp.N * sp.G * 2 for sp in one.mats)
-    copies = 1 if alg_one >= 256e6 else int(-(-512e6 // alg_one))
+    copies = cold_copies(one)
     frac = 0.0
     if not args.no_cpu:
         # the CPU baseline's row sample: about cpu_seconds / 4 per single-thread run

@@ -47,3 +47,18 @@ def test_bench_refuses_more_than_one_gpu(capsys):
         bench.main(["--gpus", "2"])
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().out
+
+
+@pytest.mark.parametrize("name", ["linear768", "mlp1b", "decode1b", "decode9b"])
+def test_cold_copies_stream_past_the_memory_side_cache(name):
+    """A workload below the 256 MB memory-side cache runs as copies in turn that
+    stream at least 512 MB of codes and scales per step; larger ones run once."""
+    import bench
+    from decode_gemv_vbq_amd import workload as wl
+    W = wl.workload(name)
+    c = bench.cold_copies(W)
+    packed = sum(sp.N * sp.K * sum(b * f for b, f in sp.mix.items()) / 8 + 2 * sp.N * sp.G for sp in W.mats)
+    if packed >= 256e6:
+        assert c == 1
+    else:
+        assert c > 1 and c * packed >= 512e6 and (c - 1) * packed < 512e6
