@@ -467,7 +467,7 @@ def bench_swiglu(torch, v, args):
                    "shared_two_output_us": round(res["shared"], 2), "alg_bytes": alg},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": None,
-                     "kernel": "k_gemv_plan<1, 2> SwiGLU epilogue (vbq_gemv_planned_swiglu)"},
+                     "kernel": "k_gemv_plan1<2, KP> SwiGLU epilogue, preloaded arguments (vbq_gemv_planned_swiglu)"},
         "cpu_baseline": None}), flush=True)
 
 

@@ -826,10 +826,10 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     plan_body<MT, OM, KP>(a);
 }
 
-// One matrix, one token, plain rows: the record's fields as scalar arguments,
-// which the dispatch preloads into SGPRs, so no wavefront waits for a load of
-// its arguments.
-template <int KP>
+// One matrix, one token, plain rows or the SwiGLU epilogue: the record's fields
+// as scalar arguments, which the dispatch preloads into SGPRs, so no wavefront
+// waits for a load of its arguments.
+template <int OM, int KP>
 __global__ __launch_bounds__(kT) void k_gemv_plan1(const uint8_t *plan, void *y, const uint16_t *x, uint32_t region,
                                                    int N, int rows, int passes, int per_wave, uint32_t g_yt, int smax)
 {
@@ -850,7 +850,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan1(const uint8_t *plan, void *y,
     a[13] = g_yt;
     a[14] = 0x7fffffffu;
     a[15] = (uint32_t)smax;
-    plan_body<1, kRows, KP>(a);
+    plan_body<1, OM, KP>(a);
 }
 
 // Two matrices of one shape that share x (a layer's gate and up projections),
@@ -933,14 +933,16 @@ vbq_status lds_attribute_once(const void *fn) { return dynamic_lds_once(fn, kLds
 template <int MT, int OM, int KP>
 vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
-    if constexpr (MT == 1 && OM == kRows) {
+    if constexpr (MT == 1 && (OM == kRows || OM == kSwiglu)) {
         if (grid.y == 1) {
             const PRec &r = a.rec[0];
-            VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan1<KP>));
-            hipLaunchKernelGGL((k_gemv_plan1<KP>), dim3(grid), dim3(kT), lds, stream, r.plan, r.y, r.x, r.region, r.N,
-                               r.rows, r.passes, r.per_wave, r.g_yt, r.smax);
+            VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan1<OM, KP>));
+            hipLaunchKernelGGL((k_gemv_plan1<OM, KP>), dim3(grid), dim3(kT), lds, stream, r.plan, r.y, r.x, r.region,
+                               r.N, r.rows, r.passes, r.per_wave, r.g_yt, r.smax);
             return launch_status();
         }
+    }
+    if constexpr (MT == 1 && OM == kRows) {
         const PRec &r0 = a.rec[0], &r1 = a.rec[1];
         const int G = (int)(r0.g_yt & 0xffffu);
         if (grid.y == 2 && r0.x == r1.x && r0.g_yt == r1.g_yt && r0.N == r1.N && r0.rows == r1.rows &&
