@@ -31,11 +31,13 @@
 // tiles, for the LDS) share a compute unit
 // (four wavefronts per SIMD hide each other's LDS, matrix-core and memory
 // latencies).  Per chunk, in one of two LDS buffers: the 4 groups' activations
-// as fp16 pairs (wavefront w stages group w), their offset constants, and per
-// wavefront the byte offset, width and scale of its 16 rows' 4 groups (lane
-// (q, n) works out group q of row n).  While chunk c is computed, chunk c+1 is
-// staged and its code words are loaded into registers, and the inputs of chunk
-// c+2 (activations, width planes, slice offset, scale) are loaded.
+// as fp16 pairs (wavefront w stages group w) and their offset constants.  The
+// byte offset, width and scale of a row's 4 groups are worked out by the lanes
+// (q, n) for group q of row n and handed to every lane of row n with the
+// gfx950 lane swaps (v_permlane32_swap, v_permlane16_swap), in registers.
+// While chunk c is computed, chunk c+1 is staged and its code words are loaded
+// into registers, and the inputs of chunk c+2 (activations, width planes,
+// slice offset, scale) are loaded.
 //
 // K segments.  A matrix with too few row blocks to fill the device has its
 // chunks cut into segments (from the shape and the device's compute units
@@ -60,8 +62,6 @@ constexpr int kChunk = 4;              // groups per chunk: wavefront w stages g
 constexpr int kTok = 144;              // LDS bytes per token of a staged group (128 + 16 against bank conflicts)
 constexpr int kXGroup = 16 * kTok;     // one staged group, one tile of 16 tokens
 constexpr int kCGroup = 4 * 16 * 4;    // offset constants of one group and tile: [width code][token] fp32
-constexpr int kMWave = kChunk * 16 * 8; // one wavefront's metadata: [group][row] {offset | code, scale}
-constexpr int kMBytes = kWaves * kMWave;
 constexpr int kBufs = 2;
 constexpr int kTabBytes = 5 * 48;      // B operands of the offset constants: [width code, or 4 = zero][Bm0 Bm1 Bo]
 constexpr int kMaxSplits = 16;
@@ -69,13 +69,13 @@ constexpr int kMaxTiles = 2;           // token tiles of 16 per call
 
 // Per token-tile count T (a call of up to 16 T tokens): one LDS buffer holds
 // the chunk's activations [group][tile][token] and offset constants
-// [group][tile][width][token], then the wavefronts' metadata.  One tile leaves
-// room for four workgroups per compute unit, two tiles for three.
+// [group][tile][width][token].  One tile leaves room for four workgroups per
+// compute unit, two tiles for three.
 template <int T>
 struct Geo {
     static constexpr int kXBytes = kChunk * T * kXGroup;
     static constexpr int kCBytes = kChunk * T * kCGroup;
-    static constexpr int kBufBytes = kXBytes + kCBytes + kMBytes;
+    static constexpr int kBufBytes = kXBytes + kCBytes;
     static constexpr int kLdsBytes = kBufs * kBufBytes + kTabBytes;
     static constexpr int kBlocksPerCu = T == 1 ? 4 : 3;
 };
@@ -125,6 +125,20 @@ __device__ __forceinline__ hf8 as_hf8(uint32_t a, uint32_t b, uint32_t c, uint32
 {
     const u32x4 v = {a, b, c, d};
     return __builtin_bit_cast(hf8, v);
+}
+
+// v of the lanes with the same n in rows (q) 0..3 of the wavefront, in every
+// lane: v_permlane32_swap pairs rows 0,1 with 2,3 and v_permlane16_swap rows
+// 0 with 1 and 2 with 3 (lane layout checked on the device).
+__device__ __forceinline__ void rows4(uint32_t v, uint32_t (&o)[4])
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);       // [v0 v1 v0 v1], [v2 v3 v2 v3]
+    const auto lo = __builtin_amdgcn_permlane16_swap(p[0], p[0], false, false); // v0, v1 in every row
+    const auto hi = __builtin_amdgcn_permlane16_swap(p[1], p[1], false, false); // v2, v3 in every row
+    o[0] = lo[0];
+    o[1] = lo[1];
+    o[2] = hi[0];
+    o[3] = hi[1];
 }
 
 __device__ __forceinline__ f32x4 mfma(hf8 a, hf8 b, f32x4 c)
@@ -231,9 +245,10 @@ __global__ __launch_bounds__(kThreads, Geo<T>::kBlocksPerCu) void k_gemv_mfma(MA
             rb, mon ? a.off_scales + 2u * ((uint32_t)row * (uint32_t)a.G + (uint32_t)gi) : kNone, 0, 0);
     };
 
-    // stage chunk ch into buffer bi: activations, offset constants, this
-    // wavefront's metadata
-    auto stage = [&](int ch, int bi, const ChunkIn<T> &in) {
+    // stage chunk ch into buffer bi (activations, offset constants); offs and
+    // ms: the code offset | width and the width | scale << 16 of groups 0..3
+    // of this lane's row
+    auto stage = [&](int ch, int bi, const ChunkIn<T> &in, uint32_t (&offs)[4], uint32_t (&ms)[4]) {
         uint8_t *buf = smem + bi * kBufBytes;
         const u32x4 *tb = reinterpret_cast<const u32x4 *>(tab + 48 * (n < 4 ? n : 4));
         const u32x4 bm0 = tb[0], bm1 = tb[1], bo = tb[2];
@@ -270,21 +285,20 @@ __global__ __launch_bounds__(kThreads, Geo<T>::kBlocksPerCu) void k_gemv_mfma(MA
         const uint32_t rank = (uint32_t)__popc(pick4(wm.m, c) & ((1u << i) - 1u));
         const uint32_t off = row_base + in.so + start + (rank << (3 + c));
         const bool ok = live && ch < c1 && gi < a.G;
-        *reinterpret_cast<u32x2 *>(buf + kXBytes + kCBytes + wave * kMWave + q * 128 + n * 8) =
-            u32x2{ok ? off | (uint32_t)c : 0u, ok ? in.sc : 0u};
+        // entry 0 (no group: a row past N, a chunk past the range) reads the
+        // blob's first 16 bytes, which the scale 0 or the skipped group discards
+        rows4(ok ? off | (uint32_t)c : 0u, offs);
+        rows4(ok ? (uint32_t)c | (in.sc << 16) : 0u, ms);
     };
 
     // code words of the staged chunk in buffer bi, this lane's quarter (byte
     // offset (2q << c) & ~3 in the group: quarter q of a 1-bit group is the
     // half-word 2q of its words)
     const uint32_t qq = 2u * (uint32_t)q;
-    auto load_codes = [&](int bi, u32x4 *cw) {
-        const uint8_t *mb = smem + bi * kBufBytes + kXBytes + kCBytes + wave * kMWave;
+    auto load_codes = [&](const uint32_t (&offs)[4], u32x4 *cw) {
 #pragma unroll
         for (int gl = 0; gl < kChunk; gl++) {
-            // entry 0 (no group: a row past N, a chunk past the range) reads the
-            // blob's first 16 bytes, which the scale 0 or the skipped group discards
-            const uint32_t e = *reinterpret_cast<const uint32_t *>(mb + gl * 128 + n * 8);
+            const uint32_t e = offs[gl];
             const uint32_t off = (e & ~3u) + ((qq << (e & 3u)) & ~3u);
             cw[gl] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
         }
@@ -296,14 +310,13 @@ __global__ __launch_bounds__(kThreads, Geo<T>::kBlocksPerCu) void k_gemv_mfma(MA
         acc[t] = total[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t rot = 8u * (uint32_t)(q & 1);
 
-    auto compute = [&](int ch, int bi, const u32x4 *cw) {
+    auto compute = [&](int ch, int bi, const u32x4 *cw, const uint32_t (&ms)[4]) {
         const uint8_t *buf = smem + bi * kBufBytes;
-        const uint8_t *mb = buf + kXBytes + kCBytes + wave * kMWave;
 #pragma unroll
         for (int gl = 0; gl < kChunk; gl++) {
             if (ch < c1 && ch * kChunk + gl < a.G) { // uniform
-                const u32x2 e = *reinterpret_cast<const u32x2 *>(mb + gl * 128 + n * 8);
-                const int c = (int)(e.x & 3u);
+                const uint32_t e = ms[gl];
+                const int c = (int)(e & 3u);
                 // the tiles' activations and offset constants first, so that
                 // their LDS latency overlaps the unpack
                 u32x4 x0[T], x1[T];
@@ -324,7 +337,7 @@ __global__ __launch_bounds__(kThreads, Geo<T>::kBlocksPerCu) void k_gemv_mfma(MA
                 case 2: unpack_quarter<2>(cw[gl], rot, h); break;
                 default: unpack_quarter<3>(cw[gl], rot, h); break;
                 }
-                const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)e.y);
+                const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
                 const hf8 B0 = as_hf8(h[0], h[1], h[2], h[3]), B1 = as_hf8(h[4], h[5], h[6], h[7]);
 #pragma unroll
                 for (int t = 0; t < T; t++) {
@@ -355,22 +368,23 @@ __global__ __launch_bounds__(kThreads, Geo<T>::kBlocksPerCu) void k_gemv_mfma(MA
     // waits stay exact counts.
     ChunkIn<T> in;
     u32x4 cw0[kChunk], cw1[kChunk];
+    uint32_t offs[4], ms0[4], ms1[4];
     load_in(c0, in);
     __syncthreads(); // the constant table
-    stage(c0, 0, in);
-    load_codes(0, cw0);
+    stage(c0, 0, in, offs, ms0);
+    load_codes(offs, cw0);
     load_in(c0 + 1, in);
     __syncthreads();
     for (int ch = c0; ch < c1; ch += 2) {
-        stage(ch + 1, 1, in);
-        load_codes(1, cw1);
+        stage(ch + 1, 1, in, offs, ms1);
+        load_codes(offs, cw1);
         load_in(ch + 2, in);
-        compute(ch, 0, cw0);
+        compute(ch, 0, cw0, ms0);
         __syncthreads();
-        stage(ch + 2, 0, in);
-        load_codes(0, cw0);
+        stage(ch + 2, 0, in, offs, ms0);
+        load_codes(offs, cw0);
         load_in(ch + 3, in);
-        compute(ch + 1, 1, cw1);
+        compute(ch + 1, 1, cw1, ms1);
         __syncthreads();
     }
 
