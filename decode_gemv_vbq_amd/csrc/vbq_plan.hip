@@ -34,6 +34,7 @@
 // records are ready; every partial is written), then the rows are summed in
 // a fixed order, so the result does not depend on timing.
 #include <algorithm>
+#include <type_traits>
 
 #include "vbq_common.h"
 #include "vbq_host.h"
@@ -371,12 +372,27 @@ __device__ __forceinline__ float dpp_f(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
 }
 
+// v of the lane 16 (x16) or 32 (x32) lanes away, by the gfx950 lane swaps
+// (VALU, no LDS round trip as a lane shuffle would take): v_permlane16_swap
+// of v with itself gives the 16-lane rows (0, 0, 2, 2) and (1, 1, 3, 3),
+// v_permlane32_swap gives (0, 1, 0, 1) and (2, 3, 2, 3).
+__device__ __forceinline__ float lanes_x16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lanes_x32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // Sum of v over each aligned group of L lanes (L = 8, 16, 32, 64), the same
 // value in every lane of the group, in a fixed order: pairs and quads (DPP
 // quad permutations), then the two quads of each 8 lanes (row_half_mirror:
 // once every lane of a quad holds the quad's sum, the mirrored lane holds the
 // other quad's), then the two halves of each 16-lane row (row_mirror), then
-// across rows.  Lane moves inside a row cost no LDS traffic.
+// across rows (lanes_x16, lanes_x32).  No lane move goes through LDS.
 template <int L>
 __device__ __forceinline__ float group_sum(float v)
 {
@@ -386,9 +402,9 @@ __device__ __forceinline__ float group_sum(float v)
     if (L >= 16)
         v += dpp_f<0x140>(v); // row_mirror
     if (L >= 32)
-        v += __shfl_xor(v, 16, 64);
+        v += lanes_x16(v);
     if (L >= 64)
-        v += __shfl_xor(v, 32, 64);
+        v += lanes_x32(v);
     return v;
 }
 
@@ -579,6 +595,13 @@ constexpr int kRows = 0;
 constexpr int kArgmax = 1;
 constexpr int kSwiglu = 2;
 
+// Outputs are stored through global (address space 1) pointers: a store
+// through a generic pointer is a flat store, which also counts on the counter
+// the LDS reads of the row sums wait on, so that every wait for them would
+// also wait for the previous row's store.
+typedef __attribute__((address_space(1))) uint16_t gu16_t;
+typedef __attribute__((address_space(1))) float gf32_t;
+
 struct YOut {
     void *y;
     int ldy, n0, yt, smax;
@@ -596,61 +619,124 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t row)
     return ((unsigned long long)ord << 32) | (unsigned long long)(~row);
 }
 
-// Row-sum item t: rows (64 / L) t .. of the block, L lanes per row.  The
-// partials of row j sit at column * stride + j; lane q sums columns q, q + L,
-// ... (four interleaved chains) and the L lanes combine in a fixed order
-// (group_sum).
-template <int MT, int OM, int L>
-__device__ __forceinline__ void rowsum_item_l(int t, int R, int stride, int G, int ps, const float *psum, float *ybuf,
-                                              const YOut &yo)
+// Sum of the C partials of one row that one lane adds (pg: the first, step:
+// the distance to the next), all loaded at once, in the order of the general
+// loop below: four chains over whole rounds of four columns, the remaining
+// columns into the first chain, then (chain 0 + chain 1) + (chain 2 + chain 3).
+template <int C>
+__device__ __forceinline__ float cols_sum(const float *pg, int step)
 {
-    const int lane = threadIdx.x & 63;
-    constexpr int per = 64 / L;
-    const int j = per * t + lane / L, q = lane & (L - 1);
+    float x[C];
 #pragma unroll
-    for (int m = 0; m < MT; m++) {
-        float v = 0.f;
-        if (j < R) {
-            const float *p = psum + m * ps + j;
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-            int g = q;
-            const int step = L * stride; // column g + L of the row sits L * stride further
-            const float *pg = p + g * stride;
-            for (; g + 3 * L < G; g += 4 * L, pg += 4 * step) {
-                a0 += pg[0];
-                a1 += pg[step];
-                a2 += pg[2 * step];
-                a3 += pg[3 * step];
+    for (int k = 0; k < C; k++)
+        x[k] = pg[k * step];
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < C / 4 * 4; k++)
+        a[k & 3] += x[k];
+#pragma unroll
+    for (int k = C / 4 * 4; k < C; k++)
+        a[0] += x[k];
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// Row sums of the block, L lanes per row.  Item t (t = wave, wave + kW, ...)
+// covers rows (64 / L) t .. of the block.  The partials of row j sit at
+// column * stride + j; lane q adds its columns q, q + L, ... in four chains
+// (cols_sum: whole rounds of four first, the rest into the first chain) and
+// the L lanes of the row combine in a fixed order (group_sum).  C > 0: every
+// lane has C columns (G = C * L), a straight run of loads and adds; C = 0: any
+// G, the same additions as loops.  Both give the same bits for a row.
+template <int MT, int OM, int L, int C>
+__device__ __forceinline__ void row_sums_lc(int wave, int R, int stride, int G, int ps, const float *psum,
+                                            float *ybuf, const YOut &yo)
+{
+    constexpr int per = 64 / L;
+    const int lane = threadIdx.x & 63;
+    const int q = lane & (L - 1);
+    const int nsum = (R * L + 63) / 64;
+    const int step = L * stride; // column g + L of the row sits L * stride further
+    for (int t = wave; t < nsum; t += kW) {
+        const int j = per * t + lane / L;
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            float v = 0.f;
+            if constexpr (C > 0) {
+                // a lane past the last row sums row R - 1 again (not stored)
+                v = cols_sum<C>(psum + m * ps + min(j, R - 1) + q * stride, step);
+            } else if (j < R) {
+                const float *pg = psum + m * ps + j + q * stride;
+                float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+                int g = q;
+                for (; g + 3 * L < G; g += 4 * L, pg += 4 * step) {
+                    a0 += pg[0];
+                    a1 += pg[step];
+                    a2 += pg[2 * step];
+                    a3 += pg[3 * step];
+                }
+                for (; g < G; g += L, pg += step)
+                    a0 += pg[0];
+                v = (a0 + a1) + (a2 + a3);
             }
-            for (; g < G; g += L, pg += step)
-                a0 += pg[0];
-            v = (a0 + a1) + (a2 + a3);
-        }
-        v = group_sum<L>(v);
-        if (q == 0 && j < R) {
-            const uint64_t o = (uint64_t)m * yo.ldy + yo.n0 + j;
-            if constexpr (OM == kArgmax)
-                atomicMax(yo.best + m, argmax_key(v, (uint32_t)(yo.n0 + j)));
-            else if constexpr (OM == kSwiglu)
-                ybuf[m * yo.smax + j] = v;
-            else if (yo.yt == VBQ_F16)
-                reinterpret_cast<__half *>(yo.y)[o] = __float2half_rn(v);
-            else
-                reinterpret_cast<float *>(yo.y)[o] = v;
+            v = group_sum<L>(v);
+            if (q == 0 && j < R) {
+                const uint64_t o = (uint64_t)m * yo.ldy + yo.n0 + j;
+                if constexpr (OM == kArgmax)
+                    atomicMax(yo.best + m, argmax_key(v, (uint32_t)(yo.n0 + j)));
+                else if constexpr (OM == kSwiglu)
+                    ybuf[m * yo.smax + j] = v;
+                else if (yo.yt == VBQ_F16)
+                    ((gu16_t *)yo.y)[o] = __half_as_ushort(__float2half_rn(v));
+                else
+                    ((gf32_t *)yo.y)[o] = v;
+            }
         }
     }
 }
 
-template <int MT, int OM>
-__device__ __forceinline__ void rowsum_item(int t, int R, int stride, int G, int ps, const float *psum, float *ybuf,
-                                            const YOut &yo)
+// Row shape of a launch as one number, L * 16 + C: L lanes per row (by G) and
+// C columns per lane when every lane has the same number and it is 4, 7 or 8
+// (G = 4L, 7L or 8L: every decode shape of the 1B and 9B steps), else C = 0.
+// (Four columns per lane only occur at L = 8: from G = 65 on, L >= 16 and
+// G / L > 4.)
+__host__ __device__ constexpr int row_shape_of(int G)
 {
-    switch (sum_lanes(G)) {
-    case 8: rowsum_item_l<MT, OM, 8>(t, R, stride, G, ps, psum, ybuf, yo); break;
-    case 16: rowsum_item_l<MT, OM, 16>(t, R, stride, G, ps, psum, ybuf, yo); break;
-    case 32: rowsum_item_l<MT, OM, 32>(t, R, stride, G, ps, psum, ybuf, yo); break;
-    default: rowsum_item_l<MT, OM, 64>(t, R, stride, G, ps, psum, ybuf, yo); break;
+    const int L = sum_lanes_of(G), c = G / L;
+    return L * 16 + ((c * L == G && (c == 4 || c == 7 || c == 8)) ? c : 0);
+}
+
+// The row-sum code of a launch.  A launch ends shortly after it, and every
+// wavefront of the last workgroups runs it at once, so what it executes there
+// (scalar work included) is on the launch's critical path.  RS > 0: the row
+// shape is a template argument (the launches with preloaded arguments; the
+// host picks the kernel); RS = 0: chosen by G at run time.  Measured on a 9B
+// decode step: the straight run for G = 8L chosen by the host against one
+// general loop chosen per item, -3.5%.
+template <int MT, int OM, int RS>
+__device__ __forceinline__ void row_sums(int wave, int R, int stride, int G, int ps, const float *psum, float *ybuf,
+                                         const YOut &yo)
+{
+#define VBQ_ROWS(S_) row_sums_lc<MT, OM, (S_) / 16, (S_) % 16>(wave, R, stride, G, ps, psum, ybuf, yo)
+    if constexpr (RS > 0) {
+        VBQ_ROWS(RS);
+    } else {
+        switch (row_shape_of(G)) {
+        case 8 * 16 + 8: VBQ_ROWS(8 * 16 + 8); break;
+        case 8 * 16 + 7: VBQ_ROWS(8 * 16 + 7); break;
+        case 8 * 16 + 4: VBQ_ROWS(8 * 16 + 4); break;
+        case 8 * 16: VBQ_ROWS(8 * 16); break;
+        case 16 * 16 + 8: VBQ_ROWS(16 * 16 + 8); break;
+        case 16 * 16 + 7: VBQ_ROWS(16 * 16 + 7); break;
+        case 16 * 16: VBQ_ROWS(16 * 16); break;
+        case 32 * 16 + 8: VBQ_ROWS(32 * 16 + 8); break;
+        case 32 * 16 + 7: VBQ_ROWS(32 * 16 + 7); break;
+        case 32 * 16: VBQ_ROWS(32 * 16); break;
+        case 64 * 16 + 8: VBQ_ROWS(64 * 16 + 8); break;
+        case 64 * 16 + 7: VBQ_ROWS(64 * 16 + 7); break;
+        default: VBQ_ROWS(64 * 16); break;
+        }
     }
+#undef VBQ_ROWS
 }
 
 // Merge this workgroup's keys into the call's (agent-scope atomics on the
@@ -684,7 +770,7 @@ __device__ void argmax_finish(unsigned long long *key, uint32_t *count, int32_t 
 
 constexpr int kDepth = 3; // passes in flight per wavefront besides the one computed
 
-template <int MT, int OM, int KP>
+template <int MT, int OM, int KP, int RS>
 __device__ __forceinline__ void plan_body(const u32x16 a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -787,9 +873,7 @@ __device__ __forceinline__ void plan_body(const u32x16 a)
     }
     __syncthreads(); // every partial of the block is in psum
 
-    const int nsum = (R * sum_lanes(G) + 63) / 64;
-    for (int t = wave; t < nsum; t += kW)
-        rowsum_item<MT, OM>(t, R, stride, G, ps, psum, ybuf, yo);
+    row_sums<MT, OM, RS>(wave, R, stride, G, ps, psum, ybuf, yo);
     if constexpr (OM == kArgmax) {
         __syncthreads(); // every row's key is in best[]
         if (tid == 0) {
@@ -809,9 +893,9 @@ __device__ __forceinline__ void plan_body(const u32x16 a)
             const float h = g / (1.0f + expf(-g)) * u; // silu(gate) * up
             const uint64_t o = (uint64_t)m * ldy + n0 / 2 + p;
             if (yt == VBQ_F16)
-                reinterpret_cast<__half *>(yptr)[o] = __float2half_rn(h);
+                ((gu16_t *)yptr)[o] = __half_as_ushort(__float2half_rn(h));
             else
-                reinterpret_cast<float *>(yptr)[o] = h;
+                ((gf32_t *)yptr)[o] = h;
         }
     }
 }
@@ -823,13 +907,13 @@ __global__ __launch_bounds__(kT) void k_gemv_plan(PArgs /* read through kernarg_
     const u32x16 a = kernarg_line((uint32_t)blockIdx.y * (uint32_t)sizeof(PRec));
     if ((int)blockIdx.x >= (int)a[14])
         return; // the launch spans the largest matrix; a smaller one has fewer blocks
-    plan_body<MT, OM, KP>(a);
+    plan_body<MT, OM, KP, 0>(a);
 }
 
 // One matrix, one token, plain rows or the SwiGLU epilogue: the record's fields
 // as scalar arguments, which the dispatch preloads into SGPRs, so no wavefront
-// waits for a load of its arguments.
-template <int OM, int KP>
+// waits for a load of its arguments.  RS: the row shape (row_shape_of(G)).
+template <int OM, int KP, int RS>
 __global__ __launch_bounds__(kT) void k_gemv_plan1(const uint8_t *plan, void *y, const uint16_t *x, uint32_t region,
                                                    int N, int rows, int passes, int per_wave, uint32_t g_yt, int smax)
 {
@@ -850,7 +934,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan1(const uint8_t *plan, void *y,
     a[13] = g_yt;
     a[14] = 0x7fffffffu;
     a[15] = (uint32_t)smax;
-    plan_body<1, OM, KP>(a);
+    plan_body<1, OM, KP, RS>(a);
 }
 
 // Two matrices of one shape that share x (a layer's gate and up projections),
@@ -858,7 +942,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan1(const uint8_t *plan, void *y,
 // (n_rows = N | rows << 20, passes = passes of matrix 0 | of matrix 1 << 16;
 // per-wave bytes, region and position stride follow from them); blockIdx.y
 // picks the matrix.
-template <int KP>
+template <int KP, int RS>
 __global__ __launch_bounds__(kT) void k_gemv_plan2(const uint8_t *plan0, const uint8_t *plan1, void *y0, void *y1,
                                                    const uint16_t *x, uint32_t n_rows, uint32_t passes01, uint32_t g_yt)
 {
@@ -884,7 +968,7 @@ __global__ __launch_bounds__(kT) void k_gemv_plan2(const uint8_t *plan0, const u
     a[13] = g_yt;
     a[14] = 0x7fffffffu; // both matrices have the launch's block count
     a[15] = (uint32_t)pos_stride(rows, (int)(g_yt & 0xffffu));
-    plan_body<1, kRows, KP>(a);
+    plan_body<1, kRows, KP, RS>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -930,16 +1014,44 @@ PrepArgs prep_args(const vbq_layout *L, const void *blob, const vbq_plan *P)
 
 vbq_status lds_attribute_once(const void *fn) { return dynamic_lds_once(fn, kLdsBudget); }
 
+// f(std::integral_constant<int, RS>) for the row shape rs of a one-token
+// launch whose activation staging takes KP items per thread (KP = 1: G <= 128,
+// L = 8 or 16; KP = 2: L = 32; KP = 4: L = 64); false if rs is not one of them.
+template <int KP, typename F>
+bool with_row_shape(int rs, F &&f, vbq_status &st)
+{
+#define VBQ_RS(S_)                                                                                                  \
+    case S_: st = f(std::integral_constant<int, S_>{}); return true;
+    if constexpr (KP == 1) {
+        switch (rs) {
+            VBQ_RS(8 * 16 + 8) VBQ_RS(8 * 16 + 7) VBQ_RS(8 * 16 + 4) VBQ_RS(8 * 16)
+            VBQ_RS(16 * 16 + 8) VBQ_RS(16 * 16 + 7) VBQ_RS(16 * 16)
+        }
+    } else if constexpr (KP == 2) {
+        switch (rs) { VBQ_RS(32 * 16 + 8) VBQ_RS(32 * 16 + 7) VBQ_RS(32 * 16) }
+    } else if constexpr (KP == 4) {
+        switch (rs) { VBQ_RS(64 * 16 + 8) VBQ_RS(64 * 16 + 7) VBQ_RS(64 * 16) }
+    }
+#undef VBQ_RS
+    return false;
+}
+
 template <int MT, int OM, int KP>
 vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
+    vbq_status st = VBQ_OK;
     if constexpr (MT == 1 && (OM == kRows || OM == kSwiglu)) {
         if (grid.y == 1) {
             const PRec &r = a.rec[0];
-            VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan1<OM, KP>));
-            hipLaunchKernelGGL((k_gemv_plan1<OM, KP>), dim3(grid), dim3(kT), lds, stream, r.plan, r.y, r.x, r.region,
-                               r.N, r.rows, r.passes, r.per_wave, r.g_yt, r.smax);
-            return launch_status();
+            auto go = [&](auto rsc) -> vbq_status {
+                constexpr int RS = decltype(rsc)::value;
+                VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan1<OM, KP, RS>));
+                hipLaunchKernelGGL((k_gemv_plan1<OM, KP, RS>), dim3(grid), dim3(kT), lds, stream, r.plan, r.y, r.x,
+                                   r.region, r.N, r.rows, r.passes, r.per_wave, r.g_yt, r.smax);
+                return launch_status();
+            };
+            if (with_row_shape<KP>(row_shape_of((int)(r.g_yt & 0xffffu)), go, st))
+                return st;
         }
     }
     if constexpr (MT == 1 && OM == kRows) {
@@ -949,11 +1061,16 @@ vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t st
             r0.wgs == (int)grid.x && r1.wgs == (int)grid.x && r0.N < (1 << 20) && r0.rows < (1 << 12) &&
             r0.passes < (1 << 16) && r1.passes < (1 << 16) && r0.smax == pos_stride(r0.rows, G) &&
             r0.smax == r1.smax) {
-            VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan2<KP>));
-            hipLaunchKernelGGL((k_gemv_plan2<KP>), dim3(grid), dim3(kT), lds, stream, r0.plan, r1.plan, r0.y, r1.y,
-                               r0.x, (uint32_t)r0.N | ((uint32_t)r0.rows << 20),
-                               (uint32_t)r0.passes | ((uint32_t)r1.passes << 16), r0.g_yt);
-            return launch_status();
+            auto go = [&](auto rsc) -> vbq_status {
+                constexpr int RS = decltype(rsc)::value;
+                VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan2<KP, RS>));
+                hipLaunchKernelGGL((k_gemv_plan2<KP, RS>), dim3(grid), dim3(kT), lds, stream, r0.plan, r1.plan, r0.y,
+                                   r1.y, r0.x, (uint32_t)r0.N | ((uint32_t)r0.rows << 20),
+                                   (uint32_t)r0.passes | ((uint32_t)r1.passes << 16), r0.g_yt);
+                return launch_status();
+            };
+            if (with_row_shape<KP>(row_shape_of(G), go, st))
+                return st;
         }
     }
     VBQ_TRY(lds_attribute_once((const void *)k_gemv_plan<MT, OM, KP>));
