@@ -340,6 +340,7 @@ struct XRegs {
 template <int MT, int KP>
 __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<KP> &xs)
 {
+    static_assert(MT <= 2, "the planned path takes one or two tokens");
     // x is 8-byte aligned and ldx a multiple of 4 (checked on the host): two
     // 8-byte buffer loads per item.  Every load is issued (so that the wait
     // for them is exact), and a compiler barrier keeps them ahead of the pass
@@ -351,9 +352,11 @@ __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<
 #pragma unroll
     for (int k = 0; k < KP; k++) {
         const int i = tid + k * kT;
+        // item i: token m, group g, quarter q (at most two tokens: a compare,
+        // not a division by G, which would delay the loads)
+        const int q = i & 7, m = (MT > 1 && (i >> 3) >= G) ? 1 : 0, g = (i >> 3) - m * G;
         // a lane past the last item gets an offset past the buffer: the load
         // returns zeros without a memory access
-        const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
         const int off = i < items ? (m * ldx + 64 * g + 4 * q) * 2 : nrec;
         const u32x2 va = __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0);
         const u32x2 vb = __builtin_amdgcn_raw_buffer_load_b64(xr, off + 64, 0, 0);
@@ -418,7 +421,9 @@ __device__ __forceinline__ void x_store(int G, const XRegs<KP> &xs, uint32_t *xr
         const int i = tid + k * kT;
         if (i >= items) // whole groups of 8 lanes drop out together
             break;
-        const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
+        // item i: token m, group g, quarter q (at most two tokens: a compare,
+        // not a division by G, which would delay the loads)
+        const int q = i & 7, m = (MT > 1 && (i >> 3) >= G) ? 1 : 0, g = (i >> 3) - m * G;
         U4 o;
         o.v[0] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x05040100u); // (x_p, x_{p+32})
         o.v[1] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x07060302u);
