@@ -368,49 +368,6 @@ __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<
     asm volatile("" ::: "memory");
 }
 
-// v from another lane of the same DPP row (ctrl: a DPP control code).
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
-}
-
-// v of the lane 16 (x16) or 32 (x32) lanes away, by the gfx950 lane swaps
-// (VALU, no LDS round trip as a lane shuffle would take): v_permlane16_swap
-// of v with itself gives the 16-lane rows (0, 0, 2, 2) and (1, 1, 3, 3),
-// v_permlane32_swap gives (0, 1, 0, 1) and (2, 3, 2, 3).
-__device__ __forceinline__ float lanes_x16(float v)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float lanes_x32(float v)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
-
-// Sum of v over each aligned group of L lanes (L = 8, 16, 32, 64), the same
-// value in every lane of the group, in a fixed order: pairs and quads (DPP
-// quad permutations), then the two quads of each 8 lanes (row_half_mirror:
-// once every lane of a quad holds the quad's sum, the mirrored lane holds the
-// other quad's), then the two halves of each 16-lane row (row_mirror), then
-// across rows (lanes_x16, lanes_x32).  No lane move goes through LDS.
-template <int L>
-__device__ __forceinline__ float group_sum(float v)
-{
-    v += dpp_f<0xB1>(v);  // quad_perm [1, 0, 3, 2]
-    v += dpp_f<0x4E>(v);  // quad_perm [2, 3, 0, 1]
-    v += dpp_f<0x141>(v); // row_half_mirror
-    if (L >= 16)
-        v += dpp_f<0x140>(v); // row_mirror
-    if (L >= 32)
-        v += lanes_x16(v);
-    if (L >= 64)
-        v += lanes_x32(v);
-    return v;
-}
-
 template <int MT, int KP>
 __device__ __forceinline__ void x_store(int G, const XRegs<KP> &xs, uint32_t *xrec)
 {

@@ -565,13 +565,11 @@ __device__ __forceinline__ void stage_x_store(const Ctx &c, const XStage<MT> &xs
             c2 = fmaf((float)(1 << (10 - pair_pos<2>(t & 7))), sp, c2);
             c4 = fmaf((float)(1 << (10 - pair_pos<4>(t & 3))), sp, c4);
         }
-#pragma unroll
-        for (int d = 1; d < 8; d <<= 1) { // fixed-order tree over the 8 quarters
-            X += __shfl_xor(X, d, 8);
-            c1 += __shfl_xor(c1, d, 8);
-            c2 += __shfl_xor(c2, d, 8);
-            c4 += __shfl_xor(c4, d, 8);
-        }
+        // fixed-order tree over the 8 quarters (DPP lane moves, no LDS)
+        X = group_sum<8>(X);
+        c1 = group_sum<8>(c1);
+        c2 = group_sum<8>(c2);
+        c4 = group_sum<8>(c4);
         if (q == 0)
             *reinterpret_cast<U4 *>(xr + 32) = U4{{__float_as_uint(fmaf(0.5f, X, c1)),
                                                     __float_as_uint(fmaf(1.5f, X, c2)),
@@ -775,9 +773,7 @@ __global__ __launch_bounds__(kT) void k_gemv_stream(SArgs args)
                     float v = 0.f;
                     for (int k = q; k < G; k += 8)
                         v += ps[k];
-                    v += __shfl_xor(v, 4, 8);
-                    v += __shfl_xor(v, 2, 8);
-                    v += __shfl_xor(v, 1, 8);
+                    v = group_sum<8>(v);
                     if (q == 0)
                         ybuf[m * a.rows + ra + j] = v;
                 }
