@@ -190,6 +190,11 @@ __global__ __launch_bounds__(kT) void k_prepare(PrepArgs a)
     uint8_t *region = a.plan + (uint64_t)blockIdx.x * a.region;
     const int stride = pos_stride(a.rows, a.G);
     const uint32_t dummy = (uint32_t)(stride * G) << 16; // scale 0 at the spare position
+    // Word area of a pass of width code c: group k's word at the 2^c u32 slots
+    // k 2^c .. (k + 1) 2^c - 1, so that the 8 bytes lane l loads (slots 2l,
+    // 2l + 1) hold the words of the groups lane l works on: groups 2l, 2l + 1
+    // of a one-bit pass, the one group of the lane otherwise (the 512 bytes
+    // are full for every width).
     // the empty places of each width's last pass: zero codes, the spare position
     for (int c = 0; c < 4; c++) {
         const int per = groups_per_pass(c);
@@ -201,7 +206,8 @@ __global__ __launch_bounds__(kT) void k_prepare(PrepArgs a)
             uint32_t *d32 = reinterpret_cast<uint32_t *>(rec + k * (8 << c));
             for (int d = 0; d < (2 << c); d++)
                 d32[d] = 0u;
-            reinterpret_cast<uint32_t *>(rec + kCodeArea)[k] = dummy;
+            for (int d = 0; d < (1 << c); d++)
+                reinterpret_cast<uint32_t *>(rec + kCodeArea)[(k << c) + d] = dummy;
         }
     }
     // the groups: thread g walks column g's rows, so each bucket's rows follow in order
@@ -231,7 +237,9 @@ __global__ __launch_bounds__(kT) void k_prepare(PrepArgs a)
             for (int d = 0; d < (2 << c); d++)
                 d32[d] = s32[d];
             const uint32_t e = (uint32_t)g * (uint32_t)stride + (uint32_t)r;
-            reinterpret_cast<uint32_t *>(rec + kCodeArea)[k] = (uint32_t)scales[(uint64_t)nn * G + g] | (e << 16);
+            const uint32_t word = (uint32_t)scales[(uint64_t)nn * G + g] | (e << 16);
+            for (int d = 0; d < (1 << c); d++)
+                reinterpret_cast<uint32_t *>(rec + kCodeArea)[(k << c) + d] = word;
         }
     }
     // width bytes, wave-major: pass w + 16 j at byte w * per_wave + j
@@ -472,22 +480,12 @@ __device__ __forceinline__ void pass_b1(const PBuf &b, const PCtx &cx)
     }
 }
 
-// The word of group (lane >> SH) of a pass: lane (lane >> (SH + 1)) loaded
-// words 2i and 2i+1 of the word area.
-template <int SH>
-__device__ __forceinline__ uint32_t word_of(const PBuf &b)
-{
-    const int lane = threadIdx.x & 63;
-    const int src = lane >> (SH + 1);
-    const uint32_t a = (uint32_t)__shfl((int)b.w[0], src, 64), c = (uint32_t)__shfl((int)b.w[1], src, 64);
-    return ((lane >> SH) & 1) ? c : a;
-}
-
-// Two-bit pass: group l (16 code bytes).
+// Two-bit pass: group l (16 code bytes; its word is the first of the lane's
+// two word-area slots, as for the four- and eight-bit passes).
 template <int MT>
 __device__ __forceinline__ void pass_b2(const PBuf &b, const PCtx &cx)
 {
-    const uint32_t se = word_of<0>(b), e = se >> 16;
+    const uint32_t se = b.w[0], e = se >> 16;
     const uint32_t w[4] = {b.c[0], b.c[1], b.c[2], b.c[3]};
     uint32_t hp[32];
     unpack_pairs<2>(w, hp);
@@ -505,7 +503,7 @@ template <int MT>
 __device__ __forceinline__ void pass_b4(const PBuf &b, const PCtx &cx)
 {
     const int lane = threadIdx.x & 63, h = lane & 1;
-    const uint32_t se = word_of<1>(b), e = se >> 16;
+    const uint32_t se = b.w[0], e = se >> 16;
     const uint32_t w[4] = {b.c[0], b.c[1], b.c[2], b.c[3]};
     uint32_t hp[16];
     unpack_words<4, 4>(w, hp);
@@ -527,7 +525,7 @@ template <int MT>
 __device__ __forceinline__ void pass_b8(const PBuf &b, const PCtx &cx)
 {
     const int lane = threadIdx.x & 63, q = lane & 3;
-    const uint32_t se = word_of<2>(b), e = se >> 16;
+    const uint32_t se = b.w[0], e = se >> 16;
     const uint32_t w[4] = {b.c[0], b.c[1], b.c[2], b.c[3]};
     uint32_t hp[8];
     unpack_words<8, 4>(w, hp);

@@ -262,8 +262,11 @@ vbq_status vbq_gemv_shared(const vbq_gemv_item *items /* host */, int n, int M, 
  * partly filled).  Pass p of a block is the 1536-byte record at p * 1536:
  *   bytes [0, 1024): group k's code record (8*b bytes, copied verbatim from
  *     the blob) at k * 8*b;
- *   bytes [1024, 1536): u32 per group k at 1024 + 4k: fp16 scale bits |
- *     e << 16, e = column * S + (row - first row of the block); the position
+ *   bytes [1024, 1536): the word of group k, fp16 scale bits | e << 16, in
+ *     the 2^c u32 slots k 2^c .. (k + 1) 2^c - 1 (c = log2(b): one slot for a
+ *     one-bit group, 2, 4 or 8 copies otherwise, so the 512 bytes are full and
+ *     the 8 bytes GEMV lane l loads hold the words of the groups it works on);
+ *     e = column * S + (row - first row of the block); the position
  *     stride S = max(rows, 2) below 32 rows, else the smallest S >= rows with
  *     S = 64 / L (mod 32), L = 8, 16, 32 or 64 for G <= 64, <= 128, <= 256 or
  *     more;
@@ -277,7 +280,7 @@ vbq_status vbq_gemv_shared(const vbq_gemv_item *items /* host */, int n, int M, 
  * 16 * per_wave rounded up to 256.  Bytes of a region past what its block
  * uses are never read for arithmetic.
  */
-#define VBQ_PLAN_MAGIC 0x32504256u
+#define VBQ_PLAN_MAGIC 0x33504256u
 
 typedef struct vbq_plan {
     uint32_t magic;        /* VBQ_PLAN_MAGIC */

@@ -162,7 +162,7 @@ def test_gemv_shared_argument_checks_fail_before_launch():
 def fake_plan(v, N=4, K=4096, M=1, passes=1):
     """A plan struct that passes the host checks (one row block of N rows)."""
     P = v.Plan()
-    P.magic = 0x32504256
+    P.magic = 0x33504256
     P.N, P.K, P.G, P.M = N, K, K // 64, M
     P.wgs, P.rows = 1, N
     P.passes = passes

@@ -207,7 +207,8 @@ def test_plan_passes_cover_every_group_once(N, K, wgs):
     sits in exactly one pass of its width, with the blob's code record (the
     independent numpy packer's bytes for its codes), its scale and its
     position; (column, row) ascend within a width; empty places hold zero
-    codes, scale 0 and the spare position."""
+    codes, scale 0 and the spare position; the word area holds each group's
+    word once per lane that works on the group (all 512 bytes used)."""
     v = vbq()
     q, bits, s, x = draw(N, K, seed=5)
     _, (blob, L, plan, P, _) = planned(v, q, bits, s, x, wgs=wgs)
@@ -236,7 +237,10 @@ def test_plan_passes_cover_every_group_once(N, K, wgs):
             c = int(width_byte[p]) - 1
             wbits, per = 1 << c, 128 >> c
             rec = buf[base + p * 1536:base + (p + 1) * 1536]
-            words = rec[1024:1024 + 4 * per].view(np.uint32)
+            # group k's word repeated in the 2^c slots k 2^c .. (k + 1) 2^c - 1
+            slots = rec[1024:1536].view(np.uint32).reshape(per, 1 << c)
+            assert np.all(slots == slots[:, :1])
+            words = slots[:, 0]
             for k in range(per):
                 e = int(words[k]) >> 16
                 code = rec[k * 8 * wbits:(k + 1) * 8 * wbits]
