@@ -4,7 +4,10 @@
 * vbq_gemv / vbq_gemv_batched: |y - y_ref| <= 1e-3 * sum|w||x| per output,
   at sizes spanning several row tiles, several K-slices and ragged tails.
 * Invariants: x = e_k gives column k of the dequantized matrix bit-exactly,
-  repeated runs are bit-identical, batched rows equal single-token runs.
+  repeated runs are bit-identical, a matrix in a shared launch gives the bits
+  it gives alone; a token of a batch of 3+ (matrix cores) and the same token
+  alone (streaming kernel) add in different orders and are each held to the
+  bound.
 """
 import numpy as np
 import pytest
