@@ -481,495 +481,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a)
     }
 }
 
-// ---------------------------------------------------------------------------
-// Wave-independent variant for M <= 2 (the decode case).  x is staged once per
-// workgroup for the whole K; after that single barrier every wavefront owns
-// whole row tiles and runs its own units with no further synchronisation, so
-// eight independent instruction streams per CU keep loads in flight.
-//
-// x record per (token, group): 32 fp16 pairs (x_p, x_{p+32}) + the 4 width
-// corrections, 144 bytes.  The odd number of 16-byte chunks per record staggers
-// the LDS bank groups of consecutive groups without any address swizzle, so
-// every LDS read of a slot uses one base address plus constant offsets.
-
-constexpr int kWThreads = 1024;
-constexpr int kWWaves = kWThreads / 64;
-constexpr int kXRec = 36;   // dwords per x record
-constexpr int kMaxRSW = 32; // row-slices per wave unit
-
-// passes per batch for width code c (16 code words per lane)
-__host__ __device__ constexpr int batch_passes(int c) { return c == 0 ? 8 : c == 1 ? 4 : c == 2 ? 2 : 1; }
-
-struct WUnit {
-    int tile, t0, ns;
-};
-
-struct WMeta {
-    uint32_t p0, p1, row_off, slice_off; // lane = row-slice of the unit
-};
-
-// Row-slice record of the current unit (64 bytes).  Built by the lane that
-// owns the row-slice, read back by the 32 lanes that own its groups.
-struct RS2 {
-    uint32_t p0, p1, base, rs;   // planes; record start from the unit's first code byte; row | slice << 8 | ng << 16
-    uint32_t m[4];               // groups of width code c
-    uint32_t bbpre[4];           // slot base of (width c, groups 0..15) | bucket start in 8-byte units << 16
-    uint32_t pre1[4];            // slot base of (width c, groups 16..31)
-};
-
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Inclusive prefix sum over the 64 lanes with DPP row shifts and row broadcasts.
-__device__ __forceinline__ int wave_scan_incl(int v)
-{
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31
-    return v;
-}
-
-__device__ __forceinline__ WUnit wunit_next(WUnit u, const GemvArgs &a, int tw)
-{
-    int t = u.t0 + u.ns;
-    if (t >= a.nS) {
-        u.tile += tw;
-        t = 0;
-    }
-    u.t0 = t;
-    u.ns = min(a.SG, a.nS - t);
-    return u;
-}
-
-// lane = row-slice l = r * ns + s
-__device__ __forceinline__ void wfetch_meta(const WUnit &u, const GemvArgs &a, WMeta &m)
-{
-    const int lane = threadIdx.x & 63;
-    m.p0 = m.p1 = m.row_off = m.slice_off = 0;
-    if (u.tile >= a.tiles || lane >= a.R * u.ns)
-        return;
-    const int r = u.ns == 1 ? lane : lane / u.ns;
-    const int s = lane - r * u.ns;
-    const int n = u.tile * a.R + r;
-    if (n >= a.N)
-        return;
-    const uint32_t *row_off = reinterpret_cast<const uint32_t *>(a.blob + a.off_row_off);
-    const uint32_t *slice_off = reinterpret_cast<const uint32_t *>(a.blob + a.off_slice_off);
-    const uint32_t *wmap = reinterpret_cast<const uint32_t *>(a.blob + a.off_wmap);
-    const uint32_t rs = (uint32_t)n * a.nS + u.t0 + s;
-    m.p0 = wmap[2 * (uint64_t)rs];
-    m.p1 = wmap[2 * (uint64_t)rs + 1];
-    m.row_off = row_off[n];
-    m.slice_off = slice_off[rs];
-}
-
-struct WState { // wave-uniform bookkeeping of the current unit
-    int total[4], tbase[4], n0, t0, ns;
-    const uint8_t *codes;   // first code byte of the unit
-    const uint16_t *scales; // scale of (row n0, group 32*t0)
-};
-
-// Passes of ONE width held in registers: entries, scales and code words.
-template <int B>
-struct BatchT {
-    static constexpr int C = B == 1 ? 0 : B == 2 ? 1 : B == 4 ? 2 : 3;
-    static constexpr int BP = batch_passes(C);
-    uint32_t hi[BP], sc[BP];
-    uint32_t w[2 * B * BP];
-};
-
-template <int B>
-__device__ __forceinline__ void issue_t(BatchT<B> &bt, int first, const WState &st, const GemvArgs &a,
-                                        const uint2 *table)
-{
-    constexpr int C = BatchT<B>::C, BP = BatchT<B>::BP;
-    const int lane = threadIdx.x & 63;
-    uint2 ent[BP];
-#pragma unroll
-    for (int j = 0; j < BP; j++) { // all table reads first, one LDS round trip
-        const int slot = (first + j) * 64 + lane;
-        ent[j] = slot < st.total[C] ? table[st.tbase[C] + slot] : make_uint2(0u, 0xffffffffu);
-    }
-#pragma unroll
-    for (int j = 0; j < BP; j++) {
-        uint32_t sc = 0;
-        if (ent[j].y != 0xffffffffu) {
-            const uint8_t *src = st.codes + ent[j].x;
-            if constexpr (B == 1) {
-                U2 v = *reinterpret_cast<const U2 *>(src);
-                bt.w[2 * j] = v.v[0];
-                bt.w[2 * j + 1] = v.v[1];
-            } else {
-#pragma unroll
-                for (int k = 0; k < B / 2; k++) {
-                    U4 v = *reinterpret_cast<const U4 *>(src + 16 * k);
-#pragma unroll
-                    for (int q = 0; q < 4; q++)
-                        bt.w[2 * B * j + 4 * k + q] = v.v[q];
-                }
-            }
-            const uint32_t r = ent[j].y >> 16, gl = ent[j].y & 0xffffu;
-            sc = st.scales[r * (uint32_t)a.G + gl];
-        }
-        bt.hi[j] = ent[j].y;
-        bt.sc[j] = sc;
-    }
-}
-
-template <int B, int MT>
-__device__ __forceinline__ void compute_t(const BatchT<B> &bt, int first, const WState &st, const GemvArgs &a,
-                                          const uint32_t *xrec, float *psum)
-{
-    constexpr int C = BatchT<B>::C, BP = BatchT<B>::BP;
-    const uint32_t CHG = (uint32_t)a.nS * 32;
-#pragma unroll
-    for (int j = 0; j < BP; j++) {
-        if (bt.hi[j] == 0xffffffffu)
-            continue;
-        uint32_t h[32];
-        unpack_pairs<B>(&bt.w[2 * B * j], h);
-        const uint32_t gl = bt.hi[j] & 0xffffu;
-        const float s = __half2float(__ushort_as_half((unsigned short)bt.sc[j]));
-#pragma unroll
-        for (int m = 0; m < MT; m++) {
-            if (m < a.M) {
-                const uint32_t *xr = xrec + (m * CHG + 32 * st.t0 + gl) * kXRec;
-                float acc0 = 0.f, acc1 = 0.f; // two chains for instruction-level parallelism
-#pragma unroll
-                for (int k = 0; k < 8; k += 2) {
-                    U4 xa = *reinterpret_cast<const U4 *>(xr + 4 * k);
-                    U4 xb = *reinterpret_cast<const U4 *>(xr + 4 * k + 4);
-                    acc0 = dot2(h[4 * k + 0], xa.v[0], acc0);
-                    acc1 = dot2(h[4 * k + 4], xb.v[0], acc1);
-                    acc0 = dot2(h[4 * k + 1], xa.v[1], acc0);
-                    acc1 = dot2(h[4 * k + 5], xb.v[1], acc1);
-                    acc0 = dot2(h[4 * k + 2], xa.v[2], acc0);
-                    acc1 = dot2(h[4 * k + 6], xb.v[2], acc1);
-                    acc0 = dot2(h[4 * k + 3], xa.v[3], acc0);
-                    acc1 = dot2(h[4 * k + 7], xb.v[3], acc1);
-                }
-                const float Cc = __uint_as_float(xr[32 + C]);
-                // partial of (row-slice, group) in natural group order: distinct
-                // addresses, no atomics, and row-slice sums read 32 contiguous floats
-                psum[m * a.slots + (bt.hi[j] >> 16) * (uint32_t)st.ns * 32u + gl] = s * ((acc0 + acc1) - Cc);
-            }
-        }
-    }
-}
-
-// All passes of width B, one register batch at a time.
-template <int B, int MT>
-__device__ __forceinline__ void run_width(const WState &st, const GemvArgs &a, const uint2 *table,
-                                          const uint32_t *xrec, float *psum)
-{
-    constexpr int C = BatchT<B>::C, BP = BatchT<B>::BP;
-    const int np = (st.total[C] + 63) / 64;
-    for (int f = 0; f < np; f += BP) {
-        BatchT<B> bt;
-        issue_t<B>(bt, f, st, a, table);
-        compute_t<B, MT>(bt, f, st, a, xrec, psum);
-    }
-}
-
-// x records for all of K: pairs, then C_b = sum_p magic_b(p)(x_p + x_{p+32}) + c_b sum x.
-template <int MT>
-__device__ void stage_xrec(const GemvArgs &a, uint32_t *xrec)
-{
-    const int tid = threadIdx.x;
-    const int CHG = a.nS * 32;
-    const bool vec = (a.ldx % 4) == 0 && ((uintptr_t)a.x % 8) == 0;
-    // 4 pairs per item: x[p..p+3] with x[p+32..p+35]
-    for (int i = tid; i < a.M * a.G * 8; i += kWThreads) {
-        int q = i & 7, g = (i >> 3) % a.G, m = (i >> 3) / a.G;
-        const uint16_t *xs = a.x + (uint64_t)m * a.ldx + 64ull * g + 4 * q;
-        uint32_t lo0, lo1, hi0, hi1;
-        if (vec) {
-            uint2 va = *reinterpret_cast<const uint2 *>(xs);
-            uint2 vb = *reinterpret_cast<const uint2 *>(xs + 32);
-            lo0 = va.x; lo1 = va.y; hi0 = vb.x; hi1 = vb.y;
-        } else {
-            lo0 = xs[0] | ((uint32_t)xs[1] << 16);
-            lo1 = xs[2] | ((uint32_t)xs[3] << 16);
-            hi0 = xs[32] | ((uint32_t)xs[33] << 16);
-            hi1 = xs[34] | ((uint32_t)xs[35] << 16);
-        }
-        U4 o;
-        o.v[0] = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u); // (x_p, x_{p+32})
-        o.v[1] = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
-        o.v[2] = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
-        o.v[3] = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
-        *reinterpret_cast<U4 *>(xrec + (m * CHG + g) * kXRec + 4 * q) = o;
-    }
-    __syncthreads();
-    for (int i = tid; i < a.M * a.G; i += kWThreads) {
-        int g = i % a.G, m = i / a.G;
-        uint32_t *xr = xrec + (m * CHG + g) * kXRec;
-        float X2[32];
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            U4 v = *reinterpret_cast<const U4 *>(xr + 4 * k);
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-                X2[4 * k + q] = dot2(v.v[q], 0x3c003c00u, 0.f);
-        }
-        float S16[16], S8[8], S4[4];
-#pragma unroll
-        for (int j = 0; j < 16; j++)
-            S16[j] = X2[j] + X2[j + 16];
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-            S8[j] = S16[j] + S16[j + 8];
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            S4[j] = S8[j] + S8[j + 4];
-        float C0 = 0.f, C1 = 0.f, C2 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; j++)
-            C0 = fmaf((float)(1 << (10 - pair_pos<1>(j))), S16[j], C0);
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-            C1 = fmaf((float)(1 << (10 - pair_pos<2>(j))), S8[j], C1);
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            C2 = fmaf((float)(1 << (10 - pair_pos<4>(j))), S4[j], C2);
-        float X = (S4[0] + S4[1]) + (S4[2] + S4[3]);
-        xr[32] = __float_as_uint(fmaf(0.5f, X, C0));
-        xr[33] = __float_as_uint(fmaf(1.5f, X, C1));
-        xr[34] = __float_as_uint(fmaf(7.5f, X, C2));
-        xr[35] = __float_as_uint(fmaf(127.5f, X, 1024.f * X));
-    }
-    __syncthreads();
-}
-
-template <int MT>
-__global__ __launch_bounds__(kWThreads) void k_gemv_wave(GemvArgs a)
-{
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const size_t xbytes = (size_t)MT * a.nS * 32 * kXRec * 4;
-    const size_t wbytes = (size_t)a.slots * 8 + (size_t)MT * a.slots * 4 + MT * kMaxRows * 4 + kMaxRSW * sizeof(RS2);
-    uint32_t *xrec = reinterpret_cast<uint32_t *>(smem);
-    uint8_t *wmem = smem + xbytes + wave * wbytes;
-    uint2 *table = reinterpret_cast<uint2 *>(wmem);
-    float *psum = reinterpret_cast<float *>(table + a.slots);
-    float *racc = psum + MT * a.slots;
-    RS2 *rsl = reinterpret_cast<RS2 *>(racc + MT * kMaxRows);
-    const uint8_t *codes = a.blob + a.off_codes;
-    const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.blob + a.off_scales);
-
-    stage_xrec<MT>(a, xrec);
-
-    const int tw = gridDim.x * kWWaves;
-    WUnit u;
-    u.tile = blockIdx.x * kWWaves + wave;
-    u.t0 = 0;
-    u.ns = min(a.SG, a.nS);
-    WMeta meta;
-    wfetch_meta(u, a, meta);
-    if (lane < MT * kMaxRows / 2) {
-        racc[lane] = 0.f;
-        racc[lane + MT * kMaxRows / 2] = 0.f;
-    }
-
-    while (u.tile < a.tiles) {
-        const WUnit nu = wunit_next(u, a, tw);
-        WState st;
-        st.n0 = u.tile * a.R;
-        st.t0 = u.t0;
-        st.ns = u.ns;
-        const int nrs = a.R * u.ns;
-        // ---- row-slice records and slot prefix sums (lane = row-slice)
-        {
-            const int r = u.ns == 1 ? lane : lane / u.ns;
-            const int s = lane - r * u.ns;
-            const bool live = lane < nrs && st.n0 + r < a.N;
-            const int ng = max(0, min(32, a.G - 32 * (u.t0 + s)));
-            WidthMasks wm = width_masks(meta.p0, meta.p1, ng);
-            // record starts relative to lane 0's (row n0, slice t0): they fit in 32 bits
-            const uint64_t ubase = 128ull * __builtin_amdgcn_readfirstlane(meta.row_off) +
-                                   __builtin_amdgcn_readfirstlane(meta.slice_off);
-            const uint64_t start = 128ull * meta.row_off + meta.slice_off;
-            // slots of width c are ordered (group half, row-slice, rank): a 16-lane
-            // LDS phase then reads x records of equal g (broadcast) or of distinct
-            // g inside one 16-group window (distinct bank groups): no conflicts
-            int cnt[4], c0[4], incl0[4], incl1[4], tot0[4];
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                cnt[c] = live ? __popc(wm.m[c]) : 0;
-                c0[c] = live ? __popc(wm.m[c] & 0xffffu) : 0;
-                incl0[c] = wave_scan_incl(c0[c]);
-                incl1[c] = wave_scan_incl(cnt[c] - c0[c]);
-            }
-            int tb = 0;
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                tot0[c] = __builtin_amdgcn_readlane(incl0[c], 63);
-                st.total[c] = tot0[c] + __builtin_amdgcn_readlane(incl1[c], 63);
-                st.tbase[c] = tb;
-                tb += st.total[c];
-            }
-            if (lane < nrs) {
-                RS2 rr;
-                rr.p0 = live ? meta.p0 : 0u;
-                rr.p1 = live ? meta.p1 : 0u;
-                rr.base = (uint32_t)(start - ubase);
-                rr.rs = (uint32_t)r | ((uint32_t)s << 8) | (live ? 0u : 0x80000000u);
-#pragma unroll
-                for (int c = 0; c < 4; c++)
-                    rr.m[c] = live ? wm.m[c] : 0u;
-                int bb = 0;
-#pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    rr.bbpre[c] = (uint32_t)(st.tbase[c] + incl0[c] - c0[c]) | ((uint32_t)bb << 16);
-                    rr.pre1[c] = (uint32_t)(st.tbase[c] + tot0[c] + incl1[c] - (cnt[c] - c0[c]));
-                    bb += cnt[c] << c;
-                }
-                rsl[lane] = rr;
-            }
-            st.codes = codes + ubase;
-            st.scales = scales + (uint64_t)st.n0 * a.G + 32 * u.t0;
-        }
-        wave_lds_sync();
-        // ---- slot table: item i -> row-slice i/32 (shared by a half-wave: broadcast
-        // LDS reads), group i%32; all reads of an item are independent of its width
-        {
-            const int gi = lane & 31;
-            const uint32_t lt = (1u << gi) - 1u;
-            for (int k = 0; k < nrs; k += 2) {
-                const int l = k + (lane >> 5);
-                if (l >= nrs)
-                    continue;
-                const RS2 rr = rsl[l];
-                const bool ok = !(rr.rs & 0x80000000u) && ((rr.m[0] | rr.m[1] | rr.m[2] | rr.m[3]) >> gi & 1u);
-                if (!ok)
-                    continue;
-                const int c = (int)((rr.p0 >> gi) & 1u) | (int)(((rr.p1 >> gi) & 1u) << 1);
-                const uint32_t mask = pick4(rr.m, c);
-                const uint32_t bp = pick4(rr.bbpre, c);
-                const uint32_t p1 = pick4(rr.pre1, c);
-                const uint32_t rank = __popc(mask & lt);
-                const uint32_t slot = gi < 16 ? (bp & 0xffffu) + rank : p1 + __popc(mask & lt & 0xffff0000u);
-                const uint32_t lo = rr.base + 8u * ((bp >> 16) + (rank << c));
-                const uint32_t hi = (32u * ((rr.rs >> 8) & 0xffu) + (uint32_t)gi) | ((rr.rs & 0xffu) << 16);
-                table[slot] = make_uint2(lo, hi);
-            }
-        }
-        wave_lds_sync();
-        // ---- next unit's metadata in flight during this unit
-        wfetch_meta(nu, a, meta);
-        // ---- widths one after the other, one register batch at a time
-        run_width<1, MT>(st, a, table, xrec, psum);
-        run_width<2, MT>(st, a, table, xrec, psum);
-        run_width<4, MT>(st, a, table, xrec, psum);
-        run_width<8, MT>(st, a, table, xrec, psum);
-        wave_lds_sync();
-        // ---- per row-slice: its groups' partials in natural order; then per
-        // row over its row-slices
-        if (lane < nrs) {
-            const int sl = lane - (u.ns == 1 ? lane : lane / u.ns) * u.ns;
-            const int ng = max(0, min(32, a.G - 32 * (u.t0 + sl)));
-#pragma unroll
-            for (int m = 0; m < MT; m++) {
-                if (m >= a.M)
-                    continue;
-                const float4 *ps = reinterpret_cast<const float4 *>(psum + m * a.slots + lane * 32);
-                float v = 0.f;
-#pragma unroll
-                for (int k = 0; k < 8; k++) {
-                    const float4 q = ps[k];
-                    v += 4 * k + 0 < ng ? q.x : 0.f;
-                    v += 4 * k + 1 < ng ? q.y : 0.f;
-                    v += 4 * k + 2 < ng ? q.z : 0.f;
-                    v += 4 * k + 3 < ng ? q.w : 0.f;
-                }
-                reinterpret_cast<float *>(table)[m * kMaxRSW + lane] = v; // table is free now
-            }
-        }
-        wave_lds_sync();
-        if (lane < a.R) {
-            const float *rsum = reinterpret_cast<const float *>(table);
-#pragma unroll
-            for (int m = 0; m < MT; m++) {
-                if (m >= a.M)
-                    continue;
-                float v = racc[m * kMaxRows + lane];
-                for (int sl = 0; sl < u.ns; sl++)
-                    v += rsum[m * kMaxRSW + lane * u.ns + sl];
-                racc[m * kMaxRows + lane] = v;
-            }
-        }
-        // ---- a finished tile: row sums to y, accumulators back to zero
-        if (u.t0 + u.ns >= a.nS) {
-            wave_lds_sync();
-            const int n = st.n0 + lane;
-            if (lane < a.R) {
-#pragma unroll
-                for (int m = 0; m < MT; m++) {
-                    if (m >= a.M)
-                        continue;
-                    const float t = racc[m * kMaxRows + lane];
-                    racc[m * kMaxRows + lane] = 0.f;
-                    if (n < a.N) {
-                        if (a.yt == VBQ_F16)
-                            reinterpret_cast<__half *>(a.y)[(uint64_t)m * a.ldy + n] = __float2half_rn(t);
-                        else
-                            reinterpret_cast<float *>(a.y)[(uint64_t)m * a.ldy + n] = t;
-                    }
-                }
-            }
-        }
-        wave_lds_sync();
-        u = nu;
-    }
-}
-
-struct WavePlan {
-    bool ok;
-    int R, SG, slots, tiles;
-    size_t smem;
-};
-
-size_t wave_bytes(int MT, int slots)
-{
-    return (size_t)slots * 8 + (size_t)MT * slots * 4 + (size_t)MT * kMaxRows * 4 + kMaxRSW * sizeof(RS2);
-}
-
-WavePlan make_wave_plan(const vbq_layout *L, int MT, int cus)
-{
-    WavePlan p;
-    p.ok = false;
-    if (MT > 2)
-        return p;
-    const int G = (int)L->G, nS = (int)L->nS, N = (int)L->N;
-    const size_t xbytes = (size_t)MT * nS * 32 * kXRec * 4;
-    const size_t cap = 160 * 1024;
-    for (int slots : {512, 256}) {
-        int R, SG;
-        if (G <= slots && nS <= kMaxRSW) {
-            SG = nS; // whole rows per unit
-            int rmax = std::min(std::min(kMaxRows, slots / G), kMaxRSW / nS);
-            int total_waves = cus * kWWaves;
-            R = std::max(1, std::min(rmax, (N + total_waves - 1) / total_waves));
-        } else {
-            SG = 1; // one slice at a time
-            R = std::min(kMaxRSW, slots / 32);
-        }
-        size_t smem = xbytes + (size_t)kWWaves * wave_bytes(MT, slots);
-        if (smem > cap)
-            continue;
-        p.ok = true;
-        p.R = R;
-        p.SG = SG;
-        p.slots = slots;
-        p.tiles = (N + R - 1) / R;
-        p.smem = smem;
-        return p;
-    }
-    return p;
-}
-
 int tokens_template(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
 struct Plan {
@@ -1018,24 +529,6 @@ vbq_status launch(GemvArgs a, const Plan &p, hipStream_t stream)
 }
 
 
-template <int MT>
-vbq_status launch_wave(GemvArgs a, const WavePlan &p, int cus, hipStream_t stream)
-{
-    VBQ_TRY(dynamic_lds_once((const void *)k_gemv_wave<MT>, 160 * 1024));
-    int per_cu = 0;
-    VBQ_TRY(hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv_wave<MT>,
-                                                                     kWThreads, p.smem)));
-    if (per_cu < 1)
-        return VBQ_ERR_SHAPE;
-    int grid = std::min(per_cu * cus, (p.tiles + kWWaves - 1) / kWWaves);
-    a.R = p.R;
-    a.SG = p.SG;
-    a.CHK = (int)a.nS;
-    a.tiles = p.tiles;
-    a.slots = p.slots;
-    hipLaunchKernelGGL(k_gemv_wave<MT>, dim3(grid), dim3(kWThreads), p.smem, stream, a);
-    return launch_status();
-}
 
 
 } // namespace
@@ -1084,9 +577,7 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
         if (mfma)
             return mfma_gemv(call, ws, ws_bytes);
     }
-    int MT = tokens_template(M);
-    const int cus = current_device_cus();
-    WavePlan wp = make_wave_plan(L, MT, cus);
+    const int MT = tokens_template(M);
     Plan p = make_plan(L, MT);
     GemvArgs a;
     a.blob = (const uint8_t *)blob;
@@ -1105,8 +596,6 @@ vbq_status vbq_gemv_batched(const vbq_layout *L, const void *blob, int M, const 
     a.y = y;
     a.ldy = ldy;
     a.yt = (int)yt;
-    if (wp.ok)
-        return MT == 1 ? launch_wave<1>(a, wp, cus, stream) : launch_wave<2>(a, wp, cus, stream);
     switch (MT) {
     case 1: return launch<1>(a, p, stream);
     case 2: return launch<2>(a, p, stream);
