@@ -23,7 +23,7 @@
 //    out wave-major for the 16 wavefronts of the GEMV workgroup.
 //
 // The GEMV kernel: one 1024-thread workgroup per row block; wavefront w takes
-// passes w, w+16, w+32, ... and keeps the next three of them in flight from
+// passes w, w+16, w+32, ... and keeps the next two of them in flight from
 // HBM straight into registers while it computes one (16 bytes of codes and 8
 // bytes of words per lane, the same two loads for every width).  Lane l holds
 // groups 2l and 2l+1 of a one-bit pass, group l of a two-bit pass, half of
@@ -728,7 +728,11 @@ __device__ void argmax_finish(unsigned long long *key, uint32_t *count, int32_t 
     __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kDepth = 3; // passes in flight per wavefront besides the one computed
+// Passes in flight per wavefront besides the one computed.  Two is the
+// measured optimum on MI355X (same-box runs of the 9B and 1B decode steps):
+// three cost 3.5% and four 10% more per step, one 3% more; more requests in
+// flight per compute unit raise every load's latency more than they hide.
+constexpr int kDepth = 2;
 
 template <int MT, int OM, int KP, int RS>
 __device__ __forceinline__ void plan_body(const u32x16 a)
@@ -785,12 +789,13 @@ __device__ __forceinline__ void plan_body(const u32x16 a)
     };
     // in the order the loop issues them (codes, then words, pass by pass), so
     // that its waits are the same on the first trip as on every later one.
-    // Only the first two passes go out before the activations are staged:
-    // with every wavefront of the device holding four passes in flight, the
-    // activation loads queue behind tens of megabytes of pass loads and the
-    // first barrier comes late (measured: two ahead is 7% faster on a 9B
-    // step, 10% on a 1B step, than four ahead, and also faster than none)
-    PBuf b0, b1, b2, b3;
+    // The first two passes go out before the activations are staged, the
+    // third after the barrier: with more pass loads of every wavefront of the
+    // device in flight, the activation loads queue behind them and the first
+    // barrier comes late (measured: two ahead is 7% faster on a 9B step, 10%
+    // on a 1B step, than four ahead, and also faster than none; one ahead
+    // and two after is the same as two and one)
+    PBuf b0, b1, b2;
     issue(b0, 0);
     asm volatile("" ::: "memory");
     issue(b1, 1);
@@ -800,8 +805,6 @@ __device__ __forceinline__ void plan_body(const u32x16 a)
         best[tid] = 0ull;
     __syncthreads();
     issue(b2, 2);
-    asm volatile("" ::: "memory");
-    issue(b3, 3);
 
     const PCtx cx{xrec, psum, G, ps, 0xffffffffu / (uint32_t)stride + 1u};
     // passes of this wavefront: its width bytes are nonzero up to the first 0
@@ -825,11 +828,10 @@ __device__ __forceinline__ void plan_body(const u32x16 a)
         }
         issue(b, i + kDepth + 1);
     };
-    for (int i = 0; i < npw; i += 4) {
+    for (int i = 0; i < npw; i += 3) {
         step(b0, i);
         step(b1, i + 1);
         step(b2, i + 2);
-        step(b3, i + 3);
     }
     __syncthreads(); // every partial of the block is in psum
 
