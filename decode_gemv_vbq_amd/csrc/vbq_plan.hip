@@ -433,7 +433,7 @@ struct PCtx {
 };
 
 // Dot products of NP pairs of one group (its pairs p0 .. p0 + NP - 1) with
-// every token's x record of column `col`: two fp32 chains, the first starting
+// every token's x record of column `col`: one fp32 chain, starting
 // from the group's -C_b when this lane carries the correction.
 template <int C, int NP, int MT>
 __device__ __forceinline__ void dot_pairs(const uint32_t *hp, int p0, bool corr, uint32_t col, const PCtx &cx,
@@ -443,23 +443,25 @@ __device__ __forceinline__ void dot_pairs(const uint32_t *hp, int p0, bool corr,
     for (int m = 0; m < MT; m++) {
         const uint32_t *xr = cx.xrec + ((uint32_t)m * cx.G + col) * kXRec;
         const float c0 = __uint_as_float(xr[32 + C]);
-        float a0 = corr ? c0 : 0.f, a1 = 0.f;
+        float a = corr ? c0 : 0.f;
 #pragma unroll
         for (int k = 0; k < NP / 4; k++) {
             const U4 xa = *reinterpret_cast<const U4 *>(xr + p0 + 4 * k);
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
-                if (k < NP / 8)
-                    a0 = dot2(hp[4 * k + t], xa.v[t], a0);
-                else
-                    a1 = dot2(hp[4 * k + t], xa.v[t], a1);
-            }
+            for (int t = 0; t < 4; t++)
+                a = dot2(hp[4 * k + t], xa.v[t], a);
         }
-        acc[m] = a0 + a1;
+        acc[m] = a;
     }
 }
 
 __device__ __forceinline__ float scale_of(uint32_t se) { return __half2float(__ushort_as_half((uint16_t)(se & 0xffffu))); }
+
+// s * v for the fp16 scale s in the low half of se.  (A hand-written
+// mixed-precision fma saves the conversion, but the compiler does not insert
+// the wait states a VALU read of a v_dot2c result needs when the reader is
+// inline asm, so it read a stale sum on gfx950.)
+__device__ __forceinline__ float scaled(uint32_t se, float v) { return scale_of(se) * v; }
 
 // One-bit pass: this lane's groups 2l and 2l+1 (8 code bytes and one word each).
 template <int MT>
@@ -473,10 +475,9 @@ __device__ __forceinline__ void pass_b1(const PBuf &b, const PCtx &cx)
         const uint32_t se = b.w[h], e = se >> 16;
         float acc[MT];
         dot_pairs<0, 32, MT>(hp, 0, true, __umulhi(e, cx.inv), cx, acc);
-        const float s = scale_of(se);
 #pragma unroll
         for (int m = 0; m < MT; m++)
-            cx.psum[m * cx.ps + e] = s * acc[m];
+            cx.psum[m * cx.ps + e] = scaled(se, acc[m]);
     }
 }
 
@@ -491,10 +492,9 @@ __device__ __forceinline__ void pass_b2(const PBuf &b, const PCtx &cx)
     unpack_pairs<2>(w, hp);
     float acc[MT];
     dot_pairs<1, 32, MT>(hp, 0, true, __umulhi(e, cx.inv), cx, acc);
-    const float s = scale_of(se);
 #pragma unroll
     for (int m = 0; m < MT; m++)
-        cx.psum[m * cx.ps + e] = s * acc[m];
+        cx.psum[m * cx.ps + e] = scaled(se, acc[m]);
 }
 
 // Four-bit pass: half h = l & 1 of group l >> 1 (its words 4h..4h+3, pairs
@@ -509,12 +509,11 @@ __device__ __forceinline__ void pass_b4(const PBuf &b, const PCtx &cx)
     unpack_words<4, 4>(w, hp);
     float acc[MT];
     dot_pairs<2, 16, MT>(hp, 16 * h, h == 0, __umulhi(e, cx.inv), cx, acc);
-    const float s = scale_of(se);
 #pragma unroll
     for (int m = 0; m < MT; m++) {
         const float v = acc[m] + dpp_f<0xB1>(acc[m]); // quad_perm [1, 0, 3, 2]
         if (h == 0)
-            cx.psum[m * cx.ps + e] = s * v;
+            cx.psum[m * cx.ps + e] = scaled(se, v);
     }
 }
 
@@ -531,13 +530,12 @@ __device__ __forceinline__ void pass_b8(const PBuf &b, const PCtx &cx)
     unpack_words<8, 4>(w, hp);
     float acc[MT];
     dot_pairs<3, 8, MT>(hp, 8 * q, q == 0, __umulhi(e, cx.inv), cx, acc);
-    const float s = scale_of(se);
 #pragma unroll
     for (int m = 0; m < MT; m++) {
         float v = acc[m] + dpp_f<0xB1>(acc[m]); // quad_perm [1, 0, 3, 2]
         v += dpp_f<0x4E>(v);                    // quad_perm [2, 3, 0, 1]
         if (q == 0)
-            cx.psum[m * cx.ps + e] = s * v;
+            cx.psum[m * cx.ps + e] = scaled(se, v);
     }
 }
 
