@@ -11,12 +11,14 @@
 // x 128 columns (two groups); in a tile the groups are bucketed by width so
 // that a wavefront dequantizes 64 groups of one width at a time.
 //
-// Kernel (256 threads, one workgroup per 128-row block x 32*MT tokens x one
-// K-split):
+// Kernel (512 threads, one workgroup per 128-row block x 32*MT tokens x one
+// K-split; the buffers fill the LDS, so one workgroup per compute unit and two
+// wavefronts per SIMD, which hide each other's LDS and matrix-core latencies):
 //   - a ring of 3 LDS slots receives the raw tiles by LDS-DMA, two tiles
-//     ahead of the one being dequantized;
+//     ahead of the one being dequantized (wavefronts 0..3 copy);
 //   - the tile of chunk k+1 is dequantized into the free half of a double
-//     buffer W[2][128 rows][128 k-slots] while the MFMAs consume chunk k;
+//     buffer W[2][128 rows][128 k-slots] while the MFMAs consume chunk k
+//     (every wavefront takes its share of both);
 //   - the tokens' activations of chunk k+1 are copied by LDS-DMA into
 //     X[2][32*MT][128 k-slots] from a copy of X in the same k-slot order
 //     that a first kernel writes into the workspace.
@@ -38,8 +40,10 @@ namespace {
 
 constexpr int kBN = 128;     // weight rows per tile
 constexpr int kTG = 2;       // groups per tile (128 columns)
-constexpr int kGT = 256;     // threads per workgroup
-constexpr int kGW = kGT / 64;
+constexpr int kGT = 256;     // threads per workgroup of the preparation kernels
+constexpr int kGW = kGT / 64; // wavefronts that copy by LDS-DMA in the GEMM kernel
+constexpr int kMT = 512;     // threads per workgroup of the GEMM kernel: two wavefronts per SIMD
+constexpr int kMW = kMT / 64;
 static_assert(kBN * kTG == kGT, "the preparation kernels take one cell of a tile per thread");
 constexpr int kGHdr = 16;    // tile header bytes
 constexpr int kRing = 3;     // tiles in the LDS ring
@@ -393,25 +397,52 @@ __device__ __forceinline__ void dequant_pass(const uint8_t *tile, int lp, uint32
         dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
 }
 
-// Every group of the tile in ring slot `tile` into the W chunk `wchunk`.
-__device__ __forceinline__ void dequant_tile(const uint8_t *tile, uint32_t *wchunk)
+// The width buckets of a tile in a ring slot, from its header: pass p of the
+// tile (64 groups of one width; the 8-bit passes first, then 4, 2, 1) is
+// dequantized by dequant_one.
+struct TileHdr {
+    uint32_t c8, c4, c2, c1, se_off, o4, o2, o1;
+    int b4, b2, b1, np; // first pass of the 4-, 2- and 1-bit buckets, pass count
+};
+
+__device__ __forceinline__ TileHdr tile_hdr(const uint8_t *tile)
 {
     const uint4 h = *reinterpret_cast<const uint4 *>(tile);
-    const uint32_t c8 = h.x & 0xffffu, c4 = h.x >> 16, c2 = h.y & 0xffffu, c1 = h.y >> 16, se_off = h.w;
-    const int n8 = (int)((c8 + 63) >> 6), n4 = (int)((c4 + 63) >> 6), n2 = (int)((c2 + 63) >> 6),
-              n1 = (int)((c1 + 63) >> 6);
-    const uint32_t o4 = kGHdr + 64u * c8, o2 = o4 + 32u * c4, o1 = o2 + 16u * c2;
-    const int b4 = n8, b2 = b4 + n4, b1 = b2 + n2, np = b1 + n1;
-    for (int p = threadIdx.x >> 6; p < np; p += kGW) {
-        if (p < b4)
-            dequant_pass<8>(tile, p, c8, kGHdr, 0u, se_off, wchunk);
-        else if (p < b2)
-            dequant_pass<4>(tile, p - b4, c4, o4, c8, se_off, wchunk);
-        else if (p < b1)
-            dequant_pass<2>(tile, p - b2, c2, o2, c8 + c4, se_off, wchunk);
-        else
-            dequant_pass<1>(tile, p - b1, c1, o1, c8 + c4 + c2, se_off, wchunk);
-    }
+    TileHdr t;
+    t.c8 = h.x & 0xffffu;
+    t.c4 = h.x >> 16;
+    t.c2 = h.y & 0xffffu;
+    t.c1 = h.y >> 16;
+    t.se_off = h.w;
+    t.o4 = kGHdr + 64u * t.c8;
+    t.o2 = t.o4 + 32u * t.c4;
+    t.o1 = t.o2 + 16u * t.c2;
+    t.b4 = (int)((t.c8 + 63) >> 6);
+    t.b2 = t.b4 + (int)((t.c4 + 63) >> 6);
+    t.b1 = t.b2 + (int)((t.c2 + 63) >> 6);
+    t.np = t.b1 + (int)((t.c1 + 63) >> 6);
+    return t;
+}
+
+__device__ __forceinline__ void dequant_one(const uint8_t *tile, const TileHdr &t, int p, uint32_t *wchunk)
+{
+    if (p < t.b4)
+        dequant_pass<8>(tile, p, t.c8, kGHdr, 0u, t.se_off, wchunk);
+    else if (p < t.b2)
+        dequant_pass<4>(tile, p - t.b4, t.c4, t.o4, t.c8, t.se_off, wchunk);
+    else if (p < t.b1)
+        dequant_pass<2>(tile, p - t.b2, t.c2, t.o2, t.c8 + t.c4, t.se_off, wchunk);
+    else
+        dequant_pass<1>(tile, p - t.b1, t.c1, t.o1, t.c8 + t.c4 + t.c2, t.se_off, wchunk);
+}
+
+// Every group of the tile in ring slot `tile` into the W chunk `wchunk`
+// (wavefront w of the GEMM workgroup takes passes w, w + 8, ...).
+__device__ __forceinline__ void dequant_tile(const uint8_t *tile, uint32_t *wchunk)
+{
+    const TileHdr t = tile_hdr(tile);
+    for (int p = threadIdx.x >> 6; p < t.np; p += kMW)
+        dequant_one(tile, t, p, wchunk);
 }
 
 // X in k-slot order: xp[m][64 g + 2 j + h] = x[m][64 g + j + 32 h] (j < 32),
@@ -475,15 +506,25 @@ __device__ __forceinline__ void dma_tile(const uint8_t *src, uint32_t dst, int F
 }
 
 template <int MT>
-__global__ __launch_bounds__(kGT) void k_gemm(GArgs a)
+__global__ __launch_bounds__(kMT) void k_gemm(GArgs a)
 {
     constexpr int BM = 32 * MT;
+    // Eight wavefronts, two per SIMD: wavefront w runs the MFMAs of rows
+    // 32 (w % 4) .. + 31 for token tiles t0 .. t0 + TW - 1 (the first half of
+    // the tiles for w < 4, the second half for w >= 4; with one tile, only
+    // w < 4), and every wavefront takes its share of the dequantization passes.
+    // The LDS-DMA copies (and their waits) stay with wavefronts 0..3.
+    constexpr int TW = MT > 1 ? MT / 2 : 1;
     extern __shared__ __align__(16) uint8_t smem[];
     uint32_t *wbuf = reinterpret_cast<uint32_t *>(smem);                          // [2][kBN][kLdw / 2] words
     uint32_t *xbuf = reinterpret_cast<uint32_t *>(smem + 2 * kWBytes);            // [2][BM][kLdw / 2] words
     uint8_t *ring = smem + 2 * kWBytes + 2 * BM * kLdw * 2;
     const uint32_t slot_bytes = 4096u * (uint32_t)a.F;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rsl = wave & 3;                    // row slice of this wavefront's MFMAs
+    const int t0 = MT > 1 ? (wave >> 2) * TW : 0; // its first token tile
+    const bool mf = MT > 1 || wave < 4;          // it runs MFMAs
+    const bool dma = wave < kGW;                 // it issues the LDS-DMA copies
     const int nbi = blockIdx.x, mbi = blockIdx.y, z = blockIdx.z;
     const int m0 = mbi * BM;
     const int kbeg = (int)((int64_t)z * a.kc / a.S), kend = (int)((int64_t)(z + 1) * a.kc / a.S);
@@ -505,17 +546,19 @@ __global__ __launch_bounds__(kGT) void k_gemm(GArgs a)
     constexpr uint32_t xchunk = BM * kLdw * 2; // bytes of one X chunk
 
     // ---- prologue: tiles 0..2 in flight with the activations of chunk 0
-    dma_x<MT>(a.xp, a.K, m0, kbeg, xbuf0);
-    for (int k = 0; k < kRing && k < nk; k++)
-        dma_tile(tile_src(k), ring0 + (uint32_t)k * slot_bytes, a.F);
-    wait_vm0();
+    if (dma) {
+        dma_x<MT>(a.xp, a.K, m0, kbeg, xbuf0);
+        for (int k = 0; k < kRing && k < nk; k++)
+            dma_tile(tile_src(k), ring0 + (uint32_t)k * slot_bytes, a.F);
+        wait_vm0();
+    }
     __syncthreads();
     dequant_tile(ring, wbuf);
     __syncthreads();
 
-    f32x16 acc[MT];
+    f32x16 acc[TW];
 #pragma unroll
-    for (int t = 0; t < MT; t++)
+    for (int t = 0; t < TW; t++)
 #pragma unroll
         for (int r = 0; r < 16; r++)
             acc[t][r] = 0.f;
@@ -523,32 +566,46 @@ __global__ __launch_bounds__(kGT) void k_gemm(GArgs a)
     for (int k = 0; k < nk; k++) {
         const int cur = k & 1;
         const bool more = k + 1 < nk, fetch = k + kRing < nk;
-        if (more) // into the X chunk of chunk k - 1, consumed before the last barrier
+        if (more && dma) // into the X chunk of chunk k - 1, consumed before the last barrier
             dma_x<MT>(a.xp, a.K, m0, kbeg + k + 1, xbuf0 + (uint32_t)(cur ^ 1) * xchunk);
-        if (fetch) // into the slot of tile k, dequantized before the last barrier
+        if (fetch && dma) // into the slot of tile k, dequantized before the last barrier
             dma_tile(tile_src(k + kRing), ring0 + (uint32_t)(k % kRing) * slot_bytes, a.F);
-        // ---- MFMAs of chunk k
+        // ---- MFMAs of chunk k, with this wavefront's dequantization passes of
+        // tile k + 1 between every second step, so that the matrix cores work
+        // through the issued MFMAs while the same wavefront runs the passes'
+        // vector instructions (the passes write the other W buffer)
         {
             const _Float16 *wb = reinterpret_cast<const _Float16 *>(wbuf + cur * (kWBytes / 4)) +
-                                 (32 * wave + (lane & 31)) * kLdw + 8 * (lane >> 5);
+                                 (32 * rsl + (lane & 31)) * kLdw + 8 * (lane >> 5);
             const _Float16 *xb = reinterpret_cast<const _Float16 *>(xbuf + cur * (BM * kLdw / 2)) +
-                                 (lane & 31) * kLdw + 8 * (lane >> 5);
-            const int steps = 4 * group_count(k);
+                                 (32 * t0 + (lane & 31)) * kLdw + 8 * (lane >> 5);
+            const int steps = mf ? 4 * group_count(k) : 0;
+            const uint8_t *ntile = ring + (uint32_t)((k + 1) % kRing) * slot_bytes;
+            uint32_t *nw = wbuf + (cur ^ 1) * (kWBytes / 4);
+            TileHdr th{};
+            if (more)
+                th = tile_hdr(ntile);
+            int p = more ? wave : th.np; // this wavefront's next pass of tile k + 1
 #pragma unroll
             for (int s = 0; s < 4 * kTG; s++) {
                 if (s < steps) {
                     const int ko = (s >> 2) * 64 + (s & 3) * 16;
                     const hf8 b = *reinterpret_cast<const hf8 *>(wb + ko);
 #pragma unroll
-                    for (int t = 0; t < MT; t++) {
+                    for (int t = 0; t < TW; t++) {
                         const hf8 xa = *reinterpret_cast<const hf8 *>(xb + t * 32 * kLdw + ko);
                         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, b, acc[t], 0, 0, 0);
                     }
                 }
+                if ((s & 1) && p < th.np) {
+                    dequant_one(ntile, th, p, nw);
+                    p += kMW;
+                }
             }
+            for (; p < th.np; p += kMW)
+                dequant_one(ntile, th, p, nw);
         }
-        if (more) {
-            dequant_tile(ring + (uint32_t)((k + 1) % kRing) * slot_bytes, wbuf + (cur ^ 1) * (kWBytes / 4));
+        if (more && dma) {
             // everything but this iteration's tile copies: the activations of
             // chunk k + 1 and the tile of chunk k + 2
             if (fetch)
@@ -559,15 +616,18 @@ __global__ __launch_bounds__(kGT) void k_gemm(GArgs a)
         __syncthreads();
     }
 
-    // ---- outputs: lane l, register r of token tile t holds row
-    // 32 t + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 wave + l % 32
-    const int nl = 32 * wave + (lane & 31), n = nbi * kBN + nl;
+    // ---- outputs: lane l, register r of this wavefront's token tile t0 + t
+    // holds token 32 (t0 + t) + 8 (r / 4) + 4 (l / 32) + r % 4 of the block and
+    // row 32 (w % 4) + l % 32
+    const int nl = 32 * rsl + (lane & 31), n = nbi * kBN + nl;
     if (a.S == 1) {
+        if (!mf)
+            return;
 #pragma unroll
-        for (int t = 0; t < MT; t++)
+        for (int t = 0; t < TW; t++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int m = m0 + 32 * t + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int m = m0 + 32 * (t0 + t) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (m < a.M && n < a.N) {
                     const uint64_t o = (uint64_t)m * a.ldy + n;
                     if (a.yt == VBQ_F16)
@@ -582,11 +642,13 @@ __global__ __launch_bounds__(kGT) void k_gemm(GArgs a)
     // arrive adds the S tiles in split order and writes the outputs
     const int mb = gridDim.y;
     float *mine = a.part + (((uint64_t)z * mb + mbi) * a.nb + nbi) * (uint64_t)(BM * kBN);
+    if (mf) {
 #pragma unroll
-    for (int t = 0; t < MT; t++)
+        for (int t = 0; t < TW; t++)
 #pragma unroll
-        for (int r = 0; r < 16; r++)
-            mine[(32 * t + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kBN + nl] = acc[t][r];
+            for (int r = 0; r < 16; r++)
+                mine[(32 * (t0 + t) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kBN + nl] = acc[t][r];
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     uint32_t *flag = xbuf; // the X chunks are no longer read
@@ -601,7 +663,7 @@ __global__ __launch_bounds__(kGT) void k_gemm(GArgs a)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const float *p0 = a.part + ((uint64_t)mbi * a.nb + nbi) * (uint64_t)(BM * kBN);
     const uint64_t zstride = (uint64_t)mb * a.nb * (uint64_t)(BM * kBN);
-    for (int i = tid; i < BM * kBN; i += kGT) {
+    for (int i = tid; i < BM * kBN; i += kMT) {
         const int mi = i / kBN, ni = i % kBN;
         const int m = m0 + mi, nn = nbi * kBN + ni;
         float v = p0[i];
@@ -705,7 +767,7 @@ template <int MT>
 vbq_status launch_gemm(const GArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
     VBQ_TRY(dynamic_lds_once((const void *)k_gemm<MT>, kGLds));
-    hipLaunchKernelGGL(k_gemm<MT>, grid, dim3(kGT), lds, stream, a);
+    hipLaunchKernelGGL(k_gemm<MT>, grid, dim3(kMT), lds, stream, a);
     return launch_status();
 }
 
