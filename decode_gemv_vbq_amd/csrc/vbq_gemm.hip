@@ -305,10 +305,23 @@ struct GArgs {
 };
 
 // Dequantize one 64-weight group of width B (code words cw, fp16 scale bits
-// sb) into 32 pair words: word j = fp16(s * (q_j - c)) | fp16(s * (q_{j+32} - c)) << 16,
+// sb) into 32 pair words, stored four at a time to dst[0..7] (so that few of
+// them are live at once): word j = fp16(s * (q_j - c)) | fp16(s * (q_{j+32} - c)) << 16,
 // c = (2^B - 1) / 2, each product rounded once to nearest even.
 template <int B>
-__device__ __forceinline__ void dequant_group(const uint32_t (&cw)[2 * B], uint32_t sb, uint32_t (&out)[32])
+__device__ __forceinline__ uint32_t code_pair(const uint32_t (&cw)[2 * B], int j)
+{
+    // 0x6400 | q is the fp16 value 1024 + q, for both halves
+    constexpr uint32_t mask = (1u << B) - 1u;
+    const int d = j / (16 / B), i = j % (16 / B);
+    if constexpr (B == 8)
+        return __builtin_amdgcn_perm(0x64646464u, cw[d], i ? 0x04030401u : 0x04020400u);
+    else
+        return ((cw[d] >> (B * i)) & (mask * 0x10001u)) | 0x64006400u;
+}
+
+template <int B>
+__device__ __forceinline__ void dequant_group(const uint32_t (&cw)[2 * B], uint32_t sb, uint4 *dst)
 {
     const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sb);
     if constexpr (B == 1) {
@@ -320,44 +333,47 @@ __device__ __forceinline__ void dequant_group(const uint32_t (&cw)[2 * B], uint3
         for (int d = 0; d < 2; d++) {
             const uint32_t nw = ~cw[d];
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                out[16 * d + i] = base ^ ((nw << (15 - i)) & 0x80008000u);
+            for (int c4 = 0; c4 < 4; c4++) {
+                uint32_t o[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    o[u] = base ^ ((nw << (15 - (4 * c4 + u))) & 0x80008000u);
+                dst[4 * d + c4] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
         }
     } else {
-        // 0x6400 | q is the fp16 value h = 1024 + q.  For a finite s,
-        // s * h - (1024 + c) * s is one fp32 fma whose terms and result are
-        // exact (at most 23 significant bits), so the only rounding is the
-        // conversion of s * (q - c) to fp16.  An infinite s takes the exact
-        // fp16 steps (h - 1024) - c, then the product.
-        constexpr uint32_t mask = (1u << B) - 1u;
-        constexpr float c = 0.5f * (float)mask;
+        // h = 1024 + q.  For a finite s, s * h - (1024 + c) * s is one fp32
+        // fma whose terms and result are exact (at most 23 significant bits),
+        // so the only rounding is the conversion of s * (q - c) to fp16.  An
+        // infinite s takes the exact fp16 steps (h - 1024) - c, then the product.
+        constexpr float c = 0.5f * (float)((1u << B) - 1u);
         const float sf = (float)s;
-        uint32_t h[32];
-#pragma unroll
-        for (int d = 0; d < 2 * B; d++)
-#pragma unroll
-            for (int i = 0; i < 16 / B; i++) {
-                if constexpr (B == 8)
-                    h[d * (16 / B) + i] = __builtin_amdgcn_perm(0x64646464u, cw[d], i ? 0x04030401u : 0x04020400u);
-                else
-                    h[d * (16 / B) + i] = ((cw[d] >> (B * i)) & (mask * 0x10001u)) | 0x64006400u;
-            }
         if (__builtin_isfinite(sf)) {
             const float t = -(1024.0f + c) * sf;
 #pragma unroll
-            for (int j = 0; j < 32; j++) {
-                const hf2 v = u2h(h[j]);
-                hf2 w;
-                w.x = (_Float16)__builtin_fmaf((float)v.x, sf, t);
-                w.y = (_Float16)__builtin_fmaf((float)v.y, sf, t);
-                out[j] = h2u(w);
+            for (int c4 = 0; c4 < 8; c4++) {
+                uint32_t o[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const hf2 v = u2h(code_pair<B>(cw, 4 * c4 + u));
+                    hf2 w;
+                    w.x = (_Float16)__builtin_fmaf((float)v.x, sf, t);
+                    w.y = (_Float16)__builtin_fmaf((float)v.y, sf, t);
+                    o[u] = h2u(w);
+                }
+                dst[c4] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         } else {
             const _Float16 k0 = (_Float16)-1024.0f, k1 = (_Float16)-c;
             const hf2 o0 = {k0, k0}, o1 = {k1, k1}, s2 = {s, s};
 #pragma unroll
-            for (int j = 0; j < 32; j++)
-                out[j] = h2u(((u2h(h[j]) + o0) + o1) * s2);
+            for (int c4 = 0; c4 < 8; c4++) {
+                uint32_t o[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    o[u] = h2u(((u2h(code_pair<B>(cw, 4 * c4 + u)) + o0) + o1) * s2);
+                dst[c4] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
         }
     }
 }
@@ -388,13 +404,8 @@ __device__ __forceinline__ void dequant_pass(const uint8_t *tile, int lp, uint32
         }
     }
     const uint32_t se = reinterpret_cast<const uint32_t *>(tile + se_off)[slot0 + s];
-    uint32_t out[32];
-    dequant_group<B>(cw, se & 0xffffu, out);
     const uint32_t r = (se >> 16) & (kBN - 1), gl = (se >> 23) & 1u;
-    uint4 *dst = reinterpret_cast<uint4 *>(wchunk + r * (kLdw / 2) + gl * 32u);
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-        dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+    dequant_group<B>(cw, se & 0xffffu, reinterpret_cast<uint4 *>(wchunk + r * (kLdw / 2) + gl * 32u));
 }
 
 // The width buckets of a tile in a ring slot, from its header: pass p of the
