@@ -41,7 +41,7 @@ namespace {
 constexpr int kBN = 128;     // weight rows per tile
 constexpr int kTG = 2;       // groups per tile (128 columns)
 constexpr int kGT = 256;     // threads per workgroup of the preparation kernels
-constexpr int kGW = kGT / 64; // wavefronts that copy by LDS-DMA in the GEMM kernel
+constexpr int kGW = kGT / 64; // their wavefronts; also the GEMM kernel's LDS-DMA wavefronts
 constexpr int kMT = 512;     // threads per workgroup of the GEMM kernel: two wavefronts per SIMD
 constexpr int kMW = kMT / 64;
 static_assert(kBN * kTG == kGT, "the preparation kernels take one cell of a tile per thread");
