@@ -334,15 +334,25 @@ __host__ __device__ inline PLayout p_layout(int MT, int G, int smax)
 // of different columns over the LDS banks): the fp16 pairs (x_p, x_{p+32}),
 // then the negated corrections -C_b for the widths 1, 2, 4, 8, where
 // C_b = sum_p 2^(10-pos_b(p)) (x_p + x_{p+32}) + (2^b-1)/2 sum_j x_j.
-// Item = (token, group, quarter q): pairs 4q..4q+3; the 8 items of a group are
-// 8 adjacent lanes.  Loads and stores are separate so that the loads go out
+// Item = (token, group, part r): pairs 8r..8r+7, from one 16-byte load of
+// x_{8r..8r+7} and one of x_{32+8r..32+8r+7}; the 4 items of a group are 4
+// adjacent lanes.  Loads and stores are separate so that the loads go out
 // before the first passes' loads and the wait for them leaves those in flight.
-// KP items per thread: MT * G * 8 items rounded up to a power of two over the
+// KP items per thread: MT * G * 4 items rounded up to a power of two over the
 // workgroup (chosen per launch, so that no more loads are issued than needed).
+// Sum of v over each aligned group of 4 lanes, the same value in every lane of
+// the group, in a fixed order: pairs, then the two pairs (DPP quad permutations).
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += dpp_f<0xB1>(v); // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v); // quad_perm [2, 3, 0, 1]
+    return v;
+}
+
 template <int KP>
 struct XRegs {
     static constexpr int kPer = KP;
-    uint32_t lo0[KP], lo1[KP], hi0[KP], hi1[KP];
+    u32x4 lo[KP], hi[KP];
 };
 
 template <int MT, int KP>
@@ -350,28 +360,25 @@ __device__ __forceinline__ void x_load(const uint16_t *x, int ldx, int G, XRegs<
 {
     static_assert(MT <= 2, "the planned path takes one or two tokens");
     // x is 8-byte aligned and ldx a multiple of 4 (checked on the host): two
-    // 8-byte buffer loads per item.  Every load is issued (so that the wait
-    // for them is exact), and a compiler barrier keeps them ahead of the pass
-    // loads, so that this wait leaves those in flight.
+    // 16-byte buffer loads per item (dword-aligned, as buffer loads need).
+    // Every load is issued (so that the wait for them is exact), and a
+    // compiler barrier keeps them ahead of the pass loads, so that this wait
+    // leaves those in flight.
     const int tid = threadIdx.x;
-    const int items = MT * G * 8;
+    const int items = MT * G * 4;
     const int nrec = (int)(((MT - 1) * (uint32_t)ldx + 64u * (uint32_t)G) * 2u); // < 2^31: checked on the host
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, nrec, 0x00020000);
 #pragma unroll
     for (int k = 0; k < KP; k++) {
         const int i = tid + k * kT;
-        // item i: token m, group g, quarter q (at most two tokens: a compare,
+        // item i: token m, group g, part r (at most two tokens: a compare,
         // not a division by G, which would delay the loads)
-        const int q = i & 7, m = (MT > 1 && (i >> 3) >= G) ? 1 : 0, g = (i >> 3) - m * G;
+        const int r = i & 3, m = (MT > 1 && (i >> 2) >= G) ? 1 : 0, g = (i >> 2) - m * G;
         // a lane past the last item gets an offset past the buffer: the load
         // returns zeros without a memory access
-        const int off = i < items ? (m * ldx + 64 * g + 4 * q) * 2 : nrec;
-        const u32x2 va = __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0);
-        const u32x2 vb = __builtin_amdgcn_raw_buffer_load_b64(xr, off + 64, 0, 0);
-        xs.lo0[k] = va.x;
-        xs.lo1[k] = va.y;
-        xs.hi0[k] = vb.x;
-        xs.hi1[k] = vb.y;
+        const int off = i < items ? (m * ldx + 64 * g + 8 * r) * 2 : nrec;
+        xs.lo[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+        xs.hi[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 64, 0, 0);
     }
     asm volatile("" ::: "memory");
 }
@@ -380,38 +387,38 @@ template <int MT, int KP>
 __device__ __forceinline__ void x_store(int G, const XRegs<KP> &xs, uint32_t *xrec)
 {
     const int tid = threadIdx.x;
-    const int items = MT * G * 8;
+    const int items = MT * G * 4;
 #pragma unroll
     for (int k = 0; k < KP; k++) {
         const int i = tid + k * kT;
-        if (i >= items) // whole groups of 8 lanes drop out together
+        if (i >= items) // whole groups of 4 lanes drop out together
             break;
-        // item i: token m, group g, quarter q (at most two tokens: a compare,
-        // not a division by G, which would delay the loads)
-        const int q = i & 7, m = (MT > 1 && (i >> 3) >= G) ? 1 : 0, g = (i >> 3) - m * G;
-        U4 o;
-        o.v[0] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x05040100u); // (x_p, x_{p+32})
-        o.v[1] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x07060302u);
-        o.v[2] = __builtin_amdgcn_perm(xs.hi1[k], xs.lo1[k], 0x05040100u);
-        o.v[3] = __builtin_amdgcn_perm(xs.hi1[k], xs.lo1[k], 0x07060302u);
+        const int r = i & 3, m = (MT > 1 && (i >> 2) >= G) ? 1 : 0, g = (i >> 2) - m * G;
+        uint32_t pr[8];
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+            pr[2 * h] = __builtin_amdgcn_perm(xs.hi[k][h], xs.lo[k][h], 0x05040100u);     // (x_p, x_{p+32})
+            pr[2 * h + 1] = __builtin_amdgcn_perm(xs.hi[k][h], xs.lo[k][h], 0x07060302u); // next p
+        }
         uint32_t *xr = xrec + ((uint32_t)m * G + g) * kXRec;
-        *reinterpret_cast<U4 *>(xr + 4 * q) = o;
+        *reinterpret_cast<U4 *>(xr + 8 * r) = U4{{pr[0], pr[1], pr[2], pr[3]}};
+        *reinterpret_cast<U4 *>(xr + 8 * r + 4) = U4{{pr[4], pr[5], pr[6], pr[7]}};
         float X = 0.f, c1 = 0.f, c2 = 0.f, c4 = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int t = 4 * q + j; // pair index in the group
-            const float sp = dot2(o.v[j], 0x3c003c00u, 0.f); // x_t + x_{t+32}, exact in fp32
+        for (int j = 0; j < 8; j++) {
+            const int t = 8 * r + j; // pair index in the group
+            const float sp = dot2(pr[j], 0x3c003c00u, 0.f); // x_t + x_{t+32}, exact in fp32
             X += sp;
             c1 = fmaf((float)(1 << (10 - pair_pos<1>(t & 15))), sp, c1);
             c2 = fmaf((float)(1 << (10 - pair_pos<2>(t & 7))), sp, c2);
             c4 = fmaf((float)(1 << (10 - pair_pos<4>(t & 3))), sp, c4);
         }
-        // fixed-order tree over the 8 quarters of the group
-        X = group_sum<8>(X);
-        c1 = group_sum<8>(c1);
-        c2 = group_sum<8>(c2);
-        c4 = group_sum<8>(c4);
-        if (q == 0)
+        // fixed-order tree over the 4 parts of the group
+        X = quad_sum(X);
+        c1 = quad_sum(c1);
+        c2 = quad_sum(c2);
+        c4 = quad_sum(c4);
+        if (r == 0)
             *reinterpret_cast<U4 *>(xr + 32) =
                 U4{{__float_as_uint(-fmaf(0.5f, X, c1)), __float_as_uint(-fmaf(1.5f, X, c2)),
                     __float_as_uint(-fmaf(7.5f, X, c4)), __float_as_uint(-fmaf(127.5f, X, 1024.f * X))}};
@@ -975,8 +982,8 @@ PrepArgs prep_args(const vbq_layout *L, const void *blob, const vbq_plan *P)
 vbq_status lds_attribute_once(const void *fn) { return dynamic_lds_once(fn, kLdsBudget); }
 
 // f(std::integral_constant<int, RS>) for the row shape rs of a one-token
-// launch whose activation staging takes KP items per thread (KP = 1: G <= 128,
-// L = 8 or 16; KP = 2: L = 32; KP = 4: L = 64); false if rs is not one of them.
+// launch whose activation staging takes KP items per thread (KP = 1: G <= 256,
+// L = 8, 16 or 32; KP = 2: L = 64); false if rs is not one of them.
 template <int KP, typename F>
 bool with_row_shape(int rs, F &&f, vbq_status &st)
 {
@@ -986,10 +993,9 @@ bool with_row_shape(int rs, F &&f, vbq_status &st)
         switch (rs) {
             VBQ_RS(8 * 16 + 8) VBQ_RS(8 * 16 + 7) VBQ_RS(8 * 16 + 4) VBQ_RS(8 * 16)
             VBQ_RS(16 * 16 + 8) VBQ_RS(16 * 16 + 7) VBQ_RS(16 * 16)
+            VBQ_RS(32 * 16 + 8) VBQ_RS(32 * 16 + 7) VBQ_RS(32 * 16)
         }
     } else if constexpr (KP == 2) {
-        switch (rs) { VBQ_RS(32 * 16 + 8) VBQ_RS(32 * 16 + 7) VBQ_RS(32 * 16) }
-    } else if constexpr (KP == 4) {
         switch (rs) { VBQ_RS(64 * 16 + 8) VBQ_RS(64 * 16 + 7) VBQ_RS(64 * 16) }
     }
 #undef VBQ_RS
@@ -1041,7 +1047,7 @@ vbq_status launch_plan_t(const PArgs &a, dim3 grid, uint32_t lds, hipStream_t st
 template <int MT, int OM>
 vbq_status launch_plan_kp(int G, const PArgs &a, dim3 grid, uint32_t lds, hipStream_t stream)
 {
-    const int per = (MT * G * 8 + kT - 1) / kT; // activation items per thread
+    const int per = (MT * G * 4 + kT - 1) / kT; // activation items per thread
     if (per <= 1)
         return launch_plan_t<MT, OM, 1>(a, grid, lds, stream);
     if (per <= 2)
