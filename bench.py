@@ -689,7 +689,9 @@ def main(argv=None):
         f"median {dist['median']} us, p10 {dist['p10']}, p90 {dist['p90']}")
 
     # per-launch kernel durations: for each stage kind, that kind's launches of
-    # one step captured back to back in a graph (events on the launch stream)
+    # one step captured back to back in a graph (events on the launch stream);
+    # a kind with fewer than 8 launches per step (the LM head) is repeated to 8
+    # in its graph, so that the graph's own launch cost is spread as for the others
     kinds = {}
     kern_ms = 0.0
     names = []
@@ -698,11 +700,12 @@ def main(argv=None):
             names.append(step.stage_name(st))
     for name in ([] if args.no_kinds else names):
         sts = [st for st in step.stages if step.stage_name(st) == name]
-        g = step.capture_stages(sts)
+        rep_in = -(-8 // len(sts))
+        g = step.capture_stages(sts * rep_in)
         for _ in range(2):
             g.replay()
         reps = max(2, args.kernel_steps)
-        t = time_steps(torch, g.replay, reps) / len(sts)  # ms per launch
+        t = time_steps(torch, g.replay, reps) / (len(sts) * rep_in)  # ms per launch
         del g
         bts = sum(acc.vbq_read_bytes(step.mats[i].L, step.M) for st in sts for i in st) / len(sts)
         kinds[name] = {"launches": len(sts) // copies, "us": round(t * 1e3, 2), "GBps": round(bts / (t * 1e-3) / 1e9, 1)}
