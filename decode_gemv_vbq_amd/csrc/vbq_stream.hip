@@ -495,13 +495,14 @@ __device__ __forceinline__ void run_pass(const Ctx &c, int p, int end_slot, cons
 
 // x records for all of K: fp16 pairs (x_p, x_{p+32}), then per width
 // C_b = sum_p 2^(10-pos_b(p)) (x_p + x_{p+32}) + (2^b-1)/2 sum_j x_j.
-// Item = (token, group, quarter q): pairs 4q..4q+3; the 8 items of a group are
-// 8 adjacent lanes.  Loading and storing are separate so the loads can be
-// issued together with the other prologue loads.
+// Item = (token, group, part r): pairs 8r..8r+7, from x_{8r..8r+7} and
+// x_{32+8r..32+8r+7} (two 16-byte loads where x allows); the 4 items of a
+// group are 4 adjacent lanes.  Loading and storing are separate so the loads
+// can be issued together with the other prologue loads.
 template <int MT>
 struct XStage {
-    static constexpr int kPer = (MT * 256 * 8 + kT - 1) / kT; // items per thread (G < 256)
-    uint32_t lo0[kPer], lo1[kPer], hi0[kPer], hi1[kPer];
+    static constexpr int kPer = (MT * 256 * 4 + kT - 1) / kT; // items per thread (G < 256)
+    uint4 lo[kPer], hi[kPer];
 };
 
 template <int MT>
@@ -509,30 +510,34 @@ __device__ __forceinline__ void stage_x_load(const Ctx &c, XStage<MT> &xs)
 {
     const int tid = threadIdx.x;
     const int G = c.a.G;
-    const int items = MT * G * 8;
-    const bool vec = (c.a.ldx % 4) == 0 && ((uintptr_t)c.a.x % 8) == 0;
+    const int items = MT * G * 4;
+    const bool vec = (c.a.ldx % 4) == 0 && ((uintptr_t)c.a.x % 8) == 0; // dword-aligned 16-byte loads
 #pragma unroll
     for (int k = 0; k < XStage<MT>::kPer; k++) {
         const int i = tid + k * kT;
-        xs.lo0[k] = xs.lo1[k] = xs.hi0[k] = xs.hi1[k] = 0u;
+        xs.lo[k] = xs.hi[k] = make_uint4(0u, 0u, 0u, 0u);
         if (i < items) {
-            const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
-            const uint16_t *p = c.a.x + (uint64_t)m * c.a.ldx + 64ull * g + 4 * q;
+            const int r = i & 3, g = (i >> 2) % G, m = (i >> 2) / G;
+            const uint16_t *p = c.a.x + (uint64_t)m * c.a.ldx + 64ull * g + 8 * r;
             if (vec) {
-                const uint2 va = *reinterpret_cast<const uint2 *>(p);
-                const uint2 vb = *reinterpret_cast<const uint2 *>(p + 32);
-                xs.lo0[k] = va.x;
-                xs.lo1[k] = va.y;
-                xs.hi0[k] = vb.x;
-                xs.hi1[k] = vb.y;
+                xs.lo[k] = *reinterpret_cast<const uint4 *>(p);
+                xs.hi[k] = *reinterpret_cast<const uint4 *>(p + 32);
             } else {
-                xs.lo0[k] = p[0] | ((uint32_t)p[1] << 16);
-                xs.lo1[k] = p[2] | ((uint32_t)p[3] << 16);
-                xs.hi0[k] = p[32] | ((uint32_t)p[33] << 16);
-                xs.hi1[k] = p[34] | ((uint32_t)p[35] << 16);
+                xs.lo[k] = make_uint4(p[0] | ((uint32_t)p[1] << 16), p[2] | ((uint32_t)p[3] << 16),
+                                      p[4] | ((uint32_t)p[5] << 16), p[6] | ((uint32_t)p[7] << 16));
+                xs.hi[k] = make_uint4(p[32] | ((uint32_t)p[33] << 16), p[34] | ((uint32_t)p[35] << 16),
+                                      p[36] | ((uint32_t)p[37] << 16), p[38] | ((uint32_t)p[39] << 16));
             }
         }
     }
+}
+
+// Sum over each aligned group of 4 lanes, in a fixed order (DPP quad moves).
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += dpp_f<0xB1>(v); // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v); // quad_perm [2, 3, 0, 1]
+    return v;
 }
 
 template <int MT>
@@ -540,37 +545,41 @@ __device__ __forceinline__ void stage_x_store(const Ctx &c, const XStage<MT> &xs
 {
     const int tid = threadIdx.x;
     const int G = c.a.G;
-    const int items = MT * G * 8;
+    const int items = MT * G * 4;
 #pragma unroll
     for (int k = 0; k < XStage<MT>::kPer; k++) {
         const int i = tid + k * kT;
-        if (i >= items) // whole groups of 8 lanes drop out together
+        if (i >= items) // whole groups of 4 lanes drop out together
             break;
-        const int q = i & 7, g = (i >> 3) % G, m = (i >> 3) / G;
-        U4 o;
-        o.v[0] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x05040100u); // (x_p, x_{p+32})
-        o.v[1] = __builtin_amdgcn_perm(xs.hi0[k], xs.lo0[k], 0x07060302u);
-        o.v[2] = __builtin_amdgcn_perm(xs.hi1[k], xs.lo1[k], 0x05040100u);
-        o.v[3] = __builtin_amdgcn_perm(xs.hi1[k], xs.lo1[k], 0x07060302u);
+        const int r = i & 3, g = (i >> 2) % G, m = (i >> 2) / G;
+        const uint32_t lo[4] = {xs.lo[k].x, xs.lo[k].y, xs.lo[k].z, xs.lo[k].w};
+        const uint32_t hi[4] = {xs.hi[k].x, xs.hi[k].y, xs.hi[k].z, xs.hi[k].w};
+        uint32_t pr[8];
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+            pr[2 * h] = __builtin_amdgcn_perm(hi[h], lo[h], 0x05040100u);     // (x_p, x_{p+32})
+            pr[2 * h + 1] = __builtin_amdgcn_perm(hi[h], lo[h], 0x07060302u); // next p
+        }
         uint32_t *xr = xrec + ((uint32_t)m * G + g) * kXRec;
-        *reinterpret_cast<U4 *>(xr + 4 * q) = o;
+        *reinterpret_cast<U4 *>(xr + 8 * r) = U4{{pr[0], pr[1], pr[2], pr[3]}};
+        *reinterpret_cast<U4 *>(xr + 8 * r + 4) = U4{{pr[4], pr[5], pr[6], pr[7]}};
         float X = 0.f, c1 = 0.f, c2 = 0.f, c4 = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int t = 4 * q + j; // pair index in the group
-            const float sp = dot2(o.v[j], 0x3c003c00u, 0.f); // x_t + x_{t+32}, exact in fp32
+        for (int j = 0; j < 8; j++) {
+            const int t = 8 * r + j; // pair index in the group
+            const float sp = dot2(pr[j], 0x3c003c00u, 0.f); // x_t + x_{t+32}, exact in fp32
             X += sp;
             // the mantissa position of pair t depends on its index inside its word
             c1 = fmaf((float)(1 << (10 - pair_pos<1>(t & 15))), sp, c1);
             c2 = fmaf((float)(1 << (10 - pair_pos<2>(t & 7))), sp, c2);
             c4 = fmaf((float)(1 << (10 - pair_pos<4>(t & 3))), sp, c4);
         }
-        // fixed-order tree over the 8 quarters (DPP lane moves, no LDS)
-        X = group_sum<8>(X);
-        c1 = group_sum<8>(c1);
-        c2 = group_sum<8>(c2);
-        c4 = group_sum<8>(c4);
-        if (q == 0)
+        // fixed-order tree over the 4 parts (DPP lane moves, no LDS)
+        X = quad_sum(X);
+        c1 = quad_sum(c1);
+        c2 = quad_sum(c2);
+        c4 = quad_sum(c4);
+        if (r == 0)
             *reinterpret_cast<U4 *>(xr + 32) = U4{{__float_as_uint(fmaf(0.5f, X, c1)),
                                                     __float_as_uint(fmaf(1.5f, X, c2)),
                                                     __float_as_uint(fmaf(7.5f, X, c4)),
